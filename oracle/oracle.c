@@ -1,0 +1,277 @@
+/*
+ * Plain fp64 CPU oracle for multi-head scaled dot-product attention (forward).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call
+ * this file: only the test suite, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header, table or helper with the
+ * HIP library; the two meet only through the seeded input generator.
+ *
+ * Every function is the textbook definition written out in loops, in double
+ * precision, with no blocking, no fusion and no skipping of masked work:
+ *
+ *   Q = Xq Wq^T + bq,  K = Xkv Wk^T + bk,  V = Xkv Wv^T + bv
+ *       (four d_model x d_model linear layers, stored [out, in] as a torch
+ *        linear layer stores them; "Transformer" study notes, multi-head
+ *        attention section: formula, parameter list and class code)
+ *   head split: head hd owns features [hd*d_k, (hd+1)*d_k) of each row
+ *       (same section: view to [B, L, h, d_k] then transpose to [B, h, L, d_k])
+ *   s_ij = (q_i . k_j) / sqrt(d_k)          (The Annotated Transformer,
+ *       "Attention" section; d_k is the per-head width of the query)
+ *   masked entries are REPLACED by -1e9 after scaling (same section:
+ *       masked_fill(mask == 0, -1e9))
+ *   p_i = softmax over the key axis, o_i = sum_j p_ij v_j   (same section)
+ *   merge heads back to [B, L, h*d_v], then out = Ocat Wo^T + bo
+ *       ("Transformer" study notes, multi-head attention: Concat(head_1..h) W^O)
+ *
+ * Masks.  A key j is allowed for query i of batch b when
+ *   (valid_lens == NULL or j < valid_lens[b])  and  (!causal or j <= i).
+ * The valid_lens rule is the d2l reading (d2l Transformer digest, multi-head
+ * attention prerequisites: valid lengths are repeated over the heads, and no
+ * query attends to padded keys); the causal rule is the lower-triangular
+ * "subsequent mask" whose 5x5 print keeps the diagonal ("Transformer" study
+ * notes, mask-generation section; The Annotated Transformer, decoder section).
+ * The two masks are combined by logical AND.  One mask serves every head.
+ *
+ * Softmax is evaluated as exp(s_j - max_k s_k) / sum exp(s_k - max): the same
+ * number as the plain quotient, written so that large logits cannot overflow.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_MASK_FILL (-1e9)
+
+/* Round a double to the nearest bfloat16 value (8-bit significand, fp32
+ * exponent range), ties to even.  Used only by the optional "bf16 storage"
+ * mode below; exposed for its own test against torch's conversion. */
+double oracle_round_bf16_f64(double x)
+{
+    if (x == 0.0 || isnan(x) || isinf(x)) return x;
+    int e;
+    double m = frexp(fabs(x), &e);          /* |x| = m * 2^e, m in [0.5, 1) */
+    /* bf16 keeps 8 significant bits for normals (2^-126 <= |x|); below that
+     * the spacing is fixed at 2^-133. */
+    int bits = 8;
+    if (e - 1 < -126) bits = 8 - (-126 - (e - 1));
+    if (bits < 0) return copysign(0.0, x);
+    double scaled = ldexp(m, bits);          /* in [2^(bits-1), 2^bits) */
+    double fl = floor(scaled);
+    double rem = scaled - fl;
+    double r;
+    if (rem > 0.5) r = fl + 1.0;
+    else if (rem < 0.5) r = fl;
+    else r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+    double y = ldexp(r, e - bits);
+    if (y > 3.3895313892515355e38) y = INFINITY;  /* beyond the largest bf16 */
+    return copysign(y, x);
+}
+
+/* y[m, n] = sum_c x[m, c] * w[n, c] + (b ? b[n] : 0), ascending c. */
+void oracle_linear_f64(const double* x, const double* w, const double* b,
+                       double* y, long M, int Din, int Dout)
+{
+    long m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        for (int n = 0; n < Dout; ++n) {
+            double acc = 0.0;
+            for (int c = 0; c < Din; ++c) acc += x[m * Din + c] * w[(long)n * Din + c];
+            y[m * Dout + n] = acc + (b ? b[n] : 0.0);
+        }
+    }
+}
+
+static int key_allowed(const int* valid_lens, int causal, int b, int i, int j)
+{
+    if (valid_lens && !(j < valid_lens[b])) return 0;
+    if (causal && j > i) return 0;
+    return 1;
+}
+
+/* One query row of one (batch, head): the attention definition, every key. */
+static void attend_row(const double* qi, const double* k, const double* v,
+                       double* oi, double* pi, double* s,
+                       int Lk, int dk, int dv,
+                       const int* valid_lens, int causal, int b, int i)
+{
+    const double scale = 1.0 / sqrt((double)dk);
+    for (int j = 0; j < Lk; ++j) {
+        double dot = 0.0;
+        for (int t = 0; t < dk; ++t) dot += qi[t] * k[(long)j * dk + t];
+        s[j] = dot * scale;
+        if (!key_allowed(valid_lens, causal, b, i, j)) s[j] = ORACLE_MASK_FILL;
+    }
+    double mx = s[0];
+    for (int j = 1; j < Lk; ++j) if (s[j] > mx) mx = s[j];
+    double den = 0.0;
+    for (int j = 0; j < Lk; ++j) { s[j] = exp(s[j] - mx); den += s[j]; }
+    for (int j = 0; j < Lk; ++j) s[j] /= den;
+    for (int t = 0; t < dv; ++t) {
+        double acc = 0.0;
+        for (int j = 0; j < Lk; ++j) acc += s[j] * v[(long)j * dv + t];
+        oi[t] = acc;
+    }
+    if (pi) memcpy(pi, s, sizeof(double) * (size_t)Lk);
+}
+
+/*
+ * Scaled dot-product attention on already split heads.
+ *   q [B, h, Lq, dk], k [B, h, Lk, dk], v [B, h, Lk, dv]   (contiguous)
+ *   o [B, h, R, dv] and, if p != NULL, p [B, h, R, Lk], where the R rows are
+ *   rows[0..n_rows) (query indices) or, when rows == NULL, all Lq queries.
+ * Returns 0, or -1 on a bad argument / allocation failure.
+ */
+int oracle_sdpa_f64(const double* q, const double* k, const double* v,
+                    double* o, double* p,
+                    int B, int h, int Lq, int Lk, int dk, int dv,
+                    const int* valid_lens, int causal,
+                    const int* rows, int n_rows)
+{
+    if (B < 0 || h <= 0 || Lq < 0 || Lk <= 0 || dk <= 0 || dv <= 0) return -1;
+    const int R = rows ? n_rows : Lq;
+    if (rows)
+        for (int r = 0; r < R; ++r) if (rows[r] < 0 || rows[r] >= Lq) return -1;
+    int bad = 0;
+    long bh;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (bh = 0; bh < (long)B * h; ++bh) {
+        const int b = (int)(bh / h);
+        double* s = (double*)malloc(sizeof(double) * (size_t)Lk);
+        if (!s) { bad = 1; continue; }
+        const double* qb = q + bh * (long)Lq * dk;
+        const double* kb = k + bh * (long)Lk * dk;
+        const double* vb = v + bh * (long)Lk * dv;
+        for (int r = 0; r < R; ++r) {
+            const int i = rows ? rows[r] : r;
+            attend_row(qb + (long)i * dk, kb, vb,
+                       o + (bh * R + r) * (long)dv,
+                       p ? p + (bh * R + r) * (long)Lk : NULL, s,
+                       Lk, dk, dv, valid_lens, causal, b, i);
+        }
+        free(s);
+    }
+    return bad ? -1 : 0;
+}
+
+static void round_all(double* a, long n)
+{
+    for (long i = 0; i < n; ++i) a[i] = oracle_round_bf16_f64(a[i]);
+}
+
+/*
+ * Multi-head attention forward.
+ *   xq [B, Lq, D], xkv [B, Lk, D]; w_* [D, D] stored [out, in]; b_* [D] or NULL.
+ *   out [B, R, D] for the R query rows selected as in oracle_sdpa_f64.
+ *   h heads of width dk = D / h (D must be a multiple of h).
+ *   bf16_stages != 0: Q, K, V and the merged head output are rounded to the
+ *   nearest bfloat16 before the next step reads them (the storage precision a
+ *   bf16 pipeline gives those intermediates); 0 keeps everything in fp64.
+ * Returns 0, or -1 on a bad argument / allocation failure.
+ */
+int oracle_mha_f64(const double* xq, const double* xkv,
+                   const double* w_q, const double* b_q,
+                   const double* w_k, const double* b_k,
+                   const double* w_v, const double* b_v,
+                   const double* w_o, const double* b_o,
+                   double* out, int B, int Lq, int Lk, int D, int h,
+                   const int* valid_lens, int causal,
+                   const int* rows, int n_rows, int bf16_stages)
+{
+    if (B < 0 || Lq < 0 || Lk <= 0 || D <= 0 || h <= 0 || D % h != 0) return -1;
+    const int dk = D / h;
+    const int R = rows ? n_rows : Lq;
+    if (rows)
+        for (int r = 0; r < R; ++r) if (rows[r] < 0 || rows[r] >= Lq) return -1;
+    if (B == 0 || R == 0) return 0;
+
+    /* Gather the selected query rows of X_q, then project. */
+    double* xsel = (double*)malloc(sizeof(double) * (size_t)B * R * D);
+    double* Qf = (double*)malloc(sizeof(double) * (size_t)B * R * D);
+    double* Kf = (double*)malloc(sizeof(double) * (size_t)B * Lk * D);
+    double* Vf = (double*)malloc(sizeof(double) * (size_t)B * Lk * D);
+    double* qh = (double*)malloc(sizeof(double) * (size_t)B * R * D);
+    double* kh = (double*)malloc(sizeof(double) * (size_t)B * Lk * D);
+    double* vh = (double*)malloc(sizeof(double) * (size_t)B * Lk * D);
+    double* oh = (double*)malloc(sizeof(double) * (size_t)B * R * D);
+    double* ocat = (double*)malloc(sizeof(double) * (size_t)B * R * D);
+    int rc = 0;
+    if (!xsel || !Qf || !Kf || !Vf || !qh || !kh || !vh || !oh || !ocat) { rc = -1; goto done; }
+
+    for (int b = 0; b < B; ++b)
+        for (int r = 0; r < R; ++r) {
+            const int i = rows ? rows[r] : r;
+            memcpy(xsel + ((long)b * R + r) * D, xq + ((long)b * Lq + i) * D, sizeof(double) * (size_t)D);
+        }
+    oracle_linear_f64(xsel, w_q, b_q, Qf, (long)B * R, D, D);
+    oracle_linear_f64(xkv, w_k, b_k, Kf, (long)B * Lk, D, D);
+    oracle_linear_f64(xkv, w_v, b_v, Vf, (long)B * Lk, D, D);
+    if (bf16_stages) {
+        round_all(Qf, (long)B * R * D);
+        round_all(Kf, (long)B * Lk * D);
+        round_all(Vf, (long)B * Lk * D);
+    }
+
+    /* Head split: [B, L, h, dk] -> [B, h, L, dk]. */
+    for (int b = 0; b < B; ++b)
+        for (int hd = 0; hd < h; ++hd) {
+            for (int r = 0; r < R; ++r)
+                for (int t = 0; t < dk; ++t)
+                    qh[(((long)b * h + hd) * R + r) * dk + t] = Qf[((long)b * R + r) * D + hd * dk + t];
+            for (int j = 0; j < Lk; ++j)
+                for (int t = 0; t < dk; ++t) {
+                    kh[(((long)b * h + hd) * Lk + j) * dk + t] = Kf[((long)b * Lk + j) * D + hd * dk + t];
+                    vh[(((long)b * h + hd) * Lk + j) * dk + t] = Vf[((long)b * Lk + j) * D + hd * dk + t];
+                }
+        }
+
+    /* Attention per head.  The query rows were already gathered, but the
+     * causal rule needs each row's original index, so attend row by row with
+     * that index. */
+    {
+        long bh;
+        int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+        for (bh = 0; bh < (long)B * h; ++bh) {
+            const int b = (int)(bh / h);
+            double* s = (double*)malloc(sizeof(double) * (size_t)Lk);
+            if (!s) { bad = 1; continue; }
+            for (int r = 0; r < R; ++r) {
+                const int i = rows ? rows[r] : r;
+                attend_row(qh + (bh * R + r) * (long)dk, kh + bh * (long)Lk * dk,
+                           vh + bh * (long)Lk * dk, oh + (bh * R + r) * (long)dk, NULL, s,
+                           Lk, dk, dk, valid_lens, causal, b, i);
+            }
+            free(s);
+        }
+        if (bad) { rc = -1; goto done; }
+    }
+
+    /* Head merge: [B, h, R, dk] -> [B, R, h*dk]. */
+    for (int b = 0; b < B; ++b)
+        for (int hd = 0; hd < h; ++hd)
+            for (int r = 0; r < R; ++r)
+                for (int t = 0; t < dk; ++t)
+                    ocat[((long)b * R + r) * D + hd * dk + t] = oh[(((long)b * h + hd) * R + r) * dk + t];
+    if (bf16_stages) round_all(ocat, (long)B * R * D);
+
+    oracle_linear_f64(ocat, w_o, b_o, out, (long)B * R, D, D);
+
+done:
+    free(xsel); free(Qf); free(Kf); free(Vf);
+    free(qh); free(kh); free(vh); free(oh); free(ocat);
+    return rc;
+}
+
+/* Number of OpenMP threads the oracle runs with (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,55 @@
+"""Plant a plausible mistake in a copy of the oracle (CPU only) and require
+that at least one pin catches it.  This checks the pins, not the oracle."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, text in oracle.c, replacement)
+MUTATIONS = [
+    ("scale_without_sqrt", "1.0 / sqrt((double)dk)", "1.0 / (double)dk"),
+    ("causal_drops_diagonal", "if (causal && j > i)", "if (causal && j >= i)"),
+    ("valid_len_off_by_one", "!(j < valid_lens[b])", "!(j <= valid_lens[b])"),
+    ("fill_added_not_replaced", "s[j] = ORACLE_MASK_FILL;", "s[j] += ORACLE_MASK_FILL;"),
+    ("fill_too_small", "#define ORACLE_MASK_FILL (-1e9)", "#define ORACLE_MASK_FILL (-1e1)"),
+    ("weight_transposed", "w[(long)n * Din + c]", "w[(long)c * Dout + n]"),
+    ("bias_dropped", "acc + (b ? b[n] : 0.0)", "acc"),
+    ("head_split_interleaved",
+     "Qf[((long)b * R + r) * D + hd * dk + t]", "Qf[((long)b * R + r) * D + t * h + hd]"),
+    ("head_merge_interleaved",
+     "ocat[((long)b * R + r) * D + hd * dk + t]", "ocat[((long)b * R + r) * D + t * h + hd]"),
+    ("value_index_transposed", "v[(long)j * dv + t]", "v[(long)t * Lk + j]"),
+    ("softmax_not_normalised", "s[j] /= den;", "s[j] /= (den > 1.0 ? 1.0 : den);"),
+    ("bf16_ties_away", "(fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0", "fl + 1.0"),
+    ("bf16_merge_not_rounded", "if (bf16_stages) round_all(ocat", "if (0) round_all(ocat"),
+    ("mask_uses_query_length", "if (valid_lens && !(j < valid_lens[b]))",
+     "if (valid_lens && !(i < valid_lens[b]))"),
+]
+
+
+def _first_failing_pin():
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except AssertionError:
+            return pin.__name__
+    return None
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique in oracle.c"
+    src = tmp_path / "oracle_mut.c"
+    src.write_text(text.replace(old, new))
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fopenmp", "-fPIC",
+                    "-shared", str(src), "-o", str(lib), "-lm"], check=True)
+    with oracle.use_library(str(lib)):
+        caught = _first_failing_pin()
+    assert caught is not None, f"no pin detects the planted mistake {name}"
