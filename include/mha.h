@@ -1,0 +1,153 @@
+/*
+ * mha.h -- C ABI of the MI355X (gfx950) multi-head scaled dot-product
+ * attention forward library, libmha.so.
+ *
+ * What is computed (the pages' definitions):
+ *   Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V over the key axis, with
+ *   masked scores replaced by -1e9 after scaling (The Annotated Transformer,
+ *   "Attention" section; "Transformer" study notes, attention-mechanism
+ *   section).  MultiHead(Xq, Xkv) = Concat(head_1..head_h) W_O^T + b_O with
+ *   head_i = Attention(Q_i, K_i, V_i), Q = Xq W_Q^T + b_Q, K = Xkv W_K^T + b_K,
+ *   V = Xkv W_V^T + b_V, and head i owning features [i*d_k, (i+1)*d_k)
+ *   ("Transformer" study notes, multi-head attention formula, parameter list
+ *   and class: four d_model x d_model linear layers, view/transpose split,
+ *   transpose/view merge).
+ *
+ * Masks.  For query i of batch b, key j is allowed when
+ *   (valid_lens == NULL || j < valid_lens[b]) && (!causal || j <= i).
+ *   valid_lens is the d2l key-padding length, one per batch, shared by every
+ *   head (d2l Transformer digest, multi-head attention prerequisites; no
+ *   query attends padded keys).  causal is the lower-triangular subsequent
+ *   mask that keeps the diagonal ("Transformer" study notes, mask-generation
+ *   section, printed 5x5 example).  Both together are combined by AND.
+ *   Because the fill REPLACES the score with -1e9, a query whose keys are all
+ *   masked (valid_lens[b] <= 0) weights all Lk keys uniformly; for every other
+ *   query a masked key contributes exactly zero.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, keeps no per-call state, and enqueues its kernels on
+ *     `stream` (a hipStream_t; NULL = the null stream).  Calls return as soon
+ *     as the work is enqueued; results are ready after the stream syncs.
+ *   - Every argument is checked on the host before anything is enqueued; on
+ *     any error nothing is written.
+ *   - Errors: MHA_EINVAL (null required pointer, negative or inconsistent
+ *     sizes, d_model != h * d_k, causal with Lq != Lk, misaligned pointers or
+ *     strides, output aliasing an input); MHA_ENOTSUP (d_k or d_v other than
+ *     64, an unsupported dtype pair); MHA_EWORKSPACE (workspace too small);
+ *     MHA_EHIP (the HIP runtime reported an error when enqueuing).  Faults of
+ *     the device itself surface when the caller synchronises the stream.
+ *   - dtypes: MHA_F32 computes in fp32 throughout (FMA, no reduced
+ *     precision).  MHA_BF16 takes bf16 inputs and weights, multiplies on bf16
+ *     MFMA with fp32 accumulation, keeps the softmax state in fp32, and writes
+ *     the output as bf16 or fp32 (out_dt).  mha_forward stores V and the
+ *     merged head output as bf16, and Q and K as a bf16 hi + lo pair (hi =
+ *     bf16(x), lo = bf16(x - hi)) whose scores are formed from three bf16
+ *     products (hi.hi + lo.hi + hi.lo): large logits, such as those of
+ *     embeddings scaled by sqrt(d_model), keep near-fp32 accuracy instead of
+ *     moving by a bf16 rounding step.  sdpa_forward's bf16 inputs are exact
+ *     bf16 values and use a single product.
+ */
+#ifndef MHA_H
+#define MHA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MHA_F32 = 0, MHA_BF16 = 1 } mha_dtype;
+
+typedef enum {
+    MHA_OK = 0,
+    MHA_EINVAL = 1,
+    MHA_ENOTSUP = 2,
+    MHA_EWORKSPACE = 3,
+    MHA_EHIP = 4
+} mha_status;
+
+/* Element strides of a [batch, head, position, feature] view whose feature
+ * axis is contiguous (stride 1).  [B, h, L, d] contiguous is
+ * {h*L*d, L*d, d}; the [B, L, h*d] layout of a linear layer's output viewed
+ * per head is {L*h*d, d, h*d}. */
+typedef struct {
+    long long b, h, l;
+} mha_strides;
+
+/*
+ * sdpa_forward -- scaled dot-product attention on split heads.
+ *
+ *   q : [B, h, Lq, d_k] per `sq`        k : [B, h, Lk, d_k] per `sk`
+ *   v : [B, h, Lk, d_v] per `sv`        o : [B, h, Lq, d_v] per `so` (written)
+ *   valid_lens : device int32 [B], or NULL for no padding mask.
+ *   causal     : nonzero applies the subsequent mask (requires Lq == Lk).
+ *   in_dt      : dtype of q, k, v.  out_dt: dtype of o.  MHA_F32 inputs
+ *                require an MHA_F32 output.
+ *   Requirements: d_k == d_v == 64; B, h, Lq >= 0; Lk >= 1; pointers 16-byte
+ *   aligned; strides multiples of 8 (bf16) or 4 (fp32) elements; o must not
+ *   overlap q, k or v.  B == 0 or Lq == 0 is a no-op.
+ * The scale is 1/sqrt(d_k) (d_k = the per-head width); it is not a parameter.
+ */
+mha_status sdpa_forward(mha_dtype in_dt, mha_dtype out_dt,
+                        const void* q, mha_strides sq,
+                        const void* k, mha_strides sk,
+                        const void* v, mha_strides sv,
+                        void* o, mha_strides so,
+                        int B, int h, int Lq, int Lk, int d_k, int d_v,
+                        const int* valid_lens, int causal, void* stream);
+
+/* Bytes of device workspace mha_forward needs: the projected Q, K, V and the
+ * merged head output, each in in_dt (plus the low planes of Q and K for
+ * MHA_BF16), each region 256-byte aligned.  Returns 0 for inconsistent
+ * arguments. */
+size_t mha_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h);
+
+/*
+ * mha_forward -- multi-head attention forward (projections, head split,
+ * attention per head, head merge, output projection).
+ *
+ *   x_q  : [B, Lq, d_model] queries' inputs (row-major, in_dt)
+ *   x_kv : [B, Lk, d_model] keys'/values' inputs; may equal x_q (self-attention)
+ *   w_q, w_k, w_v, w_o : [d_model, d_model] stored [out, in] as a torch linear
+ *          layer stores them (y = x W^T + b), in_dt
+ *   b_q, b_k, b_v, b_o : [d_model] in_dt, or NULL for no bias
+ *   out  : [B, Lq, d_model] in out_dt (written; must not overlap any input or
+ *          the workspace)
+ *   d_model == h * d_k; d_k must be 64.
+ *   valid_lens, causal: as for sdpa_forward (masks act on keys; the same mask
+ *          serves every head).
+ *   workspace : device buffer of at least mha_workspace_bytes(...) bytes,
+ *          256-byte aligned, owned by the caller; its contents are scratch.
+ */
+mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
+                       const void* x_q, const void* x_kv,
+                       const void* w_q, const void* b_q,
+                       const void* w_k, const void* b_k,
+                       const void* w_v, const void* b_v,
+                       const void* w_o, const void* b_o,
+                       void* out,
+                       int B, int Lq, int Lk, int d_model, int h, int d_k,
+                       const int* valid_lens, int causal,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* mha_status_string(mha_status s);
+
+/*
+ * Kernel timing (observability).  While enabled, every kernel the library
+ * enqueues is bracketed by a pair of HIP events recorded on the same stream.
+ * mha_timing_read() waits for the recorded events, adds their elapsed times
+ * per kernel name into `total_ms` / `count` (up to `max` entries, names are
+ * static strings) and returns the number of entries written; it also clears
+ * the record.  Returns -1 on a HIP error.  Event pairs beyond the library's
+ * fixed pool (4096 pairs) are not recorded.  Not thread-safe.
+ */
+mha_status mha_timing_enable(int on);
+int mha_timing_read(const char** names, double* total_ms, int* count, int max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHA_H */

@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/mha.h declares, and rejects bad arguments on the host
+with the documented status before anything would be enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_head_scaled_sdpa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mha.h")
+
+F32, BF16 = _lib.MHA_F32, _lib.MHA_BF16
+OK, EINVAL, ENOTSUP, EWORK = _lib.MHA_OK, _lib.MHA_EINVAL, _lib.MHA_ENOTSUP, _lib.MHA_EWORKSPACE
+
+# Fake device addresses: validation fails (or returns early) before any use.
+P = 0x10000
+ALIGNED = [ctypes.c_void_p(P + 0x100000 * n) for n in range(16)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_]+)\s*\(", text)) - {"if", "sizeof"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_functions_are_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in mha.h but not exported"
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.mha_status_string(s).decode().startswith("MHA_")
+    assert lib.mha_status_string(99) == b"unknown mha_status"
+
+
+def S(b, h, l):
+    return _lib.Strides(b, h, l)
+
+
+def sdpa(lib, **kw):
+    a = dict(in_dt=BF16, out_dt=BF16, q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], o=ALIGNED[3],
+             B=2, h=4, Lq=128, Lk=128, dk=64, dv=64, vl=None, causal=0)
+    a.update(kw)
+    st = S(4 * 128 * 64, 128 * 64, 64)
+    sq = kw.get("sq", st)
+    return lib.sdpa_forward(a["in_dt"], a["out_dt"], a["q"], sq, a["k"], st, a["v"], st, a["o"],
+                            kw.get("so", st), a["B"], a["h"], a["Lq"], a["Lk"], a["dk"], a["dv"],
+                            a["vl"], a["causal"], None)
+
+
+def test_sdpa_validation(lib):
+    assert sdpa(lib, B=0) == OK                       # empty batch: nothing to do
+    assert sdpa(lib, Lq=0) == OK
+    assert sdpa(lib, Lk=0) == EINVAL
+    assert sdpa(lib, h=0) == EINVAL
+    assert sdpa(lib, B=-1) == EINVAL
+    assert sdpa(lib, in_dt=7) == EINVAL
+    assert sdpa(lib, q=None) == EINVAL
+    assert sdpa(lib, o=None) == EINVAL
+    assert sdpa(lib, dk=32) == ENOTSUP
+    assert sdpa(lib, dv=128) == ENOTSUP
+    assert sdpa(lib, in_dt=F32, out_dt=BF16) == ENOTSUP
+    assert sdpa(lib, causal=1, Lk=100) == EINVAL     # causal mask is square only
+    assert sdpa(lib, q=ctypes.c_void_p(P + 8)) == EINVAL         # misaligned pointer
+    assert sdpa(lib, sq=S(4 * 128 * 64, 128 * 64, 60)) == EINVAL  # stride not a multiple of 8
+    assert sdpa(lib, o=ALIGNED[0]) == EINVAL         # output overlaps q
+
+
+def mha(lib, **kw):
+    a = dict(in_dt=BF16, out_dt=F32, xq=ALIGNED[0], xkv=ALIGNED[1], wq=ALIGNED[2], wk=ALIGNED[3],
+             wv=ALIGNED[4], wo=ALIGNED[5], out=ALIGNED[6], B=2, Lq=16, Lk=16, D=512, h=8, dk=64,
+             vl=None, causal=0, ws=ALIGNED[7], wsb=None)
+    a.update(kw)
+    need = lib.mha_workspace_bytes(a["in_dt"], a["B"], a["Lq"], a["Lk"], a["D"], a["h"])
+    wsb = need if a["wsb"] is None else a["wsb"]
+    return lib.mha_forward(a["in_dt"], a["out_dt"], a["xq"], a["xkv"], a["wq"], None, a["wk"], None,
+                           a["wv"], None, a["wo"], None, a["out"], a["B"], a["Lq"], a["Lk"], a["D"],
+                           a["h"], a["dk"], a["vl"], a["causal"], a["ws"], wsb, None)
+
+
+def test_mha_validation(lib):
+    assert mha(lib, B=0) == OK
+    assert mha(lib, D=500) == EINVAL                  # d_model != h * d_k
+    assert mha(lib, h=4, dk=64) == EINVAL
+    assert mha(lib, D=256, h=8, dk=32) == ENOTSUP     # d_k must be 64
+    assert mha(lib, causal=1, Lk=12) == EINVAL
+    assert mha(lib, wq=None) == EINVAL
+    assert mha(lib, ws=None) == EINVAL
+    assert mha(lib, wsb=1024) == EWORK
+    assert mha(lib, in_dt=F32, out_dt=BF16) == ENOTSUP
+    assert mha(lib, out=ALIGNED[1]) == EINVAL         # output overlaps x_kv
+    assert mha(lib, ws=ALIGNED[5]) == EINVAL          # workspace overlaps w_o
+    assert mha(lib, xq=ctypes.c_void_p(P + 4)) == EINVAL
+
+
+def test_workspace_bytes(lib):
+    # Q, K, V and merged heads (+ low planes of Q and K for bf16), each
+    # rounded up to 256 bytes.
+    assert lib.mha_workspace_bytes(BF16, 2, 10, 12, 512, 8) == 3 * 20480 + 3 * 24576
+    assert lib.mha_workspace_bytes(F32, 2, 10, 10, 512, 8) == 4 * 40960
+    assert lib.mha_workspace_bytes(F32, 2, 10, 10, 500, 8) == 0
+
+
+def test_missing_library_raises(monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libmha.so")
+    with pytest.raises(ImportError):
+        _lib.load()

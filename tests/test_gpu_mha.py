@@ -1,0 +1,97 @@
+"""GPU parity of mha_forward (projections, head split, attention, merge,
+output projection) through the C ABI against the fp64 oracle.
+
+bf16 path: graded against the plain fp64 oracle on the same bf16 inputs and
+weights.  The oracle's bf16-storage mode (Q, K, V and the merged heads
+rounded to bf16 between steps) is printed beside it as a diagnostic."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import assert_bf16, assert_fp32, errors, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(inp, out_f32=True):
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    w = inp.workload
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = {n: (None if a is None else to_device(a, dt)) for n, a in inp.tensors.items()}
+    if w.self_attn:
+        t["x_kv"] = t["x_q"]
+    out_dtype = torch.float32 if (out_f32 or w.dtype == "f32") else torch.bfloat16
+    out = mha.mha_forward(t["x_q"], t["x_kv"], t["w_q"], t["w_k"], t["w_v"], t["w_o"],
+                          t["b_q"], t["b_k"], t["b_v"], t["b_o"], h=w.h,
+                          valid_lens=inp.valid_lens, causal=w.causal, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def run_oracle(inp, bf16_stages, batches=None, rows=None):
+    t = inp.tensors
+    sel = (lambda a: a) if batches is None else (lambda a: None if a is None else a[batches])
+    vl = inp.valid_lens
+    if vl is not None and batches is not None:
+        vl = vl[batches]
+    return oracle.mha(sel(t["x_q"]), sel(t["x_kv"]), t["w_q"], t["w_k"], t["w_v"], t["w_o"],
+                      t["b_q"], t["b_k"], t["b_v"], t["b_o"], h=inp.workload.h, valid_lens=vl,
+                      causal=inp.workload.causal, rows=rows, bf16_stages=bf16_stages)
+
+
+MHA_BF16_CASES = [
+    # B, Lq, Lk, D, h, causal, vl_range, bias, self_attn
+    (2, 37, 37, 512, 8, True, (1, 37), False, True),
+    (2, 50, 90, 256, 4, False, (10, 90), True, False),
+    (3, 130, 130, 128, 2, False, (0, 130), True, True),
+    (1, 1, 1, 64, 1, False, None, False, True),
+    (2, 200, 140, 192, 3, False, None, True, False),
+]
+
+
+@pytest.mark.parametrize("B,Lq,Lk,D,h,causal,vlr,bias,self_attn", MHA_BF16_CASES)
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_mha_bf16_vs_oracle(B, Lq, Lk, D, h, causal, vlr, bias, self_attn, out_f32):
+    inp = workloads.make_mha_inputs(B, Lq, Lk, D, h, "bf16", seed=B * 100 + Lq + Lk, vl_range=vlr,
+                                    causal=causal, self_attn=self_attn, bias=bias)
+    g = run_gpu(inp, out_f32)
+    e = assert_bf16(g, run_oracle(inp, bf16_stages=False), f"mha bf16 B{B} Lq{Lq} Lk{Lk} D{D} h{h}")
+    print("vs fp64 oracle", e, "vs bf16-storage oracle", errors(g, run_oracle(inp, bf16_stages=True)))
+
+
+MHA_F32_CASES = [
+    (2, 10, 10, 512, 8, False, (3, 10), False, True),
+    (2, 33, 45, 256, 4, False, (0, 45), True, False),
+    (2, 70, 70, 128, 2, True, (1, 70), True, True),
+]
+
+
+@pytest.mark.parametrize("B,Lq,Lk,D,h,causal,vlr,bias,self_attn", MHA_F32_CASES)
+def test_mha_f32_vs_oracle(B, Lq, Lk, D, h, causal, vlr, bias, self_attn):
+    inp = workloads.make_mha_inputs(B, Lq, Lk, D, h, "f32", seed=B * 10 + Lq + Lk, vl_range=vlr,
+                                    causal=causal, self_attn=self_attn, bias=bias)
+    g = run_gpu(inp)
+    assert_fp32(g, run_oracle(inp, bf16_stages=False), f"mha f32 B{B} Lq{Lq} Lk{Lk} D{D}")
+
+
+def test_mha_empty_batch_is_noop():
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    x = torch.zeros((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((128, 128), dtype=torch.bfloat16, device="cuda")
+    out = mha.mha_forward(x, x, w, w, w, w, h=2)
+    assert out.shape == (0, 8, 128)
+
+
+def test_mha_invalid_arguments_raise():
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    x = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((128, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mha.MhaError):
+        mha.mha_forward(x, x, w, w, w, w, h=4)            # d_k = 32: unsupported
+    y = torch.zeros((1, 9, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mha.MhaError):
+        mha.mha_forward(x, y, w, w, w, w, h=2, causal=True)   # causal needs Lq == Lk

@@ -1,0 +1,110 @@
+"""GPU parity of sdpa_forward (through the C ABI) against the fp64 oracle,
+element by element, at sizes the oracle finishes in seconds that span several
+query/key tiles and ragged tails, plus the degenerate cases of the masks."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import assert_bf16, assert_fp32, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _vl(mode, B, Lk, rng):
+    if mode is None:
+        return None
+    if mode == "random":
+        return rng.integers(1, Lk, size=B, endpoint=True).astype(np.int32)
+    return np.array(mode, dtype=np.int32)
+
+
+BF16_CASES = [
+    # B, h, Lq, Lk, causal, valid_lens
+    (1, 1, 1, 1, False, None),
+    (1, 1, 4, 4, True, None),
+    (1, 2, 3, 5, False, [2]),
+    (2, 3, 130, 130, True, "random"),
+    (2, 2, 77, 200, False, "random"),
+    (3, 2, 257, 257, True, [0, 1, 257]),
+    (2, 2, 128, 64, False, [0, 64]),
+    (1, 4, 300, 1000, False, [999]),
+    (2, 2, 384, 384, True, None),
+    (1, 1, 129, 700, False, [640]),
+]
+
+
+@pytest.mark.parametrize("B,h,Lq,Lk,causal,vl", BF16_CASES)
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_sdpa_bf16_vs_oracle(B, h, Lq, Lk, causal, vl, out_f32):
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    rng = np.random.Generator(np.random.PCG64(B * 1000 + Lq * 7 + Lk))
+    inp = workloads.make_sdpa_inputs(B, h, Lq, Lk, 64, "bf16", seed=Lq + Lk, causal=causal)
+    q, k, v = (inp.tensors[n] for n in ("q", "k", "v"))
+    vls = _vl(vl, B, Lk, rng)
+    o = mha.sdpa_forward(to_device(q, torch.bfloat16), to_device(k, torch.bfloat16),
+                         to_device(v, torch.bfloat16), valid_lens=vls, causal=causal,
+                         out_dtype=torch.float32 if out_f32 else torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa(q, k, v, valid_lens=vls, causal=causal)
+    assert_bf16(to_host(o), ref, f"sdpa bf16 B{B} h{h} Lq{Lq} Lk{Lk} causal{causal} vl{vls}")
+
+
+def test_sdpa_bf16_sharp_softmax_and_strided_layout():
+    """Large logits (nearly one-hot rows) through a [B, L, h, d] strided view,
+    the layout the projections produce."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    B, h, L = 2, 4, 200
+    inp = workloads.make_sdpa_inputs(B, h, L, L, 64, "bf16", seed=77)
+    q = workloads.round_to_bf16(inp.tensors["q"] * 6.0)
+    k, v = inp.tensors["k"], inp.tensors["v"]
+    vls = np.array([150, 200], dtype=np.int32)
+    # device tensors stored [B, L, h, d]; pass [B, h, L, d] views
+    dev = lambda x: to_device(np.ascontiguousarray(x.transpose(0, 2, 1, 3)), torch.bfloat16).transpose(1, 2)
+    o = mha.sdpa_forward(dev(q), dev(k), dev(v), valid_lens=vls, causal=True)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa(q, k, v, valid_lens=vls, causal=True)
+    assert_bf16(to_host(o), ref, "sharp softmax, strided")
+
+
+F32_CASES = [
+    (2, 8, 10, 10, False, "random"),
+    (1, 1, 1, 1, False, None),
+    (2, 3, 70, 70, True, "random"),
+    (1, 2, 65, 130, False, [0]),
+    (2, 2, 100, 33, False, [33, 5]),
+]
+
+
+@pytest.mark.parametrize("B,h,Lq,Lk,causal,vl", F32_CASES)
+def test_sdpa_f32_vs_oracle(B, h, Lq, Lk, causal, vl):
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    rng = np.random.Generator(np.random.PCG64(Lq * 31 + Lk))
+    inp = workloads.make_sdpa_inputs(B, h, Lq, Lk, 64, "f32", seed=Lq * 3 + Lk, causal=causal)
+    q, k, v = (inp.tensors[n] for n in ("q", "k", "v"))
+    vls = _vl(vl, B, Lk, rng)
+    o = mha.sdpa_forward(to_device(q, torch.float32), to_device(k, torch.float32),
+                         to_device(v, torch.float32), valid_lens=vls, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa(q, k, v, valid_lens=vls, causal=causal)
+    assert_fp32(to_host(o), ref, f"sdpa f32 B{B} h{h} Lq{Lq} Lk{Lk}")
+
+
+def test_sdpa_fully_masked_rows_are_uniform():
+    """valid_len 0: the GPU must give the mean of all Lk values (uniform
+    weights), exactly as the -1e9 replacement does."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    B, h, L = 2, 2, 150
+    inp = workloads.make_sdpa_inputs(B, h, L, L, 64, "bf16", seed=5)
+    q, k, v = (inp.tensors[n] for n in ("q", "k", "v"))
+    vls = np.array([0, 0], dtype=np.int32)
+    for causal in (False, True):
+        o = to_host(mha.sdpa_forward(to_device(q, torch.bfloat16), to_device(k, torch.bfloat16),
+                                     to_device(v, torch.bfloat16), valid_lens=vls, causal=causal,
+                                     out_dtype=torch.float32))
+        mean = v.astype(np.float64).mean(axis=2, keepdims=True)
+        assert_bf16(o, np.broadcast_to(mean, o.shape), "fully masked rows")

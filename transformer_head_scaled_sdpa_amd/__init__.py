@@ -1,0 +1,157 @@
+"""MI355X (gfx950) multi-head scaled dot-product attention forward.
+
+Thin torch-facing binding over libmha.so (C ABI in include/mha.h).  It only
+marshals arguments: device pointers, strides, sizes and torch's current HIP
+stream.  Every step of the computation runs in the library's HIP kernels;
+there is no CPU or PyTorch fallback, and a missing library raises.
+
+    sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None)
+        q [B,h,Lq,64], k [B,h,Lk,64], v [B,h,Lk,64] on the GPU (bf16 or fp32)
+    mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, b_q=None, ..., h=8,
+                valid_lens=None, causal=False, out_dtype=None)
+        x_q [B,Lq,D], x_kv [B,Lk,D], W [D,D] stored [out, in], b [D]
+"""
+import ctypes
+
+from . import _lib
+from ._lib import MhaError, MHA_BF16, MHA_F32, MHA_OK, Strides
+
+__all__ = ["sdpa_forward", "mha_forward", "workspace_bytes", "kernel_timing", "MhaError", "library"]
+
+
+def library():
+    """The loaded ctypes handle of libmha.so (raises if it is not built)."""
+    return _lib.load()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt):
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return MHA_BF16
+    if dt == torch.float32:
+        return MHA_F32
+    raise TypeError(f"unsupported dtype {dt}: use torch.bfloat16 or torch.float32")
+
+
+def _check_gpu(name, t):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _strides4(t):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("attention operands are [B, h, L, d] views with a contiguous last axis")
+    s = t.stride()
+    return Strides(s[0], s[1], s[2])
+
+
+def _valid_lens(valid_lens, B, device):
+    torch = _torch()
+    if valid_lens is None:
+        return None
+    vl = torch.as_tensor(valid_lens, dtype=torch.int32, device=device).contiguous()
+    if vl.shape != (B,):
+        raise ValueError(f"valid_lens must have shape ({B},)")
+    return vl
+
+
+def _raise(status, what):
+    if status != MHA_OK:
+        raise MhaError(status, what)
+
+
+def sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None, out=None):
+    """softmax(q k^T / sqrt(d_k)) v per (batch, head) with key-padding
+    ``valid_lens`` [B] and/or the causal mask; returns o [B, h, Lq, d_v]."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_gpu(n, t)
+    B, h, Lq, dk = q.shape
+    Lk, dv = k.shape[2], v.shape[3]
+    in_dt = _dtype_code(q.dtype)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, h, Lq, dv), dtype=out_dtype, device=q.device)
+    vl = _valid_lens(valid_lens, B, q.device)
+    st = _lib.load().sdpa_forward(
+        in_dt, _dtype_code(out.dtype), _ptr(q), _strides4(q), _ptr(k), _strides4(k), _ptr(v), _strides4(v),
+        _ptr(out), _strides4(out), B, h, Lq, Lk, dk, dv, _ptr(vl), int(bool(causal)), _stream())
+    _raise(st, "sdpa_forward")
+    return out
+
+
+def workspace_bytes(dtype, B, Lq, Lk, d_model, h):
+    return int(_lib.load().mha_workspace_bytes(_dtype_code(dtype), B, Lq, Lk, d_model, h))
+
+
+def mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, b_q=None, b_k=None, b_v=None, b_o=None, h=8,
+                valid_lens=None, causal=False, out_dtype=None, out=None, workspace=None):
+    """Multi-head attention forward; returns [B, Lq, d_model]."""
+    torch = _torch()
+    args = dict(x_q=x_q, x_kv=x_kv, w_q=w_q, w_k=w_k, w_v=w_v, w_o=w_o, b_q=b_q, b_k=b_k, b_v=b_v, b_o=b_o)
+    for n, t in args.items():
+        _check_gpu(n, t)
+        if t is not None and (not t.is_contiguous() or t.dtype != x_q.dtype):
+            raise ValueError(f"{n} must be contiguous and share x_q's dtype")
+    B, Lq, D = x_q.shape
+    Lk = x_kv.shape[1]
+    in_dt = _dtype_code(x_q.dtype)
+    out_dtype = (torch.float32 if x_q.dtype == torch.bfloat16 else x_q.dtype) if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, Lq, D), dtype=out_dtype, device=x_q.device)
+    need = workspace_bytes(x_q.dtype, B, Lq, Lk, D, h)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x_q.device)
+    vl = _valid_lens(valid_lens, B, x_q.device)
+    st = _lib.load().mha_forward(
+        in_dt, _dtype_code(out.dtype), _ptr(x_q), _ptr(x_kv), _ptr(w_q), _ptr(b_q), _ptr(w_k), _ptr(b_k),
+        _ptr(w_v), _ptr(b_v), _ptr(w_o), _ptr(b_o), _ptr(out), B, Lq, Lk, D, h, D // h if h else 0,
+        _ptr(vl), int(bool(causal)), _ptr(workspace), workspace.numel(), _stream())
+    _raise(st, "mha_forward")
+    return out
+
+
+class kernel_timing:
+    """Context manager: per-kernel GPU time (HIP events around each launch).
+
+        with kernel_timing() as kt:
+            ...library calls...
+        kt.result  # {kernel name: (total_ms, launches)}
+    """
+
+    def __init__(self):
+        self.result = {}
+
+    def __enter__(self):
+        _raise(_lib.load().mha_timing_enable(1), "mha_timing_enable")
+        return self
+
+    def __exit__(self, *exc):
+        lib = _lib.load()
+        n = 16
+        names = (ctypes.c_char_p * n)()
+        tot = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int * n)()
+        k = lib.mha_timing_read(names, tot, cnt, n)
+        lib.mha_timing_enable(0)
+        if k < 0:
+            raise RuntimeError("mha_timing_read failed")
+        self.result = {names[x].decode(): (tot[x], cnt[x]) for x in range(k)}
+        return False

@@ -1,0 +1,269 @@
+// C ABI of the attention library (declared in include/mha.h).
+//
+// Every entry point validates all arguments on the host before it enqueues
+// anything; kernels run on the caller's stream.  The library allocates no
+// device memory: mha_forward's intermediates live in the caller's workspace.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mha.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kHeadDim = 64;   // d_k = d_v = d_model / h (the pages' 512 / 8)
+
+size_t elem_size(mha_dtype dt) { return dt == MHA_F32 ? 4 : 2; }
+
+bool valid_dtype(int dt) { return dt == MHA_F32 || dt == MHA_BF16; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Byte range [lo, hi) touched by a [B, h, L, d] view with the given strides.
+struct Range {
+    uintptr_t lo, hi;
+};
+
+Range view_range(const void* p, mha_strides s, int B, int h, int L, int d, size_t es) {
+    const uintptr_t base = reinterpret_cast<uintptr_t>(p);
+    const long long last = (long long)(B - 1) * s.b + (long long)(h - 1) * s.h + (long long)(L - 1) * s.l + d;
+    return Range{base, base + (uintptr_t)last * es};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// ---------------------------------------------------------------------------
+// kernel timing: a fixed pool of HIP event pairs recorded around launches
+// ---------------------------------------------------------------------------
+constexpr int kPool = 4096;
+struct TimingState {
+    bool on = false;
+    int used = 0;
+    bool created = false;
+    hipEvent_t ev[2 * kPool];
+    const char* name[kPool];
+};
+TimingState g_timing;
+
+template <typename F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+    if (!g_timing.on || g_timing.used >= kPool) return launch();
+    const int k = g_timing.used++;
+    g_timing.name[k] = name;
+    hipError_t e = hipEventRecord(g_timing.ev[2 * k], s);
+    if (e != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    return hipEventRecord(g_timing.ev[2 * k + 1], s);
+}
+
+mha_status hip_status(hipError_t e) { return e == hipSuccess ? MHA_OK : MHA_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mha_status_string(mha_status s) {
+    switch (s) {
+        case MHA_OK: return "MHA_OK: success";
+        case MHA_EINVAL: return "MHA_EINVAL: invalid argument";
+        case MHA_ENOTSUP: return "MHA_ENOTSUP: unsupported head width or dtype combination";
+        case MHA_EWORKSPACE: return "MHA_EWORKSPACE: workspace too small";
+        case MHA_EHIP: return "MHA_EHIP: HIP runtime error while enqueuing";
+    }
+    return "unknown mha_status";
+}
+
+mha_status sdpa_forward(mha_dtype in_dt, mha_dtype out_dt,
+                        const void* q, mha_strides sq,
+                        const void* k, mha_strides sk,
+                        const void* v, mha_strides sv,
+                        void* o, mha_strides so,
+                        int B, int h, int Lq, int Lk, int d_k, int d_v,
+                        const int* valid_lens, int causal, void* stream) {
+    if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
+    if (B < 0 || h <= 0 || Lq < 0 || Lk <= 0 || d_k <= 0 || d_v <= 0) return MHA_EINVAL;
+    if (causal && Lq != Lk) return MHA_EINVAL;
+    if (d_k != kHeadDim || d_v != kHeadDim) return MHA_ENOTSUP;
+    if (in_dt == MHA_F32 && out_dt != MHA_F32) return MHA_ENOTSUP;
+    if (B == 0 || Lq == 0) return MHA_OK;
+    if (!q || !k || !v || !o) return MHA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MHA_EINVAL;
+    const long long mult = in_dt == MHA_F32 ? 4 : 8;
+    const long long omult = out_dt == MHA_F32 ? 4 : 8;
+    const mha_strides in_s[3] = {sq, sk, sv};
+    for (const mha_strides& s : in_s)
+        if (s.b < 0 || s.h < 0 || s.l < 0 || s.b % mult || s.h % mult || s.l % mult) return MHA_EINVAL;
+    if (so.b < 0 || so.h < 0 || so.l < 0 || so.b % omult || so.h % omult || so.l % omult) return MHA_EINVAL;
+    const size_t ie = elem_size(in_dt), oe = elem_size(out_dt);
+    const Range ro = view_range(o, so, B, h, Lq, d_v, oe);
+    if (overlap(ro, view_range(q, sq, B, h, Lq, d_k, ie)) || overlap(ro, view_range(k, sk, B, h, Lk, d_k, ie)) ||
+        overlap(ro, view_range(v, sv, B, h, Lk, d_v, ie)))
+        return MHA_EINVAL;
+
+    mha::SdpaArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.q_lo = nullptr; a.k_lo = nullptr;
+    a.sq[0] = sq.b; a.sq[1] = sq.h; a.sq[2] = sq.l;
+    a.sk[0] = sk.b; a.sk[1] = sk.h; a.sk[2] = sk.l;
+    a.sv[0] = sv.b; a.sv[1] = sv.h; a.sv[2] = sv.l;
+    a.so[0] = so.b; a.so[1] = so.h; a.so[2] = so.l;
+    a.B = B; a.H = h; a.Lq = Lq; a.Lk = Lk;
+    a.valid_lens = valid_lens;
+    a.causal = causal ? 1 : 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (in_dt == MHA_F32) return hip_status(timed("sdpa_f32", s, [&] { return mha::launch_sdpa_f32(a, s); }));
+    return hip_status(timed("sdpa_bf16", s, [&] { return mha::launch_sdpa_bf16(a, out_dt == MHA_F32, s); }));
+}
+
+size_t mha_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h) {
+    if (!valid_dtype(in_dt) || B < 0 || Lq < 0 || Lk < 0 || d_model <= 0 || h <= 0 || d_model % h) return 0;
+    const size_t es = elem_size(in_dt);
+    const size_t q = round_up((size_t)B * Lq * d_model * es, 256);
+    const size_t kv = round_up((size_t)B * Lk * d_model * es, 256);
+    // fp32: Q, K, V, merged heads.  bf16: Q and K as hi + lo planes as well.
+    return in_dt == MHA_BF16 ? 3 * q + 3 * kv : 2 * q + 2 * kv;
+}
+
+mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
+                       const void* x_q, const void* x_kv,
+                       const void* w_q, const void* b_q,
+                       const void* w_k, const void* b_k,
+                       const void* w_v, const void* b_v,
+                       const void* w_o, const void* b_o,
+                       void* out,
+                       int B, int Lq, int Lk, int d_model, int h, int d_k,
+                       const int* valid_lens, int causal,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
+    if (B < 0 || Lq < 0 || Lk <= 0 || d_model <= 0 || h <= 0 || d_k <= 0) return MHA_EINVAL;
+    if ((long long)h * d_k != d_model) return MHA_EINVAL;
+    if (causal && Lq != Lk) return MHA_EINVAL;
+    if (d_k != kHeadDim) return MHA_ENOTSUP;
+    if (in_dt == MHA_F32 && out_dt != MHA_F32) return MHA_ENOTSUP;
+    if (B == 0 || Lq == 0) return MHA_OK;
+    if (!x_q || !x_kv || !w_q || !w_k || !w_v || !w_o || !out || !workspace) return MHA_EINVAL;
+    const void* ptrs[] = {x_q, x_kv, w_q, w_k, w_v, w_o, out, workspace, b_q, b_k, b_v, b_o};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MHA_EINVAL;
+    const size_t need = mha_workspace_bytes(in_dt, B, Lq, Lk, d_model, h);
+    if (workspace_bytes < need) return MHA_EWORKSPACE;
+
+    const size_t ie = elem_size(in_dt), oe = elem_size(out_dt);
+    const uintptr_t ob = reinterpret_cast<uintptr_t>(out);
+    const Range rout{ob, ob + (size_t)B * Lq * d_model * oe};
+    const uintptr_t wb = reinterpret_cast<uintptr_t>(workspace);
+    const Range inputs[] = {
+        {reinterpret_cast<uintptr_t>(x_q), reinterpret_cast<uintptr_t>(x_q) + (size_t)B * Lq * d_model * ie},
+        {reinterpret_cast<uintptr_t>(x_kv), reinterpret_cast<uintptr_t>(x_kv) + (size_t)B * Lk * d_model * ie},
+        {reinterpret_cast<uintptr_t>(w_q), reinterpret_cast<uintptr_t>(w_q) + (size_t)d_model * d_model * ie},
+        {reinterpret_cast<uintptr_t>(w_k), reinterpret_cast<uintptr_t>(w_k) + (size_t)d_model * d_model * ie},
+        {reinterpret_cast<uintptr_t>(w_v), reinterpret_cast<uintptr_t>(w_v) + (size_t)d_model * d_model * ie},
+        {reinterpret_cast<uintptr_t>(w_o), reinterpret_cast<uintptr_t>(w_o) + (size_t)d_model * d_model * ie},
+        {wb, wb + need},
+    };
+    for (const Range& r : inputs)
+        if (overlap(rout, r)) return MHA_EINVAL;
+    const Range rws{wb, wb + need};
+    for (int n = 0; n < 6; ++n)
+        if (overlap(rws, inputs[n])) return MHA_EINVAL;
+    const void* biases[] = {b_q, b_k, b_v, b_o};
+    for (const void* p : biases) {
+        if (!p) continue;
+        const Range rb{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (size_t)d_model * ie};
+        if (overlap(rout, rb) || overlap(rws, rb)) return MHA_EINVAL;
+    }
+
+    // Workspace: Q [B*Lq, D], K [B*Lk, D], V [B*Lk, D], merged heads [B*Lq, D]
+    // and, for bf16, the low planes of Q and K.
+    char* w = static_cast<char*>(workspace);
+    const size_t qbytes = round_up((size_t)B * Lq * d_model * ie, 256);
+    const size_t kvbytes = round_up((size_t)B * Lk * d_model * ie, 256);
+    const bool bf16 = in_dt == MHA_BF16;
+    void* Q = w;
+    void* K = w + qbytes;
+    void* V = w + qbytes + kvbytes;
+    void* Ocat = w + qbytes + 2 * kvbytes;
+    void* Qlo = bf16 ? w + 2 * qbytes + 2 * kvbytes : nullptr;
+    void* Klo = bf16 ? w + 3 * qbytes + 2 * kvbytes : nullptr;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    // 1. Q/K/V projections in one launch (three problems).
+    mha::GemmArgs g;
+    g.nprob = 3;
+    g.N = d_model;
+    g.K = d_model;
+    g.p[0] = {x_q, w_q, b_q, Q, B * Lq, Qlo};
+    g.p[1] = {x_kv, w_k, b_k, K, B * Lk, Klo};
+    g.p[2] = {x_kv, w_v, b_v, V, B * Lk, nullptr};
+    hipError_t e = timed(bf16 ? "qkv_proj_bf16" : "qkv_proj_f32", s, [&] {
+        return bf16 ? mha::launch_gemm_bf16(g, false, s) : mha::launch_gemm_f32(g, s);
+    });
+    if (e != hipSuccess) return MHA_EHIP;
+
+    // 2. Attention per head: [B*L, D] row-major viewed as [B, L, h, d_k].
+    mha::SdpaArgs a;
+    a.q = Q; a.k = K; a.v = V; a.o = Ocat;
+    a.q_lo = Qlo; a.k_lo = Klo;
+    a.sq[0] = (long long)Lq * d_model; a.sq[1] = d_k; a.sq[2] = d_model;
+    a.sk[0] = (long long)Lk * d_model; a.sk[1] = d_k; a.sk[2] = d_model;
+    a.sv[0] = (long long)Lk * d_model; a.sv[1] = d_k; a.sv[2] = d_model;
+    a.so[0] = (long long)Lq * d_model; a.so[1] = d_k; a.so[2] = d_model;
+    a.B = B; a.H = h; a.Lq = Lq; a.Lk = Lk;
+    a.valid_lens = valid_lens;
+    a.causal = causal ? 1 : 0;
+    e = timed(bf16 ? "sdpa_bf16" : "sdpa_f32", s, [&] {
+        return bf16 ? mha::launch_sdpa_bf16(a, false, s) : mha::launch_sdpa_f32(a, s);
+    });
+    if (e != hipSuccess) return MHA_EHIP;
+
+    // 3. Output projection of the merged heads.
+    mha::GemmArgs go;
+    go.nprob = 1;
+    go.N = d_model;
+    go.K = d_model;
+    go.p[0] = {Ocat, w_o, b_o, out, B * Lq, nullptr};
+    e = timed(bf16 ? "out_proj_bf16" : "out_proj_f32", s, [&] {
+        return bf16 ? mha::launch_gemm_bf16(go, out_dt == MHA_F32, s) : mha::launch_gemm_f32(go, s);
+    });
+    return hip_status(e);
+}
+
+mha_status mha_timing_enable(int on) {
+    if (on && !g_timing.created) {
+        for (int n = 0; n < 2 * kPool; ++n)
+            if (hipEventCreate(&g_timing.ev[n]) != hipSuccess) return MHA_EHIP;
+        g_timing.created = true;
+    }
+    g_timing.on = on != 0;
+    return MHA_OK;
+}
+
+int mha_timing_read(const char** names, double* total_ms, int* count, int max) {
+    int n_out = 0;
+    for (int k = 0; k < g_timing.used; ++k) {
+        if (hipEventSynchronize(g_timing.ev[2 * k + 1]) != hipSuccess) return -1;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, g_timing.ev[2 * k], g_timing.ev[2 * k + 1]) != hipSuccess) return -1;
+        int slot = -1;
+        for (int x = 0; x < n_out; ++x)
+            if (strcmp(names[x], g_timing.name[k]) == 0) slot = x;
+        if (slot < 0) {
+            if (n_out >= max) continue;
+            slot = n_out++;
+            names[slot] = g_timing.name[k];
+            total_ms[slot] = 0.0;
+            count[slot] = 0;
+        }
+        total_ms[slot] += ms;
+        count[slot] += 1;
+    }
+    g_timing.used = 0;
+    return n_out;
+}
+
+}  // extern "C"
