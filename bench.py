@@ -1,0 +1,306 @@
+"""Benchmark: multi-head attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one full multi-head attention forward (Q/K/V projections, head
+split, masked softmax attention, head merge, output projection) over one
+batch of seeded synthetic input already resident in HBM.  Prints ONE JSON
+line: the attention throughput 4*B*h*Lq*Lk*d_k per step / step time, the
+roofline of the step's dominant kernel (duration from HIP events the library
+records on its launch stream), the fp64 CPU oracle timed on the host's cores,
+and the fused attention kernel on the long causal workload.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (what the method itself must do: masked pairs skipped,
+# keys beyond the valid length not read)
+# ---------------------------------------------------------------------------
+def allowed_pairs(w, valid_lens):
+    """Number of (batch, head, query, key) pairs the masks allow."""
+    Lq, Lk = w.Lq, w.Lk
+    vl = np.full(w.B, Lk) if valid_lens is None else np.asarray(valid_lens, dtype=np.int64)
+    total = 0
+    i = np.arange(Lq)
+    for v in vl:
+        if v <= 0:
+            total += Lq * Lk          # fully masked rows weight every key
+            continue
+        v = min(int(v), Lk)
+        total += int(np.minimum(i + 1, v).sum()) if w.causal else Lq * v
+    return total * w.h
+
+
+def sdpa_alg(w, valid_lens, in_bytes, out_bytes):
+    """Algorithmic flops and HBM bytes of one fused attention launch."""
+    pairs = allowed_pairs(w, valid_lens)
+    flops = 4 * w.d_k * pairs
+    vl = np.full(w.B, w.Lk) if valid_lens is None else np.asarray(valid_lens, dtype=np.int64)
+    keys = sum(w.Lk if v <= 0 else min(int(v), w.Lk) for v in vl)   # K/V rows that carry weight
+    byts = w.h * w.d_k * (w.B * w.Lq * (in_bytes + out_bytes) + 2 * keys * in_bytes)
+    return flops, byts
+
+
+def gemm_alg(M, N, K, nprob, in_bytes, out_bytes):
+    return 2 * M * N * K * nprob, nprob * ((M * K + N * K + N) * in_bytes + M * N * out_bytes)
+
+
+def roofline(flops, byts, ms, mfma_peak):
+    t_mfma = flops / (mfma_peak * 1e12)
+    t_hbm = byts / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        ach = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(ach / mfma_peak, 4)}
+    ach = byts / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4)}
+
+
+# ---------------------------------------------------------------------------
+# GPU side
+# ---------------------------------------------------------------------------
+class PreparedMha:
+    """mha_forward with its arguments marshalled once (device pointers of
+    preallocated tensors); each call only passes torch's current stream."""
+
+    def __init__(self, inp):
+        import torch
+        import transformer_head_scaled_sdpa_amd as mha
+        from transformer_head_scaled_sdpa_amd import _lib
+        w = inp.workload
+        self.w = w
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        dev = torch.device("cuda:0")
+        self.t = {n: (None if a is None else torch.from_numpy(a).to(dev).to(dt)) for n, a in inp.tensors.items()}
+        if w.self_attn:
+            self.t["x_kv"] = self.t["x_q"]
+        self.out = torch.empty((w.B, w.Lq, w.d_model), dtype=torch.float32, device=dev)
+        need = mha.workspace_bytes(dt, w.B, w.Lq, w.Lk, w.d_model, w.h)
+        self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        self.vl = None if inp.valid_lens is None else torch.from_numpy(inp.valid_lens).to(dev)
+        self.lib = _lib.load()
+        p = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
+        t = self.t
+        self.in_dt = _lib.MHA_BF16 if w.dtype == "bf16" else _lib.MHA_F32
+        self.args = [self.in_dt, _lib.MHA_F32, p(t["x_q"]), p(t["x_kv"]), p(t["w_q"]), p(t["b_q"]),
+                     p(t["w_k"]), p(t["b_k"]), p(t["w_v"]), p(t["b_v"]), p(t["w_o"]), p(t["b_o"]),
+                     p(self.out), w.B, w.Lq, w.Lk, w.d_model, w.h, w.d_k, p(self.vl), int(w.causal),
+                     p(self.ws), need]
+        self.torch = torch
+
+    def __call__(self):
+        st = self.lib.mha_forward(*self.args, ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"mha_forward failed with status {st}")
+
+
+class PreparedSdpa:
+    def __init__(self, inp):
+        import torch
+        from transformer_head_scaled_sdpa_amd import _lib
+        w = inp.workload
+        self.w = w
+        dev = torch.device("cuda:0")
+        self.q, self.k, self.v = (torch.from_numpy(inp.tensors[n]).to(dev).to(torch.bfloat16) for n in "qkv")
+        self.o = torch.empty_like(self.q)
+        self.vl = None if inp.valid_lens is None else torch.from_numpy(inp.valid_lens).to(dev)
+        self.lib = _lib.load()
+        s = lambda x: _lib.Strides(*x.stride()[:3])
+        p = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
+        self.args = [_lib.MHA_BF16, _lib.MHA_BF16, p(self.q), s(self.q), p(self.k), s(self.k), p(self.v), s(self.v),
+                     p(self.o), s(self.o), w.B, w.h, w.Lq, w.Lk, w.d_k, w.d_k, p(self.vl), int(w.causal)]
+        self.torch = torch
+
+    def __call__(self):
+        st = self.lib.sdpa_forward(*self.args, ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"sdpa_forward failed with status {st}")
+
+
+def time_steps(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    return e0.elapsed_time(e1) / steps, wall / steps
+
+
+def kernel_times(fn, steps):
+    """Average duration (ms) per launch of each library kernel over `steps`
+    eager steps, from the HIP event pairs the library records around every
+    launch on the launch stream."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    torch.cuda.synchronize()
+    with mha.kernel_timing() as kt:
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+    return {n: tot / cnt for n, (tot, cnt) in kt.result.items()}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, untuned, on a bounded sample of the workload
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, inp, budget_s=20.0):
+    import oracle
+    t = inp.tensors
+    n_threads = oracle.num_threads()
+    if w.kind == "sdpa":
+        # sample query rows; every (batch, head) pair, all keys
+        rows = np.linspace(0, w.Lq - 1, 16).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.sdpa(t["q"], t["k"], t["v"], valid_lens=inp.valid_lens, causal=w.causal, rows=rows)
+        dt = time.perf_counter() - t0
+        flops = 4 * w.B * w.h * len(rows) * w.Lk * w.d_k
+        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": n_threads, "kind": "oracle",
+                "sample": f"{len(rows)} query rows of every (batch, head), all {w.Lk} keys; {dt:.2f} s"}
+    # MHA: whole batches, all rows.  Time one batch, then as many batches as
+    # fit the budget (at most the whole workload).
+    def run(nb):
+        sel = slice(0, nb)
+        vl = None if inp.valid_lens is None else inp.valid_lens[sel]
+        t0 = time.perf_counter()
+        oracle.mha(t["x_q"][sel], t["x_kv"][sel], t["w_q"], t["w_k"], t["w_v"], t["w_o"],
+                   t["b_q"], t["b_k"], t["b_v"], t["b_o"], h=w.h, valid_lens=vl, causal=w.causal)
+        return time.perf_counter() - t0
+    nb, dt = 1, run(1)
+    fit = int(min(w.B, max(1, budget_s // max(dt, 1e-6))))
+    if fit > 1:
+        nb, dt = fit, run(fit)
+    flops = 4 * nb * w.h * w.Lq * w.Lk * w.d_k
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": n_threads, "kind": "oracle",
+            "sample": f"{nb} of {w.B} batches, full MHA forward (projections included); {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="encoder_self", choices=sorted(workloads.BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-sdpa", action="store_true", help="skip the long causal attention kernel line")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    w = workloads.BY_NAME[args.workload]
+    inp = workloads.make_inputs(w)
+    in_b = 2 if w.dtype == "bf16" else 4
+    mfma_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    log(f"workload {w.name}: {w.description}")
+
+    fn = PreparedMha(inp) if w.kind == "mha" else PreparedSdpa(inp)
+    ms, wall_ms = time_steps(fn, args.steps, args.warmup)
+    attn_flops = w.attention_flops()
+    value = attn_flops / (ms * 1e-3) / 1e12
+    log(f"step {ms * 1e3:.2f} us (wall {wall_ms * 1e3:.2f} us)")
+
+    # per-kernel durations and the dominant kernel's roofline
+    kt = kernel_times(fn, args.steps)
+    kernels = {}
+    M_q, M_kv = w.B * w.Lq, w.B * w.Lk
+    for name, kms in kt.items():
+        if name.startswith("qkv_proj"):
+            f, b = gemm_alg(M_q, w.d_model, w.d_model, 1, in_b, in_b)
+            f2, b2 = gemm_alg(M_kv, w.d_model, w.d_model, 2, in_b, in_b)
+            f, b = f + f2, b + b2
+        elif name.startswith("out_proj"):
+            f, b = gemm_alg(M_q, w.d_model, w.d_model, 1, in_b, 4)
+        else:
+            f, b = sdpa_alg(w, inp.valid_lens, in_b, in_b if w.kind == "mha" else 2)
+        kernels[name] = {"avg_us": round(kms * 1e3, 3), "alg_flops": f, "alg_bytes": b,
+                         "roofline": roofline(f, b, kms, mfma_peak)}
+    dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
+    rl = dict(kernels[dom]["roofline"])
+    rl["kernel"] = dom
+    rl["traffic"] = None
+    rl["alg_per_launch"] = {"flops": kernels[dom]["alg_flops"], "bytes": kernels[dom]["alg_bytes"]}
+
+    result = {
+        "metric": "attention TFLOP/s (4*B*h*Lq*Lk*d_k per step / step time) and % of MI355X bf16 MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded numpy PCG64; Xavier-uniform weights, zero bias)",
+        "config": {"workload": w.description, "name": w.name, "B": w.B, "Lq": w.Lq, "Lk": w.Lk,
+                   "d_model": w.d_model, "h": w.h, "d_k": w.d_k, "causal": w.causal,
+                   "valid_lens": None if w.vl_range is None else f"U{{{w.vl_range[0]}..{w.vl_range[1]}}}",
+                   "attention_flops_per_step": attn_flops},
+        "kernels": {n: {"avg_us": k["avg_us"], "roofline_frac": k["roofline"]["frac"],
+                        "bound": k["roofline"]["bound"]} for n, k in kernels.items()},
+        "roofline": rl,
+    }
+
+    if not args.no_long_sdpa and w.name != "sdpa_long_causal":
+        lw = workloads.BY_NAME["sdpa_long_causal"]
+        linp = workloads.make_inputs(lw)
+        sf = PreparedSdpa(linp)
+        sms, _ = time_steps(sf, 20, 3)
+        f, b = sdpa_alg(lw, None, 2, 2)
+        result["sdpa_long_causal"] = {
+            "workload": lw.description, "avg_us": round(sms * 1e3, 2),
+            "alg_tflops": round(f / (sms * 1e-3) / 1e12, 2),
+            "dense_equiv_tflops": round(lw.attention_flops() / (sms * 1e-3) / 1e12, 2),
+            "frac_bf16_peak_alg": round(f / (sms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del sf
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(w, inp)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

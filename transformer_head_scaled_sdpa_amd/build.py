@@ -9,9 +9,12 @@ LIB = os.path.join(HERE, "libmha.so")
 SOURCES = ["api.hip", "sdpa_bf16.hip", "sdpa_f32.hip", "gemm.hip"]
 
 # Packed fp32 VALU ops are disabled for every HIP translation unit.
+# -fno-honor-nans: inputs are finite, so max/min need not quiet signalling
+# NaNs (otherwise every fmaxf operand gets an extra canonicalising v_max);
+# infinities keep their meaning (masked scores are -inf).
 HIP_FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-Wall", "-Wno-unused-function"]
+             "-fno-honor-nans", "-Wall", "-Wno-unused-function"]
 
 
 def build(verbose: bool = False) -> str:
