@@ -12,6 +12,7 @@ and the fused attention kernel on the long causal workload.
 """
 import argparse
 import ctypes
+import hashlib
 import json
 import math
 import os
@@ -157,18 +158,76 @@ def time_steps(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall / steps
 
 
-def kernel_times(fn, steps):
+def kernel_times(fn, steps, repeat):
     """Average duration (ms) per launch of each library kernel over `steps`
-    eager steps, from the HIP event pairs the library records around every
-    launch on the launch stream."""
+    eager steps, from the HIP event pairs the library records on the launch
+    stream; each pair brackets `repeat` back-to-back launches of one kernel."""
     import torch
     import transformer_head_scaled_sdpa_amd as mha
     torch.cuda.synchronize()
-    with mha.kernel_timing() as kt:
+    with mha.kernel_timing(repeat=repeat) as kt:
         for _ in range(steps):
             fn()
         torch.cuda.synchronize()
     return {n: tot / cnt for n, (tot, cnt) in kt.result.items()}
+
+
+COPY_CAL_BYTES = 1 << 30
+
+
+def copy_calibration():
+    """Plain streaming kernels of known size for scaling the L2-to-memory
+    byte counters: a 1 GiB device-to-device copy and a 1 GiB negation, each
+    reading 1 GiB and writing 1 GiB (larger than every cache level)."""
+    import torch
+    n = COPY_CAL_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 x copy_ and 3 x neg of {COPY_CAL_BYTES} bytes")
+    del src, dst
+
+
+# ---------------------------------------------------------------------------
+# measured HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE), valid only for
+# the kernel sources it was measured on
+# ---------------------------------------------------------------------------
+CSRC = os.path.join(ROOT, "transformer_head_scaled_sdpa_amd", "csrc")
+KERNEL_SOURCES = {
+    "qkv_proj_bf16": ["gemm.hip", "common.h", "kernels.h"],
+    "out_proj_bf16": ["gemm.hip", "common.h", "kernels.h"],
+    "sdpa_bf16": ["sdpa_bf16.hip", "common.h", "kernels.h"],
+}
+
+
+def source_digest(name):
+    files = KERNEL_SOURCES.get(name)
+    if files is None:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from profiles/traffic.json, or None when there is
+    no record for this kernel and workload or its sources have changed since
+    the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    digest = source_digest(kernel)
+    for r in rec.get("kernels", []):
+        if r["kernel"] == kernel and r["workload"] == workload and r["source_sha256"] == digest:
+            return r["bytes_per_launch"]
+    return None
 
 
 # ---------------------------------------------------------------------------
@@ -213,6 +272,10 @@ def main():
     ap.add_argument("--workload", default="encoder_self", choices=sorted(workloads.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-sdpa", action="store_true", help="skip the long causal attention kernel line")
+    ap.add_argument("--repeat", type=int, default=10,
+                    help="back-to-back launches per event pair when timing kernels (default 10)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run 1 GiB copy kernels (for scaling memory counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -225,6 +288,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        copy_calibration()
 
     w = workloads.BY_NAME[args.workload]
     inp = workloads.make_inputs(w)
@@ -239,7 +305,7 @@ def main():
     log(f"step {ms * 1e3:.2f} us (wall {wall_ms * 1e3:.2f} us)")
 
     # per-kernel durations and the dominant kernel's roofline
-    kt = kernel_times(fn, args.steps)
+    kt = kernel_times(fn, max(1, args.steps // args.repeat), args.repeat)
     kernels = {}
     M_q, M_kv = w.B * w.Lq, w.B * w.Lk
     for name, kms in kt.items():
@@ -256,7 +322,7 @@ def main():
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
     rl = dict(kernels[dom]["roofline"])
     rl["kernel"] = dom
-    rl["traffic"] = None
+    rl["traffic"] = measured_traffic(dom, w.name)
     rl["alg_per_launch"] = {"flops": kernels[dom]["alg_flops"], "bytes": kernels[dom]["alg_bytes"]}
 
     result = {

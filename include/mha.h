@@ -135,15 +135,20 @@ mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
 const char* mha_status_string(mha_status s);
 
 /*
- * Kernel timing (observability).  While enabled, every kernel the library
- * enqueues is bracketed by a pair of HIP events recorded on the same stream.
+ * Kernel timing (observability).  mha_timing_enable(repeat) with repeat in
+ * 1..1000 turns it on: every kernel the library enqueues is then launched
+ * `repeat` times in a row, bracketed by one pair of HIP events recorded on the
+ * same stream (each kernel is a pure function of its inputs, so the results
+ * are unchanged; repeat > 1 amortises the gaps the events themselves add).
+ * repeat = 0 turns it off; other values return MHA_EINVAL.
  * mha_timing_read() waits for the recorded events, adds their elapsed times
- * per kernel name into `total_ms` / `count` (up to `max` entries, names are
- * static strings) and returns the number of entries written; it also clears
- * the record.  Returns -1 on a HIP error.  Event pairs beyond the library's
- * fixed pool (4096 pairs) are not recorded.  Not thread-safe.
+ * per kernel name into `total_ms` and the number of launches into `count`
+ * (up to `max` entries, names are static strings) and returns the number of
+ * entries written; it also clears the record.  Returns -1 on a HIP error.
+ * Event pairs beyond the library's fixed pool (4096 pairs) are not recorded.
+ * Not thread-safe.
  */
-mha_status mha_timing_enable(int on);
+mha_status mha_timing_enable(int repeat);
 int mha_timing_read(const char** names, double* total_ms, int* count, int max);
 
 #ifdef __cplusplus

@@ -112,6 +112,13 @@ def test_workspace_bytes(lib):
     assert lib.mha_workspace_bytes(F32, 2, 10, 10, 500, 8) == 0
 
 
+def test_timing_repeat_range(lib):
+    # Only the argument check and switching off: both touch no device.
+    assert lib.mha_timing_enable(-1) == EINVAL
+    assert lib.mha_timing_enable(1001) == EINVAL
+    assert lib.mha_timing_enable(0) == OK
+
+
 def test_missing_library_raises(monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libmha.so")

@@ -131,16 +131,21 @@ def mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, b_q=None, b_k=None, b_v=None, b_o
 class kernel_timing:
     """Context manager: per-kernel GPU time (HIP events around each launch).
 
-        with kernel_timing() as kt:
+        with kernel_timing(repeat=10) as kt:
             ...library calls...
         kt.result  # {kernel name: (total_ms, launches)}
+
+    With repeat > 1 each kernel runs `repeat` times back to back inside one
+    event pair (same results: the kernels are pure functions of their
+    inputs), so total_ms / launches approaches the kernel's own duration.
     """
 
-    def __init__(self):
+    def __init__(self, repeat=1):
         self.result = {}
+        self.repeat = int(repeat)
 
     def __enter__(self):
-        _raise(_lib.load().mha_timing_enable(1), "mha_timing_enable")
+        _raise(_lib.load().mha_timing_enable(self.repeat), "mha_timing_enable")
         return self
 
     def __exit__(self, *exc):
