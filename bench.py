@@ -199,7 +199,7 @@ CSRC = os.path.join(ROOT, "transformer_head_scaled_sdpa_amd", "csrc")
 KERNEL_SOURCES = {
     "qkv_proj_bf16": ["gemm.hip", "common.h", "kernels.h"],
     "out_proj_bf16": ["gemm.hip", "common.h", "kernels.h"],
-    "sdpa_bf16": ["sdpa_bf16.hip", "common.h", "kernels.h"],
+    "sdpa_bf16": ["sdpa_bf16.hip", "sdpa_bf16_q64.hip", "common.h", "kernels.h"],
 }
 
 
