@@ -199,7 +199,7 @@ CSRC = os.path.join(ROOT, "transformer_head_scaled_sdpa_amd", "csrc")
 KERNEL_SOURCES = {
     "qkv_proj_bf16": ["gemm.hip", "common.h", "kernels.h"],
     "out_proj_bf16": ["gemm.hip", "common.h", "kernels.h"],
-    "sdpa_bf16": ["sdpa_bf16.hip", "sdpa_bf16_q64.hip", "common.h", "kernels.h"],
+    "sdpa_bf16": ["sdpa_bf16.hip", "sdpa_bf16_pipe.hip", "common.h", "kernels.h"],
 }
 
 
@@ -352,7 +352,7 @@ def main():
         lw = workloads.BY_NAME["sdpa_long_causal"]
         linp = workloads.make_inputs(lw)
         sf = PreparedSdpa(linp)
-        sms, _ = time_steps(sf, 20, 3)
+        sms, _ = time_steps(sf, 50, 20)
         f, b = sdpa_alg(lw, None, 2, 2)
         result["sdpa_long_causal"] = {
             "workload": lw.description, "avg_us": round(sms * 1e3, 2),

@@ -43,8 +43,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_sdpa_bf16(const SdpaArgs& a, bool out_f32, hipStream_t s);
-// Single-operand bf16 attention (q_lo / k_lo unused), 64 queries per wave.
-hipError_t launch_sdpa_bf16_q64(const SdpaArgs& a, bool out_f32, hipStream_t s);
+// Single-operand bf16 attention, software-pipelined, 32 queries per wave.
+hipError_t launch_sdpa_bf16_pipe(const SdpaArgs& a, bool out_f32, hipStream_t s);
 hipError_t launch_sdpa_f32(const SdpaArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool out_f32, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);

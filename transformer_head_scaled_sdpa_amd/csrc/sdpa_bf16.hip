@@ -352,7 +352,7 @@ hipError_t launch_sdpa_bf16(const SdpaArgs& a, bool out_f32, hipStream_t s) {
         if (c) return v ? launch_variant<true, true, false, true>(a, s) : launch_variant<true, false, false, true>(a, s);
         return v ? launch_variant<false, true, false, true>(a, s) : launch_variant<false, false, false, true>(a, s);
     }
-    return launch_sdpa_bf16_q64(a, out_f32, s);
+    return launch_sdpa_bf16_pipe(a, out_f32, s);
 }
 
 }  // namespace mha

@@ -1,0 +1,365 @@
+// Fused scaled dot-product attention forward for single bf16 operands (the
+// split-head entry point): bf16 in, fp32 accumulate, d_k = d_v = 64, gfx950.
+//
+// What it computes (The Annotated Transformer, "Attention" section):
+//   o_i = sum_j softmax_j(q_i . k_j / sqrt(d_k)) v_j
+// over the keys j allowed by the key-padding length and the causal rule.
+// Masked scores are replaced by -1e9 in the pages' code, which gives them a
+// weight of exactly zero whenever a row has an allowed key, so masked keys
+// are skipped.  A row with no allowed key (valid length <= 0) has all its
+// scores equal to -1e9, hence uniform weights over all Lk keys.
+//
+// Design.
+//  * One workgroup = 8 wave64s (two per SIMD) covering 256 consecutive
+//    queries of one (batch, head); each wave owns 32 queries and keeps their
+//    Q fragments in registers.  Keys/values stream through LDS in tiles of
+//    64 keys, copied with one 16-byte coalesced load per thread per tensor,
+//    staged in registers one tile ahead.
+//  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
+//    so every lane owns ONE query (lane % 32) and 32 keys of a tile; row sums
+//    are in-lane plus one v_permlane32_swap.  O^T += V^T P^T takes P straight
+//    from the score accumulator (the key order inside each 16-key slice is
+//    permuted identically on both operands) and reads V^T from LDS with the
+//    transpose read ds_read_b64_tr_b16.
+//  * Software pipeline inside each wave.  Stage s computes the softmax of
+//    tile s while the matrix cores run the scores of tile s+1 and the
+//    P.V product of tile s-1; the three are independent, so the scheduler
+//    interleaves the exponentials (which overlap MFMA execution) with the
+//    MFMAs instead of letting a wave alternate between MFMA-only and
+//    VALU-only phases.  K tiles are read one stage ahead of their softmax
+//    and V tiles one stage behind it, from two LDS buffers each, with one
+//    barrier per stage.
+//  * Weights are exp2(s * c - m) with c = log2(e)/sqrt(d_k) applied by one
+//    FMA on the fp32 score.  The offset m is the row max of the first tile;
+//    later tiles keep it unless a lane's sum of weights for the tile exceeds
+//    2^20, in which case the tile's row max is folded into m, the
+//    accumulators are rescaled and the tile's weights recomputed.  Weights
+//    stay below 2^20 * 32 per lane and tile, far from fp32 and bf16 limits,
+//    and no per-tile max reduction runs in the common case.  The row sum
+//    adds the bf16-rounded weights that the P.V product uses.
+//  * Causal: tiles above the diagonal are never loaded or multiplied; masks
+//    are evaluated only on the tiles that cross the diagonal or the valid
+//    length.  Workgroups are issued heaviest-first, and consecutive
+//    workgroup ids take different (batch, head) pairs.
+#include "common.h"
+#include "kernels.h"
+
+namespace mha {
+
+namespace {
+
+constexpr int kD = 64;                 // d_k = d_v
+constexpr int kBN = 64;                // keys per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = kWaves * 32;       // queries per workgroup
+// LDS row strides (bf16 elements), conflict-free on gfx950: K rows read as
+// 16-byte fragments at 144 B, V rows read with the transpose read at 192 B.
+constexpr int kLdsK = kD + 8;
+constexpr int kLdsV = kD + 32;
+constexpr int kTileK = kBN * kLdsK;
+constexpr int kTileV = kBN * kLdsV;
+constexpr float kSumLimit = 1048576.0f;   // 2^20
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// A 64 x 64 bf16 tile is 512 16-byte chunks, one per thread: chunk c holds
+// row c / 8, features (c % 8) * 8 .. +7.  The tile's base address is uniform
+// (scalar registers) and each lane adds a fixed 32-bit byte offset; only a
+// tile that runs past Lk checks rows, which then read as zero.
+__device__ __forceinline__ uint4 load_chunk(const char* tile, uint32_t lane_off, int rows_left, int tid) {
+    if (rows_left >= kBN) return *reinterpret_cast<const uint4*>(tile + lane_off);
+    return (tid >> 3) < rows_left ? *reinterpret_cast<const uint4*>(tile + lane_off) : make_uint4(0, 0, 0, 0);
+}
+
+template <int kLds>
+__device__ __forceinline__ void store_chunk(const uint4& r, bf16_t* tile, int tid) {
+    *reinterpret_cast<uint4*>(tile + (tid >> 3) * kLds + (tid & 7) * 8) = r;
+}
+
+__device__ __forceinline__ bf16x8 frag(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// V^T fragment for key slice kb (16 keys) and features tb*32 + (lane % 32):
+// in each 16-lane group, lane r points at key row base + r/4, features
+// T + (r%4)*4; the transpose read then hands lane j of the group features
+// T + j of keys base .. base+3.  Two reads cover keys base..+3 and base+8..+11.
+__device__ __forceinline__ bf16x8 v_frag(const bf16_t* vs, int kb, int tb, int hb, int lane) {
+    const int g = lane >> 4, r = lane & 15;
+    const int row = kb * 16 + hb * 4 + (r >> 2);
+    const int col = tb * 32 + (g & 1) * 16 + (r & 3) * 4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + row * kLdsV + col));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + (row + 8) * kLdsV + col));
+    // Join as whole vectors: inserting the 16-bit elements one by one is
+    // lowered incorrectly by the compiler.
+    const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, both);
+}
+
+// Raw scores q.k of one 64-key tile: s[jb] element v holds key
+// kv0 + jb*32 + (v/4)*8 + hb*4 + v%4 for query lane % 32.
+__device__ __forceinline__ void tile_scores(f32x16 (&s)[2], const bf16_t* ks, const bf16x8 (&qf)[4], int l32,
+                                            int hb) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const bf16x8 kf = frag(ks + (jb * 32 + l32) * kLdsK + kk * 16 + hb * 8);
+            s[jb] = mfma32x32x16(kf, qf[kk], kk == 0 ? f32x16{} : s[jb]);
+        }
+    }
+}
+
+// O^T += V^T P^T over one 64-key tile.
+__device__ __forceinline__ void tile_pv(f32x16 (&o)[2], const bf16_t* vs, const u32x4 (&p)[4], int hb, int lane) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 pk = __builtin_bit_cast(bf16x8, p[kb]);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) o[tb] = mfma32x32x16(v_frag(vs, kb, tb, hb, lane), pk, o[tb]);
+    }
+}
+
+// Mask rule on a tile: keys [0, key_lim) may carry weight for the row; a
+// row with no allowed key at all scores every key equally (score 0).
+__device__ __forceinline__ void apply_mask(f32x16 (&s)[2], int key_lim, bool none, int kv0, int hb) {
+    const int rel = key_lim - (kv0 + hb * 4);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int jr = (v >> 2) * 8 + (v & 3);
+        s[0][v] = jr < rel ? (none ? 0.0f : s[0][v]) : -INFINITY;
+        s[1][v] = jr + 32 < rel ? (none ? 0.0f : s[1][v]) : -INFINITY;
+    }
+}
+
+// Row max over the tile (both lane halves).
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
+    float mr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mr[r] = fmaxf(s[0][r], s[1][r]);
+#pragma unroll
+    for (int v = 4; v < 16; v += 4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mr[r] = fmaxf(mr[r], fmaxf(s[0][v + r], s[1][v + r]));
+    return pair_max(fmaxf(fmaxf(mr[0], mr[1]), fmaxf(mr[2], mr[3])));
+}
+
+// Weights exp2(s * c - m) packed as the B operand of O^T += V^T P^T: slice
+// kb covers keys kb*16 + (e/4)*8 + hb*4 + e%4 as bf16 pairs.  Returns this
+// lane's sum of the rounded weights.
+__device__ __forceinline__ float weights(const f32x16 (&s)[2], float m, float c, u32x4 (&w)[4]) {
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const int v = (kb & 1) * 8 + e;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb >> 1][v], c, -m));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb >> 1][v + 1], c, -m));
+            const bf16x2 pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
+            w[kb][e >> 1] = __builtin_bit_cast(uint32_t, pp);
+            acc[kb & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc[kb & 1], false);
+        }
+    }
+    return acc[0] + acc[1];
+}
+
+// A tile's weights outgrew the offset m: fold the tile's row max into m
+// (never lowering it), rescale the accumulators and recompute the weights.
+__device__ __forceinline__ float rescale(const f32x16 (&s)[2], float& m, float c, float& l, f32x16 (&o)[2],
+                                         u32x4 (&w)[4]) {
+    const float d = fmaxf(fmaf(tile_max(s), c, -m), 0.0f);
+    m += d;
+    const float alpha = __builtin_amdgcn_exp2f(-d);
+    l *= alpha;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        o[0][v] *= alpha;
+        o[1][v] *= alpha;
+    }
+    return weights(s, m, c, w);
+}
+
+template <bool kCausal, bool kHasVl, bool kOutF32>
+__global__ __launch_bounds__(kThreads, 1)
+void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
+    __shared__ __attribute__((aligned(16))) bf16_t kbuf[2 * kTileK];
+    __shared__ __attribute__((aligned(16))) bf16_t vbuf[2 * kTileV];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    // The wave index as a scalar: tile-range and mask decisions derived from
+    // it are then wave-uniform branches, not per-lane selects.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hb = lane >> 5, l32 = lane & 31;
+
+    // Workgroup -> (query tile, batch, head): (batch, head) varies fastest;
+    // causal issues the longest tiles first.
+    const int BH = a.B * a.H;
+    const int bh = blockIdx.x % BH;
+    int qt = blockIdx.x / BH;
+    if (kCausal) qt = n_qtiles - 1 - qt;
+    const int b = bh / a.H, hd = bh % a.H;
+
+    const int q_wg = qt * kBM;
+    const int q0 = q_wg + wave * 32;              // this wave's first query
+    const int i = q0 + l32;                       // this lane's query
+
+    const int Lk = a.Lk;
+    const int vlen = kHasVl ? a.valid_lens[b] : Lk;
+    const bool none = vlen <= 0;                  // every key masked -> uniform weights
+    const int kv_lim = none ? Lk : min(vlen, Lk); // keys [0, kv_lim) can carry weight
+    int kv_end = kv_lim;
+    if (kCausal && !none) kv_end = min(kv_end, q_wg + kBM);
+    const int n_tiles = (kv_end + kBN - 1) / kBN; // tiles the workgroup streams
+    // This wave's tiles are [0, n_w): later ones lie wholly above its queries.
+    const int n_w = (kCausal && !none) ? min(n_tiles, (q0 + 31) / kBN + 1) : n_tiles;
+    // Tiles from index t_mask on need the key-padding, causal or fully-masked rule.
+    int t_mask = none ? 0 : kv_lim / kBN;
+    if (kCausal && !none) t_mask = min(t_mask, q0 / kBN);
+    // Keys below key_lim are allowed for this lane's row.
+    const int key_lim = none ? Lk : (kCausal ? min(kv_lim, i + 1) : kv_lim);
+
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + b * a.sq[0] + hd * a.sq[1];
+    const char* kp = reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.k) + b * a.sk[0] + hd * a.sk[1]);
+    const char* vp = reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.v) + b * a.sv[0] + hd * a.sv[1]);
+    const long long ktile = a.sk[2] * (2 * kBN), vtile = a.sv[2] * (2 * kBN);   // bytes per 64 keys
+    const uint32_t koff = (uint32_t)((tid >> 3) * a.sk[2] * 2) + (tid & 7) * 16;
+    const uint32_t voff = (uint32_t)((tid >> 3) * a.sv[2] * 2) + (tid & 7) * 16;
+    auto load_k = [&](int t) { return load_chunk(kp + t * ktile, koff, Lk - t * kBN, tid); };
+    auto load_v = [&](int t) { return load_chunk(vp + t * vtile, voff, Lk - t * kBN, tid); };
+
+    // Prologue: K tiles 0 and 1 into LDS, scores of tile 0; K(2) and V(0)
+    // wait in registers for stage 0.
+    uint4 nk = load_k(0);
+    uint4 nv = n_tiles > 1 ? load_k(1) : make_uint4(0, 0, 0, 0);
+    bf16x8 qf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        if (i < a.Lq) raw = *reinterpret_cast<const uint4*>(qp + (long long)i * a.sq[2] + kk * 16 + hb * 8);
+        qf[kk] = __builtin_bit_cast(bf16x8, raw);
+    }
+    store_chunk<kLdsK>(nk, kbuf, tid);
+    if (n_tiles > 1) store_chunk<kLdsK>(nv, kbuf + kTileK, tid);
+    nk = n_tiles > 2 ? load_k(2) : make_uint4(0, 0, 0, 0);
+    nv = load_v(0);
+    __syncthreads();
+    f32x16 sc[2];                 // scores of the tile whose softmax runs next
+    tile_scores(sc, kbuf, qf, l32, hb);
+    __syncthreads();              // K(0)'s buffer is refilled in stage 0
+
+    f32x16 o[2] = {};             // O^T accumulators: features [0,32) and [32,64)
+    f32x16 sn[2];                 // scores being formed for the next stage
+    u32x4 pa[4], pb[4];           // weights of two consecutive tiles (B operand)
+    float m = 0.0f;               // exponent offset (log2 units of the scaled scores)
+    float l = 0.0f;               // this lane's share of the weight sum
+
+    // Stage s reads K(s+1) and V(s-1) and fills the other buffers with K(s+2)
+    // and V(s); every wave finished with those at the last barrier.
+    auto copy_tiles = [&](int s) {
+        if (s + 2 < n_tiles) store_chunk<kLdsK>(nk, kbuf + (s & 1) * kTileK, tid);
+        if (s < n_tiles) store_chunk<kLdsV>(nv, vbuf + (s & 1) * kTileV, tid);
+        if (s + 3 < n_tiles) nk = load_k(s + 3);
+        if (s + 1 < n_tiles) nv = load_v(s + 1);
+    };
+    // Unmasked steady state: softmax(s), scores(s+1) and P.V(s-1), independent.
+    auto fast_stage = [&](int s, f32x16 (&cur)[2], f32x16 (&nxt)[2], const u32x4 (&prev)[4], u32x4 (&pcur)[4]) {
+        copy_tiles(s);
+        const bf16_t* ks = kbuf + ((s + 1) & 1) * kTileK;
+        const bf16_t* vs = vbuf + ((s + 1) & 1) * kTileV;
+        float r = weights(cur, m, c, pcur);
+        tile_scores(nxt, ks, qf, l32, hb);
+        tile_pv(o, vs, prev, hb, lane);
+        if (__any(r > kSumLimit)) [[unlikely]] {
+            asm volatile("" ::: "memory");
+            r = rescale(cur, m, c, l, o, pcur);
+        }
+        l += r;
+        __syncthreads();
+    };
+    // Pipeline edges, masked tiles and fully masked rows.
+    auto slow_stage = [&](int s, f32x16 (&cur)[2], f32x16 (&nxt)[2], const u32x4 (&prev)[4], u32x4 (&pcur)[4]) {
+        copy_tiles(s);
+        const bf16_t* ks = kbuf + ((s + 1) & 1) * kTileK;
+        const bf16_t* vs = vbuf + ((s + 1) & 1) * kTileV;
+        if (s >= 1 && s - 1 < n_w) tile_pv(o, vs, prev, hb, lane);
+        if (s < n_w) {
+            if (s >= t_mask) apply_mask(cur, key_lim, none, s * kBN, hb);
+            // The first tile sets the offset (every row has an allowed key in
+            // tile 0).
+            if (s == 0) m = tile_max(cur) * c;
+            float r = weights(cur, m, c, pcur);
+            if (s > 0 && __any(r > kSumLimit)) r = rescale(cur, m, c, l, o, pcur);
+            l += r;
+        }
+        if (s + 1 < n_w) tile_scores(nxt, ks, qf, l32, hb);
+        __syncthreads();
+    };
+
+    // Stage 0, then unmasked stages in pairs from stage 1, then the rest.
+    // Even stages keep the current scores in sc and their weights in pa, odd
+    // stages in sn and pb, so no registers are copied between stages.
+    slow_stage(0, sc, sn, pb, pa);
+    const int fast_last = 1 + 2 * max(0, (min(n_w - 1, t_mask) - 1) / 2);   // fast stages [1, fast_last)
+    int s = 1;
+    for (; s < fast_last; s += 2) {
+        fast_stage(s, sn, sc, pa, pb);
+        fast_stage(s + 1, sc, sn, pb, pa);
+    }
+    for (; s <= n_tiles; s += 2) {
+        slow_stage(s, sn, sc, pa, pb);
+        if (s + 1 > n_tiles) break;
+        slow_stage(s + 1, sc, sn, pb, pa);
+    }
+
+    if (i >= a.Lq) return;
+    const float inv = 1.0f / pair_sum(l);
+    // O^T element v of block tb: feature tb*32 + (v/4)*8 + hb*4 + v%4, query i.
+    char* ob = static_cast<char*>(a.o);
+    const long long orow = b * a.so[0] + hd * a.so[1] + (long long)i * a.so[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int tt = tb * 32 + g4 * 8 + hb * 4;
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = o[tb][g4 * 4 + e] * inv;
+            if (kOutF32) {
+                *reinterpret_cast<float4*>(ob + (orow + tt) * 4) = make_float4(y[0], y[1], y[2], y[3]);
+            } else {
+                *reinterpret_cast<uint2*>(ob + (orow + tt) * 2) =
+                    make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+            }
+        }
+    }
+}
+
+template <bool kCausal, bool kHasVl, bool kOutF32>
+hipError_t launch_variant(const SdpaArgs& a, hipStream_t s) {
+    const int n_qtiles = (a.Lq + kBM - 1) / kBM;
+    const long long grid = (long long)n_qtiles * a.B * a.H;
+    const float c = kLog2e / 8.0f;   // log2(e) / sqrt(64)
+    hipLaunchKernelGGL((sdpa_fwd_bf16_pipe<kCausal, kHasVl, kOutF32>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                       a, n_qtiles, c);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sdpa_bf16_pipe(const SdpaArgs& a, bool out_f32, hipStream_t s) {
+    const bool c = a.causal != 0, v = a.valid_lens != nullptr;
+    if (out_f32) {
+        if (c) return v ? launch_variant<true, true, true>(a, s) : launch_variant<true, false, true>(a, s);
+        return v ? launch_variant<false, true, true>(a, s) : launch_variant<false, false, true>(a, s);
+    }
+    if (c) return v ? launch_variant<true, true, false>(a, s) : launch_variant<true, false, false>(a, s);
+    return v ? launch_variant<false, true, false>(a, s) : launch_variant<false, false, false>(a, s);
+}
+
+}  // namespace mha
