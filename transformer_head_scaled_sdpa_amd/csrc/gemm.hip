@@ -7,12 +7,29 @@
 // Up to three problems sharing N and K run in one launch; the fused Q/K/V
 // projection of self-attention is three problems over the same A.
 //
-// bf16 kernel: 128 x 128 output tile per workgroup, K in steps of 64, four
-// wave64s in a 2 x 2 grid each owning 64 x 64 = 2 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  Both operands are
-// K-contiguous in memory, so they are copied to LDS with 16-byte coalesced
-// loads and read back as 16-byte MFMA fragments; the next K step is fetched
-// into registers while the current one is multiplied.
+// bf16 kernel: 128 x BN output tile per workgroup (BN = 128, or 64 when
+// 128-wide tiles would leave CUs without a tile), four wave64s in a 2 x 2 grid each
+// owning 64 x BN/2 through v_mfma_f32_32x32x16_bf16 with fp32 accumulators;
+// K in steps of 64.
+//  * Operand tiles go from global memory straight into LDS
+//    (global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS, lane
+//    i at byte 16*i, so the per-lane source address decides the layout) in
+//    144-byte rows, the stride at which the 16-byte fragment reads are
+//    conflict-free; two LDS stages, one barrier per K step, the next step's
+//    loads in flight during the current step's MFMAs; two workgroups per CU.
+//  * The MFMA computes the transposed block C^T = W A^T, so each lane ends up
+//    owning one output row and runs of four consecutive columns; the
+//    epilogue stages the fp32 tile in LDS with 16-byte writes and stores
+//    whole output rows with 16-byte coalesced stores.
+//  * Every wave keeps eight independent accumulators (its output blocks
+//    times a split of the K steps, summed at the end): an MFMA whose
+//    accumulator was written fewer than eight MFMAs earlier issues slower.
+//  * Bias is added in the epilogue; bf16 outputs optionally get a second
+//    plane with the rounding residue x - bf16(x), rounded to bf16.
+//
+// Workgroups are mapped XCD-aware: the hardware deals workgroup ids to the
+// eight XCDs round-robin, so consecutive logical tiles (those sharing rows
+// of A) are given to ids on the same XCD and share its L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,122 +37,218 @@ namespace mha {
 
 namespace {
 
-constexpr int kTM = 128, kTN = 128, kTK = 64;
-constexpr int kLds = kTK + 8;     // bf16 per LDS row (144 B)
+constexpr int kTM = 128, kTK = 64;
+constexpr int kLds = kTK + 8;                  // bf16 per LDS row (144 B)
+constexpr int kRowBytes = kLds * 2;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
 
 struct TileMap {
     int prob, tm, tn;
 };
 
-__device__ __forceinline__ TileMap map_tile(const GemmArgs& g, int id, int tiles_n) {
-    TileMap t{0, 0, 0};
+// Logical tile t -> (problem, row tile, column tile).  When every problem
+// reads the same A (the self-attention Q/K/V projection), tiles of one row
+// block are consecutive across problems; otherwise problems are consecutive.
+__device__ __forceinline__ TileMap map_tile(const GemmArgs& g, int t, int tiles_n, bool shared_a) {
+    TileMap r{-1, 0, 0};
+    if (shared_a) {
+        const int per_row = g.nprob * tiles_n;
+        r.tm = t / per_row;
+        const int rem = t % per_row;
+        r.prob = rem / tiles_n;
+        r.tn = rem % tiles_n;
+        if (r.tm * kTM >= g.p[0].M) r.prob = -1;
+        return r;
+    }
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
         if (p >= g.nprob) break;
         const int tiles = ((g.p[p].M + kTM - 1) / kTM) * tiles_n;
-        if (id < tiles) {
-            t.prob = p;
-            t.tm = id / tiles_n;
-            t.tn = id % tiles_n;
-            return t;
+        if (t < tiles) {
+            r.prob = p;
+            r.tm = t / tiles_n;
+            r.tn = t % tiles_n;
+            return r;
         }
-        id -= tiles;
+        t -= tiles;
     }
-    t.prob = -1;
-    return t;
+    return r;
 }
 
-template <bool kOutF32>
-__global__ __launch_bounds__(256) void gemm_bf16_nt(GemmArgs g, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) bf16_t as[kTM * kLds];
-    __shared__ __attribute__((aligned(16))) bf16_t ws[kTN * kLds];
+// Per-lane element offsets of the direct-to-LDS loads of one operand tile of
+// `rows` rows: wave load i = wave + 4j fills LDS bytes [1024 i, 1024 i + 1024),
+// lane -> row x / 144, 16-byte chunk (x % 144) / 16 of that row.  Chunk 8 is
+// row padding and re-reads chunk 0; rows past `limit` re-read the last row
+// (never stored).
+template <int kRows>
+struct TileLoads {
+    static constexpr int kLoads = kRows * kRowBytes / 1024;
+    static constexpr int kPerWave = (kLoads + 3) / 4;
+    uint32_t off[kPerWave];
+    __device__ __forceinline__ void init(int wave, int lane, int r0, int limit, int K) {
+#pragma unroll
+        for (int j = 0; j < kPerWave; ++j) {
+            const int x = (wave + 4 * j) * 1024 + lane * 16;
+            const int r = x / kRowBytes;
+            int c = (x % kRowBytes) / 16;
+            if (c == 8) c = 0;
+            off[j] = (uint32_t)(min(r0 + r, limit - 1) * K + c * 8);
+        }
+    }
+    __device__ __forceinline__ void issue(const bf16_t* src, unsigned char* lds, int wave) const {
+#pragma unroll
+        for (int j = 0; j < kPerWave; ++j) {
+            const int i = wave + 4 * j;
+            if (i < kLoads)
+                __builtin_amdgcn_global_load_lds((global_cvoid*)(src + off[j]), (lds_void*)(lds + i * 1024), 16, 0, 0);
+        }
+    }
+};
 
-    const TileMap tmap = map_tile(g, blockIdx.x, tiles_n);
+template <int kTN, bool kOutF32>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, int tiles_total, int per_xcd,
+                                                       int shared_a) {
+    constexpr int kABytes = kTM * kRowBytes, kWBytes = kTN * kRowBytes;
+    constexpr int kStage = kABytes + kWBytes;
+    constexpr int kNB = kTN / 64;                  // 32-wide column blocks per wave (2 or 1)
+    constexpr int kSplit = 4 / kNB;                // K-step split: 2 x kNB x kSplit = 8 accumulators
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
+
+    // XCD-aware order: ids x, x+8, x+16, ... run on XCD x; give them a
+    // contiguous range of logical tiles.
+    const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (t >= tiles_total) return;
+    const TileMap tmap = map_tile(g, t, tiles_n, shared_a != 0);
     if (tmap.prob < 0) return;
     const GemmProblem& P = g.p[tmap.prob];
     const int M = P.M, N = g.N, K = g.K;
     const int m0 = tmap.tm * kTM, n0 = tmap.tn * kTN;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hb = lane >> 5, l32 = lane & 31;
     const int wm = wave >> 1, wn = wave & 1;
 
     const bf16_t* A = static_cast<const bf16_t*>(P.a);
     const bf16_t* W = static_cast<const bf16_t*>(P.w);
-
-    // 128 rows x 64 columns = 1024 16-byte chunks per operand: 4 per thread.
-    uint4 pa[4], pw[4];
-    auto fetch = [&](int k0) {
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int c = tid + n * 256;
-            const int r = c >> 3, col = (c & 7) * 8;
-            pa[n] = (m0 + r < M) ? *reinterpret_cast<const uint4*>(A + (long long)(m0 + r) * K + k0 + col)
-                                 : make_uint4(0, 0, 0, 0);
-            pw[n] = (n0 + r < N) ? *reinterpret_cast<const uint4*>(W + (long long)(n0 + r) * K + k0 + col)
-                                 : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto stash = [&]() {
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int c = tid + n * 256;
-            const int r = c >> 3, col = (c & 7) * 8;
-            *reinterpret_cast<uint4*>(as + r * kLds + col) = pa[n];
-            *reinterpret_cast<uint4*>(ws + r * kLds + col) = pw[n];
-        }
+    TileLoads<kTM> la;
+    TileLoads<kTN> lw;
+    la.init(wave, lane, m0, M, K);
+    lw.init(wave, lane, n0, N, K);
+    auto issue = [&](int stage, int k0) {
+        unsigned char* base = smem + stage * kStage;
+        la.issue(A + k0, base, wave);
+        lw.issue(W + k0, base + kABytes, wave);
     };
 
-    f32x16 acc[2][2] = {};
-    fetch(0);
-    for (int k0 = 0; k0 < K; k0 += kTK) {
+    // acc[mi][ni][p]: A rows wm*64 + mi*32 .., W rows wn*kTN/2 + ni*32 .., K split p.
+    f32x16 acc[2][kNB][kSplit] = {};
+    const int nk = K / kTK;
+    issue(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        // This wave's loads of step kt have landed; after the barrier every
+        // wave's have, and every wave is done reading the other stage.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        stash();
-        __syncthreads();
-        if (k0 + kTK < K) fetch(k0 + kTK);
+        if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * kTK);
+        const bf16_t* as = reinterpret_cast<const bf16_t*>(smem + (kt & 1) * kStage);
+        const bf16_t* ws = reinterpret_cast<const bf16_t*>(smem + (kt & 1) * kStage + kABytes);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            bf16x8 fa[2], fw[2];
+            bf16x8 fa[2], fw[kNB];
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
+            for (int x = 0; x < 2; ++x)
                 fa[x] = *reinterpret_cast<const bf16x8*>(as + (wm * 64 + x * 32 + l32) * kLds + kk * 16 + hb * 8);
-                fw[x] = *reinterpret_cast<const bf16x8*>(ws + (wn * 64 + x * 32 + l32) * kLds + kk * 16 + hb * 8);
-            }
+#pragma unroll
+            for (int x = 0; x < kNB; ++x)
+                fw[x] = *reinterpret_cast<const bf16x8*>(ws + (wn * (kTN / 2) + x * 32 + l32) * kLds + kk * 16 + hb * 8);
+            const int p = kk % kSplit;
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma32x32x16(fa[mi], fw[ni], acc[mi][ni]);
+                for (int ni = 0; ni < kNB; ++ni) acc[mi][ni][p] = mfma32x32x16(fw[ni], fa[mi], acc[mi][ni][p]);
         }
     }
 
-    // Epilogue: element v of block (mi, ni) is row (v/4)*8 + hb*4 + v%4, column l32.
+    // Epilogue.  Block (mi, ni) element v is output row wm*64 + mi*32 + l32,
+    // column wn*kTN/2 + ni*32 + (v/4)*8 + hb*4 + v%4 of the tile: stage the
+    // fp32 tile in LDS four columns at a time, then write whole rows with
+    // 16-byte stores.
+    constexpr int kPitch = kTN + 4;                // fp32 per staged row
+    __syncthreads();
+    float* st = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < kNB; ++ni) {
+            f32x16 y = acc[mi][ni][0];
+#pragma unroll
+            for (int p = 1; p < kSplit; ++p) y += acc[mi][ni][p];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+                *reinterpret_cast<float4*>(st + (wm * 64 + mi * 32 + l32) * kPitch + wn * (kTN / 2) + ni * 32 +
+                                           g4 * 8 + hb * 4) =
+                    make_float4(y[g4 * 4], y[g4 * 4 + 1], y[g4 * 4 + 2], y[g4 * 4 + 3]);
+        }
+    __syncthreads();
     const bf16_t* bias = static_cast<const bf16_t*>(P.bias);
+    constexpr int kChunks = kTN / 8;               // 8-column chunks per row
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-        const int n = n0 + wn * 64 + ni * 32 + l32;
-        if (n >= N) continue;
-        const float bn = bias ? bf16_to_f32(bias[n]) : 0.0f;
+    for (int j = 0; j < kTM * kChunks / 256; ++j) {
+        const int q = tid + 256 * j;
+        const int r = q / kChunks, c8 = (q % kChunks) * 8;
+        const int m = m0 + r, n = n0 + c8;
+        if (m >= M || n >= N) continue;
+        const float4 lo4 = *reinterpret_cast<const float4*>(st + r * kPitch + c8);
+        const float4 hi4 = *reinterpret_cast<const float4*>(st + r * kPitch + c8 + 4);
+        float y[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+        if (bias) {
+            const uint4 braw = *reinterpret_cast<const uint4*>(bias + n);
+            const uint32_t bw[4] = {braw.x, braw.y, braw.z, braw.w};
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = m0 + wm * 64 + mi * 32 + (v >> 2) * 8 + hb * 4 + (v & 3);
-                if (m >= M) continue;
-                const float x = acc[mi][ni][v] + bn;
-                if (kOutF32) {
-                    static_cast<float*>(P.c)[(long long)m * N + n] = x;
-                } else {
-                    const __bf16 hi = static_cast<__bf16>(x);
-                    static_cast<bf16_t*>(P.c)[(long long)m * N + n] = __builtin_bit_cast(bf16_t, hi);
-                    if (P.c_lo) {
-                        // x - hi is exact in fp32; its bf16 rounding keeps 8 more bits.
-                        const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
-                        static_cast<bf16_t*>(P.c_lo)[(long long)m * N + n] = __builtin_bit_cast(bf16_t, lo);
-                    }
-                }
+            for (int e = 0; e < 4; ++e) {
+                y[2 * e] += __uint_as_float(bw[e] << 16);
+                y[2 * e + 1] += __uint_as_float(bw[e] & 0xffff0000u);
             }
         }
+        const long long o = (long long)m * N + n;
+        if (kOutF32) {
+            float* C = static_cast<float*>(P.c) + o;
+            *reinterpret_cast<float4*>(C) = make_float4(y[0], y[1], y[2], y[3]);
+            *reinterpret_cast<float4*>(C + 4) = make_float4(y[4], y[5], y[6], y[7]);
+        } else {
+            uint32_t h[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
+                // x - bf16(x) is exact in fp32; its bf16 rounding keeps 8 more bits.
+                lo[e] = pack_bf16x2(y[2 * e] - __uint_as_float(h[e] << 16),
+                                    y[2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u));
+            }
+            *reinterpret_cast<uint4*>(static_cast<bf16_t*>(P.c) + o) = make_uint4(h[0], h[1], h[2], h[3]);
+            if (P.c_lo)
+                *reinterpret_cast<uint4*>(static_cast<bf16_t*>(P.c_lo) + o) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        }
     }
+}
+
+template <int kTN>
+hipError_t launch_bf16(const GemmArgs& g, bool out_f32, hipStream_t s, bool shared_a) {
+    const int tiles_n = (g.N + kTN - 1) / kTN;
+    long long tiles = 0;
+    for (int p = 0; p < g.nprob; ++p) tiles += (long long)((g.p[p].M + kTM - 1) / kTM) * tiles_n;
+    if (tiles == 0) return hipSuccess;
+    const int per_xcd = (int)((tiles + 7) / 8);
+    const dim3 grid(8u * per_xcd);
+    if (out_f32)
+        hipLaunchKernelGGL((gemm_bf16_nt<kTN, true>), grid, dim3(256), 0, s, g, tiles_n, (int)tiles, per_xcd,
+                           (int)shared_a);
+    else
+        hipLaunchKernelGGL((gemm_bf16_nt<kTN, false>), grid, dim3(256), 0, s, g, tiles_n, (int)tiles, per_xcd,
+                           (int)shared_a);
+    return hipGetLastError();
 }
 
 // fp32: 64 x 64 tile, K in steps of 16, each of 256 threads owns 4 x 4 outputs.
@@ -205,13 +318,16 @@ __global__ __launch_bounds__(256) void gemm_f32_nt(GemmArgs g, int tiles_n) {
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, bool out_f32, hipStream_t s) {
-    const int tiles_n = (g.N + kTN - 1) / kTN;
-    long long tiles = 0;
-    for (int p = 0; p < g.nprob; ++p) tiles += (long long)((g.p[p].M + kTM - 1) / kTM) * tiles_n;
-    if (tiles == 0) return hipSuccess;
-    if (out_f32) hipLaunchKernelGGL(gemm_bf16_nt<true>, dim3((unsigned)tiles), dim3(256), 0, s, g, tiles_n);
-    else hipLaunchKernelGGL(gemm_bf16_nt<false>, dim3((unsigned)tiles), dim3(256), 0, s, g, tiles_n);
-    return hipGetLastError();
+    // K must be a multiple of the 64-wide K step and N of the 64-wide column
+    // block (both hold for d_model = h * 64).
+    if (g.K % kTK != 0 || g.N % 64 != 0) return hipErrorInvalidValue;
+    bool shared_a = true;
+    for (int p = 1; p < g.nprob; ++p) shared_a = shared_a && g.p[p].a == g.p[0].a && g.p[p].M == g.p[0].M;
+    // 128-wide column tiles unless that leaves CUs without a tile.
+    long long tiles128 = 0;
+    for (int p = 0; p < g.nprob; ++p) tiles128 += (long long)((g.p[p].M + kTM - 1) / kTM) * ((g.N + 127) / 128);
+    if (g.N % 128 == 0 && tiles128 >= 256) return launch_bf16<128>(g, out_f32, s, shared_a);
+    return launch_bf16<64>(g, out_f32, s, shared_a);
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s) {
