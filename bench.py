@@ -69,6 +69,20 @@ def gemm_alg(M, N, K, nprob, in_bytes, out_bytes):
     return 2 * M * N * K * nprob, nprob * ((M * K + N * K + N) * in_bytes + M * N * out_bytes)
 
 
+def fused_alg(w, valid_lens, in_bytes):
+    """Algorithmic flops and HBM bytes of the kernel that projects Q, K, V and
+    attends (merged-head output in the input dtype).  K and V are needed only
+    for keys below each batch's valid length; every query row is projected."""
+    D = w.d_model
+    vl = np.full(w.B, w.Lk) if valid_lens is None else np.asarray(valid_lens, dtype=np.int64)
+    kv_rows = sum(w.Lk if v <= 0 else min(int(v), w.Lk) for v in vl)
+    f_attn, _ = sdpa_alg(w, valid_lens, in_bytes, in_bytes)
+    flops = 2 * w.B * w.Lq * D * D + 2 * 2 * kv_rows * D * D + f_attn
+    x_bytes = w.B * w.Lq * D * in_bytes + (0 if w.self_attn else w.B * w.Lk * D * in_bytes)
+    byts = x_bytes + 3 * (D * D + D) * in_bytes + w.B * w.Lq * D * in_bytes
+    return flops, byts
+
+
 def roofline(flops, byts, ms, mfma_peak):
     t_mfma = flops / (mfma_peak * 1e12)
     t_hbm = byts / (PEAK_HBM_GBS * 1e9)
@@ -197,9 +211,9 @@ def copy_calibration():
 # ---------------------------------------------------------------------------
 CSRC = os.path.join(ROOT, "transformer_head_scaled_sdpa_amd", "csrc")
 KERNEL_SOURCES = {
-    "qkv_proj_bf16": ["gemm.hip", "common.h", "kernels.h"],
-    "out_proj_bf16": ["gemm.hip", "common.h", "kernels.h"],
-    "sdpa_bf16": ["sdpa_bf16.hip", "sdpa_bf16_pipe.hip", "common.h", "kernels.h"],
+    "attn_fused_bf16": ["mha_fused.hip", "lds_tile.h", "common.h", "kernels.h"],
+    "out_proj_bf16": ["gemm.hip", "lds_tile.h", "common.h", "kernels.h"],
+    "sdpa_bf16": ["sdpa_bf16_pipe.hip", "common.h", "kernels.h"],
 }
 
 
@@ -309,7 +323,9 @@ def main():
     kernels = {}
     M_q, M_kv = w.B * w.Lq, w.B * w.Lk
     for name, kms in kt.items():
-        if name.startswith("qkv_proj"):
+        if name.startswith("attn_fused"):
+            f, b = fused_alg(w, inp.valid_lens, in_b)
+        elif name.startswith("qkv_proj"):
             f, b = gemm_alg(M_q, w.d_model, w.d_model, 1, in_b, in_b)
             f2, b2 = gemm_alg(M_kv, w.d_model, w.d_model, 2, in_b, in_b)
             f, b = f + f2, b + b2

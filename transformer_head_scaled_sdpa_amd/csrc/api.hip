@@ -112,7 +112,6 @@ mha_status sdpa_forward(mha_dtype in_dt, mha_dtype out_dt,
 
     mha::SdpaArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o;
-    a.q_lo = nullptr; a.k_lo = nullptr;
     a.sq[0] = sq.b; a.sq[1] = sq.h; a.sq[2] = sq.l;
     a.sk[0] = sk.b; a.sk[1] = sk.h; a.sk[2] = sk.l;
     a.sv[0] = sv.b; a.sv[1] = sv.h; a.sv[2] = sv.l;
@@ -130,8 +129,9 @@ size_t mha_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, 
     const size_t es = elem_size(in_dt);
     const size_t q = round_up((size_t)B * Lq * d_model * es, 256);
     const size_t kv = round_up((size_t)B * Lk * d_model * es, 256);
-    // fp32: Q, K, V, merged heads.  bf16: Q and K as hi + lo planes as well.
-    return in_dt == MHA_BF16 ? 3 * q + 3 * kv : 2 * q + 2 * kv;
+    // fp32: Q, K, V, merged heads.  bf16: the merged heads only (the
+    // projections are fused into the attention kernel).
+    return in_dt == MHA_BF16 ? q : 2 * q + 2 * kv;
 }
 
 mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
@@ -183,56 +183,63 @@ mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
         if (overlap(rout, rb) || overlap(rws, rb)) return MHA_EINVAL;
     }
 
-    // Workspace: Q [B*Lq, D], K [B*Lk, D], V [B*Lk, D], merged heads [B*Lq, D]
-    // and, for bf16, the low planes of Q and K.
-    char* w = static_cast<char*>(workspace);
-    const size_t qbytes = round_up((size_t)B * Lq * d_model * ie, 256);
-    const size_t kvbytes = round_up((size_t)B * Lk * d_model * ie, 256);
-    const bool bf16 = in_dt == MHA_BF16;
-    void* Q = w;
-    void* K = w + qbytes;
-    void* V = w + qbytes + kvbytes;
-    void* Ocat = w + qbytes + 2 * kvbytes;
-    void* Qlo = bf16 ? w + 2 * qbytes + 2 * kvbytes : nullptr;
-    void* Klo = bf16 ? w + 3 * qbytes + 2 * kvbytes : nullptr;
-
     hipStream_t s = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(workspace);
+    const bool bf16 = in_dt == MHA_BF16;
+    void* Ocat = w;
+    hipError_t e;
+    if (bf16) {
+        // 1-2. Q/K/V projections, head split, attention and head merge in one
+        // kernel: the merged heads [B*Lq, D] land in the workspace.
+        mha::FusedArgs f;
+        f.x_q = x_q; f.x_kv = x_kv;
+        f.w_q = w_q; f.w_k = w_k; f.w_v = w_v;
+        f.b_q = b_q; f.b_k = b_k; f.b_v = b_v;
+        f.o = Ocat;
+        f.B = B; f.H = h; f.Lq = Lq; f.Lk = Lk; f.D = d_model;
+        f.valid_lens = valid_lens;
+        f.causal = causal ? 1 : 0;
+        e = timed("attn_fused_bf16", s, [&] { return mha::launch_mha_attn_fused(f, s); });
+        if (e != hipSuccess) return MHA_EHIP;
+    } else {
+        // Workspace: merged heads [B*Lq, D], Q [B*Lq, D], K [B*Lk, D], V [B*Lk, D].
+        const size_t qbytes = round_up((size_t)B * Lq * d_model * ie, 256);
+        const size_t kvbytes = round_up((size_t)B * Lk * d_model * ie, 256);
+        void* Q = w + qbytes;
+        void* K = w + 2 * qbytes;
+        void* V = w + 2 * qbytes + kvbytes;
 
-    // 1. Q/K/V projections in one launch (three problems).
-    mha::GemmArgs g;
-    g.nprob = 3;
-    g.N = d_model;
-    g.K = d_model;
-    g.p[0] = {x_q, w_q, b_q, Q, B * Lq, Qlo};
-    g.p[1] = {x_kv, w_k, b_k, K, B * Lk, Klo};
-    g.p[2] = {x_kv, w_v, b_v, V, B * Lk, nullptr};
-    hipError_t e = timed(bf16 ? "qkv_proj_bf16" : "qkv_proj_f32", s, [&] {
-        return bf16 ? mha::launch_gemm_bf16(g, false, s) : mha::launch_gemm_f32(g, s);
-    });
-    if (e != hipSuccess) return MHA_EHIP;
+        // 1. Q/K/V projections in one launch (three problems).
+        mha::GemmArgs g;
+        g.nprob = 3;
+        g.N = d_model;
+        g.K = d_model;
+        g.p[0] = {x_q, w_q, b_q, Q, B * Lq};
+        g.p[1] = {x_kv, w_k, b_k, K, B * Lk};
+        g.p[2] = {x_kv, w_v, b_v, V, B * Lk};
+        e = timed("qkv_proj_f32", s, [&] { return mha::launch_gemm_f32(g, s); });
+        if (e != hipSuccess) return MHA_EHIP;
 
-    // 2. Attention per head: [B*L, D] row-major viewed as [B, L, h, d_k].
-    mha::SdpaArgs a;
-    a.q = Q; a.k = K; a.v = V; a.o = Ocat;
-    a.q_lo = Qlo; a.k_lo = Klo;
-    a.sq[0] = (long long)Lq * d_model; a.sq[1] = d_k; a.sq[2] = d_model;
-    a.sk[0] = (long long)Lk * d_model; a.sk[1] = d_k; a.sk[2] = d_model;
-    a.sv[0] = (long long)Lk * d_model; a.sv[1] = d_k; a.sv[2] = d_model;
-    a.so[0] = (long long)Lq * d_model; a.so[1] = d_k; a.so[2] = d_model;
-    a.B = B; a.H = h; a.Lq = Lq; a.Lk = Lk;
-    a.valid_lens = valid_lens;
-    a.causal = causal ? 1 : 0;
-    e = timed(bf16 ? "sdpa_bf16" : "sdpa_f32", s, [&] {
-        return bf16 ? mha::launch_sdpa_bf16(a, false, s) : mha::launch_sdpa_f32(a, s);
-    });
-    if (e != hipSuccess) return MHA_EHIP;
+        // 2. Attention per head: [B*L, D] row-major viewed as [B, L, h, d_k].
+        mha::SdpaArgs a;
+        a.q = Q; a.k = K; a.v = V; a.o = Ocat;
+            a.sq[0] = (long long)Lq * d_model; a.sq[1] = d_k; a.sq[2] = d_model;
+        a.sk[0] = (long long)Lk * d_model; a.sk[1] = d_k; a.sk[2] = d_model;
+        a.sv[0] = (long long)Lk * d_model; a.sv[1] = d_k; a.sv[2] = d_model;
+        a.so[0] = (long long)Lq * d_model; a.so[1] = d_k; a.so[2] = d_model;
+        a.B = B; a.H = h; a.Lq = Lq; a.Lk = Lk;
+        a.valid_lens = valid_lens;
+        a.causal = causal ? 1 : 0;
+        e = timed("sdpa_f32", s, [&] { return mha::launch_sdpa_f32(a, s); });
+        if (e != hipSuccess) return MHA_EHIP;
+    }
 
     // 3. Output projection of the merged heads.
     mha::GemmArgs go;
     go.nprob = 1;
     go.N = d_model;
     go.K = d_model;
-    go.p[0] = {Ocat, w_o, b_o, out, B * Lq, nullptr};
+    go.p[0] = {Ocat, w_o, b_o, out, B * Lq};
     e = timed(bf16 ? "out_proj_bf16" : "out_proj_f32", s, [&] {
         return bf16 ? mha::launch_gemm_bf16(go, out_dt == MHA_F32, s) : mha::launch_gemm_f32(go, s);
     });

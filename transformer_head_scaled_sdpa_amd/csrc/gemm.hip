@@ -24,25 +24,22 @@
 //  * Every wave keeps eight independent accumulators (its output blocks
 //    times a split of the K steps, summed at the end): an MFMA whose
 //    accumulator was written fewer than eight MFMAs earlier issues slower.
-//  * Bias is added in the epilogue; bf16 outputs optionally get a second
-//    plane with the rounding residue x - bf16(x), rounded to bf16.
+//  * Bias is added in the epilogue.
 //
 // Workgroups are mapped XCD-aware: the hardware deals workgroup ids to the
 // eight XCDs round-robin, so consecutive logical tiles (those sharing rows
 // of A) are given to ids on the same XCD and share its L2.
 #include "common.h"
 #include "kernels.h"
+#include "lds_tile.h"
 
 namespace mha {
 
 namespace {
 
 constexpr int kTM = 128, kTK = 64;
-constexpr int kLds = kTK + 8;                  // bf16 per LDS row (144 B)
-constexpr int kRowBytes = kLds * 2;
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void global_cvoid;
+constexpr int kLds = kTileLdsRow;              // bf16 per LDS row (144 B)
+constexpr int kRowBytes = kTileRowBytes;
 
 struct TileMap {
     int prob, tm, tn;
@@ -77,36 +74,6 @@ __device__ __forceinline__ TileMap map_tile(const GemmArgs& g, int t, int tiles_
     return r;
 }
 
-// Per-lane element offsets of the direct-to-LDS loads of one operand tile of
-// `rows` rows: wave load i = wave + 4j fills LDS bytes [1024 i, 1024 i + 1024),
-// lane -> row x / 144, 16-byte chunk (x % 144) / 16 of that row.  Chunk 8 is
-// row padding and re-reads chunk 0; rows past `limit` re-read the last row
-// (never stored).
-template <int kRows>
-struct TileLoads {
-    static constexpr int kLoads = kRows * kRowBytes / 1024;
-    static constexpr int kPerWave = (kLoads + 3) / 4;
-    uint32_t off[kPerWave];
-    __device__ __forceinline__ void init(int wave, int lane, int r0, int limit, int K) {
-#pragma unroll
-        for (int j = 0; j < kPerWave; ++j) {
-            const int x = (wave + 4 * j) * 1024 + lane * 16;
-            const int r = x / kRowBytes;
-            int c = (x % kRowBytes) / 16;
-            if (c == 8) c = 0;
-            off[j] = (uint32_t)(min(r0 + r, limit - 1) * K + c * 8);
-        }
-    }
-    __device__ __forceinline__ void issue(const bf16_t* src, unsigned char* lds, int wave) const {
-#pragma unroll
-        for (int j = 0; j < kPerWave; ++j) {
-            const int i = wave + 4 * j;
-            if (i < kLoads)
-                __builtin_amdgcn_global_load_lds((global_cvoid*)(src + off[j]), (lds_void*)(lds + i * 1024), 16, 0, 0);
-        }
-    }
-};
-
 template <int kTN, bool kOutF32>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, int tiles_total, int per_xcd,
                                                        int shared_a) {
@@ -133,8 +100,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, 
 
     const bf16_t* A = static_cast<const bf16_t*>(P.a);
     const bf16_t* W = static_cast<const bf16_t*>(P.w);
-    TileLoads<kTM> la;
-    TileLoads<kTN> lw;
+    LdsTileLoader<kTM, 4> la;
+    LdsTileLoader<kTN, 4> lw;
     la.init(wave, lane, m0, M, K);
     lw.init(wave, lane, n0, N, K);
     auto issue = [&](int stage, int k0) {
@@ -219,17 +186,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, 
             *reinterpret_cast<float4*>(C) = make_float4(y[0], y[1], y[2], y[3]);
             *reinterpret_cast<float4*>(C + 4) = make_float4(y[4], y[5], y[6], y[7]);
         } else {
-            uint32_t h[4], lo[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                h[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
-                // x - bf16(x) is exact in fp32; its bf16 rounding keeps 8 more bits.
-                lo[e] = pack_bf16x2(y[2 * e] - __uint_as_float(h[e] << 16),
-                                    y[2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u));
-            }
-            *reinterpret_cast<uint4*>(static_cast<bf16_t*>(P.c) + o) = make_uint4(h[0], h[1], h[2], h[3]);
-            if (P.c_lo)
-                *reinterpret_cast<uint4*>(static_cast<bf16_t*>(P.c_lo) + o) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            *reinterpret_cast<uint4*>(static_cast<bf16_t*>(P.c) + o) =
+                make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                           pack_bf16x2(y[6], y[7]));
         }
     }
 }

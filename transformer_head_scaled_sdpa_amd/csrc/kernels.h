@@ -12,11 +12,6 @@ struct SdpaArgs {
     const void* k;
     const void* v;
     void* o;
-    // bf16 only: low parts of a hi + lo split of Q and K (same strides as q
-    // and k), or nullptr.  With them the scores are formed as
-    // Kh Qh^T + Kl Qh^T + Kh Ql^T, which keeps ~16 significant bits per operand.
-    const void* q_lo;
-    const void* k_lo;
     long long sq[3], sk[3], sv[3], so[3];
     int B, H, Lq, Lk;
     const int* valid_lens;  // device int32 [B] or nullptr
@@ -24,15 +19,13 @@ struct SdpaArgs {
 };
 
 // C[m, n] = sum_k A[m, k] * W[n, k] + bias[n] for up to three problems that
-// share N and K (the fused Q/K/V projection is three problems in one launch).
+// share N and K (the fp32 Q/K/V projection is three problems in one launch).
 struct GemmProblem {
     const void* a;     // [M, K] row-major
     const void* w;     // [N, K] row-major (a linear layer's [out, in])
     const void* bias;  // [N] or nullptr
     void* c;           // [M, N] row-major
     int M;
-    void* c_lo;        // bf16 output only: [M, N] plane of c's rounding residue
-                       // (x - bf16(x), rounded to bf16), or nullptr
 };
 
 struct GemmArgs {
@@ -42,9 +35,25 @@ struct GemmArgs {
     int K;
 };
 
+// Multi-head attention with the Q/K/V projections fused in (bf16, d_k = 64):
+// writes the merged-head attention output; the output projection follows.
+struct FusedArgs {
+    const void* x_q;   // [B, Lq, D] bf16
+    const void* x_kv;  // [B, Lk, D] bf16 (may equal x_q)
+    const void* w_q;   // [D, D] bf16, [out, in]
+    const void* w_k;
+    const void* w_v;
+    const void* b_q;   // [D] bf16 or nullptr
+    const void* b_k;
+    const void* b_v;
+    void* o;           // [B, Lq, D] bf16: head h in columns h*64 .. h*64+63
+    int B, H, Lq, Lk, D;
+    const int* valid_lens;  // device int32 [B] or nullptr
+    int causal;
+};
+
 hipError_t launch_sdpa_bf16(const SdpaArgs& a, bool out_f32, hipStream_t s);
-// Single-operand bf16 attention, software-pipelined, 32 queries per wave.
-hipError_t launch_sdpa_bf16_pipe(const SdpaArgs& a, bool out_f32, hipStream_t s);
+hipError_t launch_mha_attn_fused(const FusedArgs& a, hipStream_t s);
 hipError_t launch_sdpa_f32(const SdpaArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool out_f32, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);

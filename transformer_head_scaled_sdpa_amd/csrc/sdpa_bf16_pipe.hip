@@ -352,7 +352,7 @@ hipError_t launch_variant(const SdpaArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_sdpa_bf16_pipe(const SdpaArgs& a, bool out_f32, hipStream_t s) {
+hipError_t launch_sdpa_bf16(const SdpaArgs& a, bool out_f32, hipStream_t s) {
     const bool c = a.causal != 0, v = a.valid_lens != nullptr;
     if (out_f32) {
         if (c) return v ? launch_variant<true, true, true>(a, s) : launch_variant<true, false, true>(a, s);
