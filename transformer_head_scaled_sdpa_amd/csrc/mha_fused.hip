@@ -144,13 +144,27 @@ __global__ __launch_bounds__(kThreads, 1) void mha_attn_fused_bf16(FusedArgs a, 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hb = lane >> 5, l32 = lane & 31;
 
-    // Workgroup -> (query block, batch, head); (batch, head) varies fastest and
-    // causal launches issue the longest query blocks first.
-    const int BH = a.B * a.H;
-    const int bh = blockIdx.x % BH;
-    int qt = blockIdx.x / BH;
+    // Workgroup -> (query block, batch, head).  Causal launches issue the
+    // longest query blocks first.  The hardware deals workgroup ids to the
+    // eight XCDs round-robin; when B is a multiple of 8, XCD x gets the
+    // batches b = x (mod 8) with all their heads, so every head's workgroup
+    // re-reads that batch's inputs from the same L2.
+    int qt, b, hd;
+    if (a.B % 8 == 0) {
+        const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+        const int per_q = (a.B >> 3) * a.H;
+        qt = j / per_q;
+        const int rem = j % per_q;
+        b = x + 8 * (rem / a.H);
+        hd = rem % a.H;
+    } else {
+        const int BH = a.B * a.H;
+        const int bh = blockIdx.x % BH;
+        qt = blockIdx.x / BH;
+        b = bh / a.H;
+        hd = bh % a.H;
+    }
     if (kCausal) qt = n_qtiles - 1 - qt;
-    const int b = bh / a.H, hd = bh % a.H;
     const int D = a.D, Lq = a.Lq, Lk = a.Lk;
     const int nd = D / 64;
 
@@ -177,6 +191,21 @@ __global__ __launch_bounds__(kThreads, 1) void mha_attn_fused_bf16(FusedArgs a, 
     const bf16_t* bk = a.b_k ? static_cast<const bf16_t*>(a.b_k) + hd * kHd : nullptr;
     const bf16_t* bv = a.b_v ? static_cast<const bf16_t*>(a.b_v) + hd * kHd : nullptr;
 
+    // Projection loads go to stage gstep & 1, gstep counting 64-wide slices
+    // over both phases; the last slice of one phase prefetches the first slice
+    // of the next, so no phase starts on a cold load.
+    int gstep = 0;
+    LdsTileLoader<kKC, kW> lkx;       // X_kv rows of the current key chunk
+    LdsTileLoader<kHd, kW> lkw;       // W_K[h] and W_V[h] rows 0..63 each
+    lkw.init(wave, lane, 0, kHd, D);
+    lkx.init(wave, lane, 0, Lk, D);
+    auto kv_issue = [&](int stage, int d0) {
+        unsigned char* base = smem + stage * kStageBytes;
+        lkx.issue(xkv + d0, base, wave);
+        lkw.issue(wk + d0, base + kKC * kTileRowBytes, wave);
+        lkw.issue(wv + d0, base + (kKC + kHd) * kTileRowBytes, wave);
+    };
+
     // ---------------- Q projection: Q^T (64 x 256) = W_Q[h] X_q^T -------------
     bf16x8 qh[4], ql[4];
     {
@@ -192,11 +221,12 @@ __global__ __launch_bounds__(kThreads, 1) void mha_attn_fused_bf16(FusedArgs a, 
         };
         f32x16 acc[2] = {};
         issue(0, 0);
-        for (int dt = 0; dt < nd; ++dt) {
+        for (int dt = 0; dt < nd; ++dt, ++gstep) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            if (dt + 1 < nd) issue((dt + 1) & 1, (dt + 1) * 64);
-            const bf16_t* xs = reinterpret_cast<const bf16_t*>(smem + (dt & 1) * kStageBytes);
+            if (dt + 1 < nd) issue((gstep + 1) & 1, (dt + 1) * 64);
+            else kv_issue((gstep + 1) & 1, 0);
+            const bf16_t* xs = reinterpret_cast<const bf16_t*>(smem + (gstep & 1) * kStageBytes);
             const bf16_t* ws = xs + kBQ * kTileLdsRow;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
@@ -238,28 +268,20 @@ __global__ __launch_bounds__(kThreads, 1) void mha_attn_fused_bf16(FusedArgs a, 
     f32x16 bias = {};                 // -m in every element (score accumulator start)
     bool have_m = false;              // wave-uniform: the offset has been set
     float l = 0.0f;                   // this lane's share of the weight sum
-    LdsTileLoader<kKC, kW> lx;
-    LdsTileLoader<kHd, kW> lw;
-    lw.init(wave, lane, 0, kHd, D);   // W_K[h] and W_V[h] rows 0..63 each
-    __syncthreads();                  // every wave is done with the Q projection's stages
-
     for (int k0 = 0; k0 < kv_end; k0 += kKC) {
-        lx.init(wave, lane, k0, Lk, D);
-        auto issue = [&](int stage, int d0) {
-            unsigned char* base = smem + stage * kStageBytes;
-            lx.issue(xkv + d0, base, wave);
-            lw.issue(wk + d0, base + kKC * kTileRowBytes, wave);
-            lw.issue(wv + d0, base + (kKC + kHd) * kTileRowBytes, wave);
-        };
         f32x16 acc[2] = {};
-        issue(0, 0);
-        for (int dt = 0; dt < nd; ++dt) {
+        for (int dt = 0; dt < nd; ++dt, ++gstep) {
             // Also orders the previous chunk's attention (LDS reads of K, V)
             // before this chunk's K, V are written below.
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            if (dt + 1 < nd) issue((dt + 1) & 1, (dt + 1) * 64);
-            const bf16_t* xs = reinterpret_cast<const bf16_t*>(smem + (dt & 1) * kStageBytes);
+            if (dt + 1 < nd) {
+                kv_issue((gstep + 1) & 1, (dt + 1) * 64);
+            } else if (k0 + kKC < kv_end) {
+                lkx.init(wave, lane, k0 + kKC, Lk, D);
+                kv_issue((gstep + 1) & 1, 0);
+            }
+            const bf16_t* xs = reinterpret_cast<const bf16_t*>(smem + (gstep & 1) * kStageBytes);
             const bf16_t* ws = xs + kKC * kTileLdsRow;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
