@@ -156,6 +156,45 @@ class PreparedSdpa:
             raise RuntimeError(f"sdpa_forward failed with status {st}")
 
 
+class PreparedDecode:
+    """sdpa_decode on one decoding step's query and K/V caches."""
+
+    def __init__(self, inp):
+        import torch
+        from transformer_head_scaled_sdpa_amd import _lib
+        w = inp.workload
+        self.w = w
+        dev = torch.device("cuda:0")
+        self.q = torch.from_numpy(inp.tensors["q"][:, :, 0, :]).to(dev).to(torch.bfloat16)
+        self.k, self.v = (torch.from_numpy(inp.tensors[n]).to(dev).to(torch.bfloat16) for n in "kv")
+        self.o = torch.empty_like(self.q)
+        self.lens = torch.from_numpy(inp.valid_lens).to(dev)
+        self.lib = _lib.load()
+        need = int(self.lib.sdpa_decode_workspace_bytes(w.B, w.h, w.Lk))
+        self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        s3 = lambda x: _lib.Strides(x.stride(0), x.stride(1), 0)
+        s4 = lambda x: _lib.Strides(*x.stride()[:3])
+        p = lambda x: ctypes.c_void_p(x.data_ptr())
+        self.args = [_lib.MHA_BF16, _lib.MHA_BF16, p(self.q), s3(self.q), p(self.k), s4(self.k), p(self.v),
+                     s4(self.v), p(self.o), s3(self.o), w.B, w.h, w.Lk, w.d_k, w.d_k, p(self.lens), p(self.ws),
+                     need]
+        self.torch = torch
+
+    def __call__(self):
+        st = self.lib.sdpa_decode(*self.args, ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"sdpa_decode failed with status {st}")
+
+
+def decode_alg(w, lens):
+    """Algorithmic flops and HBM bytes of one decoding step: every valid cached
+    key and value is read once, the query read and the output written."""
+    n = sum(w.Lk if v <= 0 else min(int(v), w.Lk) for v in lens)
+    flops = 4 * w.d_k * w.h * n
+    byts = w.h * w.d_k * 2 * (2 * n + 2 * w.B)
+    return flops, byts
+
+
 def time_steps(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -251,9 +290,9 @@ def cpu_baseline(w, inp, budget_s=20.0):
     import oracle
     t = inp.tensors
     n_threads = oracle.num_threads()
-    if w.kind == "sdpa":
+    if w.kind in ("sdpa", "decode"):
         # sample query rows; every (batch, head) pair, all keys
-        rows = np.linspace(0, w.Lq - 1, 16).astype(np.int32)
+        rows = np.unique(np.linspace(0, w.Lq - 1, 16).astype(np.int32))
         t0 = time.perf_counter()
         oracle.sdpa(t["q"], t["k"], t["v"], valid_lens=inp.valid_lens, causal=w.causal, rows=rows)
         dt = time.perf_counter() - t0
@@ -312,7 +351,7 @@ def main():
     mfma_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     log(f"workload {w.name}: {w.description}")
 
-    fn = PreparedMha(inp) if w.kind == "mha" else PreparedSdpa(inp)
+    fn = {"mha": PreparedMha, "sdpa": PreparedSdpa, "decode": PreparedDecode}[w.kind](inp)
     ms, wall_ms = time_steps(fn, args.steps, args.warmup)
     attn_flops = w.attention_flops()
     value = attn_flops / (ms * 1e-3) / 1e12
@@ -323,7 +362,9 @@ def main():
     kernels = {}
     M_q, M_kv = w.B * w.Lq, w.B * w.Lk
     for name, kms in kt.items():
-        if name.startswith("attn_fused"):
+        if name.startswith("sdpa_decode"):
+            f, b = decode_alg(w, inp.valid_lens)
+        elif name.startswith("attn_fused"):
             f, b = fused_alg(w, inp.valid_lens, in_b)
         elif name.startswith("qkv_proj"):
             f, b = gemm_alg(M_q, w.d_model, w.d_model, 1, in_b, in_b)
@@ -376,6 +417,18 @@ def main():
             "dense_equiv_tflops": round(lw.attention_flops() / (sms * 1e-3) / 1e12, 2),
             "frac_bf16_peak_alg": round(f / (sms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del sf
+
+    if not args.no_long_sdpa and w.name != "decode_step":
+        dw = workloads.BY_NAME["decode_step"]
+        dinp = workloads.make_inputs(dw)
+        df = PreparedDecode(dinp)
+        dms, _ = time_steps(df, 200, 20)
+        f, b = decode_alg(dw, dinp.valid_lens)
+        result["decode_step"] = {
+            "workload": dw.description, "avg_us": round(dms * 1e3, 2),
+            "alg_GBs": round(b / (dms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(b / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del df
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")

@@ -97,6 +97,40 @@ mha_status sdpa_forward(mha_dtype in_dt, mha_dtype out_dt,
                         int B, int h, int Lq, int Lk, int d_k, int d_v,
                         const int* valid_lens, int causal, void* stream);
 
+/*
+ * sdpa_decode -- one incremental-decoding step: a single new query per
+ * (batch, head) attends to that head's cached keys and values.  At
+ * prediction time the pages' decoder concatenates the keys and values of all
+ * earlier steps with the current one and attends from the current position
+ * (d2l Transformer digest, decoder block state); the result equals
+ * sdpa_forward with Lq = 1, Lk = L, valid_lens = lens and causal = 0.
+ *
+ *   q    : [B, h, d_k] per {sq.b, sq.h} (sq.l unused)
+ *   k, v : caches [B, h, L, d_k] per sk, sv (bf16); the current step's key
+ *          and value must already be stored at position lens[b] - 1.
+ *   lens : device int32 [B] (required): positions 0 .. lens[b]-1 are
+ *          attended; values above L count as L, and lens[b] <= 0 weights all
+ *          L positions uniformly (the fully masked row).
+ *   o    : [B, h, d_v] per {so.b, so.h} (written; so.l unused).
+ *   workspace : device buffer of at least sdpa_decode_workspace_bytes(B, h, L)
+ *          bytes, 16-byte aligned, caller-owned scratch for the per-split
+ *          partial results; must not overlap any tensor.
+ *   Requirements: in_dt == MHA_BF16 (MHA_ENOTSUP otherwise), d_k == d_v == 64,
+ *   B >= 0, h >= 1, L >= 1, pointers 16-byte aligned, strides multiples of 8
+ *   elements (output: 8 bf16 or 4 fp32), o must not overlap q, k, v.
+ *   B == 0 is a no-op.  Computed in fp32 from the bf16 inputs (no reduced-
+ *   precision weights), split over 256-key slices of the cache and merged.
+ */
+size_t sdpa_decode_workspace_bytes(int B, int h, int L);
+
+mha_status sdpa_decode(mha_dtype in_dt, mha_dtype out_dt,
+                       const void* q, mha_strides sq,
+                       const void* k, mha_strides sk,
+                       const void* v, mha_strides sv,
+                       void* o, mha_strides so,
+                       int B, int h, int L, int d_k, int d_v, const int* lens,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace mha_forward needs: the projected Q, K, V and the
  * merged head output, each in in_dt (plus the low planes of Q and K for
  * MHA_BF16), each region 256-byte aligned.  Returns 0 for inconsistent

@@ -124,3 +124,40 @@ def test_missing_library_raises(monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libmha.so")
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def decode(lib, **kw):
+    a = dict(in_dt=BF16, out_dt=BF16, q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], o=ALIGNED[3], B=2, h=4, L=300,
+             dk=64, dv=64, lens=ALIGNED[4], ws=ALIGNED[5], ws_bytes=1 << 20)
+    a.update(kw)
+    st = S(4 * 300 * 64, 300 * 64, 64)
+    s1 = kw.get("sq", S(4 * 64, 64, 0))
+    return lib.sdpa_decode(a["in_dt"], a["out_dt"], a["q"], s1, a["k"], kw.get("sk", st), a["v"], st, a["o"],
+                           kw.get("so", S(4 * 64, 64, 0)), a["B"], a["h"], a["L"], a["dk"], a["dv"], a["lens"],
+                           a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_workspace_bytes(lib):
+    # one partial (max, sum, 64 outputs) of fp32 per (batch, head, 256-key split), 256-byte rounded
+    assert lib.sdpa_decode_workspace_bytes(2, 4, 300) == 4352          # 2*4*2*66*4 = 4224 rounded up
+    assert lib.sdpa_decode_workspace_bytes(1, 1, 256) == 512           # 264 bytes rounded up
+    assert lib.sdpa_decode_workspace_bytes(1, 1, 257) == 768           # two splits: 528 -> 768
+    assert lib.sdpa_decode_workspace_bytes(0, 4, 300) == 0
+    assert lib.sdpa_decode_workspace_bytes(1, 0, 300) == 0
+    assert lib.sdpa_decode_workspace_bytes(1, 1, 0) == 0
+
+
+def test_decode_validation(lib):
+    assert decode(lib, B=0) == OK
+    assert decode(lib, L=0) == EINVAL
+    assert decode(lib, h=0) == EINVAL
+    assert decode(lib, lens=None) == EINVAL          # the cache length is required
+    assert decode(lib, ws=None) == EINVAL
+    assert decode(lib, q=None) == EINVAL
+    assert decode(lib, dk=32) == ENOTSUP
+    assert decode(lib, in_dt=F32, out_dt=F32) == ENOTSUP
+    assert decode(lib, ws_bytes=100) == EWORK
+    assert decode(lib, k=ctypes.c_void_p(P + 8)) == EINVAL               # misaligned
+    assert decode(lib, sk=S(4 * 300 * 64, 300 * 64, 60)) == EINVAL      # stride not a multiple of 8
+    assert decode(lib, o=ALIGNED[1]) == EINVAL       # output overlaps the key cache
+    assert decode(lib, ws=ALIGNED[2]) == EINVAL      # workspace overlaps the value cache

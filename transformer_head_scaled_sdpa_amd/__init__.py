@@ -16,7 +16,7 @@ import ctypes
 from . import _lib
 from ._lib import MhaError, MHA_BF16, MHA_F32, MHA_OK, Strides
 
-__all__ = ["sdpa_forward", "mha_forward", "workspace_bytes", "kernel_timing", "MhaError", "library"]
+__all__ = ["sdpa_forward", "sdpa_decode", "mha_forward", "workspace_bytes", "kernel_timing", "MhaError", "library"]
 
 
 def library():
@@ -94,6 +94,34 @@ def sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None, out=Non
         in_dt, _dtype_code(out.dtype), _ptr(q), _strides4(q), _ptr(k), _strides4(k), _ptr(v), _strides4(v),
         _ptr(out), _strides4(out), B, h, Lq, Lk, dk, dv, _ptr(vl), int(bool(causal)), _stream())
     _raise(st, "sdpa_forward")
+    return out
+
+
+def sdpa_decode(q, k_cache, v_cache, lens, out_dtype=None, out=None, workspace=None):
+    """One decoding step: q [B, h, d_k] attends to positions 0 .. lens[b]-1 of
+    the caches k_cache, v_cache [B, h, L, d]; returns o [B, h, d_v]."""
+    torch = _torch()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_gpu(n, t)
+    B, h, dk = q.shape
+    L, dv = k_cache.shape[2], v_cache.shape[3]
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, h, dv), dtype=out_dtype, device=q.device)
+    ln = _valid_lens(lens, B, q.device)
+    if ln is None:
+        raise ValueError("lens is required")
+    lib = _lib.load()
+    need = int(lib.sdpa_decode_workspace_bytes(B, h, L))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    S3 = lambda t: _lib.Strides(t.stride(0), t.stride(1), 0)
+    st = lib.sdpa_decode(_dtype_code(q.dtype), _dtype_code(out.dtype), _ptr(q), S3(q), _ptr(k_cache),
+                         _strides4(k_cache), _ptr(v_cache), _strides4(v_cache), _ptr(out), S3(out), B, h, L, dk, dv,
+                         _ptr(ln), _ptr(workspace), workspace.numel(), _stream())
+    _raise(st, "sdpa_decode")
     return out
 
 

@@ -18,8 +18,8 @@ MHA_EWORKSPACE = 3
 MHA_EHIP = 4
 
 # Every function the header declares; tests check that each is exported.
-EXPORTED = ("sdpa_forward", "mha_workspace_bytes", "mha_forward", "mha_status_string",
-            "mha_timing_enable", "mha_timing_read")
+EXPORTED = ("sdpa_forward", "sdpa_decode_workspace_bytes", "sdpa_decode", "mha_workspace_bytes", "mha_forward",
+            "mha_status_string", "mha_timing_enable", "mha_timing_read")
 
 
 class Strides(ctypes.Structure):
@@ -48,6 +48,11 @@ def load():
     lib.sdpa_forward.restype = i
     lib.sdpa_forward.argtypes = [i, i, vp, Strides, vp, Strides, vp, Strides, vp, Strides,
                                  i, i, i, i, i, i, vp, i, vp]
+    lib.sdpa_decode_workspace_bytes.restype = sz
+    lib.sdpa_decode_workspace_bytes.argtypes = [i, i, i]
+    lib.sdpa_decode.restype = i
+    lib.sdpa_decode.argtypes = [i, i, vp, Strides, vp, Strides, vp, Strides, vp, Strides,
+                                i, i, i, i, i, vp, vp, sz, vp]
     lib.mha_workspace_bytes.restype = sz
     lib.mha_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.mha_forward.restype = i

@@ -124,6 +124,58 @@ mha_status sdpa_forward(mha_dtype in_dt, mha_dtype out_dt,
     return hip_status(timed("sdpa_bf16", s, [&] { return mha::launch_sdpa_bf16(a, out_dt == MHA_F32, s); }));
 }
 
+size_t sdpa_decode_workspace_bytes(int B, int h, int L) {
+    if (B < 0 || h <= 0 || L <= 0) return 0;
+    return round_up(mha::decode_workspace_bytes(B, h, L), 256);
+}
+
+mha_status sdpa_decode(mha_dtype in_dt, mha_dtype out_dt,
+                       const void* q, mha_strides sq,
+                       const void* k, mha_strides sk,
+                       const void* v, mha_strides sv,
+                       void* o, mha_strides so,
+                       int B, int h, int L, int d_k, int d_v, const int* lens,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
+    if (B < 0 || h <= 0 || L <= 0 || d_k <= 0 || d_v <= 0) return MHA_EINVAL;
+    if (d_k != kHeadDim || d_v != kHeadDim || in_dt != MHA_BF16) return MHA_ENOTSUP;
+    if (B == 0) return MHA_OK;
+    if (!q || !k || !v || !o || !lens || !workspace) return MHA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
+        return MHA_EINVAL;
+    const long long omult = out_dt == MHA_F32 ? 4 : 8;
+    const mha_strides in_s[3] = {sq, sk, sv};
+    for (const mha_strides& s : in_s)
+        if (s.b < 0 || s.h < 0 || s.l < 0 || s.b % 8 || s.h % 8 || s.l % 8) return MHA_EINVAL;
+    if (so.b < 0 || so.h < 0 || so.b % omult || so.h % omult) return MHA_EINVAL;
+    const size_t need = sdpa_decode_workspace_bytes(B, h, L);
+    if (workspace_bytes < need) return MHA_EWORKSPACE;
+    const size_t oe = elem_size(out_dt);
+    const mha_strides so1{so.b, so.h, 0};
+    const Range ro = view_range(o, so1, B, h, 1, d_v, oe);
+    const uintptr_t wb = reinterpret_cast<uintptr_t>(workspace);
+    const Range rw{wb, wb + need};
+    const mha_strides sq1{sq.b, sq.h, 0};
+    const Range ins[3] = {view_range(q, sq1, B, h, 1, d_k, 2), view_range(k, sk, B, h, L, d_k, 2),
+                          view_range(v, sv, B, h, L, d_v, 2)};
+    for (const Range& r : ins)
+        if (overlap(ro, r) || overlap(rw, r)) return MHA_EINVAL;
+    if (overlap(ro, rw)) return MHA_EINVAL;
+
+    mha::DecodeArgs d;
+    d.q = q; d.k = k; d.v = v; d.o = o;
+    d.sq[0] = sq.b; d.sq[1] = sq.h;
+    d.sk[0] = sk.b; d.sk[1] = sk.h; d.sk[2] = sk.l;
+    d.sv[0] = sv.b; d.sv[1] = sv.h; d.sv[2] = sv.l;
+    d.so[0] = so.b; d.so[1] = so.h;
+    d.B = B; d.H = h; d.L = L;
+    d.lens = lens;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(timed("sdpa_decode", s, [&] {
+        return mha::launch_sdpa_decode(d, out_dt == MHA_F32, workspace, s);
+    }));
+}
+
 size_t mha_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h) {
     if (!valid_dtype(in_dt) || B < 0 || Lq < 0 || Lk < 0 || d_model <= 0 || h <= 0 || d_model % h) return 0;
     const size_t es = elem_size(in_dt);

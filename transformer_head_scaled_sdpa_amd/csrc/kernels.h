@@ -52,7 +52,22 @@ struct FusedArgs {
     int causal;
 };
 
+// One decoding step: a single query per (batch, head) against cached keys
+// and values [B, H, L, 64] (bf16), keys j < lens[b] attended.
+struct DecodeArgs {
+    const void* q;     // [B, H, 64]: element strides sq[0] (batch), sq[1] (head)
+    const void* k;     // [B, H, L, 64]: strides {batch, head, position}
+    const void* v;
+    void* o;           // [B, H, 64]: strides so[0], so[1]
+    long long sq[2], sk[3], sv[3], so[2];
+    int B, H, L;
+    const int* lens;   // device int32 [B]
+};
+
 hipError_t launch_sdpa_bf16(const SdpaArgs& a, bool out_f32, hipStream_t s);
+int decode_splits(int L);
+size_t decode_workspace_bytes(int B, int H, int L);
+hipError_t launch_sdpa_decode(const DecodeArgs& a, bool out_f32, void* workspace, hipStream_t s);
 hipError_t launch_mha_attn_fused(const FusedArgs& a, hipStream_t s);
 hipError_t launch_sdpa_f32(const SdpaArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool out_f32, hipStream_t s);

@@ -1,0 +1,209 @@
+// One decoding step of attention: a single new query per (batch, head)
+// against its cache of keys and values, d_k = d_v = 64, bf16 in, fp32
+// arithmetic.  The pages' decoder, when predicting, concatenates the keys and
+// values of every earlier step with the current one and attends from the
+// current position only (d2l Transformer digest, decoder block: the state
+// keeps the per-layer key/value history at prediction time); the mask is the
+// key-padding rule with the cache length as valid length, so this is exactly
+//   o = sum_j softmax_j(q . k_j / sqrt(d_k)) v_j,  j < len[b]
+// (len[b] <= 0: every score is the -1e9 fill, uniform weights over all L
+// cached positions, as for a fully masked row).
+//
+// The step reads every cached key and value once and does 4*d_k flops per
+// key, so it is HBM-bound; the keys are split over many workgroups (split-K,
+// "flash decoding") so the whole GPU streams the cache:
+//  * Kernel 1: one workgroup (4 wave64s) per (batch, head, 256-key split).
+//    Each thread computes two keys' scores in fp32 from 16-byte loads, the
+//    split's max and weight sum are block reductions, and P.V accumulates
+//    64 features x 8 key groups from 16-byte V loads, reduced through LDS.
+//    The split's (max, sum, unnormalised output) goes to the workspace.
+//  * Kernel 2: per (batch, head), merges the splits by rescaling each to the
+//    common max (the online-softmax merge) and writes the normalised output.
+#include "common.h"
+#include "kernels.h"
+
+namespace mha {
+
+namespace {
+
+constexpr int kD = 64;
+constexpr int kThreads = 256;
+constexpr int kSplit = 256;            // keys per workgroup
+constexpr int kPart = kD + 2;          // floats per partial: max, sum, 64 outputs
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// 8 bf16 -> fp32
+__device__ __forceinline__ void unpack8(const uint4& r, float (&f)[8]) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(w[e] << 16);
+        f[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a, int n_split, float c, float* part) {
+    __shared__ float sc[kSplit];
+    __shared__ float red[kThreads / 64];
+    __shared__ float ored[8][kD];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int split = blockIdx.x % n_split;
+    const int bh = blockIdx.x / n_split;
+    const int b = bh / a.H, hd = bh % a.H;
+    const int len = a.lens[b];
+    const bool none = len <= 0;                 // every position masked -> uniform weights
+    const int n = none ? a.L : min(len, a.L);   // positions that carry weight
+    const int j0 = split * kSplit;
+    float* out = part + ((long long)bh * n_split + split) * kPart;
+    if (j0 >= n) {                              // empty split: contributes nothing
+        if (tid == 0) {
+            out[0] = -INFINITY;
+            out[1] = 0.0f;
+        }
+        return;
+    }
+    const int cnt = min(kSplit, n - j0);
+
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + b * a.sq[0] + hd * a.sq[1];
+    const bf16_t* kp = static_cast<const bf16_t*>(a.k) + b * a.sk[0] + hd * a.sk[1];
+    const bf16_t* vp = static_cast<const bf16_t*>(a.v) + b * a.sv[0] + hd * a.sv[1];
+
+    // ---- scores: thread t -> keys j0 + t (and + 128 via the second pass),
+    // 8 features per 16-byte load, 8 loads per key.  Thread pairs share a
+    // key: the pair's halves hold features [0,32) and [32,64).
+    const int half = tid & 1;
+    float qf[32];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        float f[8];
+        unpack8(*reinterpret_cast<const uint4*>(qp + half * 32 + x * 8), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[x * 8 + e] = f[e];
+    }
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int jl = pass * (kThreads / 2) + (tid >> 1);   // key within the split
+        float acc = 0.0f;
+        if (jl < cnt) {
+            const bf16_t* kr = kp + (long long)(j0 + jl) * a.sk[2] + half * 32;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                float f[8];
+                unpack8(*reinterpret_cast<const uint4*>(kr + x * 8), f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaf(qf[x * 8 + e], f[e], acc);
+            }
+        }
+        acc += __shfl_xor(acc, 1);
+        if (half == 0) sc[jl] = jl < cnt ? (none ? 0.0f : acc * c) : -INFINITY;
+    }
+    __syncthreads();
+
+    // ---- split max and weights ----
+    float m = -INFINITY;
+    for (int j = tid; j < kSplit; j += kThreads) m = fmaxf(m, sc[j]);
+    m = wave_max(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float s = 0.0f;
+    for (int j = tid; j < kSplit; j += kThreads) {
+        const float p = __builtin_amdgcn_exp2f(sc[j] - m);   // exp2(-inf) = 0 past cnt
+        sc[j] = p;
+        s += p;
+    }
+    s = wave_sum(s);
+    if (lane == 0) red[wave] = s;
+    __syncthreads();
+    s = (red[0] + red[1]) + (red[2] + red[3]);
+
+    // ---- unnormalised output: thread t -> features (t % 8) * 8 .. +7 of
+    // keys j = t / 8, t / 8 + 32, ...; the 32 key groups are summed in LDS.
+    const int f8 = (tid & 7) * 8, jg = tid >> 3;
+    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int jl = jg; jl < cnt; jl += kThreads / 8) {
+        const float p = sc[jl];
+        float f[8];
+        unpack8(*reinterpret_cast<const uint4*>(vp + (long long)(j0 + jl) * a.sv[2] + f8), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(p, f[e], o[e]);
+    }
+    // groups jg and jg ^ 16, ^ 8, ^ 4 share a wave (jg = 8 * wave + lane / 8);
+    // reduce those with shuffles, then the 4 waves' partials in LDS.
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        o[e] += __shfl_xor(o[e], 32);
+        o[e] += __shfl_xor(o[e], 16);
+        o[e] += __shfl_xor(o[e], 8);
+    }
+    if (lane < 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ored[wave][f8 + e] = o[e];
+    }
+    __syncthreads();
+    if (tid < kD) {
+        out[2 + tid] = (ored[0][tid] + ored[1][tid]) + (ored[2][tid] + ored[3][tid]);
+        if (tid == 0) {
+            out[0] = m;
+            out[1] = s;
+        }
+    }
+}
+
+template <bool kOutF32>
+__global__ __launch_bounds__(kD) void decode_merge(DecodeArgs a, int n_split, const float* part) {
+    const int bh = blockIdx.x, t = threadIdx.x;
+    const int b = bh / a.H, hd = bh % a.H;
+    const float* pp = part + (long long)bh * n_split * kPart;
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, pp[s * kPart]);
+    float l = 0.0f, acc = 0.0f;
+    for (int s = 0; s < n_split; ++s) {
+        const float ms = pp[s * kPart];
+        if (ms == -INFINITY) continue;          // empty split
+        const float w = __builtin_amdgcn_exp2f(ms - M);
+        l = fmaf(pp[s * kPart + 1], w, l);
+        acc = fmaf(pp[s * kPart + 2 + t], w, acc);
+    }
+    const float y = acc / l;
+    const long long off = b * a.so[0] + hd * a.so[1] + t;
+    if (kOutF32) static_cast<float*>(a.o)[off] = y;
+    else static_cast<bf16_t*>(a.o)[off] = __builtin_bit_cast(bf16_t, static_cast<__bf16>(y));
+}
+
+}  // namespace
+
+int decode_splits(int L) { return (L + kSplit - 1) / kSplit; }
+
+size_t decode_workspace_bytes(int B, int H, int L) {
+    return (size_t)B * H * decode_splits(L) * kPart * sizeof(float);
+}
+
+hipError_t launch_sdpa_decode(const DecodeArgs& a, bool out_f32, void* workspace, hipStream_t s) {
+    const int n_split = decode_splits(a.L);
+    const long long grid = (long long)a.B * a.H * n_split;
+    if (grid == 0) return hipSuccess;
+    float* part = static_cast<float*>(workspace);
+    const float c = kLog2e / 8.0f;   // log2(e) / sqrt(64)
+    hipLaunchKernelGGL(decode_split, dim3((unsigned)grid), dim3(kThreads), 0, s, a, n_split, c, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (out_f32) hipLaunchKernelGGL(decode_merge<true>, dim3(a.B * a.H), dim3(kD), 0, s, a, n_split, part);
+    else hipLaunchKernelGGL(decode_merge<false>, dim3(a.B * a.H), dim3(kD), 0, s, a, n_split, part);
+    return hipGetLastError();
+}
+
+}  // namespace mha

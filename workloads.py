@@ -39,7 +39,7 @@ import numpy as np
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "mha" or "sdpa"
+    kind: str                 # "mha", "sdpa" or "decode" (sdpa with one query against a cache)
     dtype: str                # "f32" or "bf16"
     B: int
     Lq: int
@@ -78,6 +78,12 @@ WORKLOADS = [
                          "d_model=1024 h=16, source valid_lens U{192..384}"),
     Workload("sdpa_long_causal", "sdpa", "bf16", 4, 4096, 4096, 16, 64, True, None, seed=5,
              description="long causal SDPA core bf16, B=4 h=16 L=4096 d_k=64"),
+    # One incremental-decoding step of the decoder workload's shape: a single
+    # query per (batch, head) against a 512-position cache holding U{256..512}
+    # valid keys.
+    Workload("decode_step", "decode", "bf16", 64, 1, 512, 8, 64, False, (256, 512), seed=6,
+             description="decoding step bf16, B=64 h=8 d_k=64, one query against a K/V cache of "
+                         "512 positions with U{256..512} valid"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -170,7 +176,7 @@ def make_inputs(w: Workload, bias: bool = False) -> Inputs:
     rng = np.random.Generator(np.random.PCG64(w.seed))
     vl = draw_valid_lens(rng, w.B, w.vl_range)
     t = {}
-    if w.kind == "sdpa":
+    if w.kind in ("sdpa", "decode"):
         for name in ("q", "k", "v"):
             L = w.Lq if name == "q" else w.Lk
             t[name] = _finish(rng.standard_normal((w.B, w.h, L, w.d_k)), w.dtype)
