@@ -40,13 +40,15 @@
  *   - dtypes: MHA_F32 computes in fp32 throughout (FMA, no reduced
  *     precision).  MHA_BF16 takes bf16 inputs and weights, multiplies on bf16
  *     MFMA with fp32 accumulation, keeps the softmax state in fp32, and writes
- *     the output as bf16 or fp32 (out_dt).  mha_forward stores V and the
- *     merged head output as bf16, and Q and K as a bf16 hi + lo pair (hi =
- *     bf16(x), lo = bf16(x - hi)) whose scores are formed from three bf16
- *     products (hi.hi + lo.hi + hi.lo): large logits, such as those of
- *     embeddings scaled by sqrt(d_model), keep near-fp32 accuracy instead of
- *     moving by a bf16 rounding step.  sdpa_forward's bf16 inputs are exact
- *     bf16 values and use a single product.
+ *     the output as bf16 or fp32 (out_dt).  With MHA_BF16, mha_forward
+ *     projects each head's Q, K and V inside its attention kernel and keeps
+ *     them on chip: Q (times log2(e)/sqrt(d_k)) and K as bf16 hi + lo pairs
+ *     (hi = bf16(x), lo = bf16(x - hi)) whose scores are formed from three
+ *     bf16 products (hi.hi + lo.hi + hi.lo), so large logits, such as those
+ *     of embeddings scaled by sqrt(d_model), keep near-fp32 accuracy instead
+ *     of moving by a bf16 rounding step; V and the merged head output are
+ *     rounded to bf16.  sdpa_forward's and sdpa_decode's bf16 inputs are
+ *     exact bf16 values and use a single product.
  */
 #ifndef MHA_H
 #define MHA_H
@@ -131,10 +133,10 @@ mha_status sdpa_decode(mha_dtype in_dt, mha_dtype out_dt,
                        int B, int h, int L, int d_k, int d_v, const int* lens,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace mha_forward needs: the projected Q, K, V and the
- * merged head output, each in in_dt (plus the low planes of Q and K for
- * MHA_BF16), each region 256-byte aligned.  Returns 0 for inconsistent
- * arguments. */
+/* Bytes of device workspace mha_forward needs: for MHA_BF16 the merged head
+ * output [B*Lq, d_model] in bf16; for MHA_F32 the projected Q, K, V and the
+ * merged head output in fp32.  Each region is 256-byte aligned.  Returns 0
+ * for inconsistent arguments. */
 size_t mha_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h);
 
 /*

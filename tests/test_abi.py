@@ -105,8 +105,8 @@ def test_mha_validation(lib):
 
 
 def test_workspace_bytes(lib):
-    # Q, K, V and merged heads (+ low planes of Q and K for bf16), each
-    # rounded up to 256 bytes.
+    # bf16: the merged heads only (2 * 10 * 512 bf16 = 20480 bytes); fp32: Q,
+    # K, V and merged heads; each region rounded up to 256 bytes.
     assert lib.mha_workspace_bytes(BF16, 2, 10, 12, 512, 8) == 20480
     assert lib.mha_workspace_bytes(F32, 2, 10, 10, 512, 8) == 4 * 40960
     assert lib.mha_workspace_bytes(F32, 2, 10, 10, 500, 8) == 0

@@ -84,4 +84,4 @@ def test_decode_step_workload_full_size():
     q, k, v = (inp.tensors[n] for n in ("q", "k", "v"))
     g = _run(q[:, :, 0, :], k, v, inp.valid_lens, torch.bfloat16)
     ref = oracle.sdpa(q, k, v, valid_lens=inp.valid_lens)[:, :, 0, :]
-    assert_bf16(g, ref, "decode_step full")
+    print("decode_step", assert_bf16(g, ref, "decode_step full"))
