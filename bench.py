@@ -250,7 +250,7 @@ def copy_calibration():
 # ---------------------------------------------------------------------------
 CSRC = os.path.join(ROOT, "transformer_head_scaled_sdpa_amd", "csrc")
 KERNEL_SOURCES = {
-    "attn_fused_bf16": ["mha_fused.hip", "lds_tile.h", "common.h", "kernels.h"],
+    "attn_fused_bf16": ["mha_fused.hip", "mha_fused_small.hip", "lds_tile.h", "common.h", "kernels.h"],
     "out_proj_bf16": ["gemm.hip", "lds_tile.h", "common.h", "kernels.h"],
     "sdpa_bf16": ["sdpa_bf16_pipe.hip", "common.h", "kernels.h"],
     "sdpa_decode": ["sdpa_decode.hip", "common.h", "kernels.h"],

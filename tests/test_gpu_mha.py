@@ -48,6 +48,12 @@ MHA_BF16_CASES = [
     (3, 130, 130, 128, 2, False, (0, 130), True, True),
     (1, 1, 1, 64, 1, False, None, False, True),
     (2, 200, 140, 192, 3, False, None, True, False),
+    # self-attention with L <= 128 takes the single-pass kernel: full 128
+    # rows with fully masked rows possible, a causal length between the key
+    # halves, and exactly one key half
+    (4, 128, 128, 256, 4, False, (0, 128), True, True),
+    (2, 100, 100, 128, 2, True, None, False, True),
+    (3, 64, 64, 192, 3, False, (1, 64), True, True),
 ]
 
 

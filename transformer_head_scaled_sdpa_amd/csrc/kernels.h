@@ -69,6 +69,11 @@ int decode_splits(int L);
 size_t decode_workspace_bytes(int B, int H, int L);
 hipError_t launch_sdpa_decode(const DecodeArgs& a, bool out_f32, void* workspace, hipStream_t s);
 hipError_t launch_mha_attn_fused(const FusedArgs& a, hipStream_t s);
+// Self-attention with L <= 128 (x_q == x_kv, Lq == Lk): one projection pass
+// and the attention split over two key halves.  launch_mha_attn_fused picks
+// it by itself when it fits.
+bool mha_attn_fused_small_fits(const FusedArgs& a);
+hipError_t launch_mha_attn_fused_small(const FusedArgs& a, hipStream_t s);
 hipError_t launch_sdpa_f32(const SdpaArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool out_f32, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
