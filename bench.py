@@ -211,6 +211,24 @@ def time_steps(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall / steps
 
 
+def time_steps_cold(fn, steps):
+    """Average step time with the caches cold: before every step a 512 MiB
+    buffer is streamed (larger than the 256 MB last-level cache), and only
+    the step itself lies between the two events."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    fn()
+    for e0, e1 in evs:
+        flush.fill_(1)
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    del flush
+    return sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+
+
 def kernel_times(fn, steps, repeat):
     """Average duration (ms) per launch of each library kernel over `steps`
     eager steps, from the HIP event pairs the library records on the launch
@@ -354,6 +372,7 @@ def main():
 
     fn = {"mha": PreparedMha, "sdpa": PreparedSdpa, "decode": PreparedDecode}[w.kind](inp)
     ms, wall_ms = time_steps(fn, args.steps, args.warmup)
+    cold_ms = time_steps_cold(fn, 20)
     attn_flops = w.attention_flops()
     value = attn_flops / (ms * 1e-3) / 1e12
     log(f"step {ms * 1e3:.2f} us (wall {wall_ms * 1e3:.2f} us)")
@@ -404,6 +423,8 @@ def main():
         "kernels": {n: {"avg_us": k["avg_us"], "roofline_frac": k["roofline"]["frac"],
                         "bound": k["roofline"]["bound"]} for n, k in kernels.items()},
         "roofline": rl,
+        "cold_cache": {"ms_per_step": round(cold_ms, 6), "value": round(attn_flops / (cold_ms * 1e-3) / 1e12, 3),
+                       "note": "512 MiB streamed before each of 20 steps; events bracket the step only"},
     }
 
     if not args.no_long_sdpa and w.name != "sdpa_long_causal":
