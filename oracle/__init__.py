@@ -46,10 +46,10 @@ def _open(path):
     lib.oracle_linear_f64.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_long, ctypes.c_int, ctypes.c_int]
     lib.oracle_sdpa_f64.restype = ctypes.c_int
     lib.oracle_sdpa_f64.argtypes = [_dp, _dp, _dp, _dp, _dp] + [ctypes.c_int] * 6 + [
-        _ip, ctypes.c_int, _ip, ctypes.c_int]
+        _ip, ctypes.c_int, ctypes.c_int, _ip, ctypes.c_int]
     lib.oracle_mha_f64.restype = ctypes.c_int
     lib.oracle_mha_f64.argtypes = [_dp] * 11 + [ctypes.c_int] * 5 + [
-        _ip, ctypes.c_int, _ip, ctypes.c_int, ctypes.c_int]
+        _ip, ctypes.c_int, ctypes.c_int, _ip, ctypes.c_int, ctypes.c_int]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     return lib
@@ -140,14 +140,14 @@ def sdpa(q, k, v, valid_lens=None, causal=False, rows=None, return_weights=False
     assert k.shape == (B, h, Lk, dk) and v.shape == (B, h, Lk, dv)
     vl = _i32(valid_lens)
     if vl is not None:
-        assert vl.shape == (B,)
+        assert vl.shape in ((B,), (B, Lq))
     rr = _i32(rows)
     R = Lq if rr is None else int(rr.shape[0])
     o = np.empty((B, h, R, dv), dtype=np.float64)
     p = np.empty((B, h, R, Lk), dtype=np.float64) if return_weights else None
     rc = _load().oracle_sdpa_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(p),
-                                 B, h, Lq, Lk, dk, dv, _iptr(vl), int(bool(causal)),
-                                 _iptr(rr), 0 if rr is None else R)
+                                 B, h, Lq, Lk, dk, dv, _iptr(vl), int(vl is not None and vl.ndim == 2),
+                                 int(bool(causal)), _iptr(rr), 0 if rr is None else R)
     if rc != 0:
         raise ValueError("oracle_sdpa_f64 rejected its arguments")
     return (o, p) if return_weights else o
@@ -165,13 +165,16 @@ def mha(x_q, x_kv, w_q, w_k, w_v, w_o, b_q=None, b_k=None, b_v=None, b_o=None,
         assert w.shape == (D, D)
     bs = [None if b is None else _f64(b) for b in (b_q, b_k, b_v, b_o)]
     vl = _i32(valid_lens)
+    if vl is not None:
+        assert vl.shape in ((B,), (B, Lq))
     rr = _i32(rows)
     R = Lq if rr is None else int(rr.shape[0])
     out = np.empty((B, R, D), dtype=np.float64)
     rc = _load().oracle_mha_f64(_ptr(xq), _ptr(xkv),
                                 _ptr(ws[0]), _ptr(bs[0]), _ptr(ws[1]), _ptr(bs[1]),
                                 _ptr(ws[2]), _ptr(bs[2]), _ptr(ws[3]), _ptr(bs[3]),
-                                _ptr(out), B, Lq, Lk, D, h, _iptr(vl), int(bool(causal)),
+                                _ptr(out), B, Lq, Lk, D, h, _iptr(vl), int(vl is not None and vl.ndim == 2),
+                                int(bool(causal)),
                                 _iptr(rr), 0 if rr is None else R, int(bool(bf16_stages)))
     if rc != 0:
         raise ValueError("oracle_mha_f64 rejected its arguments")

@@ -24,10 +24,14 @@
  *       ("Transformer" study notes, multi-head attention: Concat(head_1..h) W^O)
  *
  * Masks.  A key j is allowed for query i of batch b when
- *   (valid_lens == NULL or j < valid_lens[b])  and  (!causal or j <= i).
+ *   (valid_lens == NULL or j < len(b, i))  and  (!causal or j <= i),
+ * where len(b, i) = valid_lens[b] for lengths per batch [B] and
+ * valid_lens[b*Lq + i] for lengths per query [B, Lq].
  * The valid_lens rule is the d2l reading (d2l Transformer digest, multi-head
  * attention prerequisites: valid lengths are repeated over the heads, and no
- * query attends to padded keys); the causal rule is the lower-triangular
+ * query attends to padded keys; its masked softmax takes them either per
+ * sequence or per query, and the decoder's training pass gives query i the
+ * length i + 1); the causal rule is the lower-triangular
  * "subsequent mask" whose 5x5 print keeps the diagonal ("Transformer" study
  * notes, mask-generation section; The Annotated Transformer, decoder section).
  * The two masks are combined by logical AND.  One mask serves every head.
@@ -85,9 +89,13 @@ void oracle_linear_f64(const double* x, const double* w, const double* b,
     }
 }
 
-static int key_allowed(const int* valid_lens, int causal, int b, int i, int j)
+static int key_allowed(const int* valid_lens, int vl_per_query, int Lq, int causal, int b, int i, int j)
 {
-    if (valid_lens && !(j < valid_lens[b])) return 0;
+    if (vl_per_query) {
+        if (valid_lens && !(j < valid_lens[(long)b * Lq + i])) return 0;
+    } else {
+        if (valid_lens && !(j < valid_lens[b])) return 0;
+    }
     if (causal && j > i) return 0;
     return 1;
 }
@@ -95,15 +103,15 @@ static int key_allowed(const int* valid_lens, int causal, int b, int i, int j)
 /* One query row of one (batch, head): the attention definition, every key. */
 static void attend_row(const double* qi, const double* k, const double* v,
                        double* oi, double* pi, double* s,
-                       int Lk, int dk, int dv,
-                       const int* valid_lens, int causal, int b, int i)
+                       int Lq, int Lk, int dk, int dv,
+                       const int* valid_lens, int vl_per_query, int causal, int b, int i)
 {
     const double scale = 1.0 / sqrt((double)dk);
     for (int j = 0; j < Lk; ++j) {
         double dot = 0.0;
         for (int t = 0; t < dk; ++t) dot += qi[t] * k[(long)j * dk + t];
         s[j] = dot * scale;
-        if (!key_allowed(valid_lens, causal, b, i, j)) s[j] = ORACLE_MASK_FILL;
+        if (!key_allowed(valid_lens, vl_per_query, Lq, causal, b, i, j)) s[j] = ORACLE_MASK_FILL;
     }
     double mx = s[0];
     for (int j = 1; j < Lk; ++j) if (s[j] > mx) mx = s[j];
@@ -123,12 +131,13 @@ static void attend_row(const double* qi, const double* k, const double* v,
  *   q [B, h, Lq, dk], k [B, h, Lk, dk], v [B, h, Lk, dv]   (contiguous)
  *   o [B, h, R, dv] and, if p != NULL, p [B, h, R, Lk], where the R rows are
  *   rows[0..n_rows) (query indices) or, when rows == NULL, all Lq queries.
+ *   valid_lens: NULL, [B] (vl_per_query == 0) or [B, Lq] (vl_per_query == 1).
  * Returns 0, or -1 on a bad argument / allocation failure.
  */
 int oracle_sdpa_f64(const double* q, const double* k, const double* v,
                     double* o, double* p,
                     int B, int h, int Lq, int Lk, int dk, int dv,
-                    const int* valid_lens, int causal,
+                    const int* valid_lens, int vl_per_query, int causal,
                     const int* rows, int n_rows)
 {
     if (B < 0 || h <= 0 || Lq < 0 || Lk <= 0 || dk <= 0 || dv <= 0) return -1;
@@ -150,7 +159,7 @@ int oracle_sdpa_f64(const double* q, const double* k, const double* v,
             attend_row(qb + (long)i * dk, kb, vb,
                        o + (bh * R + r) * (long)dv,
                        p ? p + (bh * R + r) * (long)Lk : NULL, s,
-                       Lk, dk, dv, valid_lens, causal, b, i);
+                       Lq, Lk, dk, dv, valid_lens, vl_per_query, causal, b, i);
         }
         free(s);
     }
@@ -178,7 +187,7 @@ int oracle_mha_f64(const double* xq, const double* xkv,
                    const double* w_v, const double* b_v,
                    const double* w_o, const double* b_o,
                    double* out, int B, int Lq, int Lk, int D, int h,
-                   const int* valid_lens, int causal,
+                   const int* valid_lens, int vl_per_query, int causal,
                    const int* rows, int n_rows, int bf16_stages)
 {
     if (B < 0 || Lq < 0 || Lk <= 0 || D <= 0 || h <= 0 || D % h != 0) return -1;
@@ -243,7 +252,7 @@ int oracle_mha_f64(const double* xq, const double* xkv,
                 const int i = rows ? rows[r] : r;
                 attend_row(qh + (bh * R + r) * (long)dk, kh + bh * (long)Lk * dk,
                            vh + bh * (long)Lk * dk, oh + (bh * R + r) * (long)dk, NULL, s,
-                           Lk, dk, dk, valid_lens, causal, b, i);
+                           Lq, Lk, dk, dk, valid_lens, vl_per_query, causal, b, i);
             }
             free(s);
         }

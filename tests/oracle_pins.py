@@ -284,6 +284,62 @@ def pin_valid_lens_per_query_equals_causal():
         _close(oi[:, :, 0], oc[:, :, i], 0.0)
 
 
+def pin_valid_lens_2d_lengths_i_plus_1_equal_causal():
+    """Lengths per query [B, Lq] with row i holding i + 1 (the d2l decoder's
+    training-time valid lengths, one row per batch) give the causal mask, in
+    one call over all rows."""
+    r = _rng(41)
+    B, h, L, d = 3, 2, 7, 4
+    q, k, v = (r.standard_normal((B, h, L, d)) for _ in range(3))
+    vl2 = np.tile(np.arange(1, L + 1, dtype=np.int32), (B, 1))
+    _close(oracle.sdpa(q, k, v, valid_lens=vl2), oracle.sdpa(q, k, v, causal=True), 0.0)
+
+
+def pin_valid_lens_2d_each_row_is_its_own_length():
+    """Row i of batch b under lengths per query equals a one-row call with a
+    per-batch length equal to vl2[b, i] (brute force over every (b, i));
+    Lq != B so a transposed (b, i) index is caught."""
+    r = _rng(42)
+    B, h, Lq, Lk, d = 2, 2, 5, 6, 3
+    q = r.standard_normal((B, h, Lq, d))
+    k, v = (r.standard_normal((B, h, Lk, d)) for _ in range(2))
+    vl2 = r.integers(0, Lk + 1, size=(B, Lq)).astype(np.int32)
+    vl2[0, 1] = 0                            # a fully masked row
+    o2 = oracle.sdpa(q, k, v, valid_lens=vl2)
+    for b in range(B):
+        for i in range(Lq):
+            o1 = oracle.sdpa(q[b:b + 1], k[b:b + 1], v[b:b + 1], valid_lens=[vl2[b, i]], rows=[i])
+            _close(o2[b:b + 1, :, i], o1[:, :, 0], 0.0)
+    # closed form of the fully masked row: uniform weights over every key
+    _close(o2[0, :, 1], v[0].mean(axis=1), 1e-12)
+
+
+def pin_valid_lens_2d_constant_rows_equal_per_batch():
+    """Lengths per query that repeat the batch's length in every row equal
+    lengths per batch, for sdpa and for the multi-head layer."""
+    r = _rng(43)
+    B, h, Lq, Lk, d = 2, 2, 4, 5, 3
+    q = r.standard_normal((B, h, Lq, d))
+    k, v = (r.standard_normal((B, h, Lk, d)) for _ in range(2))
+    vl = np.array([2, 5], dtype=np.int32)
+    vl2 = np.repeat(vl[:, None], Lq, axis=1)
+    _close(oracle.sdpa(q, k, v, valid_lens=vl2), oracle.sdpa(q, k, v, valid_lens=vl), 0.0)
+    D = 8
+    xq, xkv = r.standard_normal((B, Lq, D)), r.standard_normal((B, Lk, D))
+    w = [r.standard_normal((D, D)) * 0.3 for _ in range(4)]
+    _close(oracle.mha(xq, xkv, *w, h=2, valid_lens=vl2), oracle.mha(xq, xkv, *w, h=2, valid_lens=vl), 0.0)
+
+
+def pin_mha_valid_lens_2d_lengths_i_plus_1_equal_causal():
+    """The multi-head layer with query lengths i + 1 equals its causal form."""
+    r = _rng(44)
+    B, L, D = 2, 5, 8
+    x = r.standard_normal((B, L, D))
+    w = [r.standard_normal((D, D)) * 0.3 for _ in range(4)]
+    vl2 = np.tile(np.arange(1, L + 1, dtype=np.int32), (B, 1))
+    _close(oracle.mha(x, x, *w, h=2, valid_lens=vl2), oracle.mha(x, x, *w, h=2, causal=True), 0.0)
+
+
 def pin_row_subset_consistent():
     r = _rng(37)
     x = r.standard_normal((2, 9, 16))

@@ -29,6 +29,8 @@ MUTATIONS = [
     ("bf16_merge_not_rounded", "if (bf16_stages) round_all(ocat", "if (0) round_all(ocat"),
     ("mask_uses_query_length", "if (valid_lens && !(j < valid_lens[b]))",
      "if (valid_lens && !(i < valid_lens[b]))"),
+    ("per_query_length_rows_reversed", "valid_lens[(long)b * Lq + i]", "valid_lens[(long)b * Lq + (Lq - 1 - i)]"),
+    ("per_query_length_ignores_query", "valid_lens[(long)b * Lq + i]", "valid_lens[(long)b * Lq]"),
 ]
 
 
