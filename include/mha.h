@@ -167,6 +167,62 @@ mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
                        const int* valid_lens, int causal,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The inspection entry points: the attention function of The Annotated
+ * Transformer ("Attention" section) returns its weights p_attn beside the
+ * output, and the multi-head layer keeps them for visualisation; the d2l
+ * Transformer digest's masked softmax takes valid lengths per sequence or per
+ * query (its decoder trains with query i given length i + 1).
+ *
+ * sdpa_forward_ex -- sdpa_forward plus:
+ *   vl_rank : 1 -> valid_lens is [B] (as sdpa_forward); 2 -> valid_lens is
+ *             [B, Lq] row-major, one length per query, shared by every head.
+ *             Ignored when valid_lens is NULL.  Other values: MHA_EINVAL.
+ *             A query whose length is <= 0 weights all Lk keys uniformly.
+ *   p_attn  : NULL, or a device fp32 [B, h, Lq, Lk] buffer with element
+ *             strides `sp` (batch, head, query) and unit stride over keys,
+ *             4-byte aligned, not overlapping any other argument.  It receives the normalised weights
+ *             softmax_j(q_i . k_j / sqrt(d_k)) with masked keys exactly 0.
+ * With p_attn == NULL and lengths per sequence this is sdpa_forward.  Else
+ * it runs the inspection kernel: fp32 arithmetic, two passes over the keys
+ * (slower than sdpa_forward; meant for debugging and visualisation).
+ */
+mha_status sdpa_forward_ex(mha_dtype in_dt, mha_dtype out_dt,
+                           const void* q, mha_strides sq,
+                           const void* k, mha_strides sk,
+                           const void* v, mha_strides sv,
+                           void* o, mha_strides so,
+                           int B, int h, int Lq, int Lk, int d_k, int d_v,
+                           const int* valid_lens, int vl_rank, int causal,
+                           float* p_attn, mha_strides sp, void* stream);
+
+/* Bytes of device workspace mha_forward_ex needs on its inspection path:
+ * the merged heads in in_dt, then Q [B*Lq, d_model], K and V [B*Lk, d_model]
+ * in fp32, each 256-byte aligned (always >= mha_workspace_bytes).  Returns 0
+ * for inconsistent arguments. */
+size_t mha_workspace_bytes_ex(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h);
+
+/*
+ * mha_forward_ex -- mha_forward plus lengths per query (vl_rank 2, valid_lens
+ * [B, Lq]) and the per-head weights p_attn [B, h, Lq, Lk] (fp32, as for
+ * sdpa_forward_ex).  With p_attn == NULL and lengths per sequence this is
+ * mha_forward (workspace: mha_workspace_bytes); otherwise the projections
+ * run to fp32 Q, K, V in the workspace (mha_workspace_bytes_ex), the
+ * inspection kernel attends and writes the weights, and the output
+ * projection follows as in mha_forward.
+ */
+mha_status mha_forward_ex(mha_dtype in_dt, mha_dtype out_dt,
+                          const void* x_q, const void* x_kv,
+                          const void* w_q, const void* b_q,
+                          const void* w_k, const void* b_k,
+                          const void* w_v, const void* b_v,
+                          const void* w_o, const void* b_o,
+                          void* out,
+                          int B, int Lq, int Lk, int d_model, int h, int d_k,
+                          const int* valid_lens, int vl_rank, int causal,
+                          float* p_attn, mha_strides sp,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* mha_status_string(mha_status s);
 

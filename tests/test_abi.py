@@ -161,3 +161,58 @@ def test_decode_validation(lib):
     assert decode(lib, sk=S(4 * 300 * 64, 300 * 64, 60)) == EINVAL      # stride not a multiple of 8
     assert decode(lib, o=ALIGNED[1]) == EINVAL       # output overlaps the key cache
     assert decode(lib, ws=ALIGNED[2]) == EINVAL      # workspace overlaps the value cache
+
+
+def sdpa_ex(lib, **kw):
+    a = dict(in_dt=BF16, out_dt=BF16, q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], o=ALIGNED[3], B=2, h=4, Lq=128,
+             Lk=128, dk=64, dv=64, vl=ALIGNED[4], vl_rank=2, causal=0, p=ALIGNED[5])
+    a.update(kw)
+    st = S(4 * 128 * 64, 128 * 64, 64)
+    sp = kw.get("sp", S(4 * 128 * 128, 128 * 128, 128))
+    return lib.sdpa_forward_ex(a["in_dt"], a["out_dt"], a["q"], st, a["k"], st, a["v"], st, a["o"], st, a["B"],
+                               a["h"], a["Lq"], a["Lk"], a["dk"], a["dv"], a["vl"], a["vl_rank"], a["causal"], a["p"],
+                               sp, None)
+
+
+def test_sdpa_ex_validation(lib):
+    assert sdpa_ex(lib, B=0) == OK
+    assert sdpa_ex(lib, vl_rank=3) == EINVAL              # lengths are [B] or [B, Lq]
+    assert sdpa_ex(lib, vl_rank=0) == EINVAL
+    assert sdpa_ex(lib, dk=32) == ENOTSUP
+    assert sdpa_ex(lib, p=ctypes.c_void_p(P + 0x500000 + 2)) == EINVAL     # weights not float-aligned
+    assert sdpa_ex(lib, sp=S(4 * 128 * 128, 128 * 128, -128)) == EINVAL    # negative weight stride
+    assert sdpa_ex(lib, p=ALIGNED[0]) == EINVAL           # weights overlap q
+    assert sdpa_ex(lib, p=ALIGNED[3]) == EINVAL           # weights overlap o
+    assert sdpa_ex(lib, causal=1, Lk=100) == EINVAL
+
+
+def test_workspace_bytes_ex(lib):
+    # merged heads in in_dt, then fp32 Q [B*Lq, D], K and V [B*Lk, D], each rounded up to 256 bytes
+    assert lib.mha_workspace_bytes_ex(BF16, 2, 10, 12, 512, 8) == 20480 + 40960 + 2 * 49152
+    assert lib.mha_workspace_bytes_ex(F32, 2, 10, 10, 512, 8) == 4 * 40960
+    assert lib.mha_workspace_bytes_ex(F32, 2, 10, 10, 500, 8) == 0
+    for dt in (F32, BF16):
+        assert lib.mha_workspace_bytes_ex(dt, 3, 70, 90, 256, 4) >= lib.mha_workspace_bytes(dt, 3, 70, 90, 256, 4)
+
+
+def mha_ex(lib, **kw):
+    a = dict(in_dt=BF16, out_dt=F32, xq=ALIGNED[0], xkv=ALIGNED[1], wq=ALIGNED[2], wk=ALIGNED[3], wv=ALIGNED[4],
+             wo=ALIGNED[5], out=ALIGNED[6], B=2, Lq=16, Lk=16, D=512, h=8, dk=64, vl=ALIGNED[8], vl_rank=2, causal=0,
+             p=ALIGNED[9], ws=ALIGNED[7], wsb=None)
+    a.update(kw)
+    need = lib.mha_workspace_bytes_ex(a["in_dt"], a["B"], a["Lq"], a["Lk"], a["D"], a["h"])
+    wsb = need if a["wsb"] is None else a["wsb"]
+    return lib.mha_forward_ex(a["in_dt"], a["out_dt"], a["xq"], a["xkv"], a["wq"], None, a["wk"], None, a["wv"], None,
+                              a["wo"], None, a["out"], a["B"], a["Lq"], a["Lk"], a["D"], a["h"], a["dk"], a["vl"],
+                              a["vl_rank"], a["causal"], a["p"], S(8 * 16 * 16, 16 * 16, 16), a["ws"], wsb, None)
+
+
+def test_mha_ex_validation(lib):
+    assert mha_ex(lib, B=0) == OK
+    assert mha_ex(lib, vl_rank=5) == EINVAL
+    # the inspection path needs the larger workspace
+    small = lib.mha_workspace_bytes(BF16, 2, 16, 16, 512, 8)
+    assert mha_ex(lib, wsb=small) == EWORK
+    assert mha_ex(lib, p=ALIGNED[6]) == EINVAL            # weights overlap the output
+    assert mha_ex(lib, p=ALIGNED[7]) == EINVAL            # weights overlap the workspace
+    assert mha_ex(lib, p=ctypes.c_void_p(P + 0x900000 + 2)) == EINVAL

@@ -5,11 +5,20 @@ marshals arguments: device pointers, strides, sizes and torch's current HIP
 stream.  Every step of the computation runs in the library's HIP kernels;
 there is no CPU or PyTorch fallback, and a missing library raises.
 
-    sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None)
+    sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None,
+                 return_weights=False)
         q [B,h,Lq,64], k [B,h,Lk,64], v [B,h,Lk,64] on the GPU (bf16 or fp32)
     mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, b_q=None, ..., h=8,
-                valid_lens=None, causal=False, out_dtype=None)
+                valid_lens=None, causal=False, out_dtype=None,
+                return_weights=False)
         x_q [B,Lq,D], x_kv [B,Lk,D], W [D,D] stored [out, in], b [D]
+    sdpa_decode(q, k_cache, v_cache, lens)
+        one decoding step: q [B,h,64] against caches [B,h,L,64]
+
+valid_lens is [B] (one length per sequence) or [B, Lq] (one per query).
+return_weights=True also returns the attention weights [B, h, Lq, Lk]
+(fp32).  Lengths per query or the weights take the inspection path
+(sdpa_forward_ex / mha_forward_ex: fp32 arithmetic, two passes).
 """
 import ctypes
 
@@ -60,13 +69,14 @@ def _strides4(t):
     return Strides(s[0], s[1], s[2])
 
 
-def _valid_lens(valid_lens, B, device):
+def _valid_lens(valid_lens, B, device, Lq=None):
+    """Lengths as a device int32 tensor: [B], or [B, Lq] when Lq is given."""
     torch = _torch()
     if valid_lens is None:
         return None
     vl = torch.as_tensor(valid_lens, dtype=torch.int32, device=device).contiguous()
-    if vl.shape != (B,):
-        raise ValueError(f"valid_lens must have shape ({B},)")
+    if vl.shape != (B,) and (Lq is None or vl.shape != (B, Lq)):
+        raise ValueError(f"valid_lens must have shape ({B},)" + ("" if Lq is None else f" or ({B}, {Lq})"))
     return vl
 
 
@@ -75,9 +85,11 @@ def _raise(status, what):
         raise MhaError(status, what)
 
 
-def sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None, out=None):
+def sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None, out=None, return_weights=False):
     """softmax(q k^T / sqrt(d_k)) v per (batch, head) with key-padding
-    ``valid_lens`` [B] and/or the causal mask; returns o [B, h, Lq, d_v]."""
+    ``valid_lens`` ([B] or [B, Lq]) and/or the causal mask; returns
+    o [B, h, Lq, d_v], and the weights [B, h, Lq, Lk] (fp32) when
+    ``return_weights``."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check_gpu(n, t)
@@ -89,12 +101,18 @@ def sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None, out=Non
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((B, h, Lq, dv), dtype=out_dtype, device=q.device)
-    vl = _valid_lens(valid_lens, B, q.device)
-    st = _lib.load().sdpa_forward(
-        in_dt, _dtype_code(out.dtype), _ptr(q), _strides4(q), _ptr(k), _strides4(k), _ptr(v), _strides4(v),
-        _ptr(out), _strides4(out), B, h, Lq, Lk, dk, dv, _ptr(vl), int(bool(causal)), _stream())
-    _raise(st, "sdpa_forward")
-    return out
+    vl = _valid_lens(valid_lens, B, q.device, Lq)
+    lib = _lib.load()
+    head = (in_dt, _dtype_code(out.dtype), _ptr(q), _strides4(q), _ptr(k), _strides4(k), _ptr(v), _strides4(v),
+            _ptr(out), _strides4(out), B, h, Lq, Lk, dk, dv, _ptr(vl))
+    if not return_weights and (vl is None or vl.dim() == 1):
+        _raise(lib.sdpa_forward(*head, int(bool(causal)), _stream()), "sdpa_forward")
+        return out
+    p = torch.empty((B, h, Lq, Lk), dtype=torch.float32, device=q.device) if return_weights else None
+    sp = _strides4(p) if p is not None else Strides(0, 0, 0)
+    st = lib.sdpa_forward_ex(*head, 1 if vl is None else vl.dim(), int(bool(causal)), _ptr(p), sp, _stream())
+    _raise(st, "sdpa_forward_ex")
+    return (out, p) if return_weights else out
 
 
 def sdpa_decode(q, k_cache, v_cache, lens, out_dtype=None, out=None, workspace=None):
@@ -130,8 +148,9 @@ def workspace_bytes(dtype, B, Lq, Lk, d_model, h):
 
 
 def mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, b_q=None, b_k=None, b_v=None, b_o=None, h=8,
-                valid_lens=None, causal=False, out_dtype=None, out=None, workspace=None):
-    """Multi-head attention forward; returns [B, Lq, d_model]."""
+                valid_lens=None, causal=False, out_dtype=None, out=None, workspace=None, return_weights=False):
+    """Multi-head attention forward; returns [B, Lq, d_model], and the
+    per-head weights [B, h, Lq, Lk] (fp32) when ``return_weights``."""
     torch = _torch()
     args = dict(x_q=x_q, x_kv=x_kv, w_q=w_q, w_k=w_k, w_v=w_v, w_o=w_o, b_q=b_q, b_k=b_k, b_v=b_v, b_o=b_o)
     for n, t in args.items():
@@ -144,16 +163,24 @@ def mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, b_q=None, b_k=None, b_v=None, b_o
     out_dtype = (torch.float32 if x_q.dtype == torch.bfloat16 else x_q.dtype) if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((B, Lq, D), dtype=out_dtype, device=x_q.device)
-    need = workspace_bytes(x_q.dtype, B, Lq, Lk, D, h)
+    vl = _valid_lens(valid_lens, B, x_q.device, Lq)
+    ex = return_weights or (vl is not None and vl.dim() == 2)
+    lib = _lib.load()
+    need = int((lib.mha_workspace_bytes_ex if ex else lib.mha_workspace_bytes)(in_dt, B, Lq, Lk, D, h))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x_q.device)
-    vl = _valid_lens(valid_lens, B, x_q.device)
-    st = _lib.load().mha_forward(
-        in_dt, _dtype_code(out.dtype), _ptr(x_q), _ptr(x_kv), _ptr(w_q), _ptr(b_q), _ptr(w_k), _ptr(b_k),
-        _ptr(w_v), _ptr(b_v), _ptr(w_o), _ptr(b_o), _ptr(out), B, Lq, Lk, D, h, D // h if h else 0,
-        _ptr(vl), int(bool(causal)), _ptr(workspace), workspace.numel(), _stream())
-    _raise(st, "mha_forward")
-    return out
+    head = (in_dt, _dtype_code(out.dtype), _ptr(x_q), _ptr(x_kv), _ptr(w_q), _ptr(b_q), _ptr(w_k), _ptr(b_k),
+            _ptr(w_v), _ptr(b_v), _ptr(w_o), _ptr(b_o), _ptr(out), B, Lq, Lk, D, h, D // h if h else 0, _ptr(vl))
+    if not ex:
+        st = lib.mha_forward(*head, int(bool(causal)), _ptr(workspace), workspace.numel(), _stream())
+        _raise(st, "mha_forward")
+        return out
+    p = torch.empty((B, h, Lq, Lk), dtype=torch.float32, device=x_q.device) if return_weights else None
+    sp = _strides4(p) if p is not None else Strides(0, 0, 0)
+    st = lib.mha_forward_ex(*head, 1 if vl is None else vl.dim(), int(bool(causal)), _ptr(p), sp,
+                            _ptr(workspace), workspace.numel(), _stream())
+    _raise(st, "mha_forward_ex")
+    return (out, p) if return_weights else out
 
 
 class kernel_timing:

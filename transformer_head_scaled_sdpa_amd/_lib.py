@@ -18,8 +18,9 @@ MHA_EWORKSPACE = 3
 MHA_EHIP = 4
 
 # Every function the header declares; tests check that each is exported.
-EXPORTED = ("sdpa_forward", "sdpa_decode_workspace_bytes", "sdpa_decode", "mha_workspace_bytes", "mha_forward",
-            "mha_status_string", "mha_timing_enable", "mha_timing_read")
+EXPORTED = ("sdpa_forward", "sdpa_forward_ex", "sdpa_decode_workspace_bytes", "sdpa_decode", "mha_workspace_bytes",
+            "mha_workspace_bytes_ex", "mha_forward", "mha_forward_ex", "mha_status_string", "mha_timing_enable",
+            "mha_timing_read")
 
 
 class Strides(ctypes.Structure):
@@ -48,6 +49,9 @@ def load():
     lib.sdpa_forward.restype = i
     lib.sdpa_forward.argtypes = [i, i, vp, Strides, vp, Strides, vp, Strides, vp, Strides,
                                  i, i, i, i, i, i, vp, i, vp]
+    lib.sdpa_forward_ex.restype = i
+    lib.sdpa_forward_ex.argtypes = [i, i, vp, Strides, vp, Strides, vp, Strides, vp, Strides,
+                                    i, i, i, i, i, i, vp, i, i, vp, Strides, vp]
     lib.sdpa_decode_workspace_bytes.restype = sz
     lib.sdpa_decode_workspace_bytes.argtypes = [i, i, i]
     lib.sdpa_decode.restype = i
@@ -58,6 +62,11 @@ def load():
     lib.mha_forward.restype = i
     lib.mha_forward.argtypes = [i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 i, i, i, i, i, i, vp, i, vp, sz, vp]
+    lib.mha_workspace_bytes_ex.restype = sz
+    lib.mha_workspace_bytes_ex.argtypes = [i, i, i, i, i, i]
+    lib.mha_forward_ex.restype = i
+    lib.mha_forward_ex.argtypes = [i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   i, i, i, i, i, i, vp, i, i, vp, Strides, vp, sz, vp]
     lib.mha_status_string.restype = ctypes.c_char_p
     lib.mha_status_string.argtypes = [i]
     lib.mha_timing_enable.restype = i

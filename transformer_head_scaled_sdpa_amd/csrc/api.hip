@@ -83,14 +83,22 @@ const char* mha_status_string(mha_status s) {
     return "unknown mha_status";
 }
 
-mha_status sdpa_forward(mha_dtype in_dt, mha_dtype out_dt,
-                        const void* q, mha_strides sq,
-                        const void* k, mha_strides sk,
-                        const void* v, mha_strides sv,
-                        void* o, mha_strides so,
-                        int B, int h, int Lq, int Lk, int d_k, int d_v,
-                        const int* valid_lens, int causal, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// sdpa_forward and sdpa_forward_ex: lengths per sequence (vl_rank 1) or per
+// query (2), optional weights p_attn.
+mha_status sdpa_impl(mha_dtype in_dt, mha_dtype out_dt,
+                     const void* q, mha_strides sq,
+                     const void* k, mha_strides sk,
+                     const void* v, mha_strides sv,
+                     void* o, mha_strides so,
+                     int B, int h, int Lq, int Lk, int d_k, int d_v,
+                     const int* valid_lens, int vl_rank, int causal,
+                     float* p_attn, mha_strides sp, void* stream) {
     if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
+    if (valid_lens && vl_rank != 1 && vl_rank != 2) return MHA_EINVAL;
     if (B < 0 || h <= 0 || Lq < 0 || Lk <= 0 || d_k <= 0 || d_v <= 0) return MHA_EINVAL;
     if (causal && Lq != Lk) return MHA_EINVAL;
     if (d_k != kHeadDim || d_v != kHeadDim) return MHA_ENOTSUP;
@@ -106,9 +114,33 @@ mha_status sdpa_forward(mha_dtype in_dt, mha_dtype out_dt,
     if (so.b < 0 || so.h < 0 || so.l < 0 || so.b % omult || so.h % omult || so.l % omult) return MHA_EINVAL;
     const size_t ie = elem_size(in_dt), oe = elem_size(out_dt);
     const Range ro = view_range(o, so, B, h, Lq, d_v, oe);
-    if (overlap(ro, view_range(q, sq, B, h, Lq, d_k, ie)) || overlap(ro, view_range(k, sk, B, h, Lk, d_k, ie)) ||
-        overlap(ro, view_range(v, sv, B, h, Lk, d_v, ie)))
-        return MHA_EINVAL;
+    const Range rq = view_range(q, sq, B, h, Lq, d_k, ie), rk = view_range(k, sk, B, h, Lk, d_k, ie),
+                rv = view_range(v, sv, B, h, Lk, d_v, ie);
+    if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv)) return MHA_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p_attn || (valid_lens && vl_rank == 2)) {
+        if (p_attn) {
+            if (reinterpret_cast<uintptr_t>(p_attn) & 3u) return MHA_EINVAL;
+            if (sp.b < 0 || sp.h < 0 || sp.l < 0) return MHA_EINVAL;
+            const Range rp = view_range(p_attn, sp, B, h, Lq, Lk, 4);
+            if (overlap(rp, ro) || overlap(rp, rq) || overlap(rp, rk) || overlap(rp, rv)) return MHA_EINVAL;
+        }
+        mha::WeightsArgs w;
+        w.q = q; w.k = k; w.v = v; w.o = o;
+        w.sq[0] = sq.b; w.sq[1] = sq.h; w.sq[2] = sq.l;
+        w.sk[0] = sk.b; w.sk[1] = sk.h; w.sk[2] = sk.l;
+        w.sv[0] = sv.b; w.sv[1] = sv.h; w.sv[2] = sv.l;
+        w.so[0] = so.b; w.so[1] = so.h; w.so[2] = so.l;
+        w.B = B; w.H = h; w.Lq = Lq; w.Lk = Lk;
+        w.valid_lens = valid_lens;
+        w.vl_rank = valid_lens ? vl_rank : 0;
+        w.causal = causal ? 1 : 0;
+        w.in_f32 = in_dt == MHA_F32;
+        w.out_f32 = out_dt == MHA_F32;
+        w.p = p_attn;
+        w.sp[0] = sp.b; w.sp[1] = sp.h; w.sp[2] = sp.l;
+        return hip_status(timed("sdpa_weights", s, [&] { return mha::launch_sdpa_weights(w, s); }));
+    }
 
     mha::SdpaArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o;
@@ -119,9 +151,35 @@ mha_status sdpa_forward(mha_dtype in_dt, mha_dtype out_dt,
     a.B = B; a.H = h; a.Lq = Lq; a.Lk = Lk;
     a.valid_lens = valid_lens;
     a.causal = causal ? 1 : 0;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     if (in_dt == MHA_F32) return hip_status(timed("sdpa_f32", s, [&] { return mha::launch_sdpa_f32(a, s); }));
     return hip_status(timed("sdpa_bf16", s, [&] { return mha::launch_sdpa_bf16(a, out_dt == MHA_F32, s); }));
+}
+
+}  // namespace
+
+extern "C" {
+
+mha_status sdpa_forward(mha_dtype in_dt, mha_dtype out_dt,
+                        const void* q, mha_strides sq,
+                        const void* k, mha_strides sk,
+                        const void* v, mha_strides sv,
+                        void* o, mha_strides so,
+                        int B, int h, int Lq, int Lk, int d_k, int d_v,
+                        const int* valid_lens, int causal, void* stream) {
+    return sdpa_impl(in_dt, out_dt, q, sq, k, sk, v, sv, o, so, B, h, Lq, Lk, d_k, d_v, valid_lens, 1, causal,
+                     nullptr, mha_strides{0, 0, 0}, stream);
+}
+
+mha_status sdpa_forward_ex(mha_dtype in_dt, mha_dtype out_dt,
+                           const void* q, mha_strides sq,
+                           const void* k, mha_strides sk,
+                           const void* v, mha_strides sv,
+                           void* o, mha_strides so,
+                           int B, int h, int Lq, int Lk, int d_k, int d_v,
+                           const int* valid_lens, int vl_rank, int causal,
+                           float* p_attn, mha_strides sp, void* stream) {
+    return sdpa_impl(in_dt, out_dt, q, sq, k, sk, v, sv, o, so, B, h, Lq, Lk, d_k, d_v, valid_lens, vl_rank,
+                     causal, p_attn, sp, stream);
 }
 
 size_t sdpa_decode_workspace_bytes(int B, int h, int L) {
@@ -186,17 +244,32 @@ size_t mha_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, 
     return in_dt == MHA_BF16 ? q : 2 * q + 2 * kv;
 }
 
-mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
-                       const void* x_q, const void* x_kv,
-                       const void* w_q, const void* b_q,
-                       const void* w_k, const void* b_k,
-                       const void* w_v, const void* b_v,
-                       const void* w_o, const void* b_o,
-                       void* out,
-                       int B, int Lq, int Lk, int d_model, int h, int d_k,
-                       const int* valid_lens, int causal,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+size_t mha_workspace_bytes_ex(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h) {
+    if (!valid_dtype(in_dt) || B < 0 || Lq < 0 || Lk < 0 || d_model <= 0 || h <= 0 || d_model % h) return 0;
+    // merged heads in in_dt, then Q, K, V in fp32
+    return round_up((size_t)B * Lq * d_model * elem_size(in_dt), 256) + round_up((size_t)B * Lq * d_model * 4, 256) +
+           2 * round_up((size_t)B * Lk * d_model * 4, 256);
+}
+
+}  // extern "C"
+
+namespace {
+
+// mha_forward and mha_forward_ex (lengths per query, optional weights).
+mha_status mha_impl(mha_dtype in_dt, mha_dtype out_dt,
+                    const void* x_q, const void* x_kv,
+                    const void* w_q, const void* b_q,
+                    const void* w_k, const void* b_k,
+                    const void* w_v, const void* b_v,
+                    const void* w_o, const void* b_o,
+                    void* out,
+                    int B, int Lq, int Lk, int d_model, int h, int d_k,
+                    const int* valid_lens, int vl_rank, int causal, float* p_attn, mha_strides sp,
+                    void* workspace, size_t workspace_bytes, void* stream) {
     if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
+    if (valid_lens && vl_rank != 1 && vl_rank != 2) return MHA_EINVAL;
+    // The inspection path: projections to fp32, attention with the weights.
+    const bool ex = p_attn || (valid_lens && vl_rank == 2);
     if (B < 0 || Lq < 0 || Lk <= 0 || d_model <= 0 || h <= 0 || d_k <= 0) return MHA_EINVAL;
     if ((long long)h * d_k != d_model) return MHA_EINVAL;
     if (causal && Lq != Lk) return MHA_EINVAL;
@@ -207,7 +280,8 @@ mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
     const void* ptrs[] = {x_q, x_kv, w_q, w_k, w_v, w_o, out, workspace, b_q, b_k, b_v, b_o};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MHA_EINVAL;
-    const size_t need = mha_workspace_bytes(in_dt, B, Lq, Lk, d_model, h);
+    const size_t need = ex ? mha_workspace_bytes_ex(in_dt, B, Lq, Lk, d_model, h)
+                           : mha_workspace_bytes(in_dt, B, Lq, Lk, d_model, h);
     if (workspace_bytes < need) return MHA_EWORKSPACE;
 
     const size_t ie = elem_size(in_dt), oe = elem_size(out_dt);
@@ -234,13 +308,51 @@ mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
         const Range rb{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (size_t)d_model * ie};
         if (overlap(rout, rb) || overlap(rws, rb)) return MHA_EINVAL;
     }
+    if (p_attn) {
+        if (reinterpret_cast<uintptr_t>(p_attn) & 3u) return MHA_EINVAL;
+        if (sp.b < 0 || sp.h < 0 || sp.l < 0) return MHA_EINVAL;
+        const Range rp = view_range(p_attn, sp, B, h, Lq, Lk, 4);
+        if (overlap(rp, rout)) return MHA_EINVAL;
+        for (const Range& r : inputs)
+            if (overlap(rp, r)) return MHA_EINVAL;
+    }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* w = static_cast<char*>(workspace);
     const bool bf16 = in_dt == MHA_BF16;
     void* Ocat = w;
     hipError_t e;
-    if (bf16) {
+    if (ex) {
+        // Workspace: merged heads [B*Lq, D] (in_dt), then fp32 Q [B*Lq, D], K, V [B*Lk, D].
+        char* Q = w + round_up((size_t)B * Lq * d_model * ie, 256);
+        char* K = Q + round_up((size_t)B * Lq * d_model * 4, 256);
+        char* V = K + round_up((size_t)B * Lk * d_model * 4, 256);
+        mha::GemmArgs g;
+        g.nprob = 3;
+        g.N = d_model;
+        g.K = d_model;
+        g.p[0] = {x_q, w_q, b_q, Q, B * Lq};
+        g.p[1] = {x_kv, w_k, b_k, K, B * Lk};
+        g.p[2] = {x_kv, w_v, b_v, V, B * Lk};
+        e = timed("qkv_proj_ex", s, [&] { return bf16 ? mha::launch_gemm_bf16(g, true, s) : mha::launch_gemm_f32(g, s); });
+        if (e != hipSuccess) return MHA_EHIP;
+        mha::WeightsArgs a;
+        a.q = Q; a.k = K; a.v = V; a.o = Ocat;
+        a.sq[0] = (long long)Lq * d_model; a.sq[1] = d_k; a.sq[2] = d_model;
+        a.sk[0] = (long long)Lk * d_model; a.sk[1] = d_k; a.sk[2] = d_model;
+        a.sv[0] = (long long)Lk * d_model; a.sv[1] = d_k; a.sv[2] = d_model;
+        a.so[0] = (long long)Lq * d_model; a.so[1] = d_k; a.so[2] = d_model;
+        a.B = B; a.H = h; a.Lq = Lq; a.Lk = Lk;
+        a.valid_lens = valid_lens;
+        a.vl_rank = valid_lens ? vl_rank : 0;
+        a.causal = causal ? 1 : 0;
+        a.in_f32 = true;
+        a.out_f32 = !bf16;
+        a.p = p_attn;
+        a.sp[0] = sp.b; a.sp[1] = sp.h; a.sp[2] = sp.l;
+        e = timed("sdpa_weights", s, [&] { return mha::launch_sdpa_weights(a, s); });
+        if (e != hipSuccess) return MHA_EHIP;
+    } else if (bf16) {
         // 1-2. Q/K/V projections, head split, attention and head merge in one
         // kernel: the merged heads [B*Lq, D] land in the workspace.
         mha::FusedArgs f;
@@ -296,6 +408,38 @@ mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
         return bf16 ? mha::launch_gemm_bf16(go, out_dt == MHA_F32, s) : mha::launch_gemm_f32(go, s);
     });
     return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
+                       const void* x_q, const void* x_kv,
+                       const void* w_q, const void* b_q,
+                       const void* w_k, const void* b_k,
+                       const void* w_v, const void* b_v,
+                       const void* w_o, const void* b_o,
+                       void* out,
+                       int B, int Lq, int Lk, int d_model, int h, int d_k,
+                       const int* valid_lens, int causal,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    return mha_impl(in_dt, out_dt, x_q, x_kv, w_q, b_q, w_k, b_k, w_v, b_v, w_o, b_o, out, B, Lq, Lk, d_model, h,
+                    d_k, valid_lens, 1, causal, nullptr, mha_strides{0, 0, 0}, workspace, workspace_bytes, stream);
+}
+
+mha_status mha_forward_ex(mha_dtype in_dt, mha_dtype out_dt,
+                          const void* x_q, const void* x_kv,
+                          const void* w_q, const void* b_q,
+                          const void* w_k, const void* b_k,
+                          const void* w_v, const void* b_v,
+                          const void* w_o, const void* b_o,
+                          void* out,
+                          int B, int Lq, int Lk, int d_model, int h, int d_k,
+                          const int* valid_lens, int vl_rank, int causal, float* p_attn, mha_strides sp,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return mha_impl(in_dt, out_dt, x_q, x_kv, w_q, b_q, w_k, b_k, w_v, b_v, w_o, b_o, out, B, Lq, Lk, d_model, h,
+                    d_k, valid_lens, vl_rank, causal, p_attn, sp, workspace, workspace_bytes, stream);
 }
 
 mha_status mha_timing_enable(int repeat) {

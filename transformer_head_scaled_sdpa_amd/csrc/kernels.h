@@ -64,6 +64,23 @@ struct DecodeArgs {
     const int* lens;   // device int32 [B]
 };
 
+// The inspection path: lengths per sequence or per query, optional fp32
+// attention weights [B, H, Lq, Lk] (unit stride over keys), fp32 arithmetic.
+struct WeightsArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    long long sq[3], sk[3], sv[3], so[3];   // element strides (batch, head, position)
+    int B, H, Lq, Lk;
+    const int* valid_lens;                  // device int32 [B] or [B, Lq] (vl_rank 1, 2), or nullptr
+    int vl_rank;                            // 0 (no lengths), 1, 2
+    int causal;
+    bool in_f32, out_f32;
+    float* p;                               // weights or nullptr
+    long long sp[3];
+};
+
 hipError_t launch_sdpa_bf16(const SdpaArgs& a, bool out_f32, hipStream_t s);
 int decode_splits(int L);
 size_t decode_workspace_bytes(int B, int H, int L);
@@ -75,6 +92,7 @@ hipError_t launch_mha_attn_fused(const FusedArgs& a, hipStream_t s);
 bool mha_attn_fused_small_fits(const FusedArgs& a);
 hipError_t launch_mha_attn_fused_small(const FusedArgs& a, hipStream_t s);
 hipError_t launch_sdpa_f32(const SdpaArgs& a, hipStream_t s);
+hipError_t launch_sdpa_weights(const WeightsArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool out_f32, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 
