@@ -15,6 +15,9 @@ Functions and the passages they follow:
   ``valid_lens`` (d2l Transformer digest, multi-head attention prerequisites)
   and the lower-triangular causal mask ("Transformer" study notes,
   mask-generation section), combined by AND.
+* ``sdpa_backward`` -- the gradients of ``sdpa`` with respect to q, k, v
+  for a given gradient of the output: the softmax Jacobian written out
+  (the pages train these models end to end).
 * ``mha``     -- the four projections, head split, sdpa per head, head merge
   and the output projection ("Transformer" study notes, multi-head attention
   formula and class).
@@ -50,6 +53,8 @@ def _open(path):
     lib.oracle_mha_f64.restype = ctypes.c_int
     lib.oracle_mha_f64.argtypes = [_dp] * 11 + [ctypes.c_int] * 5 + [
         _ip, ctypes.c_int, ctypes.c_int, _ip, ctypes.c_int, ctypes.c_int]
+    lib.oracle_sdpa_backward_f64.restype = ctypes.c_int
+    lib.oracle_sdpa_backward_f64.argtypes = [_dp] * 7 + [ctypes.c_int] * 6 + [_ip, ctypes.c_int, ctypes.c_int]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     return lib
@@ -151,6 +156,26 @@ def sdpa(q, k, v, valid_lens=None, causal=False, rows=None, return_weights=False
     if rc != 0:
         raise ValueError("oracle_sdpa_f64 rejected its arguments")
     return (o, p) if return_weights else o
+
+
+def sdpa_backward(q, k, v, dout, valid_lens=None, causal=False):
+    """Gradients (dq, dk, dv) of ``sdpa(q, k, v, valid_lens, causal)`` for the
+    output gradient ``dout`` [B,h,Lq,dv]."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, h, Lq, dk = q.shape
+    Lk = k.shape[2]
+    dv = v.shape[3]
+    assert k.shape == (B, h, Lk, dk) and v.shape == (B, h, Lk, dv) and g.shape == (B, h, Lq, dv)
+    vl = _i32(valid_lens)
+    if vl is not None:
+        assert vl.shape in ((B,), (B, Lq))
+    dq, dkk, dvv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    rc = _load().oracle_sdpa_backward_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dq), _ptr(dkk), _ptr(dvv),
+                                          B, h, Lq, Lk, dk, dv, _iptr(vl), int(vl is not None and vl.ndim == 2),
+                                          int(bool(causal)))
+    if rc != 0:
+        raise ValueError("oracle_sdpa_backward_f64 rejected its arguments")
+    return dq, dkk, dvv
 
 
 def mha(x_q, x_kv, w_q, w_k, w_v, w_o, b_q=None, b_k=None, b_v=None, b_o=None,

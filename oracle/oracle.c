@@ -275,6 +275,76 @@ done:
     return rc;
 }
 
+/*
+ * Gradients of the attention above (the backward pass the pages' training
+ * loops take through it: The Annotated Transformer and the d2l digest train
+ * these models end to end).  For one (batch, head), with tau = 1/sqrt(dk),
+ * p_i = softmax of row i as in attend_row and a loss whose gradient with
+ * respect to o is do:
+ *   dv_j  = sum_i p_ij do_i
+ *   dp_ij = do_i . v_j
+ *   ds_ij = p_ij (dp_ij - sum_l p_il dp_il)          (softmax Jacobian)
+ *   dq_i  = tau sum_j ds_ij k_j,   dk_j = tau sum_i ds_ij q_i
+ * where a masked score is the constant fill, so ds_ij of a masked pair does
+ * not reach q or k (its p_ij is 0 anyway unless the whole row is masked).
+ *   q, k, v, do as for oracle_sdpa_f64 (do shaped like o, all Lq rows);
+ *   dq [B, h, Lq, dk], dk [B, h, Lk, dk], dv [B, h, Lk, dv] are written.
+ * Returns 0, or -1 on a bad argument / allocation failure.
+ */
+int oracle_sdpa_backward_f64(const double* q, const double* k, const double* v, const double* dout,
+                             double* dq, double* dk, double* dv,
+                             int B, int h, int Lq, int Lk, int dk_, int dv_,
+                             const int* valid_lens, int vl_per_query, int causal)
+{
+    if (B < 0 || h <= 0 || Lq < 0 || Lk <= 0 || dk_ <= 0 || dv_ <= 0) return -1;
+    const double tau = 1.0 / sqrt((double)dk_);
+    int bad = 0;
+    long bh;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (bh = 0; bh < (long)B * h; ++bh) {
+        const int b = (int)(bh / h);
+        double* p = (double*)malloc(sizeof(double) * (size_t)Lk);
+        double* s = (double*)malloc(sizeof(double) * (size_t)Lk);
+        double* o = (double*)malloc(sizeof(double) * (size_t)dv_);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)Lk);
+        if (!p || !s || !o || !dp) { bad = 1; free(p); free(s); free(o); free(dp); continue; }
+        const double* qb = q + bh * (long)Lq * dk_;
+        const double* kb = k + bh * (long)Lk * dk_;
+        const double* vb = v + bh * (long)Lk * dv_;
+        const double* gb = dout + bh * (long)Lq * dv_;
+        double* dqb = dq + bh * (long)Lq * dk_;
+        double* dkb = dk + bh * (long)Lk * dk_;
+        double* dvb = dv + bh * (long)Lk * dv_;
+        for (long x = 0; x < (long)Lq * dk_; ++x) dqb[x] = 0.0;
+        for (long x = 0; x < (long)Lk * dk_; ++x) dkb[x] = 0.0;
+        for (long x = 0; x < (long)Lk * dv_; ++x) dvb[x] = 0.0;
+        for (int i = 0; i < Lq; ++i) {
+            const double* qi = qb + (long)i * dk_;
+            const double* gi = gb + (long)i * dv_;
+            /* the forward row: weights p_i */
+            attend_row(qi, kb, vb, o, p, s, Lq, Lk, dk_, dv_, valid_lens, vl_per_query, causal, b, i);
+            double rowsum = 0.0;
+            for (int j = 0; j < Lk; ++j) {
+                double acc = 0.0;
+                for (int t = 0; t < dv_; ++t) acc += gi[t] * vb[(long)j * dv_ + t];
+                dp[j] = acc;
+                rowsum += p[j] * dp[j];
+            }
+            for (int j = 0; j < Lk; ++j) {
+                for (int t = 0; t < dv_; ++t) dvb[(long)j * dv_ + t] += p[j] * gi[t];
+                if (!key_allowed(valid_lens, vl_per_query, Lq, causal, b, i, j)) continue;
+                const double ds = p[j] * (dp[j] - rowsum);
+                for (int t = 0; t < dk_; ++t) {
+                    dqb[(long)i * dk_ + t] += tau * ds * kb[(long)j * dk_ + t];
+                    dkb[(long)j * dk_ + t] += tau * ds * qi[t];
+                }
+            }
+        }
+        free(p); free(s); free(o); free(dp);
+    }
+    return bad ? -1 : 0;
+}
+
 /* Number of OpenMP threads the oracle runs with (1 without OpenMP). */
 int oracle_num_threads(void)
 {

@@ -340,6 +340,82 @@ def pin_mha_valid_lens_2d_lengths_i_plus_1_equal_causal():
     _close(oracle.mha(x, x, *w, h=2, valid_lens=vl2), oracle.mha(x, x, *w, h=2, causal=True), 0.0)
 
 
+def _fd_grads(q, k, v, g, **mask):
+    """Central finite differences of sum(sdpa(q, k, v) * g) in each element."""
+    out = []
+    for x in (q, k, v):
+        d = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            e = 1e-6
+            x[idx] += e
+            up = np.sum(oracle.sdpa(q, k, v, **mask) * g)
+            x[idx] -= 2 * e
+            dn = np.sum(oracle.sdpa(q, k, v, **mask) * g)
+            x[idx] += e
+            d[idx] = (up - dn) / (2 * e)
+        out.append(d)
+    return out
+
+
+def pin_backward_matches_finite_differences():
+    """The gradients equal central differences of the forward oracle, with
+    key padding (a fully masked sequence included), the causal rule, and
+    lengths per query."""
+    r = _rng(51)
+    B, h, Lq, Lk, d = 2, 1, 3, 4, 3
+    q = r.standard_normal((B, h, Lq, d))
+    k = r.standard_normal((B, h, Lk, d))
+    v = r.standard_normal((B, h, Lk, d))
+    g = r.standard_normal((B, h, Lq, d))
+    for mask in ({}, {"valid_lens": [2, 0]}, {"valid_lens": np.array([[1, 3, 0], [4, 2, 2]], np.int32)}):
+        fd = _fd_grads(q, k, v, g, **mask)
+        for a, b in zip(oracle.sdpa_backward(q, k, v, g, **mask), fd):
+            _close(a, b, 1e-7)
+    qs = r.standard_normal((1, 2, 4, d))
+    ks, vs, gs = (r.standard_normal((1, 2, 4, d)) for _ in range(3))
+    fd = _fd_grads(qs, ks, vs, gs, causal=True)
+    for a, b in zip(oracle.sdpa_backward(qs, ks, vs, gs, causal=True), fd):
+        _close(a, b, 1e-7)
+
+
+def pin_backward_matches_torch_float64_autograd():
+    """torch's float64 CPU autograd through the pages' printed attention
+    (scores, masked_fill with -1e9, softmax, product with V)."""
+    import torch
+    r = _rng(52)
+    B, h, Lq, Lk, d = 2, 3, 5, 6, 4
+    q, k, v = (r.standard_normal(s) for s in ((B, h, Lq, d), (B, h, Lk, d), (B, h, Lk, d)))
+    g = r.standard_normal((B, h, Lq, d))
+    vl = np.array([4, 6], np.int32)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    sc = torch.matmul(tq, tk.transpose(-2, -1)) / math.sqrt(d)
+    allowed = torch.arange(Lk)[None, None, None, :] < torch.tensor(vl)[:, None, None, None]
+    sc = sc.masked_fill(~allowed, -1e9)
+    o = torch.matmul(torch.softmax(sc, dim=-1), tv)
+    (o * torch.tensor(g)).sum().backward()
+    for a, b in zip(oracle.sdpa_backward(q, k, v, g, valid_lens=vl), (tq.grad, tk.grad, tv.grad)):
+        _close(a, b.numpy(), 1e-12)
+
+
+def pin_backward_closed_forms():
+    """One allowed key: the weights are constant, so dq = dk = 0 and dv of
+    that key is the sum of the output gradients.  Identical keys: uniform
+    weights, dq = 0 and dv_j = sum_i do_i / Lk."""
+    r = _rng(53)
+    B, h, Lq, Lk, d = 1, 2, 4, 5, 3
+    q, k, v = (r.standard_normal(s) for s in ((B, h, Lq, d), (B, h, Lk, d), (B, h, Lk, d)))
+    g = r.standard_normal((B, h, Lq, d))
+    dq, dk, dv = oracle.sdpa_backward(q, k, v, g, valid_lens=[1])
+    _close(dq, np.zeros_like(dq))
+    _close(dk, np.zeros_like(dk))
+    _close(dv[:, :, 0], g.sum(axis=2))
+    _close(dv[:, :, 1:], np.zeros_like(dv[:, :, 1:]))
+    ks = np.repeat(k[:, :, :1], Lk, axis=2)
+    dq, dk, dv = oracle.sdpa_backward(q, ks, v, g)
+    _close(dq, np.zeros_like(dq))
+    _close(dv, np.repeat(g.sum(axis=2, keepdims=True) / Lk, Lk, axis=2))
+
+
 def pin_row_subset_consistent():
     r = _rng(37)
     x = r.standard_normal((2, 9, 16))

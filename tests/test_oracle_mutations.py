@@ -30,6 +30,11 @@ MUTATIONS = [
     ("mask_uses_query_length", "if (valid_lens && !(j < valid_lens[b]))",
      "if (valid_lens && !(i < valid_lens[b]))"),
     ("per_query_length_rows_reversed", "valid_lens[(long)b * Lq + i]", "valid_lens[(long)b * Lq + (Lq - 1 - i)]"),
+    ("backward_dq_without_scale", "dqb[(long)i * dk_ + t] += tau * ds", "dqb[(long)i * dk_ + t] += ds"),
+    ("backward_rowsum_unweighted", "rowsum += p[j] * dp[j];", "rowsum += dp[j];"),
+    ("backward_dv_uses_ds", "dvb[(long)j * dv_ + t] += p[j] * gi[t];", "dvb[(long)j * dv_ + t] += dp[j] * gi[t];"),
+    ("backward_masked_pairs_propagate",
+     "if (!key_allowed(valid_lens, vl_per_query, Lq, causal, b, i, j)) continue;", ""),
     ("per_query_length_ignores_query", "valid_lens[(long)b * Lq + i]", "valid_lens[(long)b * Lq]"),
 ]
 
