@@ -133,6 +133,40 @@ mha_status sdpa_decode(mha_dtype in_dt, mha_dtype out_dt,
                        int B, int h, int L, int d_k, int d_v, const int* lens,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sdpa_backward -- gradients of sdpa_forward with respect to q, k and v for
+ * the gradient `dout` of its output (the backward pass the pages' training
+ * loops take through the attention function of The Annotated Transformer).
+ * With tau = 1/sqrt(d_k), p the attention weights and D_i = dout_i . o_i:
+ *   dv_j = sum_i p_ij dout_i,   ds_ij = p_ij (dout_i . v_j - D_i),
+ *   dq_i = tau sum_j ds_ij k_j, dk_j = tau sum_i ds_ij q_i   (allowed pairs)
+ *   q, k, v, o, dout : the forward's inputs and output and the output's
+ *          gradient, all in in_dt, [B, h, L, 64] views as for sdpa_forward.
+ *   dq, dk, dv : written in out_dt, same shapes as q, k, v; no overlap with
+ *          each other, the inputs or the workspace.
+ *   valid_lens, vl_rank, causal : the forward's masks (as sdpa_forward_ex).
+ *   workspace : device buffer of at least sdpa_backward_workspace_bytes(B,
+ *          h, Lq) bytes, 16-byte aligned; it receives each query's
+ *          log-sum-exp and D_i.
+ * Arithmetic is fp32 (FMA): each row's weights are recomputed from a first
+ * pass over the keys, then dq is accumulated per query and dk, dv per key.
+ * Requirements otherwise as for sdpa_forward.
+ */
+size_t sdpa_backward_workspace_bytes(int B, int h, int Lq);
+
+mha_status sdpa_backward(mha_dtype in_dt, mha_dtype out_dt,
+                         const void* q, mha_strides sq,
+                         const void* k, mha_strides sk,
+                         const void* v, mha_strides sv,
+                         const void* o, mha_strides so,
+                         const void* dout, mha_strides sdo,
+                         void* dq, mha_strides sdq,
+                         void* dk, mha_strides sdk,
+                         void* dv, mha_strides sdv,
+                         int B, int h, int Lq, int Lk, int d_k, int d_v,
+                         const int* valid_lens, int vl_rank, int causal,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace mha_forward needs: for MHA_BF16 the merged head
  * output [B*Lq, d_model] in bf16; for MHA_F32 the projected Q, K, V and the
  * merged head output in fp32.  Each region is 256-byte aligned.  Returns 0

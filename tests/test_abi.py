@@ -216,3 +216,32 @@ def test_mha_ex_validation(lib):
     assert mha_ex(lib, p=ALIGNED[6]) == EINVAL            # weights overlap the output
     assert mha_ex(lib, p=ALIGNED[7]) == EINVAL            # weights overlap the workspace
     assert mha_ex(lib, p=ctypes.c_void_p(P + 0x900000 + 2)) == EINVAL
+
+
+def bwd(lib, **kw):
+    a = dict(in_dt=BF16, out_dt=F32, B=2, h=4, Lq=64, Lk=64, dk=64, dv=64, vl=None, vl_rank=1, causal=0,
+             ws=ALIGNED[8], wsb=None, dq=ALIGNED[5], dk_=ALIGNED[6], dv_=ALIGNED[7])
+    a.update(kw)
+    st = S(4 * 64 * 64, 64 * 64, 64)
+    need = lib.sdpa_backward_workspace_bytes(a["B"], a["h"], a["Lq"])
+    wsb = need if a["wsb"] is None else a["wsb"]
+    return lib.sdpa_backward(a["in_dt"], a["out_dt"], ALIGNED[0], st, ALIGNED[1], st, ALIGNED[2], st, ALIGNED[3], st,
+                             ALIGNED[4], st, a["dq"], st, a["dk_"], st, a["dv_"], st, a["B"], a["h"], a["Lq"], a["Lk"],
+                             a["dk"], a["dv"], a["vl"], a["vl_rank"], a["causal"], a["ws"], wsb, None)
+
+
+def test_backward_workspace_and_validation(lib):
+    # (log-sum-exp, D) per query in fp32, rounded up to 256 bytes
+    assert lib.sdpa_backward_workspace_bytes(2, 4, 64) == 2 * 4 * 64 * 8
+    assert lib.sdpa_backward_workspace_bytes(1, 1, 3) == 256
+    assert lib.sdpa_backward_workspace_bytes(1, 0, 3) == 0
+    assert bwd(lib, B=0) == OK
+    assert bwd(lib, dk=32) == ENOTSUP
+    assert bwd(lib, in_dt=F32, out_dt=BF16) == ENOTSUP
+    assert bwd(lib, causal=1, Lk=60) == EINVAL
+    assert bwd(lib, vl=ALIGNED[9], vl_rank=4) == EINVAL
+    assert bwd(lib, wsb=100) == EWORK
+    assert bwd(lib, dq=ALIGNED[1]) == EINVAL        # dq overlaps k
+    assert bwd(lib, dv_=ALIGNED[6]) == EINVAL       # dv overlaps dk
+    assert bwd(lib, ws=ALIGNED[5]) == EINVAL        # workspace overlaps dq
+    assert bwd(lib, dk_=ctypes.c_void_p(P + 0x600000 + 8)) == EINVAL

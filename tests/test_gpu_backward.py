@@ -1,0 +1,77 @@
+"""GPU parity of sdpa_backward (dq, dk, dv) through the C ABI against the
+fp64 oracle's backward.
+
+The kernels compute in fp32 on the exact input values.  fp32 inputs are held
+to the fp32 bar (norm-wise 1e-5).  bf16 inputs carry the forward output o
+rounded to bf16, which enters D_i = do_i . o_i, so they are held to the bf16
+bar."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import assert_bf16, assert_fp32, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # B, h, Lq, Lk, causal, lengths, dtype
+    (2, 3, 70, 70, True, None, "f32"),
+    (2, 2, 45, 100, False, "2d", "bf16"),
+    (2, 4, 130, 77, False, "1d", "f32"),
+    (2, 2, 33, 33, True, "2d", "bf16"),
+    (3, 1, 64, 96, False, "1d", "bf16"),
+    (2, 4, 512, 512, True, None, "bf16"),
+]
+
+
+def _lengths(kind, rng, B, Lq, Lk):
+    if kind is None:
+        return None
+    if kind == "1d":
+        vl = rng.integers(1, Lk + 1, size=B).astype(np.int32)
+        vl[0] = 0                                            # a fully masked sequence
+        return vl
+    vl = rng.integers(-1, Lk + 3, size=(B, Lq)).astype(np.int32)
+    vl[0, :3] = [0, 1, Lk]
+    return vl
+
+
+@pytest.mark.parametrize("B,h,Lq,Lk,causal,kind,dt", CASES)
+def test_backward_vs_oracle(B, h, Lq, Lk, causal, kind, dt):
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    rng = np.random.Generator(np.random.PCG64(B * 7919 + Lq * 31 + Lk))
+    q = workloads._finish(rng.standard_normal((B, h, Lq, 64)), dt)
+    k = workloads._finish(rng.standard_normal((B, h, Lk, 64)), dt)
+    v = workloads._finish(rng.standard_normal((B, h, Lk, 64)), dt)
+    g = workloads._finish(rng.standard_normal((B, h, Lq, 64)), dt)
+    vl = _lengths(kind, rng, B, Lq, Lk)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    tq, tk, tv, tg = (to_device(x, tdt) for x in (q, k, v, g))
+    o = mha.sdpa_forward(tq, tk, tv, valid_lens=vl, causal=causal)          # the forward output, in dt
+    gq, gk, gv = mha.sdpa_backward(tq, tk, tv, o, tg, valid_lens=vl, causal=causal, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.sdpa_backward(q, k, v, g, valid_lens=vl, causal=causal)
+    check = assert_fp32 if dt == "f32" else assert_bf16
+    for name, got, ref in (("dq", gq, rq), ("dk", gk, rk), ("dv", gv, rv)):
+        e = check(to_host(got), ref, f"{name} B{B} h{h} Lq{Lq} Lk{Lk} causal={causal} lengths={kind} {dt}")
+        print(name, e)
+
+
+def test_backward_bf16_outputs_and_strided_views():
+    """bf16 gradients into [B, L, h, d] views (strided), lengths per sequence."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    rng = np.random.Generator(np.random.PCG64(99))
+    B, h, L = 2, 3, 90
+    x = [workloads._finish(rng.standard_normal((B, L, h, 64)), "bf16") for _ in range(4)]
+    vl = np.array([90, 41], np.int32)
+    tq, tk, tv, tg = (to_device(a, torch.bfloat16).transpose(1, 2) for a in x)   # [B, h, L, d] views
+    o = mha.sdpa_forward(tq, tk, tv, valid_lens=vl)
+    gq, gk, gv = mha.sdpa_backward(tq, tk, tv, o, tg, valid_lens=vl)
+    torch.cuda.synchronize()
+    q, k, v, g = (a.transpose(0, 2, 1, 3) for a in x)
+    for got, ref in zip((gq, gk, gv), oracle.sdpa_backward(q, k, v, g, valid_lens=vl)):
+        assert got.dtype == torch.bfloat16
+        assert_bf16(to_host(got), ref, "bf16 gradients")

@@ -12,6 +12,8 @@ there is no CPU or PyTorch fallback, and a missing library raises.
                 valid_lens=None, causal=False, out_dtype=None,
                 return_weights=False)
         x_q [B,Lq,D], x_kv [B,Lk,D], W [D,D] stored [out, in], b [D]
+    sdpa_backward(q, k, v, o, dout, valid_lens=None, causal=False)
+        -> dq, dk, dv (gradients of sdpa_forward for the output gradient dout)
     sdpa_decode(q, k_cache, v_cache, lens)
         one decoding step: q [B,h,64] against caches [B,h,L,64]
 
@@ -25,7 +27,7 @@ import ctypes
 from . import _lib
 from ._lib import MhaError, MHA_BF16, MHA_F32, MHA_OK, Strides
 
-__all__ = ["sdpa_forward", "sdpa_decode", "mha_forward", "workspace_bytes", "kernel_timing", "MhaError", "library"]
+__all__ = ["sdpa_forward", "sdpa_backward", "sdpa_decode", "mha_forward", "workspace_bytes", "kernel_timing", "MhaError", "library"]
 
 
 def library():
@@ -113,6 +115,35 @@ def sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None, out=Non
     st = lib.sdpa_forward_ex(*head, 1 if vl is None else vl.dim(), int(bool(causal)), _ptr(p), sp, _stream())
     _raise(st, "sdpa_forward_ex")
     return (out, p) if return_weights else out
+
+
+def sdpa_backward(q, k, v, o, dout, valid_lens=None, causal=False, out_dtype=None, workspace=None):
+    """Gradients (dq, dk, dv) of sdpa_forward(q, k, v, valid_lens, causal),
+    whose output was ``o``, for the output gradient ``dout``."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_gpu(n, t)
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, o and dout must share one dtype")
+    B, h, Lq, dk = q.shape
+    Lk, dv = k.shape[2], v.shape[3]
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    gq = torch.empty((B, h, Lq, dk), dtype=out_dtype, device=q.device)
+    gk = torch.empty((B, h, Lk, dk), dtype=out_dtype, device=q.device)
+    gv = torch.empty((B, h, Lk, dv), dtype=out_dtype, device=q.device)
+    vl = _valid_lens(valid_lens, B, q.device, Lq)
+    lib = _lib.load()
+    need = int(lib.sdpa_backward_workspace_bytes(B, h, Lq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    args = []
+    for t in (q, k, v, o, dout, gq, gk, gv):
+        args += [_ptr(t), _strides4(t)]
+    st = lib.sdpa_backward(_dtype_code(q.dtype), _dtype_code(out_dtype), *args, B, h, Lq, Lk, dk, dv, _ptr(vl),
+                           1 if vl is None else vl.dim(), int(bool(causal)), _ptr(workspace), workspace.numel(),
+                           _stream())
+    _raise(st, "sdpa_backward")
+    return gq, gk, gv
 
 
 def sdpa_decode(q, k_cache, v_cache, lens, out_dtype=None, out=None, workspace=None):

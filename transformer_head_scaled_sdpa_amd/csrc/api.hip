@@ -182,6 +182,77 @@ mha_status sdpa_forward_ex(mha_dtype in_dt, mha_dtype out_dt,
                      causal, p_attn, sp, stream);
 }
 
+size_t sdpa_backward_workspace_bytes(int B, int h, int Lq) {
+    if (B < 0 || h <= 0 || Lq < 0) return 0;
+    return round_up(mha::backward_workspace_bytes(B, h, Lq), 256);
+}
+
+mha_status sdpa_backward(mha_dtype in_dt, mha_dtype out_dt,
+                         const void* q, mha_strides sq,
+                         const void* k, mha_strides sk,
+                         const void* v, mha_strides sv,
+                         const void* o, mha_strides so,
+                         const void* dout, mha_strides sdo,
+                         void* dq, mha_strides sdq,
+                         void* dk, mha_strides sdk,
+                         void* dv, mha_strides sdv,
+                         int B, int h, int Lq, int Lk, int d_k, int d_v,
+                         const int* valid_lens, int vl_rank, int causal,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
+    if (valid_lens && vl_rank != 1 && vl_rank != 2) return MHA_EINVAL;
+    if (B < 0 || h <= 0 || Lq < 0 || Lk <= 0 || d_k <= 0 || d_v <= 0) return MHA_EINVAL;
+    if (causal && Lq != Lk) return MHA_EINVAL;
+    if (d_k != kHeadDim || d_v != kHeadDim) return MHA_ENOTSUP;
+    if (in_dt == MHA_F32 && out_dt != MHA_F32) return MHA_ENOTSUP;
+    if (B == 0 || Lq == 0) return MHA_OK;
+    const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return MHA_EINVAL;
+    const size_t need = sdpa_backward_workspace_bytes(B, h, Lq);
+    if (workspace_bytes < need) return MHA_EWORKSPACE;
+    const long long mult = in_dt == MHA_F32 ? 4 : 8, omult = out_dt == MHA_F32 ? 4 : 8;
+    const mha_strides in_s[5] = {sq, sk, sv, so, sdo};
+    for (const mha_strides& st : in_s)
+        if (st.b < 0 || st.h < 0 || st.l < 0 || st.b % mult || st.h % mult || st.l % mult) return MHA_EINVAL;
+    const mha_strides out_s[3] = {sdq, sdk, sdv};
+    for (const mha_strides& st : out_s)
+        if (st.b < 0 || st.h < 0 || st.l < 0 || st.b % omult || st.h % omult || st.l % omult) return MHA_EINVAL;
+    const size_t ie = elem_size(in_dt), oe = elem_size(out_dt);
+    const uintptr_t wb = reinterpret_cast<uintptr_t>(workspace);
+    const Range ins[] = {view_range(q, sq, B, h, Lq, d_k, ie), view_range(k, sk, B, h, Lk, d_k, ie),
+                         view_range(v, sv, B, h, Lk, d_v, ie), view_range(o, so, B, h, Lq, d_v, ie),
+                         view_range(dout, sdo, B, h, Lq, d_v, ie)};
+    const Range outs[] = {view_range(dq, sdq, B, h, Lq, d_k, oe), view_range(dk, sdk, B, h, Lk, d_k, oe),
+                          view_range(dv, sdv, B, h, Lk, d_v, oe), Range{wb, wb + need}};
+    for (int x = 0; x < 4; ++x) {
+        for (const Range& r : ins)
+            if (overlap(outs[x], r)) return MHA_EINVAL;
+        for (int y = x + 1; y < 4; ++y)
+            if (overlap(outs[x], outs[y])) return MHA_EINVAL;
+    }
+
+    mha::BackwardArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    const mha_strides* all[8] = {&sq, &sk, &sv, &so, &sdo, &sdq, &sdk, &sdv};
+    long long* dst[8] = {a.sq, a.sk, a.sv, a.so, a.sdo, a.sdq, a.sdk, a.sdv};
+    for (int x = 0; x < 8; ++x) {
+        dst[x][0] = all[x]->b;
+        dst[x][1] = all[x]->h;
+        dst[x][2] = all[x]->l;
+    }
+    a.B = B; a.H = h; a.Lq = Lq; a.Lk = Lk;
+    a.valid_lens = valid_lens;
+    a.vl_rank = valid_lens ? vl_rank : 0;
+    a.causal = causal ? 1 : 0;
+    a.in_f32 = in_dt == MHA_F32;
+    a.out_f32 = out_dt == MHA_F32;
+    a.rows = static_cast<float*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(timed("sdpa_backward", s, [&] { return mha::launch_sdpa_backward(a, s); }));
+}
+
 size_t sdpa_decode_workspace_bytes(int B, int h, int L) {
     if (B < 0 || h <= 0 || L <= 0) return 0;
     return round_up(mha::decode_workspace_bytes(B, h, L), 256);

@@ -81,6 +81,27 @@ struct WeightsArgs {
     long long sp[3];
 };
 
+// Attention backward: dq, dk, dv for the output gradient dout (fp32
+// arithmetic).  `rows` is the workspace: (log-sum-exp in log2 units, D) per
+// query, [B, H, Lq, 2] floats.
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    long long sq[3], sk[3], sv[3], so[3], sdo[3], sdq[3], sdk[3], sdv[3];
+    int B, H, Lq, Lk;
+    const int* valid_lens;
+    int vl_rank;                            // 0 (no lengths), 1 ([B]), 2 ([B, Lq])
+    int causal;
+    bool in_f32, out_f32;
+    float* rows;
+};
+
 hipError_t launch_sdpa_bf16(const SdpaArgs& a, bool out_f32, hipStream_t s);
 int decode_splits(int L);
 size_t decode_workspace_bytes(int B, int H, int L);
@@ -93,6 +114,8 @@ bool mha_attn_fused_small_fits(const FusedArgs& a);
 hipError_t launch_mha_attn_fused_small(const FusedArgs& a, hipStream_t s);
 hipError_t launch_sdpa_f32(const SdpaArgs& a, hipStream_t s);
 hipError_t launch_sdpa_weights(const WeightsArgs& a, hipStream_t s);
+size_t backward_workspace_bytes(int B, int H, int Lq);
+hipError_t launch_sdpa_backward(const BackwardArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool out_f32, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 
