@@ -195,6 +195,67 @@ def decode_alg(w, lens):
     return flops, byts
 
 
+class PreparedBackward:
+    """sdpa_backward on q, k, v, the forward output and an output gradient."""
+
+    def __init__(self, inp):
+        import torch
+        import transformer_head_scaled_sdpa_amd as mha
+        from transformer_head_scaled_sdpa_amd import _lib
+        w = inp.workload
+        dev = torch.device("cuda:0")
+        self.t = [torch.from_numpy(inp.tensors[n]).to(dev).to(torch.bfloat16) for n in "qkv"]
+        rng = np.random.Generator(np.random.PCG64(w.seed + 1000))
+        self.g = torch.from_numpy(rng.standard_normal(self.t[0].shape).astype(np.float32)).to(dev).to(torch.bfloat16)
+        self.vl = None if inp.valid_lens is None else torch.from_numpy(inp.valid_lens).to(dev)
+        self.o = mha.sdpa_forward(*self.t, valid_lens=self.vl, causal=w.causal)
+        self.grads = [torch.empty(x.shape, dtype=torch.float32, device=dev) for x in self.t]
+        self.lib = _lib.load()
+        need = int(self.lib.sdpa_backward_workspace_bytes(w.B, w.h, w.Lq))
+        self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        s4 = lambda x: _lib.Strides(*x.stride()[:3])
+        p = lambda x: ctypes.c_void_p(x.data_ptr())
+        args = []
+        for x in self.t + [self.o, self.g] + self.grads:
+            args += [p(x), s4(x)]
+        self.args = [_lib.MHA_BF16, _lib.MHA_F32] + args + [w.B, w.h, w.Lq, w.Lk, 64, 64,
+                                                             None if self.vl is None else p(self.vl), 1,
+                                                             int(w.causal), p(self.ws), need]
+        self.torch = torch
+
+    def __call__(self):
+        st = self.lib.sdpa_backward(*self.args, ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"sdpa_backward failed with status {st}")
+
+
+class PreparedWeights:
+    """sdpa_forward_ex returning the attention weights (inspection path)."""
+
+    def __init__(self, inp):
+        import torch
+        from transformer_head_scaled_sdpa_amd import _lib
+        w = inp.workload
+        dev = torch.device("cuda:0")
+        self.t = [torch.from_numpy(inp.tensors[n]).to(dev).to(torch.bfloat16) for n in "qkv"]
+        self.o = torch.empty_like(self.t[0])
+        self.p = torch.empty((w.B, w.h, w.Lq, w.Lk), dtype=torch.float32, device=dev)
+        self.vl = None if inp.valid_lens is None else torch.from_numpy(inp.valid_lens).to(dev)
+        self.lib = _lib.load()
+        s4 = lambda x: _lib.Strides(*x.stride()[:3])
+        p = lambda x: ctypes.c_void_p(x.data_ptr())
+        q, k, v = self.t
+        self.args = [_lib.MHA_BF16, _lib.MHA_BF16, p(q), s4(q), p(k), s4(k), p(v), s4(v), p(self.o), s4(self.o),
+                     w.B, w.h, w.Lq, w.Lk, 64, 64, None if self.vl is None else p(self.vl), 1, int(w.causal),
+                     p(self.p), s4(self.p)]
+        self.torch = torch
+
+    def __call__(self):
+        st = self.lib.sdpa_forward_ex(*self.args, ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"sdpa_forward_ex failed with status {st}")
+
+
 def time_steps(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -451,6 +512,34 @@ def main():
             "alg_GBs": round(b / (dms * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(b / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         del df
+
+    if not args.no_long_sdpa:
+        # backward: algorithmic 8*d_k flops per allowed pair (the four
+        # gradient products dv, dp, dq, dk; the recomputed scores not counted)
+        bw = workloads.BY_NAME["backward_causal"]
+        binp = workloads.make_inputs(bw)
+        bf = PreparedBackward(binp)
+        bms, _ = time_steps(bf, 10, 3)
+        pairs = allowed_pairs(bw, binp.valid_lens)
+        bfl = 8 * bw.d_k * pairs
+        result["sdpa_backward"] = {
+            "workload": bw.description, "avg_us": round(bms * 1e3, 2),
+            "alg_tflops": round(bfl / (bms * 1e-3) / 1e12, 2),
+            "frac_fp32_alu_peak": round(bfl / (bms * 1e-3) / 1e12 / PEAK_F32_TFLOPS, 4), "bound": "alu"}
+        del bf
+        # inspection path: the weights written (fp32) plus q, k, v read and o written
+        iw = workloads.BY_NAME["inspect_weights"]
+        iinp = workloads.make_inputs(iw)
+        wf = PreparedWeights(iinp)
+        wms, _ = time_steps(wf, 10, 3)
+        wbytes = iw.B * iw.h * (iw.Lq * iw.Lk * 4 + (2 * iw.Lq + 2 * iw.Lk) * iw.d_k * 2)
+        wfl = 2 * 4 * iw.d_k * allowed_pairs(iw, iinp.valid_lens)    # two passes of scores, one of P.V
+        result["sdpa_weights"] = {
+            "workload": iw.description, "avg_us": round(wms * 1e3, 2),
+            "GBs": round(wbytes / (wms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(wbytes / (wms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "fp32_tflops": round(wfl / (wms * 1e-3) / 1e12, 2),
+            "frac_fp32_alu_peak": round(wfl / (wms * 1e-3) / 1e12 / PEAK_F32_TFLOPS, 4)}
+        del wf
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")

@@ -84,6 +84,14 @@ WORKLOADS = [
     Workload("decode_step", "decode", "bf16", 64, 1, 512, 8, 64, False, (256, 512), seed=6,
              description="decoding step bf16, B=64 h=8 d_k=64, one query against a K/V cache of "
                          "512 positions with U{256..512} valid"),
+    # The backward pass over a decoder-sized causal attention (q, k, v and the
+    # output gradient ~ N(0,1)).
+    Workload("backward_causal", "sdpa", "bf16", 4, 1024, 1024, 8, 64, True, None, seed=7,
+             description="attention backward bf16 in / fp32 gradients, B=4 h=8 L=1024 d_k=64, causal"),
+    # The inspection path: weights of a padded self-attention, B=4 h=8 L=512
+    # with per-sequence lengths U{256..512}.
+    Workload("inspect_weights", "sdpa", "bf16", 4, 512, 512, 8, 64, False, (256, 512), seed=8,
+             description="attention with weights export bf16, B=4 h=8 L=512 d_k=64, valid_lens U{256..512}"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
