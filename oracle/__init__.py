@@ -21,6 +21,13 @@ Functions and the passages they follow:
 * ``mha``     -- the four projections, head split, sdpa per head, head merge
   and the output projection ("Transformer" study notes, multi-head attention
   formula and class).
+* ``layer_norm`` -- per-row normalisation in the two forms the pages print:
+  The Annotated Transformer's class (std with Bessel's correction, eps added
+  to the std) and the study notes' torch layer (biased variance, eps inside
+  the root).
+* ``mha_sublayer`` -- the pre-norm residual sublayer around attention, x +
+  attention(norm(x), ...) (The Annotated Transformer, sublayer connection;
+  no dropout at inference).
 * ``round_bf16`` -- nearest bfloat16, ties to even (used by the optional
   bf16-storage mode of ``mha``).
 
@@ -55,6 +62,9 @@ def _open(path):
         _ip, ctypes.c_int, ctypes.c_int, _ip, ctypes.c_int, ctypes.c_int]
     lib.oracle_sdpa_backward_f64.restype = ctypes.c_int
     lib.oracle_sdpa_backward_f64.argtypes = [_dp] * 7 + [ctypes.c_int] * 6 + [_ip, ctypes.c_int, ctypes.c_int]
+    lib.oracle_layer_norm_f64.restype = None
+    lib.oracle_layer_norm_f64.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_double]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     return lib
@@ -176,6 +186,31 @@ def sdpa_backward(q, k, v, dout, valid_lens=None, causal=False):
     if rc != 0:
         raise ValueError("oracle_sdpa_backward_f64 rejected its arguments")
     return dq, dkk, dvv
+
+
+def layer_norm(x, gain=None, bias=None, kind=0, eps=1e-6):
+    """Normalise each row of x [..., D]: kind 0 (std with Bessel's correction,
+    eps added to the std) or kind 1 (biased variance, eps inside the root)."""
+    x = _f64(x)
+    D = x.shape[-1]
+    y = np.empty_like(x)
+    a = None if gain is None else _f64(gain)
+    b = None if bias is None else _f64(bias)
+    _load().oracle_layer_norm_f64(_ptr(x), _ptr(a), _ptr(b), _ptr(y), x.size // D, D, int(kind), float(eps))
+    return y
+
+
+def mha_sublayer(x, w_q, w_k, w_v, w_o, b_q=None, b_k=None, b_v=None, b_o=None, h=8, ln_gain=None,
+                 ln_bias=None, ln_kind=0, ln_eps=1e-6, memory=None, valid_lens=None, causal=False, rows=None):
+    """x + MHA(norm(x), kv, kv) with kv = norm(x) (self-attention) or the
+    given memory (source attention); the result's rows ``rows`` if given."""
+    x = _f64(x)
+    xn = layer_norm(x, ln_gain, ln_bias, ln_kind, ln_eps)
+    kv = xn if memory is None else _f64(memory)
+    att = mha(xn, kv, w_q, w_k, w_v, w_o, b_q, b_k, b_v, b_o, h=h, valid_lens=valid_lens, causal=causal,
+              rows=rows)
+    xr = x if rows is None else x[:, np.asarray(rows)]
+    return xr + att
 
 
 def mha(x_q, x_kv, w_q, w_k, w_v, w_o, b_q=None, b_k=None, b_v=None, b_o=None,

@@ -345,6 +345,34 @@ int oracle_sdpa_backward_f64(const double* q, const double* k, const double* v, 
     return bad ? -1 : 0;
 }
 
+/*
+ * Layer normalisation of each row of x [M, D] (per-feature gain a and bias b,
+ * NULL meaning 1 and 0).  The pages print two forms:
+ *   kind 0 (The Annotated Transformer, LayerNorm class):
+ *       a * (x - mean) / (std + eps) + b, std with Bessel's correction (n-1)
+ *   kind 1 (the "Transformer" study notes' code, a torch LayerNorm layer):
+ *       a * (x - mean) / sqrt(var + eps) + b, var without correction (n)
+ */
+void oracle_layer_norm_f64(const double* x, const double* a, const double* b, double* y,
+                           long M, int D, int kind, double eps)
+{
+    long m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        const double* xr = x + m * D;
+        double mean = 0.0;
+        for (int c = 0; c < D; ++c) mean += xr[c];
+        mean /= D;
+        double ss = 0.0;
+        for (int c = 0; c < D; ++c) ss += (xr[c] - mean) * (xr[c] - mean);
+        double den;
+        if (kind == 0) den = sqrt(ss / (D - 1)) + eps;
+        else den = sqrt(ss / D + eps);
+        for (int c = 0; c < D; ++c)
+            y[m * D + c] = (a ? a[c] : 1.0) * (xr[c] - mean) / den + (b ? b[c] : 0.0);
+    }
+}
+
 /* Number of OpenMP threads the oracle runs with (1 without OpenMP). */
 int oracle_num_threads(void)
 {

@@ -416,6 +416,51 @@ def pin_backward_closed_forms():
     _close(dv, np.repeat(g.sum(axis=2, keepdims=True) / Lk, Lk, axis=2))
 
 
+def pin_layer_norm_hand_example():
+    """x = [1, 2, 3, 4]: mean 2.5, squared deviations summing to 5, so the
+    Annotated Transformer's std (n - 1) is sqrt(5/3) and the torch layer's
+    root of the biased variance is sqrt(5/4); gain and bias act per feature."""
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    dev = np.array([-1.5, -0.5, 0.5, 1.5])
+    _close(oracle.layer_norm(x, kind=0, eps=0.0)[0], dev / math.sqrt(5 / 3))
+    _close(oracle.layer_norm(x, kind=1, eps=0.0)[0], dev / math.sqrt(5 / 4))
+    a, b = np.array([2.0, 1.0, 0.5, -1.0]), np.array([1.0, 0.0, -2.0, 3.0])
+    _close(oracle.layer_norm(x, a, b, kind=0, eps=0.5)[0], a * dev / (math.sqrt(5 / 3) + 0.5) + b)
+    _close(oracle.layer_norm(x, a, b, kind=1, eps=0.75)[0], a * dev / math.sqrt(5 / 4 + 0.75) + b)
+
+
+def pin_layer_norm_torch_layer_and_invariants():
+    """Kind 1 is torch's layer norm (float64 CPU); the two kinds differ by
+    sqrt((D-1)/D) when eps = 0; both ignore a constant shift of the row."""
+    import torch
+    r = _rng(61)
+    x = r.standard_normal((5, 7, 24)) * 3 + 1
+    a, b = r.standard_normal(24), r.standard_normal(24)
+    ref = torch.nn.functional.layer_norm(torch.tensor(x), (24,), torch.tensor(a), torch.tensor(b), eps=1e-5)
+    _close(oracle.layer_norm(x, a, b, kind=1, eps=1e-5), ref.numpy())
+    _close(oracle.layer_norm(x, kind=0, eps=0.0), oracle.layer_norm(x, kind=1, eps=0.0) * math.sqrt(23 / 24))
+    for kind in (0, 1):
+        _close(oracle.layer_norm(x + 7.25, a, b, kind=kind), oracle.layer_norm(x, a, b, kind=kind), 1e-11)
+
+
+def pin_sublayer_residual_closed_forms():
+    """With a zero output projection the sublayer returns x + b_O; with one
+    head, identity projections and a single position it returns
+    x + norm(x) (attention over one key returns its value)."""
+    r = _rng(62)
+    B, L, D, h = 2, 5, 8, 2
+    x = r.standard_normal((B, L, D))
+    w = [r.standard_normal((D, D)) for _ in range(3)]
+    bo = r.standard_normal(D)
+    out = oracle.mha_sublayer(x, *w, np.zeros((D, D)), b_o=bo, h=h, ln_kind=1, ln_eps=1e-5)
+    _close(out, x + bo)
+    x1 = r.standard_normal((3, 1, D))
+    g, bb = r.standard_normal(D), r.standard_normal(D)
+    eye = np.eye(D)
+    out = oracle.mha_sublayer(x1, eye, eye, eye, eye, h=1, ln_gain=g, ln_bias=bb)
+    _close(out, x1 + oracle.layer_norm(x1, g, bb, kind=0, eps=1e-6), 1e-12)
+
+
 def pin_row_subset_consistent():
     r = _rng(37)
     x = r.standard_normal((2, 9, 16))

@@ -35,6 +35,9 @@ MUTATIONS = [
     ("backward_dv_uses_ds", "dvb[(long)j * dv_ + t] += p[j] * gi[t];", "dvb[(long)j * dv_ + t] += dp[j] * gi[t];"),
     ("backward_masked_pairs_propagate",
      "if (!key_allowed(valid_lens, vl_per_query, Lq, causal, b, i, j)) continue;", ""),
+    ("layer_norm_biased_std_for_kind0", "den = sqrt(ss / (D - 1)) + eps;", "den = sqrt(ss / D) + eps;"),
+    ("layer_norm_eps_inside_root_for_kind0", "den = sqrt(ss / (D - 1)) + eps;", "den = sqrt(ss / (D - 1) + eps);"),
+    ("layer_norm_eps_outside_root_for_kind1", "else den = sqrt(ss / D + eps);", "else den = sqrt(ss / D) + eps;"),
     ("per_query_length_ignores_query", "valid_lens[(long)b * Lq + i]", "valid_lens[(long)b * Lq]"),
 ]
 
