@@ -257,6 +257,45 @@ mha_status mha_forward_ex(mha_dtype in_dt, mha_dtype out_dt,
                           float* p_attn, mha_strides sp,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * mha_sublayer_forward -- the pre-norm residual sublayer around multi-head
+ * attention, out = x + MHA(norm(x), kv, kv) (The Annotated Transformer,
+ * sublayer connection, which applies the norm first; no dropout at
+ * inference), with kv = norm(x) for self-attention (memory == NULL) or the
+ * given memory [B, Lk, d_model] for source attention.
+ *   norm : a layer normalisation of each row with gain ln_gain and bias
+ *          ln_bias ([d_model] in in_dt, NULL meaning 1 and 0) in one of the
+ *          two forms the pages print:
+ *            ln_kind 0 (The Annotated Transformer's LayerNorm class):
+ *              gain * (x - mean) / (std + eps) + bias, std with Bessel's
+ *              correction (n - 1); the class's default eps is 1e-6;
+ *            ln_kind 1 (the "Transformer" study notes' torch layer):
+ *              gain * (x - mean) / sqrt(var + eps) + bias, biased variance;
+ *              torch's default eps is 1e-5.
+ *   x : [B, L, d_model] in in_dt; out : [B, L, d_model] in out_dt, not
+ *          overlapping x, memory or the workspace.  Weights, biases,
+ *          valid_lens, causal and the dtype rules as for mha_forward
+ *          (memory == NULL requires Lk == L).
+ *   workspace : at least mha_sublayer_workspace_bytes(...) bytes.
+ * Fusion: in bf16 self-attention with L <= 128 the normalisation runs inside
+ * the attention kernel on the staged rows of x (no normalised copy in HBM);
+ * otherwise a row-wise kernel writes norm(x) to the workspace first.  The
+ * residual add is always fused into the output projection's epilogue.
+ */
+size_t mha_sublayer_workspace_bytes(mha_dtype in_dt, int B, int L, int Lk, int d_model, int h);
+
+mha_status mha_sublayer_forward(mha_dtype in_dt, mha_dtype out_dt,
+                                const void* x, const void* memory,
+                                const void* ln_gain, const void* ln_bias, int ln_kind, float ln_eps,
+                                const void* w_q, const void* b_q,
+                                const void* w_k, const void* b_k,
+                                const void* w_v, const void* b_v,
+                                const void* w_o, const void* b_o,
+                                void* out,
+                                int B, int L, int Lk, int d_model, int h, int d_k,
+                                const int* valid_lens, int causal,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* mha_status_string(mha_status s);
 

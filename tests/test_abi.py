@@ -245,3 +245,29 @@ def test_backward_workspace_and_validation(lib):
     assert bwd(lib, dv_=ALIGNED[6]) == EINVAL       # dv overlaps dk
     assert bwd(lib, ws=ALIGNED[5]) == EINVAL        # workspace overlaps dq
     assert bwd(lib, dk_=ctypes.c_void_p(P + 0x600000 + 8)) == EINVAL
+
+
+def sub(lib, **kw):
+    a = dict(in_dt=BF16, out_dt=F32, x=ALIGNED[0], mem=None, g=None, b=None, kind=0, eps=1e-6, out=ALIGNED[6], B=2,
+             L=10, Lk=10, D=512, h=8, dk=64, ws=ALIGNED[7], wsb=None)
+    a.update(kw)
+    need = lib.mha_sublayer_workspace_bytes(a["in_dt"], a["B"], a["L"], a["Lk"], a["D"], a["h"])
+    wsb = need if a["wsb"] is None else a["wsb"]
+    return lib.mha_sublayer_forward(a["in_dt"], a["out_dt"], a["x"], a["mem"], a["g"], a["b"], a["kind"], a["eps"],
+                                    ALIGNED[2], None, ALIGNED[3], None, ALIGNED[4], None, ALIGNED[5], None, a["out"],
+                                    a["B"], a["L"], a["Lk"], a["D"], a["h"], a["dk"], None, 0, a["ws"], wsb, None)
+
+
+def test_sublayer_workspace_and_validation(lib):
+    # norm(x) in in_dt, then mha_forward's workspace
+    assert lib.mha_sublayer_workspace_bytes(BF16, 2, 10, 10, 512, 8) == 20480 + 20480
+    assert lib.mha_sublayer_workspace_bytes(F32, 2, 10, 10, 512, 8) == 40960 + 4 * 40960
+    assert sub(lib, B=0) == OK
+    assert sub(lib, kind=2) == EINVAL                  # the two printed LayerNorm forms only
+    assert sub(lib, eps=-1.0) == EINVAL
+    assert sub(lib, Lk=12) == EINVAL                   # self-attention needs Lk == L
+    assert sub(lib, out=ALIGNED[0]) == EINVAL          # out overlaps the residual input
+    assert sub(lib, wsb=1000) == EWORK
+    assert sub(lib, D=256, h=8, dk=32) == ENOTSUP
+    assert sub(lib, x=ctypes.c_void_p(P + 8)) == EINVAL
+    assert sub(lib, mem=ALIGNED[7], Lk=12) == EINVAL   # memory overlaps the workspace

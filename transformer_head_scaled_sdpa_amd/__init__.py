@@ -12,6 +12,9 @@ there is no CPU or PyTorch fallback, and a missing library raises.
                 valid_lens=None, causal=False, out_dtype=None,
                 return_weights=False)
         x_q [B,Lq,D], x_kv [B,Lk,D], W [D,D] stored [out, in], b [D]
+    mha_sublayer_forward(x, w_q, w_k, w_v, w_o, ..., ln_gain=None, ln_bias=None,
+                         ln_kind=0, ln_eps=1e-6, memory=None, ...)
+        x + MHA(norm(x), ...): the pre-norm residual sublayer
     sdpa_backward(q, k, v, o, dout, valid_lens=None, causal=False)
         -> dq, dk, dv (gradients of sdpa_forward for the output gradient dout)
     sdpa_decode(q, k_cache, v_cache, lens)
@@ -27,7 +30,7 @@ import ctypes
 from . import _lib
 from ._lib import MhaError, MHA_BF16, MHA_F32, MHA_OK, Strides
 
-__all__ = ["sdpa_forward", "sdpa_backward", "sdpa_decode", "mha_forward", "workspace_bytes", "kernel_timing", "MhaError", "library"]
+__all__ = ["sdpa_forward", "sdpa_backward", "sdpa_decode", "mha_forward", "mha_sublayer_forward", "workspace_bytes", "kernel_timing", "MhaError", "library"]
 
 
 def library():
@@ -212,6 +215,36 @@ def mha_forward(x_q, x_kv, w_q, w_k, w_v, w_o, b_q=None, b_k=None, b_v=None, b_o
                             _ptr(workspace), workspace.numel(), _stream())
     _raise(st, "mha_forward_ex")
     return (out, p) if return_weights else out
+
+
+def mha_sublayer_forward(x, w_q, w_k, w_v, w_o, b_q=None, b_k=None, b_v=None, b_o=None, h=8, ln_gain=None,
+                         ln_bias=None, ln_kind=0, ln_eps=1e-6, memory=None, valid_lens=None, causal=False,
+                         out_dtype=None, out=None, workspace=None):
+    """x + MHA(norm(x), kv, kv), kv = norm(x) or ``memory``; returns [B, L, d_model]."""
+    torch = _torch()
+    args = dict(x=x, memory=memory, w_q=w_q, w_k=w_k, w_v=w_v, w_o=w_o, b_q=b_q, b_k=b_k, b_v=b_v, b_o=b_o,
+                ln_gain=ln_gain, ln_bias=ln_bias)
+    for n, t in args.items():
+        _check_gpu(n, t)
+        if t is not None and (not t.is_contiguous() or t.dtype != x.dtype):
+            raise ValueError(f"{n} must be contiguous and share x's dtype")
+    B, L, D = x.shape
+    Lk = L if memory is None else memory.shape[1]
+    in_dt = _dtype_code(x.dtype)
+    out_dtype = (torch.float32 if x.dtype == torch.bfloat16 else x.dtype) if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, L, D), dtype=out_dtype, device=x.device)
+    lib = _lib.load()
+    need = int(lib.mha_sublayer_workspace_bytes(in_dt, B, L, Lk, D, h))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    vl = _valid_lens(valid_lens, B, x.device)
+    st = lib.mha_sublayer_forward(in_dt, _dtype_code(out.dtype), _ptr(x), _ptr(memory), _ptr(ln_gain), _ptr(ln_bias),
+                                  int(ln_kind), float(ln_eps), _ptr(w_q), _ptr(b_q), _ptr(w_k), _ptr(b_k), _ptr(w_v),
+                                  _ptr(b_v), _ptr(w_o), _ptr(b_o), _ptr(out), B, L, Lk, D, h, D // h if h else 0,
+                                  _ptr(vl), int(bool(causal)), _ptr(workspace), workspace.numel(), _stream())
+    _raise(st, "mha_sublayer_forward")
+    return out
 
 
 class kernel_timing:

@@ -20,7 +20,8 @@ MHA_EHIP = 4
 # Every function the header declares; tests check that each is exported.
 EXPORTED = ("sdpa_forward", "sdpa_forward_ex", "sdpa_backward_workspace_bytes", "sdpa_backward",
             "sdpa_decode_workspace_bytes", "sdpa_decode", "mha_workspace_bytes",
-            "mha_workspace_bytes_ex", "mha_forward", "mha_forward_ex", "mha_status_string", "mha_timing_enable",
+            "mha_workspace_bytes_ex", "mha_forward", "mha_forward_ex", "mha_sublayer_workspace_bytes",
+            "mha_sublayer_forward", "mha_status_string", "mha_timing_enable",
             "mha_timing_read")
 
 
@@ -72,6 +73,11 @@ def load():
     lib.mha_forward_ex.restype = i
     lib.mha_forward_ex.argtypes = [i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    i, i, i, i, i, i, vp, i, i, vp, Strides, vp, sz, vp]
+    lib.mha_sublayer_workspace_bytes.restype = sz
+    lib.mha_sublayer_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.mha_sublayer_forward.restype = i
+    lib.mha_sublayer_forward.argtypes = [i, i, vp, vp, vp, vp, i, ctypes.c_float] + [vp] * 9 + [i] * 6 + [
+        vp, i, vp, sz, vp]
     lib.mha_status_string.restype = ctypes.c_char_p
     lib.mha_status_string.argtypes = [i]
     lib.mha_timing_enable.restype = i

@@ -336,7 +336,9 @@ mha_status mha_impl(mha_dtype in_dt, mha_dtype out_dt,
                     void* out,
                     int B, int Lq, int Lk, int d_model, int h, int d_k,
                     const int* valid_lens, int vl_rank, int causal, float* p_attn, mha_strides sp,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+                    void* workspace, size_t workspace_bytes, void* stream,
+                    const void* ln_gain = nullptr, const void* ln_bias = nullptr, int ln_kind = -1,
+                    float ln_eps = 0.0f, const void* residual = nullptr) {
     if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
     if (valid_lens && vl_rank != 1 && vl_rank != 2) return MHA_EINVAL;
     // The inspection path: projections to fp32, attention with the weights.
@@ -434,6 +436,10 @@ mha_status mha_impl(mha_dtype in_dt, mha_dtype out_dt,
         f.B = B; f.H = h; f.Lq = Lq; f.Lk = Lk; f.D = d_model;
         f.valid_lens = valid_lens;
         f.causal = causal ? 1 : 0;
+        f.ln_gain = ln_gain;
+        f.ln_bias = ln_bias;
+        f.ln_kind = ln_kind;
+        f.ln_eps = ln_eps;
         e = timed("attn_fused_bf16", s, [&] { return mha::launch_mha_attn_fused(f, s); });
         if (e != hipSuccess) return MHA_EHIP;
     } else {
@@ -474,7 +480,7 @@ mha_status mha_impl(mha_dtype in_dt, mha_dtype out_dt,
     go.nprob = 1;
     go.N = d_model;
     go.K = d_model;
-    go.p[0] = {Ocat, w_o, b_o, out, B * Lq};
+    go.p[0] = {Ocat, w_o, b_o, out, B * Lq, residual};
     e = timed(bf16 ? "out_proj_bf16" : "out_proj_f32", s, [&] {
         return bf16 ? mha::launch_gemm_bf16(go, out_dt == MHA_F32, s) : mha::launch_gemm_f32(go, s);
     });
@@ -511,6 +517,80 @@ mha_status mha_forward_ex(mha_dtype in_dt, mha_dtype out_dt,
                           void* workspace, size_t workspace_bytes, void* stream) {
     return mha_impl(in_dt, out_dt, x_q, x_kv, w_q, b_q, w_k, b_k, w_v, b_v, w_o, b_o, out, B, Lq, Lk, d_model, h,
                     d_k, valid_lens, vl_rank, causal, p_attn, sp, workspace, workspace_bytes, stream);
+}
+
+size_t mha_sublayer_workspace_bytes(mha_dtype in_dt, int B, int L, int Lk, int d_model, int h) {
+    const size_t inner = mha_workspace_bytes(in_dt, B, L, Lk, d_model, h);
+    if (inner == 0 && !(B == 0 || L == 0)) return 0;
+    if (!valid_dtype(in_dt) || B < 0 || L < 0 || d_model <= 0) return 0;
+    return round_up((size_t)B * L * d_model * elem_size(in_dt), 256) + inner;
+}
+
+mha_status mha_sublayer_forward(mha_dtype in_dt, mha_dtype out_dt,
+                                const void* x, const void* memory,
+                                const void* ln_gain, const void* ln_bias, int ln_kind, float ln_eps,
+                                const void* w_q, const void* b_q,
+                                const void* w_k, const void* b_k,
+                                const void* w_v, const void* b_v,
+                                const void* w_o, const void* b_o,
+                                void* out,
+                                int B, int L, int Lk, int d_model, int h, int d_k,
+                                const int* valid_lens, int causal,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
+    if (ln_kind != 0 && ln_kind != 1) return MHA_EINVAL;
+    if (!(ln_eps >= 0.0f)) return MHA_EINVAL;
+    if (!memory && Lk != L) return MHA_EINVAL;
+    if (B < 0 || L < 0 || Lk <= 0 || d_model <= 1 || h <= 0 || d_k <= 0) return MHA_EINVAL;
+    if ((long long)h * d_k != d_model) return MHA_EINVAL;
+    if (d_k != kHeadDim) return MHA_ENOTSUP;
+    if (in_dt == MHA_F32 && out_dt != MHA_F32) return MHA_ENOTSUP;
+    if (B == 0 || L == 0) return MHA_OK;
+    if (!x || !out || !workspace) return MHA_EINVAL;
+    const void* ptrs[] = {x, memory, ln_gain, ln_bias, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MHA_EINVAL;
+    const size_t need = mha_sublayer_workspace_bytes(in_dt, B, L, Lk, d_model, h);
+    if (need == 0) return MHA_EINVAL;
+    if (workspace_bytes < need) return MHA_EWORKSPACE;
+    const size_t ie = elem_size(in_dt);
+    const size_t xbytes = round_up((size_t)B * L * d_model * ie, 256);
+    const uintptr_t xb = reinterpret_cast<uintptr_t>(x), wb = reinterpret_cast<uintptr_t>(workspace);
+    const Range rx{xb, xb + (size_t)B * L * d_model * ie}, rws{wb, wb + need};
+    const uintptr_t ob = reinterpret_cast<uintptr_t>(out);
+    const Range rout{ob, ob + (size_t)B * L * d_model * elem_size(out_dt)};
+    if (overlap(rx, rws) || overlap(rx, rout)) return MHA_EINVAL;
+    if (memory) {
+        const uintptr_t mb = reinterpret_cast<uintptr_t>(memory);
+        const Range rm{mb, mb + (size_t)B * Lk * d_model * ie};
+        if (overlap(rm, rws) || overlap(rm, rout)) return MHA_EINVAL;
+    }
+    for (const void* p : {ln_gain, ln_bias}) {
+        if (!p) continue;
+        const Range r{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (size_t)d_model * ie};
+        if (overlap(r, rws) || overlap(r, rout)) return MHA_EINVAL;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // Self-attention in bf16 with L <= 128: the normalisation runs inside the
+    // single-pass attention kernel.
+    mha::FusedArgs probe;
+    probe.x_q = probe.x_kv = x;
+    probe.Lq = probe.Lk = L;
+    probe.D = d_model;
+    probe.ln_kind = ln_kind;
+    if (in_dt == MHA_BF16 && !memory && mha::mha_attn_fused_small_fits(probe))
+        return mha_impl(in_dt, out_dt, x, x, w_q, b_q, w_k, b_k, w_v, b_v, w_o, b_o, out, B, L, L, d_model, h, d_k,
+                        valid_lens, 1, causal, nullptr, mha_strides{0, 0, 0}, static_cast<char*>(workspace) + xbytes,
+                        need - xbytes, stream, ln_gain, ln_bias, ln_kind, ln_eps, x);
+    // Otherwise norm(x) goes to the workspace first.
+    void* xn = workspace;
+    const hipError_t e = timed("layer_norm", s, [&] {
+        return mha::launch_layer_norm(x, ln_gain, ln_bias, xn, B * L, d_model, ln_kind, ln_eps, in_dt == MHA_F32, s);
+    });
+    if (e != hipSuccess) return MHA_EHIP;
+    return mha_impl(in_dt, out_dt, xn, memory ? memory : xn, w_q, b_q, w_k, b_k, w_v, b_v, w_o, b_o, out, B, L, Lk,
+                    d_model, h, d_k, valid_lens, 1, causal, nullptr, mha_strides{0, 0, 0},
+                    static_cast<char*>(workspace) + xbytes, need - xbytes, stream, nullptr, nullptr, -1, 0.0f, x);
 }
 
 mha_status mha_timing_enable(int repeat) {

@@ -24,7 +24,8 @@
 //  * Every wave keeps eight independent accumulators (its output blocks
 //    times a split of the K steps, summed at the end): an MFMA whose
 //    accumulator was written fewer than eight MFMAs earlier issues slower.
-//  * Bias is added in the epilogue.
+//  * Bias (and, for a residual sublayer, the residual input) is added in the
+//    epilogue.
 //
 // Workgroups are mapped XCD-aware: the hardware deals workgroup ids to the
 // eight XCDs round-robin, so consecutive logical tiles (those sharing rows
@@ -181,6 +182,15 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, 
             }
         }
         const long long o = (long long)m * N + n;
+        if (P.res) {   // residual (pre-norm sublayer: x + attention(norm(x)))
+            const uint4 rraw = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(P.res) + o);
+            const uint32_t rw[4] = {rraw.x, rraw.y, rraw.z, rraw.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                y[2 * e] += __uint_as_float(rw[e] << 16);
+                y[2 * e + 1] += __uint_as_float(rw[e] & 0xffff0000u);
+            }
+        }
         if (kOutF32) {
             float* C = static_cast<float*>(P.c) + o;
             *reinterpret_cast<float4*>(C) = make_float4(y[0], y[1], y[2], y[3]);
@@ -269,7 +279,8 @@ __global__ __launch_bounds__(256) void gemm_f32_nt(GemmArgs g, int tiles_n) {
         for (int y = 0; y < 4; ++y) {
             const int n = n0 + tx * 4 + y;
             if (n >= N) continue;
-            C[(long long)m * N + n] = acc[x][y] + (bias ? bias[n] : 0.0f);
+            const float r = P.res ? static_cast<const float*>(P.res)[(long long)m * N + n] : 0.0f;
+            C[(long long)m * N + n] = acc[x][y] + (bias ? bias[n] : 0.0f) + r;
         }
     }
 }
