@@ -256,6 +256,31 @@ class PreparedWeights:
             raise RuntimeError(f"sdpa_forward_ex failed with status {st}")
 
 
+class PreparedSublayer:
+    """mha_sublayer_forward (x + MHA(norm(x))) on an MHA workload's inputs,
+    with the Annotated Transformer's LayerNorm (gain 1, bias 0, eps 1e-6)."""
+
+    def __init__(self, inp):
+        import torch
+        from transformer_head_scaled_sdpa_amd import _lib
+        self.mha = PreparedMha(inp)
+        w = inp.workload
+        t = self.mha.t
+        self.lib = _lib.load()
+        need = int(self.lib.mha_sublayer_workspace_bytes(_lib.MHA_BF16, w.B, w.Lq, w.Lk, w.d_model, w.h))
+        self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        p = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
+        self.args = [_lib.MHA_BF16, _lib.MHA_F32, p(t["x_q"]), None, None, None, 0, 1e-6, p(t["w_q"]), p(t["b_q"]),
+                     p(t["w_k"]), p(t["b_k"]), p(t["w_v"]), p(t["b_v"]), p(t["w_o"]), p(t["b_o"]), p(self.mha.out),
+                     w.B, w.Lq, w.Lk, w.d_model, w.h, w.d_k, p(self.mha.vl), int(w.causal), p(self.ws), need]
+        self.torch = torch
+
+    def __call__(self):
+        st = self.lib.mha_sublayer_forward(*self.args, ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"mha_sublayer_forward failed with status {st}")
+
+
 def time_steps(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -512,6 +537,15 @@ def main():
             "alg_GBs": round(b / (dms * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(b / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         del df
+
+    if not args.no_long_sdpa and w.kind == "mha" and w.dtype == "bf16" and w.self_attn:
+        sf = PreparedSublayer(inp)
+        sms, _ = time_steps(sf, args.steps, args.warmup)
+        result["mha_sublayer"] = {
+            "workload": w.description + ", as the pre-norm residual sublayer x + MHA(LayerNorm(x))",
+            "ms_per_step": round(sms, 6), "value": round(attn_flops / (sms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            "vs_plain_step": round(sms / ms, 3)}
+        del sf
 
     if not args.no_long_sdpa:
         # backward: algorithmic 8*d_k flops per allowed pair (the four

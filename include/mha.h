@@ -277,10 +277,9 @@ mha_status mha_forward_ex(mha_dtype in_dt, mha_dtype out_dt,
  *          valid_lens, causal and the dtype rules as for mha_forward
  *          (memory == NULL requires Lk == L).
  *   workspace : at least mha_sublayer_workspace_bytes(...) bytes.
- * Fusion: in bf16 self-attention with L <= 128 the normalisation runs inside
- * the attention kernel on the staged rows of x (no normalised copy in HBM);
- * otherwise a row-wise kernel writes norm(x) to the workspace first.  The
- * residual add is always fused into the output projection's epilogue.
+ * A row-wise kernel writes norm(x) to the workspace (in in_dt), the
+ * attention layer runs on it, and the residual add is fused into the output
+ * projection's epilogue.
  */
 size_t mha_sublayer_workspace_bytes(mha_dtype in_dt, int B, int L, int Lk, int d_model, int h);
 

@@ -336,9 +336,7 @@ mha_status mha_impl(mha_dtype in_dt, mha_dtype out_dt,
                     void* out,
                     int B, int Lq, int Lk, int d_model, int h, int d_k,
                     const int* valid_lens, int vl_rank, int causal, float* p_attn, mha_strides sp,
-                    void* workspace, size_t workspace_bytes, void* stream,
-                    const void* ln_gain = nullptr, const void* ln_bias = nullptr, int ln_kind = -1,
-                    float ln_eps = 0.0f, const void* residual = nullptr) {
+                    void* workspace, size_t workspace_bytes, void* stream, const void* residual = nullptr) {
     if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
     if (valid_lens && vl_rank != 1 && vl_rank != 2) return MHA_EINVAL;
     // The inspection path: projections to fp32, attention with the weights.
@@ -436,10 +434,6 @@ mha_status mha_impl(mha_dtype in_dt, mha_dtype out_dt,
         f.B = B; f.H = h; f.Lq = Lq; f.Lk = Lk; f.D = d_model;
         f.valid_lens = valid_lens;
         f.causal = causal ? 1 : 0;
-        f.ln_gain = ln_gain;
-        f.ln_bias = ln_bias;
-        f.ln_kind = ln_kind;
-        f.ln_eps = ln_eps;
         e = timed("attn_fused_bf16", s, [&] { return mha::launch_mha_attn_fused(f, s); });
         if (e != hipSuccess) return MHA_EHIP;
     } else {
@@ -571,18 +565,8 @@ mha_status mha_sublayer_forward(mha_dtype in_dt, mha_dtype out_dt,
         if (overlap(r, rws) || overlap(r, rout)) return MHA_EINVAL;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // Self-attention in bf16 with L <= 128: the normalisation runs inside the
-    // single-pass attention kernel.
-    mha::FusedArgs probe;
-    probe.x_q = probe.x_kv = x;
-    probe.Lq = probe.Lk = L;
-    probe.D = d_model;
-    probe.ln_kind = ln_kind;
-    if (in_dt == MHA_BF16 && !memory && mha::mha_attn_fused_small_fits(probe))
-        return mha_impl(in_dt, out_dt, x, x, w_q, b_q, w_k, b_k, w_v, b_v, w_o, b_o, out, B, L, L, d_model, h, d_k,
-                        valid_lens, 1, causal, nullptr, mha_strides{0, 0, 0}, static_cast<char*>(workspace) + xbytes,
-                        need - xbytes, stream, ln_gain, ln_bias, ln_kind, ln_eps, x);
-    // Otherwise norm(x) goes to the workspace first.
+    // norm(x) goes to the workspace (one row-wise pass), then the attention
+    // layer runs on it with x as the residual of its output projection.
     void* xn = workspace;
     const hipError_t e = timed("layer_norm", s, [&] {
         return mha::launch_layer_norm(x, ln_gain, ln_bias, xn, B * L, d_model, ln_kind, ln_eps, in_dt == MHA_F32, s);
@@ -590,7 +574,7 @@ mha_status mha_sublayer_forward(mha_dtype in_dt, mha_dtype out_dt,
     if (e != hipSuccess) return MHA_EHIP;
     return mha_impl(in_dt, out_dt, xn, memory ? memory : xn, w_q, b_q, w_k, b_k, w_v, b_v, w_o, b_o, out, B, L, Lk,
                     d_model, h, d_k, valid_lens, 1, causal, nullptr, mha_strides{0, 0, 0},
-                    static_cast<char*>(workspace) + xbytes, need - xbytes, stream, nullptr, nullptr, -1, 0.0f, x);
+                    static_cast<char*>(workspace) + xbytes, need - xbytes, stream, x);
 }
 
 mha_status mha_timing_enable(int repeat) {

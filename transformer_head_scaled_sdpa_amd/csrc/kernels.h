@@ -51,14 +51,6 @@ struct FusedArgs {
     int B, H, Lq, Lk, D;
     const int* valid_lens;  // device int32 [B] or nullptr
     int causal;
-    // Pre-norm: when ln_kind >= 0 the kernel normalises each row of x_q
-    // (= x_kv) before projecting it: 0 = std with Bessel's correction, eps
-    // added to the std; 1 = biased variance, eps inside the root.  Gain and
-    // bias [D] bf16, nullptr meaning 1 and 0.
-    const void* ln_gain = nullptr;
-    const void* ln_bias = nullptr;
-    int ln_kind = -1;
-    float ln_eps = 0.0f;
 };
 
 // One decoding step: a single query per (batch, head) against cached keys
@@ -127,8 +119,9 @@ size_t backward_workspace_bytes(int B, int H, int Lq);
 hipError_t launch_sdpa_backward(const BackwardArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool out_f32, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
-// Row-wise layer normalisation y = norm(x) of [M, D] (kind and eps as in
-// FusedArgs), bf16 or fp32 in and out.
+// Row-wise layer normalisation y = norm(x) of [M, D], bf16 or fp32 in and
+// out: kind 0 = std with Bessel's correction, eps added to the std; kind 1 =
+// biased variance, eps inside the root.  Gain and bias [D] or nullptr.
 hipError_t launch_layer_norm(const void* x, const void* gain, const void* bias, void* y, int M, int D, int kind,
                              float eps, bool f32, hipStream_t s);
 

@@ -429,7 +429,6 @@ hipError_t launch_variant(const FusedArgs& a, hipStream_t s) {
 hipError_t launch_mha_attn_fused(const FusedArgs& a, hipStream_t s) {
     if (a.D % 64 != 0) return hipErrorInvalidValue;
     if (mha_attn_fused_small_fits(a)) return launch_mha_attn_fused_small(a, s);
-    if (a.ln_kind >= 0) return hipErrorInvalidValue;   // pre-norm is fused only into the single-pass kernel
     const bool c = a.causal != 0, v = a.valid_lens != nullptr;
     if (c) return v ? launch_variant<true, true>(a, s) : launch_variant<true, false>(a, s);
     return v ? launch_variant<false, true>(a, s) : launch_variant<false, false>(a, s);

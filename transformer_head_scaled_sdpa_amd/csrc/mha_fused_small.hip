@@ -26,12 +26,6 @@
 //    Kh Ql^T, so large logits (embeddings scaled by sqrt(d_model)) keep
 //    near-fp32 accuracy.  Waves 0-3 hand their Q fragments to waves 4-7
 //    through LDS.
-//  * Pre-norm (the residual sublayer x + attention(norm(x)) of The Annotated
-//    Transformer, with the LayerNorm of either printed form): while the first
-//    slices load, each wave computes the mean and the normaliser of 16 of the
-//    rows, and gain and bias go to LDS; every staged X slice is then
-//    normalised in place in LDS (rounded to bf16) before its MFMAs, so Q, K
-//    and V are projected from norm(x) without a normalised copy in HBM.
 //  * Attention is split over the keys: wave w takes queries 32*(w%4) .. +31
 //    against keys 64*(w/4) .. +63.  Each half is a single 64-key tile, so
 //    its weights are exp2 of the scores minus the exact row max of the tile.
@@ -60,9 +54,7 @@ constexpr int kPart = 2 * 16 + 2;        // floats a key-half wave hands over pe
 // (4 x 34 x 64 floats).
 constexpr int kStages = 3;
 constexpr int kStageBytes = (kL + 3 * kHd) * kTileRowBytes;      // 46080
-constexpr int kLnOff = kStages * kStageBytes;                    // 138240: row mean, 1/normaliser
-constexpr int kLnMaxD = 4096;                                     // gain, bias staged as bf16 [D] each
-constexpr int kLdsBytes = kLnOff + 2 * kL * 4 + 2 * kLnMaxD * 2; // 156672
+constexpr int kLdsBytes = kStages * kStageBytes;                 // 138240
 constexpr int kKhOff = 0;
 constexpr int kKlOff = kKhOff + kL * kTileRowBytes;
 constexpr int kVOff = kKlOff + kL * kTileRowBytes;
@@ -182,51 +174,6 @@ __global__ __launch_bounds__(kThreads, 1) void mha_attn_fused_small_bf16(FusedAr
         lw.issue(wk + d0, base + (kL + kHd) * kTileRowBytes, wave);
         lw.issue(wv + d0, base + (kL + 2 * kHd) * kTileRowBytes, wave);
     };
-    // ---- pre-norm statistics (the first slices are already loading) ----
-    const bool ln = a.ln_kind >= 0;
-    float* ln_mu = reinterpret_cast<float*>(smem + kLnOff);
-    float* ln_rs = ln_mu + kL;
-    bf16_t* ln_g = reinterpret_cast<bf16_t*>(ln_rs + kL);
-    bf16_t* ln_b = ln_g + kLnMaxD;
-    if (ln) {
-        const bf16_t* gp = static_cast<const bf16_t*>(a.ln_gain);
-        const bf16_t* bp = static_cast<const bf16_t*>(a.ln_bias);
-        for (int c = tid; c < D; c += kThreads) {
-            ln_g[c] = gp ? gp[c] : (bf16_t)0x3f80;     // 1.0
-            ln_b[c] = bp ? bp[c] : (bf16_t)0;
-        }
-        for (int r = wave * (kL / kW); r < (wave + 1) * (kL / kW); ++r) {
-            const bf16_t* xr = x + (long long)min(r, L - 1) * D;
-            float sum = 0.0f;
-            for (int c = lane * 8; c < D; c += 512) {
-                const uint4 w = *reinterpret_cast<const uint4*>(xr + c);
-                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sum += __uint_as_float(u[e] << 16) + __uint_as_float(u[e] & 0xffff0000u);
-            }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-            const float mean = sum / D;
-            float ss = 0.0f;
-            for (int c = lane * 8; c < D; c += 512) {
-                const uint4 w = *reinterpret_cast<const uint4*>(xr + c);
-                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float d0 = __uint_as_float(u[e] << 16) - mean, d1 = __uint_as_float(u[e] & 0xffff0000u) - mean;
-                    ss += d0 * d0 + d1 * d1;
-                }
-            }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-            const float den = a.ln_kind == 0 ? sqrtf(ss / (D - 1)) + a.ln_eps : sqrtf(ss / D + a.ln_eps);
-            if (lane == 0) {
-                ln_mu[r] = mean;
-                ln_rs[r] = 1.0f / den;
-            }
-        }
-    }
-
     // Feature blocks 0..5 are Q0, Q1, K0, K1, V0, V1 (weight rows 32*f ..);
     // wave w owns rows rb = w % 4 and feature blocks 3*(w/4) + j in acc[j].
     const bool qwave = wave < 4;
@@ -249,34 +196,6 @@ __global__ __launch_bounds__(kThreads, 1) void mha_attn_fused_small_bf16(FusedAr
         }
         __syncthreads();
         if (dt + 2 < nd) issue((dt + 2) % kStages, (dt + 2) * 64);
-        if (ln) {
-            // Normalise the staged X slice in place: 128 rows x 8 chunks of
-            // 8 features, two chunks per thread (the same 8 columns).
-            bf16_t* xw = reinterpret_cast<bf16_t*>(smem + (dt % kStages) * kStageBytes);
-            const int c8 = (tid & 7) * 8, d0 = dt * 64 + c8;
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int r = (tid >> 3) + n * (kThreads / 8);
-                uint4* p = reinterpret_cast<uint4*>(xw + r * kTileLdsRow + c8);
-                const uint4 w = *p, gw = *reinterpret_cast<const uint4*>(ln_g + d0),
-                            bw = *reinterpret_cast<const uint4*>(ln_b + d0);
-                const uint32_t u[4] = {w.x, w.y, w.z, w.w}, gu[4] = {gw.x, gw.y, gw.z, gw.w},
-                               bu[4] = {bw.x, bw.y, bw.z, bw.w};
-                const float mu = ln_mu[r], rs = ln_rs[r];
-                uint32_t o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float y0 = __uint_as_float(gu[e] << 16) * ((__uint_as_float(u[e] << 16) - mu) * rs) +
-                                     __uint_as_float(bu[e] << 16);
-                    const float y1 = __uint_as_float(gu[e] & 0xffff0000u) *
-                                         ((__uint_as_float(u[e] & 0xffff0000u) - mu) * rs) +
-                                     __uint_as_float(bu[e] & 0xffff0000u);
-                    o[e] = pack_bf16x2(y0, y1);
-                }
-                *p = make_uint4(o[0], o[1], o[2], o[3]);
-            }
-            __syncthreads();
-        }
         const bf16_t* xs = reinterpret_cast<const bf16_t*>(smem + (dt % kStages) * kStageBytes);
         const bf16_t* ws = xs + kL * kTileLdsRow;
 #pragma unroll
@@ -481,7 +400,7 @@ hipError_t launch_variant(const FusedArgs& a, hipStream_t s) {
 }  // namespace
 
 bool mha_attn_fused_small_fits(const FusedArgs& a) {
-    return a.x_q == a.x_kv && a.Lq == a.Lk && a.Lq <= kL && a.D % 64 == 0 && (a.ln_kind < 0 || a.D <= kLnMaxD);
+    return a.x_q == a.x_kv && a.Lq == a.Lk && a.Lq <= kL && a.D % 64 == 0;
 }
 
 hipError_t launch_mha_attn_fused_small(const FusedArgs& a, hipStream_t s) {
