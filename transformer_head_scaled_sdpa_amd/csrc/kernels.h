@@ -117,6 +117,8 @@ hipError_t launch_sdpa_f32(const SdpaArgs& a, hipStream_t s);
 hipError_t launch_sdpa_weights(const WeightsArgs& a, hipStream_t s);
 size_t backward_workspace_bytes(int B, int H, int Lq);
 hipError_t launch_sdpa_backward(const BackwardArgs& a, hipStream_t s);
+// bf16 inputs, d = 64, on MFMA (launch_sdpa_backward dispatches to it).
+hipError_t launch_sdpa_backward_bf16(const BackwardArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool out_f32, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 // Row-wise layer normalisation y = norm(x) of [M, D], bf16 or fp32 in and

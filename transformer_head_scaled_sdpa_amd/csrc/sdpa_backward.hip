@@ -287,9 +287,10 @@ hipError_t launch_variant(const BackwardArgs& a, hipStream_t s) {
 
 size_t backward_workspace_bytes(int B, int H, int Lq) { return (size_t)B * H * Lq * 2 * sizeof(float); }
 
+// fp32 inputs run here; bf16 inputs take the MFMA kernels.
 hipError_t launch_sdpa_backward(const BackwardArgs& a, hipStream_t s) {
     if (a.in_f32) return a.causal ? launch_variant<float, true>(a, s) : launch_variant<float, false>(a, s);
-    return a.causal ? launch_variant<bf16_t, true>(a, s) : launch_variant<bf16_t, false>(a, s);
+    return launch_sdpa_backward_bf16(a, s);
 }
 
 }  // namespace mha

@@ -1,0 +1,519 @@
+// Backward pass of scaled dot-product attention on bf16 MFMA (fp32
+// accumulate), d_k = d_v = 64, gfx950: the same gradients as the fp32 kernels
+// (dq, dk, dv for an output gradient do; see sdpa_backward.hip), for bf16
+// inputs.  With tau = 1/sqrt(d_k), p the weights, D_i = do_i . o_i:
+//   dv_j = sum_i p_ij do_i,  ds_ij = p_ij (do_i . v_j - D_i),
+//   dq_i = tau sum_j ds_ij k_j,  dk_j = tau sum_i ds_ij q_i   (allowed pairs;
+// a row with no allowed key weights all keys uniformly and passes no
+// gradient to q or k).
+//
+// Two kernels of 8 wave64s per workgroup.  A workgroup owns 64 rows (two
+// groups of 32, one row per lane column of the 32x32 MFMA tile) and streams
+// the other side in steps of 128 rows: four phases of 32, one per wave of a
+// group, so every wave works on its own tile and the four partial sums of a
+// row are added through LDS at the end.  Products run on
+// v_mfma_f32_32x32x16_bf16 in the operand layouts of the forward kernel: an
+// accumulator packed to bf16 feeds the next MFMA as its B operand, and
+// transposed tiles are read from LDS with ds_read_b64_tr_b16 (each tile is
+// stored twice: 144-byte rows for 16-byte fragment reads, 192-byte rows for
+// the transposed reads).
+//  * rows (queries; q and do fragments in registers): pass 1 over the keys
+//    finds each query's log-sum-exp (online, per lane half and phase, merged
+//    at the end); D_i from the supplied output.  Pass 2: S^T = K Q^T and
+//    dP^T = V dO^T, dS^T = P^T (dP^T - D), and dQ^T += K^T dS^T.  The
+//    log-sum-exp and D go to the workspace.
+//  * keys (k and v fragments in registers): S = Q K^T and dP = dO V^T, P and
+//    dS from the stored log-sum-exp and D, then dV^T += dO^T P and
+//    dK^T += Q^T dS.
+// dS (and P for dV) is rounded to bf16 for its products, as P is in the
+// forward.  Tiles where every pair is allowed skip the mask arithmetic.
+#include "common.h"
+#include "kernels.h"
+
+namespace mha {
+
+namespace {
+
+constexpr int kD = 64;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kGroups = 2;                   // row groups of 32 per workgroup
+constexpr int kPhases = kWaves / kGroups;    // streamed tiles per step
+constexpr int kRowsWg = 32 * kGroups;
+constexpr int kTile = 32;                    // streamed rows per phase
+constexpr int kStep = kTile * kPhases;       // streamed rows per step
+constexpr int kLdsR = kD + 8;                // 144-byte rows
+constexpr int kLdsT = kD + 32;               // 192-byte rows
+constexpr int kTileRB = kTile * kLdsR * 2;   // bytes
+constexpr int kTileTB = kTile * kLdsT * 2;
+constexpr int kChunks = kStep * 8 / kThreads;  // 16-byte chunks per thread per streamed operand
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ bf16x8 frag(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// A 32-row tile (144-byte rows) times 32 register rows: element v of the
+// result is tile row (v/4)*8 + hb*4 + v%4 against register row lane % 32.
+__device__ __forceinline__ f32x16 tile_dot(const bf16_t* t, const bf16x8 (&f)[4], int l32, int hb) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = mfma32x32x16(frag(t + l32 * kLdsR + kk * 16 + hb * 8), f[kk], acc);
+    return acc;
+}
+
+// Transposed fragment of a row-major [32 rows][64 features] LDS tile (192 B
+// rows): the A operand [32 features x 16 rows] for features tb*32 + lane%32
+// and the tile rows of slice kb in the order the packed B operands use
+// (kb*16 + hb*4 + 0..3, then + 8..11).
+__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* ts, int kb, int tb, int hb, int lane) {
+    const int g = lane >> 4, r = lane & 15;
+    const int row = kb * 16 + hb * 4 + (r >> 2);
+    const int col = tb * 32 + (g & 1) * 16 + (r & 3) * 4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ts + row * kLdsT + col));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ts + (row + 8) * kLdsT + col));
+    const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, both);
+}
+
+// Pack a 32-row accumulator (element v: row (v/4)*8 + hb*4 + v%4) as two B
+// operands: slice kb holds rows kb*16 + {hb*4 + 0..3, hb*4 + 8..11}.
+__device__ __forceinline__ void pack_b(const f32x16& x, u32x4 (&w)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pp = {static_cast<__bf16>(x[kb * 8 + e]), static_cast<__bf16>(x[kb * 8 + e + 1])};
+            w[kb][e >> 1] = __builtin_bit_cast(uint32_t, pp);
+        }
+}
+
+// Row offset of accumulator element v within its 32-row tile, less hb*4.
+__device__ __forceinline__ constexpr int acc_row(int v) { return (v >> 2) * 8 + (v & 3); }
+
+// One step of a [L, 64] bf16 operand: rows r0 .. r0+127 as 1024 chunks of 16
+// bytes (chunk n: row n / 8, features (n % 8) * 8 ..), kChunks per thread;
+// rows at or past L read as zero.
+struct Chunks {
+    uint4 c[kChunks];
+};
+__device__ __forceinline__ Chunks load_step(const bf16_t* x, long long ld, int r0, int L, int tid) {
+    Chunks t;
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n) {
+        const int ch = tid + n * kThreads, r = ch >> 3, col = (ch & 7) * 8;
+        t.c[n] = r0 + r < L ? *reinterpret_cast<const uint4*>(x + (long long)(r0 + r) * ld + col)
+                            : make_uint4(0, 0, 0, 0);
+    }
+    return t;
+}
+// Store a step into the per-phase tiles: row r goes to phase r / 32, in
+// 144-byte rows at byte offset offR of the phase area and, if offT >= 0, in
+// 192-byte rows at offT.
+__device__ __forceinline__ void store_step(const Chunks& t, char* smem, int phase_bytes, int offR, int offT, int tid) {
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n) {
+        const int ch = tid + n * kThreads, r = ch >> 3, col = (ch & 7) * 8;
+        char* base = smem + (r >> 5) * phase_bytes;
+        const int lr = r & 31;
+        *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(base + offR) + lr * kLdsR + col) = t.c[n];
+        if (offT >= 0) *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(base + offT) + lr * kLdsT + col) = t.c[n];
+    }
+}
+
+__device__ __forceinline__ int row_len(const BackwardArgs& a, int b, int i) {
+    if (a.vl_rank == 1) return a.valid_lens[b];
+    if (a.vl_rank == 2) return a.valid_lens[(long long)b * a.Lq + i];
+    return a.Lk;
+}
+
+// Keys [0, klim) are allowed for query i; a row with no allowed key (lengths
+// given, length <= 0) allows all Lk keys with equal scores (`none`).
+template <bool kCausal>
+__device__ __forceinline__ int key_limit(const BackwardArgs& a, int b, int i, bool& none) {
+    const int len = row_len(a, b, i);
+    none = a.vl_rank != 0 && len <= 0;
+    if (none) return a.Lk;
+    const int lim = min(len, a.Lk);
+    return kCausal ? min(lim, i + 1) : lim;
+}
+
+// Sum the per-phase partials of a 32-row accumulator pair through LDS: the
+// waves of phases 1..3 write theirs, the phase-0 wave of the group adds them.
+// Leaves the result in `acc` of the phase-0 waves.  `red` holds 6 slots of
+// 8 KiB; the caller brackets the calls with barriers.
+__device__ __forceinline__ void reduce_write(float* red, const f32x16 (&acc)[2], int grp, int ph, int lane) {
+    if (ph == 0) return;
+    float* slot = red + (grp * (kPhases - 1) + ph - 1) * 32 * 64;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) slot[(tb * 16 + v) * 64 + lane] = acc[tb][v];
+}
+__device__ __forceinline__ void reduce_read(const float* red, f32x16 (&acc)[2], int grp, int ph, int lane) {
+    if (ph != 0) return;
+#pragma unroll
+    for (int p = 1; p < kPhases; ++p) {
+        const float* slot = red + (grp * (kPhases - 1) + p - 1) * 32 * 64;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[tb][v] += slot[(tb * 16 + v) * 64 + lane];
+    }
+}
+
+// Store a transposed accumulator pair (element v of block tb: feature
+// tb*32 + (v/4)*8 + hb*4 + v%4, row = the lane's row) times `scale`.
+__device__ __forceinline__ void store_rowT(void* base, long long off, bool out_f32, const f32x16 (&acc)[2], float scale,
+                                           int hb) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int t = tb * 32 + g4 * 8 + hb * 4;
+            const float y0 = acc[tb][g4 * 4] * scale, y1 = acc[tb][g4 * 4 + 1] * scale,
+                        y2 = acc[tb][g4 * 4 + 2] * scale, y3 = acc[tb][g4 * 4 + 3] * scale;
+            if (out_f32)
+                *reinterpret_cast<float4*>(static_cast<float*>(base) + off + t) = make_float4(y0, y1, y2, y3);
+            else
+                *reinterpret_cast<uint2*>(static_cast<bf16_t*>(base) + off + t) =
+                    make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+        }
+}
+
+// ---------------------------------------------------------------------------
+// rows: log-sum-exp, D, dq
+// ---------------------------------------------------------------------------
+constexpr int kRowsKR = 0;                        // K, 144-byte rows
+constexpr int kRowsKT = kTileRB;                  // K, 192-byte rows
+constexpr int kRowsVR = kTileRB + kTileTB;        // V, 144-byte rows
+constexpr int kRowsPhase = 2 * kTileRB + kTileTB;
+
+template <bool kCausal>
+__global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, float c) {
+    __shared__ __attribute__((aligned(16))) char smem[kPhases * kRowsPhase];
+    __shared__ float2 stat_s[kGroups][kPhases][2][32];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave % kGroups, ph = wave / kGroups;
+    const int hb = lane >> 5, l32 = lane & 31;
+    const int BH = a.B * a.H;
+    const int bh = blockIdx.x % BH;
+    const int b = bh / a.H, hd = bh % a.H;
+    // Causal rows late in the sequence see the most keys: they go first.
+    const int n_wg = (a.Lq + kRowsWg - 1) / kRowsWg;
+    const int blk = blockIdx.x / BH;
+    const int q_wg = (kCausal ? n_wg - 1 - blk : blk) * kRowsWg;
+    const int i = q_wg + grp * 32 + l32;
+    const int Lq = a.Lq, Lk = a.Lk;
+    const bool live = i < Lq;
+
+    bool none = false;
+    const int klim = live ? key_limit<kCausal>(a, b, i, none) : Lk;
+    const float cs = none ? 0.0f : c;      // score scale (log2 units); 0: equal scores
+    const float dm = none ? 0.0f : 1.0f;   // 0: no gradient through the scores
+    int kmin = klim;                        // smallest key limit in the wave
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) kmin = min(kmin, __shfl_xor(kmin, o));
+    kmin = __builtin_amdgcn_readfirstlane(kmin);
+    // Keys this workgroup must visit: up to the causal bound unless lengths
+    // are given (a fully masked row then spans all keys).
+    const int kv_end = (kCausal && a.vl_rank == 0) ? min(Lk, q_wg + kRowsWg) : Lk;
+    const int n_steps = (kv_end + kStep - 1) / kStep;
+
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + b * a.sq[0] + hd * a.sq[1];
+    const bf16_t* gp = static_cast<const bf16_t*>(a.dout) + b * a.sdo[0] + hd * a.sdo[1];
+    const bf16_t* op = static_cast<const bf16_t*>(a.o) + b * a.so[0] + hd * a.so[1];
+    const bf16_t* kp = static_cast<const bf16_t*>(a.k) + b * a.sk[0] + hd * a.sk[1];
+    const bf16_t* vp = static_cast<const bf16_t*>(a.v) + b * a.sv[0] + hd * a.sv[1];
+
+    Chunks nk = load_step(kp, a.sk[2], 0, Lk, tid);
+
+    // Q and dO fragments (B operands: query lane%32, features kk*16 + hb*8 ..).
+    bf16x8 qf[4], gf[4];
+    float dsum = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        uint4 rq = make_uint4(0, 0, 0, 0), rg = rq, ro = rq;
+        if (live) {
+            rq = *reinterpret_cast<const uint4*>(qp + (long long)i * a.sq[2] + kk * 16 + hb * 8);
+            rg = *reinterpret_cast<const uint4*>(gp + (long long)i * a.sdo[2] + kk * 16 + hb * 8);
+            ro = *reinterpret_cast<const uint4*>(op + (long long)i * a.so[2] + kk * 16 + hb * 8);
+        }
+        qf[kk] = __builtin_bit_cast(bf16x8, rq);
+        gf[kk] = __builtin_bit_cast(bf16x8, rg);
+        const uint32_t ug[4] = {rg.x, rg.y, rg.z, rg.w}, uo[4] = {ro.x, ro.y, ro.z, ro.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dsum += __uint_as_float(ug[e] << 16) * __uint_as_float(uo[e] << 16) +
+                    __uint_as_float(ug[e] & 0xffff0000u) * __uint_as_float(uo[e] & 0xffff0000u);
+    }
+    dsum = pair_sum(dsum);                  // D_i over both lane halves
+
+    // ---- pass 1: log-sum-exp (this lane half's keys, this phase) ----
+    float m_run = -INFINITY, l_run = 0.0f;
+    for (int st = 0; st < n_steps; ++st) {
+        __syncthreads();
+        store_step(nk, smem, kRowsPhase, kRowsKR, -1, tid);
+        if (st + 1 < n_steps) nk = load_step(kp, a.sk[2], (st + 1) * kStep, Lk, tid);
+        __syncthreads();
+        const int t0 = st * kStep + ph * kTile;   // this wave's keys t0 .. t0+31
+        const f32x16 s = tile_dot(reinterpret_cast<const bf16_t*>(smem + ph * kRowsPhase + kRowsKR), qf, l32, hb);
+        if (t0 + kTile <= kmin) {
+            float mx = s[0];
+#pragma unroll
+            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+            const float m_new = fmaxf(m_run, mx * cs);
+            float rs = 0.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) rs += __builtin_amdgcn_exp2f(fmaf(s[v], cs, -m_new));
+            l_run = l_run * __builtin_amdgcn_exp2f(m_run - m_new) + rs;
+            m_run = m_new;
+        } else {
+            const int rel = klim - (t0 + hb * 4);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, acc_row(v) < rel ? s[v] : -INFINITY);
+            const float tm = mx == -INFINITY ? -INFINITY : mx * cs;
+            const float m_new = fmaxf(m_run, tm);
+            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+            float rs = 0.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(s[v], cs, -m_use));
+                rs += acc_row(v) < rel ? e : 0.0f;
+            }
+            l_run = l_run * __builtin_amdgcn_exp2f(m_run - m_use) + rs;
+            m_run = m_new;
+        }
+    }
+    stat_s[grp][ph][hb][l32] = make_float2(m_run, l_run);
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < kPhases; ++p)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) M = fmaxf(M, stat_s[grp][p][h][l32].x);
+    float L = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kPhases; ++p)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float2 x = stat_s[grp][p][h][l32];
+            L += x.x == -INFINITY ? 0.0f : x.y * __builtin_amdgcn_exp2f(x.x - M);
+        }
+    // v_log_f32 is the base-2 logarithm, matching the log2-unit scores.
+    const float lse = L > 0.0f ? M + __builtin_amdgcn_logf(L) : 0.0f;
+
+    // ---- pass 2: dq ----
+    const float ddm = dsum * dm;
+    f32x16 dq[2] = {};
+    nk = load_step(kp, a.sk[2], 0, Lk, tid);
+    Chunks nv = load_step(vp, a.sv[2], 0, Lk, tid);
+    for (int st = 0; st < n_steps; ++st) {
+        __syncthreads();
+        store_step(nk, smem, kRowsPhase, kRowsKR, kRowsKT, tid);
+        store_step(nv, smem, kRowsPhase, kRowsVR, -1, tid);
+        if (st + 1 < n_steps) {
+            nk = load_step(kp, a.sk[2], (st + 1) * kStep, Lk, tid);
+            nv = load_step(vp, a.sv[2], (st + 1) * kStep, Lk, tid);
+        }
+        __syncthreads();
+        const int t0 = st * kStep + ph * kTile;
+        const char* area = smem + ph * kRowsPhase;
+        const f32x16 s = tile_dot(reinterpret_cast<const bf16_t*>(area + kRowsKR), qf, l32, hb);
+        f32x16 ds = tile_dot(reinterpret_cast<const bf16_t*>(area + kRowsVR), gf, l32, hb);
+        if (t0 + kTile <= kmin) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) ds[v] = __builtin_amdgcn_exp2f(fmaf(s[v], cs, -lse)) * fmaf(ds[v], dm, -ddm);
+        } else {
+            const int rel = klim - (t0 + hb * 4);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = acc_row(v) < rel ? __builtin_amdgcn_exp2f(fmaf(s[v], cs, -lse)) : 0.0f;
+                ds[v] = p * fmaf(ds[v], dm, -ddm);
+            }
+        }
+        u32x4 w[2];
+        pack_b(ds, w);
+        const bf16_t* kt = reinterpret_cast<const bf16_t*>(area + kRowsKT);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 d8 = __builtin_bit_cast(bf16x8, w[kb]);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) dq[tb] = mfma32x32x16(tr_frag(kt, kb, tb, hb, lane), d8, dq[tb]);
+        }
+    }
+    __syncthreads();
+    reduce_write(reinterpret_cast<float*>(smem), dq, grp, ph, lane);
+    __syncthreads();
+    reduce_read(reinterpret_cast<const float*>(smem), dq, grp, ph, lane);
+    if (ph != 0 || !live) return;
+    if (hb == 0) {
+        a.rows[((long long)bh * Lq + i) * 2] = lse;
+        a.rows[((long long)bh * Lq + i) * 2 + 1] = dsum;
+    }
+    store_rowT(a.dq, b * a.sdq[0] + hd * a.sdq[1] + (long long)i * a.sdq[2], a.out_f32, dq, 1.0f / 8.0f, hb);
+}
+
+// ---------------------------------------------------------------------------
+// keys: dk, dv
+// ---------------------------------------------------------------------------
+constexpr int kKeysQR = 0;                        // Q, 144-byte rows
+constexpr int kKeysQT = kTileRB;                  // Q, 192-byte rows
+constexpr int kKeysGR = kTileRB + kTileTB;        // dO, 144-byte rows
+constexpr int kKeysGT = 2 * kTileRB + kTileTB;    // dO, 192-byte rows
+constexpr int kKeysPhase = 2 * kTileRB + 2 * kTileTB;
+
+template <bool kCausal>
+__global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, float c) {
+    __shared__ __attribute__((aligned(16))) char smem[kPhases * kKeysPhase];
+    __shared__ float4 rowf_s[kStep];   // per streamed query: log-sum-exp, D, score scale, gradient factor
+    __shared__ int klim_s[kStep];      // per streamed query: key limit
+    __shared__ int tmin_s[kPhases];    // per phase tile: smallest key limit (-1 if a row has none allowed)
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave % kGroups, ph = wave / kGroups;
+    const int hb = lane >> 5, l32 = lane & 31;
+    const int BH = a.B * a.H;
+    const int bh = blockIdx.x % BH;
+    const int b = bh / a.H, hd = bh % a.H;
+    const int k_wg = (blockIdx.x / BH) * kRowsWg;   // causal: early keys see the most queries and go first
+    const int j = k_wg + grp * 32 + l32;            // this lane's key
+    const int j_last = k_wg + grp * 32 + 31;
+    const int Lq = a.Lq, Lk = a.Lk;
+
+    const bf16_t* kp = static_cast<const bf16_t*>(a.k) + b * a.sk[0] + hd * a.sk[1];
+    const bf16_t* vp = static_cast<const bf16_t*>(a.v) + b * a.sv[0] + hd * a.sv[1];
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + b * a.sq[0] + hd * a.sq[1];
+    const bf16_t* gp = static_cast<const bf16_t*>(a.dout) + b * a.sdo[0] + hd * a.sdo[1];
+
+    // Causal without lengths: queries before the workgroup's first key
+    // weight none of its keys.
+    const int i_begin = (kCausal && a.vl_rank == 0) ? k_wg : 0;
+    const int n_steps = (Lq - i_begin + kStep - 1) / kStep;
+    Chunks nq = load_step(qp, a.sq[2], i_begin, Lq, tid);
+    Chunks ng = load_step(gp, a.sdo[2], i_begin, Lq, tid);
+
+    // K and V fragments (B operands: key lane%32, features kk*16 + hb*8 ..).
+    bf16x8 kf[4], vf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        uint4 rk = make_uint4(0, 0, 0, 0), rv = rk;
+        if (j < Lk) {
+            rk = *reinterpret_cast<const uint4*>(kp + (long long)j * a.sk[2] + kk * 16 + hb * 8);
+            rv = *reinterpret_cast<const uint4*>(vp + (long long)j * a.sv[2] + kk * 16 + hb * 8);
+        }
+        kf[kk] = __builtin_bit_cast(bf16x8, rk);
+        vf[kk] = __builtin_bit_cast(bf16x8, rv);
+    }
+
+    f32x16 dk[2] = {}, dv[2] = {};
+    for (int st = 0; st < n_steps; ++st) {
+        const int i0 = i_begin + st * kStep;
+        __syncthreads();
+        store_step(nq, smem, kKeysPhase, kKeysQR, kKeysQT, tid);
+        store_step(ng, smem, kKeysPhase, kKeysGR, kKeysGT, tid);
+        if (tid < kStep) {
+            const int qi = i0 + tid;
+            float lse = 0.0f, dsum = 0.0f;
+            bool none = false;
+            int kl = 0;
+            if (qi < Lq) {
+                lse = a.rows[((long long)bh * Lq + qi) * 2];
+                dsum = a.rows[((long long)bh * Lq + qi) * 2 + 1];
+                kl = key_limit<kCausal>(a, b, qi, none);
+            }
+            rowf_s[tid] = make_float4(lse, dsum, none ? 0.0f : c, none ? 0.0f : 1.0f);
+            klim_s[tid] = kl;
+            int mn = none ? -1 : kl;
+#pragma unroll
+            for (int o = 16; o >= 1; o >>= 1) mn = min(mn, __shfl_xor(mn, o));
+            if ((tid & 31) == 0) tmin_s[tid >> 5] = mn;
+        }
+        if (st + 1 < n_steps) {
+            nq = load_step(qp, a.sq[2], i0 + kStep, Lq, tid);
+            ng = load_step(gp, a.sdo[2], i0 + kStep, Lq, tid);
+        }
+        __syncthreads();
+        // S = Q K^T and dP = dO V^T: element v is query ph*32 + acc_row(v) +
+        // hb*4 of this step, key j.
+        const char* area = smem + ph * kKeysPhase;
+        f32x16 p = tile_dot(reinterpret_cast<const bf16_t*>(area + kKeysQR), kf, l32, hb);
+        f32x16 ds = tile_dot(reinterpret_cast<const bf16_t*>(area + kKeysGR), vf, l32, hb);
+        const int rb = ph * kTile + hb * 4;
+        if (j_last < __builtin_amdgcn_readfirstlane(tmin_s[ph])) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float4 rf = rowf_s[rb + acc_row(v)];
+                const float e = __builtin_amdgcn_exp2f(fmaf(p[v], c, -rf.x));
+                p[v] = e;
+                ds[v] = e * (ds[v] - rf.y);
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float4 rf = rowf_s[rb + acc_row(v)];
+                const int kl = klim_s[rb + acc_row(v)];
+                const float e = j < kl ? __builtin_amdgcn_exp2f(fmaf(p[v], rf.z, -rf.x)) : 0.0f;
+                p[v] = e;
+                ds[v] = e * (ds[v] - rf.y) * rf.w;
+            }
+        }
+        u32x4 pw[2], dw[2];
+        pack_b(p, pw);
+        pack_b(ds, dw);
+        const bf16_t* qt = reinterpret_cast<const bf16_t*>(area + kKeysQT);
+        const bf16_t* gt = reinterpret_cast<const bf16_t*>(area + kKeysGT);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 p8 = __builtin_bit_cast(bf16x8, pw[kb]), d8 = __builtin_bit_cast(bf16x8, dw[kb]);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                dv[tb] = mfma32x32x16(tr_frag(gt, kb, tb, hb, lane), p8, dv[tb]);
+                dk[tb] = mfma32x32x16(tr_frag(qt, kb, tb, hb, lane), d8, dk[tb]);
+            }
+        }
+    }
+    float* red = reinterpret_cast<float*>(smem);
+    __syncthreads();
+    reduce_write(red, dv, grp, ph, lane);
+    __syncthreads();
+    reduce_read(red, dv, grp, ph, lane);
+    __syncthreads();
+    reduce_write(red, dk, grp, ph, lane);
+    __syncthreads();
+    reduce_read(red, dk, grp, ph, lane);
+    if (ph != 0 || j >= Lk) return;
+    store_rowT(a.dk, b * a.sdk[0] + hd * a.sdk[1] + (long long)j * a.sdk[2], a.out_f32, dk, 1.0f / 8.0f, hb);
+    store_rowT(a.dv, b * a.sdv[0] + hd * a.sdv[1] + (long long)j * a.sdv[2], a.out_f32, dv, 1.0f, hb);
+}
+
+static_assert(kGroups * (kPhases - 1) * 32 * 64 * 4 <= kPhases * kRowsPhase, "reduction slots fit the rows tiles");
+static_assert(kGroups * (kPhases - 1) * 32 * 64 * 4 <= kPhases * kKeysPhase, "reduction slots fit the keys tiles");
+
+template <bool kCausal>
+hipError_t launch_variant(const BackwardArgs& a, hipStream_t s) {
+    const float c = kLog2e / 8.0f;   // log2(e) / sqrt(64)
+    const long long BH = (long long)a.B * a.H;
+    const long long gq = BH * ((a.Lq + kRowsWg - 1) / kRowsWg), gk = BH * ((a.Lk + kRowsWg - 1) / kRowsWg);
+    if (gq == 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_rows_mfma<kCausal>), dim3((unsigned)gq), dim3(kThreads), 0, s, a, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_keys_mfma<kCausal>), dim3((unsigned)gk), dim3(kThreads), 0, s, a, c);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sdpa_backward_bf16(const BackwardArgs& a, hipStream_t s) {
+    return a.causal ? launch_variant<true>(a, s) : launch_variant<false>(a, s);
+}
+
+}  // namespace mha
