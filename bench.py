@@ -559,7 +559,7 @@ def main():
         result["sdpa_backward"] = {
             "workload": bw.description, "avg_us": round(bms * 1e3, 2),
             "alg_tflops": round(bfl / (bms * 1e-3) / 1e12, 2),
-            "frac_fp32_alu_peak": round(bfl / (bms * 1e-3) / 1e12 / PEAK_F32_TFLOPS, 4), "bound": "alu"}
+            "frac_bf16_mfma_peak": round(bfl / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "bound": "mfma"}
         del bf
         # inspection path: the weights written (fp32) plus q, k, v read and o written
         iw = workloads.BY_NAME["inspect_weights"]

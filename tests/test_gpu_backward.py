@@ -1,10 +1,11 @@
 """GPU parity of sdpa_backward (dq, dk, dv) through the C ABI against the
 fp64 oracle's backward.
 
-The kernels compute in fp32 on the exact input values.  fp32 inputs are held
-to the fp32 bar (norm-wise 1e-5).  bf16 inputs carry the forward output o
-rounded to bf16, which enters D_i = do_i . o_i, so they are held to the bf16
-bar."""
+fp32 inputs run on FMA kernels in fp32 on the exact input values and are
+held to the fp32 bar (norm-wise 1e-5).  bf16 inputs run on bf16 MFMA with
+fp32 accumulation: the weights and ds are rounded to bf16 for their products
+(as the forward rounds its weights), and the forward output o, which enters
+D_i = do_i . o_i, is itself bf16; they are held to the bf16 bar."""
 import numpy as np
 import pytest
 
@@ -22,6 +23,11 @@ CASES = [
     (2, 2, 33, 33, True, "2d", "bf16"),
     (3, 1, 64, 96, False, "1d", "bf16"),
     (2, 4, 512, 512, True, None, "bf16"),
+    # several 64-row workgroups and 128-row steps with ragged tails
+    (2, 2, 300, 260, False, "1d", "bf16"),
+    (1, 3, 200, 200, True, "2d", "bf16"),
+    (2, 2, 257, 257, True, None, "bf16"),
+    (1, 2, 129, 1, False, None, "bf16"),
 ]
 
 
@@ -75,3 +81,27 @@ def test_backward_bf16_outputs_and_strided_views():
     for got, ref in zip((gq, gk, gv), oracle.sdpa_backward(q, k, v, g, valid_lens=vl)):
         assert got.dtype == torch.bfloat16
         assert_bf16(to_host(got), ref, "bf16 gradients")
+
+
+def test_backward_full_size_sampled_heads():
+    """The causal backward workload at full size (B=4 h=8 L=1024, bf16 in,
+    fp32 gradients) as the benchmark launches it; two (batch, head) slices,
+    the first and the last, are checked whole against the oracle."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    w = workloads.BY_NAME["backward_causal"]
+    inp = workloads.make_inputs(w)
+    q, k, v = (inp.tensors[n] for n in "qkv")
+    rng = np.random.Generator(np.random.PCG64(w.seed + 1000))
+    g = workloads._finish(rng.standard_normal(q.shape), "bf16")
+    tq, tk, tv, tg = (to_device(x, torch.bfloat16) for x in (q, k, v, g))
+    o = mha.sdpa_forward(tq, tk, tv, causal=True)
+    gq, gk, gv = mha.sdpa_backward(tq, tk, tv, o, tg, causal=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    gq, gk, gv = to_host(gq), to_host(gk), to_host(gv)
+    for b, hd in ((0, 0), (w.B - 1, w.h - 1)):
+        sl = lambda x: x[b:b + 1, hd:hd + 1]
+        ref = oracle.sdpa_backward(sl(q), sl(k), sl(v), sl(g), causal=True)
+        for name, got, r in (("dq", gq, ref[0]), ("dk", gk, ref[1]), ("dv", gv, ref[2])):
+            e = assert_bf16(sl(got), r, f"{name} full size b{b} h{hd}")
+            print(name, b, hd, e)
