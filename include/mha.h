@@ -121,7 +121,9 @@ mha_status sdpa_forward(mha_dtype in_dt, mha_dtype out_dt,
  *   B >= 0, h >= 1, L >= 1, pointers 16-byte aligned, strides multiples of 8
  *   elements (output: 8 bf16 or 4 fp32), o must not overlap q, k, v.
  *   B == 0 is a no-op.  Computed in fp32 from the bf16 inputs (no reduced-
- *   precision weights), split over 256-key slices of the cache and merged.
+ *   precision weights) over slices of 512 keys (256 when B*h is small); a
+ *   cache of one slice is finished in one launch, longer ones are split and
+ *   merged through the workspace.
  */
 size_t sdpa_decode_workspace_bytes(int B, int h, int L);
 

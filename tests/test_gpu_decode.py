@@ -22,12 +22,20 @@ CASES = [
     (2, 4, 700, [700, 513]),
     (2, 2, 300, [999, 300]),           # lens above L count as L
     (4, 8, 1024, "random"),
+    # grids of at least 512 workgroups take 512-key slices: one slice written
+    # in place, or several merged
+    (64, 8, 512, "random0"),
+    (32, 16, 1000, "random0"),
+    (128, 4, 200, "random0"),
 ]
 
 
 def _lens(mode, B, L, rng):
-    if mode == "random":
-        return rng.integers(1, L, size=B, endpoint=True).astype(np.int32)
+    if mode in ("random", "random0"):
+        ln = rng.integers(1, L, size=B, endpoint=True).astype(np.int32)
+        if mode == "random0":
+            ln[:3] = [0, L, 1]       # a fully masked row, a full cache, one position
+        return ln
     return np.array(mode, dtype=np.int32)
 
 

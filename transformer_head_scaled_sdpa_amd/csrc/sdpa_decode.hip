@@ -10,15 +10,21 @@
 // cached positions, as for a fully masked row).
 //
 // The step reads every cached key and value once and does 4*d_k flops per
-// key, so it is HBM-bound; the keys are split over many workgroups (split-K,
-// "flash decoding") so the whole GPU streams the cache:
-//  * Kernel 1: one workgroup (4 wave64s) per (batch, head, 256-key split).
-//    Each thread computes two keys' scores in fp32 from 16-byte loads, the
-//    split's max and weight sum are block reductions, and P.V accumulates
-//    64 features x 8 key groups from 16-byte V loads, reduced through LDS.
-//    The split's (max, sum, unnormalised output) goes to the workspace.
-//  * Kernel 2: per (batch, head), merges the splits by rescaling each to the
-//    common max (the online-softmax merge) and writes the normalised output.
+// key, so it is HBM-bound.  One workgroup (4 wave64s) per (batch, head, key
+// slice); every K and V load of the slice is issued at the start, so the
+// whole slice is in flight at once and the step costs one memory round trip:
+//  * scores: a thread pair shares a key (features [0,32) and [32,64) from
+//    16-byte loads), fp32 dot products, summed over the pair;
+//  * the slice's max and weight sum are block reductions;
+//  * P.V: thread t accumulates features (t % 8) * 8 .. +7 over keys
+//    t / 8 + 32 i from its 16-byte V loads; the 32 key groups are reduced by
+//    shuffles and LDS.
+// A cache that fits one slice (512 keys, or 256 when the grid would be too
+// small to fill the GPU) is finished in place: the normalised output is
+// written directly.  Longer caches are split over many workgroups (split-K,
+// "flash decoding"); each slice's (max, sum, unnormalised output) goes to the
+// workspace and a second kernel merges the slices by rescaling each to the
+// common max (the online-softmax merge).
 #include "common.h"
 #include "kernels.h"
 
@@ -28,7 +34,7 @@ namespace {
 
 constexpr int kD = 64;
 constexpr int kThreads = 256;
-constexpr int kSplit = 256;            // keys per workgroup
+constexpr int kSplitMin = 256;         // smallest slice: the workspace is sized for it
 constexpr int kPart = kD + 2;          // floats per partial: max, sum, 64 outputs
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -53,10 +59,13 @@ __device__ __forceinline__ void unpack8(const uint4& r, float (&f)[8]) {
     }
 }
 
+template <int kKeys, bool kDirect, bool kOutF32>
 __global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a, int n_split, float c, float* part) {
-    __shared__ float sc[kSplit];
+    constexpr int kKPass = kKeys / (kThreads / 2);   // keys per thread pair
+    constexpr int kVKeys = kKeys / (kThreads / 8);   // V rows per thread
+    __shared__ float sc[kKeys];
     __shared__ float red[kThreads / 64];
-    __shared__ float ored[8][kD];
+    __shared__ float ored[kThreads / 64][kD];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int split = blockIdx.x % n_split;
@@ -65,25 +74,39 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a, int n_spl
     const int len = a.lens[b];
     const bool none = len <= 0;                 // every position masked -> uniform weights
     const int n = none ? a.L : min(len, a.L);   // positions that carry weight
-    const int j0 = split * kSplit;
+    const int j0 = split * kKeys;
     float* out = part + ((long long)bh * n_split + split) * kPart;
-    if (j0 >= n) {                              // empty split: contributes nothing
+    if (!kDirect && j0 >= n) {                  // empty slice: contributes nothing
         if (tid == 0) {
             out[0] = -INFINITY;
             out[1] = 0.0f;
         }
         return;
     }
-    const int cnt = min(kSplit, n - j0);
+    const int cnt = min(kKeys, n - j0);         // >= 1
 
     const bf16_t* qp = static_cast<const bf16_t*>(a.q) + b * a.sq[0] + hd * a.sq[1];
     const bf16_t* kp = static_cast<const bf16_t*>(a.k) + b * a.sk[0] + hd * a.sk[1];
     const bf16_t* vp = static_cast<const bf16_t*>(a.v) + b * a.sv[0] + hd * a.sv[1];
 
-    // ---- scores: thread t -> keys j0 + t (and + 128 via the second pass),
-    // 8 features per 16-byte load, 8 loads per key.  Thread pairs share a
-    // key: the pair's halves hold features [0,32) and [32,64).
+    // ---- every load of the slice, issued up front ----
     const int half = tid & 1;
+    const int f8 = (tid & 7) * 8, jg = tid >> 3;
+    uint4 kr[kKPass][4], vr[kVKeys];
+#pragma unroll
+    for (int p = 0; p < kKPass; ++p) {
+        const int jl = p * (kThreads / 2) + (tid >> 1);
+        const bf16_t* row = kp + (long long)(j0 + jl) * a.sk[2] + half * 32;
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            kr[p][x] = jl < cnt ? *reinterpret_cast<const uint4*>(row + x * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kVKeys; ++i) {
+        const int jl = jg + i * (kThreads / 8);
+        vr[i] = jl < cnt ? *reinterpret_cast<const uint4*>(vp + (long long)(j0 + jl) * a.sv[2] + f8)
+                         : make_uint4(0, 0, 0, 0);
+    }
     float qf[32];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
@@ -92,35 +115,36 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a, int n_spl
 #pragma unroll
         for (int e = 0; e < 8; ++e) qf[x * 8 + e] = f[e];
     }
+
+    // ---- scores ----
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        const int jl = pass * (kThreads / 2) + (tid >> 1);   // key within the split
+    for (int p = 0; p < kKPass; ++p) {
+        const int jl = p * (kThreads / 2) + (tid >> 1);   // key within the slice
         float acc = 0.0f;
-        if (jl < cnt) {
-            const bf16_t* kr = kp + (long long)(j0 + jl) * a.sk[2] + half * 32;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                float f[8];
-                unpack8(*reinterpret_cast<const uint4*>(kr + x * 8), f);
+        for (int x = 0; x < 4; ++x) {
+            float f[8];
+            unpack8(kr[p][x], f);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf(qf[x * 8 + e], f[e], acc);
-            }
+            for (int e = 0; e < 8; ++e) acc = fmaf(qf[x * 8 + e], f[e], acc);
         }
         acc += __shfl_xor(acc, 1);
         if (half == 0) sc[jl] = jl < cnt ? (none ? 0.0f : acc * c) : -INFINITY;
     }
     __syncthreads();
 
-    // ---- split max and weights ----
+    // ---- slice max and weights ----
     float m = -INFINITY;
-    for (int j = tid; j < kSplit; j += kThreads) m = fmaxf(m, sc[j]);
+#pragma unroll
+    for (int j = tid; j < kKeys; j += kThreads) m = fmaxf(m, sc[j]);
     m = wave_max(m);
     if (lane == 0) red[wave] = m;
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
     float s = 0.0f;
-    for (int j = tid; j < kSplit; j += kThreads) {
+#pragma unroll
+    for (int j = tid; j < kKeys; j += kThreads) {
         const float p = __builtin_amdgcn_exp2f(sc[j] - m);   // exp2(-inf) = 0 past cnt
         sc[j] = p;
         s += p;
@@ -130,14 +154,13 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a, int n_spl
     __syncthreads();
     s = (red[0] + red[1]) + (red[2] + red[3]);
 
-    // ---- unnormalised output: thread t -> features (t % 8) * 8 .. +7 of
-    // keys j = t / 8, t / 8 + 32, ...; the 32 key groups are summed in LDS.
-    const int f8 = (tid & 7) * 8, jg = tid >> 3;
+    // ---- unnormalised output ----
     float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int jl = jg; jl < cnt; jl += kThreads / 8) {
-        const float p = sc[jl];
+#pragma unroll
+    for (int i = 0; i < kVKeys; ++i) {
+        const float p = sc[jg + i * (kThreads / 8)];          // 0 past cnt
         float f[8];
-        unpack8(*reinterpret_cast<const uint4*>(vp + (long long)(j0 + jl) * a.sv[2] + f8), f);
+        unpack8(vr[i], f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = fmaf(p, f[e], o[e]);
     }
@@ -155,10 +178,17 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a, int n_spl
     }
     __syncthreads();
     if (tid < kD) {
-        out[2 + tid] = (ored[0][tid] + ored[1][tid]) + (ored[2][tid] + ored[3][tid]);
-        if (tid == 0) {
-            out[0] = m;
-            out[1] = s;
+        const float y = (ored[0][tid] + ored[1][tid]) + (ored[2][tid] + ored[3][tid]);
+        if (kDirect) {
+            const long long off = b * a.so[0] + hd * a.so[1] + tid;
+            if (kOutF32) static_cast<float*>(a.o)[off] = y / s;
+            else static_cast<bf16_t*>(a.o)[off] = __builtin_bit_cast(bf16_t, static_cast<__bf16>(y / s));
+        } else {
+            out[2 + tid] = y;
+            if (tid == 0) {
+                out[0] = m;
+                out[1] = s;
+            }
         }
     }
 }
@@ -184,26 +214,44 @@ __global__ __launch_bounds__(kD) void decode_merge(DecodeArgs a, int n_split, co
     else static_cast<bf16_t*>(a.o)[off] = __builtin_bit_cast(bf16_t, static_cast<__bf16>(y));
 }
 
+// Keys per slice: 512 when that still gives at least 512 workgroups, else 256.
+int decode_slice(int B, int H, int L) {
+    const long long wg512 = (long long)B * H * ((L + 511) / 512);
+    return wg512 >= 512 ? 512 : 256;
+}
+
+template <int kKeys>
+hipError_t launch_slices(const DecodeArgs& a, bool out_f32, float* part, hipStream_t s) {
+    const int n_split = (a.L + kKeys - 1) / kKeys;
+    const long long grid = (long long)a.B * a.H * n_split;
+    const float c = kLog2e / 8.0f;   // log2(e) / sqrt(64)
+    if (n_split == 1) {
+        if (out_f32) hipLaunchKernelGGL((decode_split<kKeys, true, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, 1, c, part);
+        else hipLaunchKernelGGL((decode_split<kKeys, true, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, 1, c, part);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((decode_split<kKeys, false, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, n_split, c, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (out_f32) hipLaunchKernelGGL(decode_merge<true>, dim3(a.B * a.H), dim3(kD), 0, s, a, n_split, part);
+    else hipLaunchKernelGGL(decode_merge<false>, dim3(a.B * a.H), dim3(kD), 0, s, a, n_split, part);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-int decode_splits(int L) { return (L + kSplit - 1) / kSplit; }
+// The workspace holds one partial per 256-key slice, the most any launch uses.
+int decode_splits(int L) { return (L + kSplitMin - 1) / kSplitMin; }
 
 size_t decode_workspace_bytes(int B, int H, int L) {
     return (size_t)B * H * decode_splits(L) * kPart * sizeof(float);
 }
 
 hipError_t launch_sdpa_decode(const DecodeArgs& a, bool out_f32, void* workspace, hipStream_t s) {
-    const int n_split = decode_splits(a.L);
-    const long long grid = (long long)a.B * a.H * n_split;
-    if (grid == 0) return hipSuccess;
+    if ((long long)a.B * a.H == 0) return hipSuccess;
     float* part = static_cast<float*>(workspace);
-    const float c = kLog2e / 8.0f;   // log2(e) / sqrt(64)
-    hipLaunchKernelGGL(decode_split, dim3((unsigned)grid), dim3(kThreads), 0, s, a, n_split, c, part);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (out_f32) hipLaunchKernelGGL(decode_merge<true>, dim3(a.B * a.H), dim3(kD), 0, s, a, n_split, part);
-    else hipLaunchKernelGGL(decode_merge<false>, dim3(a.B * a.H), dim3(kD), 0, s, a, n_split, part);
-    return hipGetLastError();
+    return decode_slice(a.B, a.H, a.L) == 512 ? launch_slices<512>(a, out_f32, part, s)
+                                              : launch_slices<256>(a, out_f32, part, s);
 }
 
 }  // namespace mha
