@@ -17,11 +17,12 @@
 // transposed tiles are read from LDS with ds_read_b64_tr_b16 (each tile is
 // stored twice: 144-byte rows for 16-byte fragment reads, 192-byte rows for
 // the transposed reads).
-//  * rows (queries; q and do fragments in registers): pass 1 over the keys
-//    finds each query's log-sum-exp (online, per lane half and phase, merged
-//    at the end); D_i from the supplied output.  Pass 2: S^T = K Q^T and
-//    dP^T = V dO^T, dS^T = P^T (dP^T - D), and dQ^T += K^T dS^T.  The
-//    log-sum-exp and D go to the workspace.
+//  * rows (queries; q and do fragments in registers): one pass over the
+//    keys: S^T = K Q^T and dP^T = V dO^T, unnormalised weights exp2(S - m)
+//    with a lazy per-query offset m (the online softmax), dS^T = P^T (dP^T -
+//    D), and dQ^T += K^T dS^T; the phases' (m, weight sum, dq) are merged at
+//    the end and dq divided by the weight sum.  D_i comes from the supplied
+//    output.  The log-sum-exp and D go to the workspace.
 //  * keys (k and v fragments in registers): S = Q K^T and dP = dO V^T, P and
 //    dS from the stored log-sum-exp and D, then dV^T += dO^T P and
 //    dK^T += Q^T dS.
@@ -254,65 +255,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
     }
     dsum = pair_sum(dsum);                  // D_i over both lane halves
 
-    // ---- pass 1: log-sum-exp (this lane half's keys, this phase) ----
-    float m_run = -INFINITY, l_run = 0.0f;
-    for (int st = 0; st < n_steps; ++st) {
-        __syncthreads();
-        store_step(nk, smem, kRowsPhase, kRowsKR, -1, tid);
-        if (st + 1 < n_steps) nk = load_step(kp, a.sk[2], (st + 1) * kStep, Lk, tid);
-        __syncthreads();
-        const int t0 = st * kStep + ph * kTile;   // this wave's keys t0 .. t0+31
-        const f32x16 s = tile_dot(reinterpret_cast<const bf16_t*>(smem + ph * kRowsPhase + kRowsKR), qf, l32, hb);
-        if (t0 + kTile <= kmin) {
-            float mx = s[0];
-#pragma unroll
-            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-            const float m_new = fmaxf(m_run, mx * cs);
-            float rs = 0.0f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) rs += __builtin_amdgcn_exp2f(fmaf(s[v], cs, -m_new));
-            l_run = l_run * __builtin_amdgcn_exp2f(m_run - m_new) + rs;
-            m_run = m_new;
-        } else {
-            const int rel = klim - (t0 + hb * 4);
-            float mx = -INFINITY;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, acc_row(v) < rel ? s[v] : -INFINITY);
-            const float tm = mx == -INFINITY ? -INFINITY : mx * cs;
-            const float m_new = fmaxf(m_run, tm);
-            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-            float rs = 0.0f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(s[v], cs, -m_use));
-                rs += acc_row(v) < rel ? e : 0.0f;
-            }
-            l_run = l_run * __builtin_amdgcn_exp2f(m_run - m_use) + rs;
-            m_run = m_new;
-        }
-    }
-    stat_s[grp][ph][hb][l32] = make_float2(m_run, l_run);
-    __syncthreads();
-    float M = -INFINITY;
-#pragma unroll
-    for (int p = 0; p < kPhases; ++p)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) M = fmaxf(M, stat_s[grp][p][h][l32].x);
-    float L = 0.0f;
-#pragma unroll
-    for (int p = 0; p < kPhases; ++p)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float2 x = stat_s[grp][p][h][l32];
-            L += x.x == -INFINITY ? 0.0f : x.y * __builtin_amdgcn_exp2f(x.x - M);
-        }
-    // v_log_f32 is the base-2 logarithm, matching the log2-unit scores.
-    const float lse = L > 0.0f ? M + __builtin_amdgcn_logf(L) : 0.0f;
-
-    // ---- pass 2: dq ----
+    // ---- one pass: online softmax with a lazy offset ----
+    // dq accumulates exp2(s - m) (dp - D) k with the offset m of this lane's
+    // query (equal on both lane halves); m moves only when a tile's max
+    // exceeds it by more than kLazy, and then dq and the weight sum l (this
+    // lane half's keys) are rescaled.  The phases merge at the end.
+    constexpr float kLazy = 10.0f;
     const float ddm = dsum * dm;
+    float m = -INFINITY, l = 0.0f;
     f32x16 dq[2] = {};
-    nk = load_step(kp, a.sk[2], 0, Lk, tid);
     Chunks nv = load_step(vp, a.sv[2], 0, Lk, tid);
     for (int st = 0; st < n_steps; ++st) {
         __syncthreads();
@@ -323,21 +274,50 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
             nv = load_step(vp, a.sv[2], (st + 1) * kStep, Lk, tid);
         }
         __syncthreads();
-        const int t0 = st * kStep + ph * kTile;
+        const int t0 = st * kStep + ph * kTile;   // this wave's keys t0 .. t0+31
         const char* area = smem + ph * kRowsPhase;
-        const f32x16 s = tile_dot(reinterpret_cast<const bf16_t*>(area + kRowsKR), qf, l32, hb);
+        f32x16 s = tile_dot(reinterpret_cast<const bf16_t*>(area + kRowsKR), qf, l32, hb);
         f32x16 ds = tile_dot(reinterpret_cast<const bf16_t*>(area + kRowsVR), gf, l32, hb);
+        // Scores in log2 units (masked: -inf) and the tile's row max.
+        float mt;
         if (t0 + kTile <= kmin) {
+            float mx = s[0];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) ds[v] = __builtin_amdgcn_exp2f(fmaf(s[v], cs, -lse)) * fmaf(ds[v], dm, -ddm);
+            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[v] *= cs;
+            mt = mx * cs;
         } else {
             const int rel = klim - (t0 + hb * 4);
+            float mx = -INFINITY;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float p = acc_row(v) < rel ? __builtin_amdgcn_exp2f(fmaf(s[v], cs, -lse)) : 0.0f;
-                ds[v] = p * fmaf(ds[v], dm, -ddm);
+                s[v] = acc_row(v) < rel ? s[v] * cs : -INFINITY;
+                mx = fmaxf(mx, s[v]);
             }
+            mt = mx;
         }
+        mt = pair_max(mt);
+        if (__any(mt > m + kLazy)) {
+            const float m_new = mt > m + kLazy ? mt : m;
+            const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+            l *= alpha;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                dq[0][v] *= alpha;
+                dq[1][v] *= alpha;
+            }
+            m = m_new;
+        }
+        const float m_use = m == -INFINITY ? 0.0f : m;   // no allowed key yet: every weight is 0
+        float rs = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float p = __builtin_amdgcn_exp2f(s[v] - m_use);
+            rs += p;
+            ds[v] = p * fmaf(ds[v], dm, -ddm);
+        }
+        l += rs;
         u32x4 w[2];
         pack_b(ds, w);
         const bf16_t* kt = reinterpret_cast<const bf16_t*>(area + kRowsKT);
@@ -348,6 +328,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
             for (int tb = 0; tb < 2; ++tb) dq[tb] = mfma32x32x16(tr_frag(kt, kb, tb, hb, lane), d8, dq[tb]);
         }
     }
+    // Merge the phases: common offset M, total weight L, rescaled dq.
+    stat_s[grp][ph][hb][l32] = make_float2(m, l);
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < kPhases; ++p) M = fmaxf(M, stat_s[grp][p][0][l32].x);
+    float L = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kPhases; ++p)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float2 x = stat_s[grp][p][h][l32];
+            L += x.x == -INFINITY ? 0.0f : x.y * __builtin_amdgcn_exp2f(x.x - M);
+        }
+    const float own = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        dq[0][v] *= own;
+        dq[1][v] *= own;
+    }
+    // v_log_f32 is the base-2 logarithm, matching the log2-unit scores.
+    const float lse = L > 0.0f ? M + __builtin_amdgcn_logf(L) : 0.0f;
     __syncthreads();
     reduce_write(reinterpret_cast<float*>(smem), dq, grp, ph, lane);
     __syncthreads();
@@ -357,7 +359,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
         a.rows[((long long)bh * Lq + i) * 2] = lse;
         a.rows[((long long)bh * Lq + i) * 2 + 1] = dsum;
     }
-    store_rowT(a.dq, b * a.sdq[0] + hd * a.sdq[1] + (long long)i * a.sdq[2], a.out_f32, dq, 1.0f / 8.0f, hb);
+    store_rowT(a.dq, b * a.sdq[0] + hd * a.sdq[1] + (long long)i * a.sdq[2], a.out_f32, dq,
+               L > 0.0f ? 0.125f / L : 0.0f, hb);
 }
 
 // ---------------------------------------------------------------------------
@@ -413,6 +416,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, flo
         vf[kk] = __builtin_bit_cast(bf16x8, rv);
     }
 
+    // Per streamed query (threads below kStep): log-sum-exp, D and key limit,
+    // fetched one step ahead like the tiles.
+    struct RowData {
+        float lse, dsum;
+        int kl;
+        bool none;
+    };
+    auto fetch_rows = [&](int i0) {
+        RowData r = {0.0f, 0.0f, 0, false};
+        const int qi = i0 + tid;
+        if (tid < kStep && qi < Lq) {
+            r.lse = a.rows[((long long)bh * Lq + qi) * 2];
+            r.dsum = a.rows[((long long)bh * Lq + qi) * 2 + 1];
+            r.kl = key_limit<kCausal>(a, b, qi, r.none);
+        }
+        return r;
+    };
+    RowData nr = fetch_rows(i_begin);
+
     f32x16 dk[2] = {}, dv[2] = {};
     for (int st = 0; st < n_steps; ++st) {
         const int i0 = i_begin + st * kStep;
@@ -420,18 +442,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, flo
         store_step(nq, smem, kKeysPhase, kKeysQR, kKeysQT, tid);
         store_step(ng, smem, kKeysPhase, kKeysGR, kKeysGT, tid);
         if (tid < kStep) {
-            const int qi = i0 + tid;
-            float lse = 0.0f, dsum = 0.0f;
-            bool none = false;
-            int kl = 0;
-            if (qi < Lq) {
-                lse = a.rows[((long long)bh * Lq + qi) * 2];
-                dsum = a.rows[((long long)bh * Lq + qi) * 2 + 1];
-                kl = key_limit<kCausal>(a, b, qi, none);
-            }
-            rowf_s[tid] = make_float4(lse, dsum, none ? 0.0f : c, none ? 0.0f : 1.0f);
-            klim_s[tid] = kl;
-            int mn = none ? -1 : kl;
+            rowf_s[tid] = make_float4(nr.lse, nr.dsum, nr.none ? 0.0f : c, nr.none ? 0.0f : 1.0f);
+            klim_s[tid] = nr.kl;
+            int mn = nr.none ? -1 : nr.kl;
 #pragma unroll
             for (int o = 16; o >= 1; o >>= 1) mn = min(mn, __shfl_xor(mn, o));
             if ((tid & 31) == 0) tmin_s[tid >> 5] = mn;
@@ -439,6 +452,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, flo
         if (st + 1 < n_steps) {
             nq = load_step(qp, a.sq[2], i0 + kStep, Lq, tid);
             ng = load_step(gp, a.sdo[2], i0 + kStep, Lq, tid);
+            nr = fetch_rows(i0 + kStep);
         }
         __syncthreads();
         // S = Q K^T and dP = dO V^T: element v is query ph*32 + acc_row(v) +
