@@ -131,3 +131,19 @@ def test_mha_weights_and_lengths_per_query(B, Lq, Lk, D, h, causal, kind, dt, se
         assert_bf16(to_host(out), ref, "mha output")
         assert_bf16(to_host(p), rp, "mha weights")
     assert np.all(to_host(p)[rp == 0.0] == 0.0)
+
+
+def test_inspect_weights_workload_full_size():
+    """The weights-export workload at full size (B=4 h=8 L=512, per-sequence
+    lengths) as the benchmark launches it: every weight and output."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    w = workloads.BY_NAME["inspect_weights"]
+    inp = workloads.make_inputs(w)
+    q, k, v = (inp.tensors[n] for n in ("q", "k", "v"))
+    tq, tk, tv = (to_device(x, torch.bfloat16) for x in (q, k, v))
+    o, p = mha.sdpa_forward(tq, tk, tv, valid_lens=inp.valid_lens, out_dtype=torch.bfloat16, return_weights=True)
+    torch.cuda.synchronize()
+    ro, rp = oracle.sdpa(q, k, v, valid_lens=inp.valid_lens, return_weights=True)
+    print("weights", assert_fp32(to_host(p), rp, "inspect_weights weights"))
+    print("output", assert_bf16(to_host(o), ro, "inspect_weights output (bf16, as benchmarked)"))
