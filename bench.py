@@ -561,18 +561,20 @@ def main():
             "alg_tflops": round(bfl / (bms * 1e-3) / 1e12, 2),
             "frac_bf16_mfma_peak": round(bfl / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "bound": "mfma"}
         del bf
-        # inspection path: the weights written (fp32) plus q, k, v read and o written
+        # inspection path: the weights written (fp32) plus q, k, v read and o
+        # written; on bf16 MFMA the scores run twice (2 * 2 * d_k flops per
+        # allowed pair) and P.V once with P as two bf16 terms (2 * 2 * d_k)
         iw = workloads.BY_NAME["inspect_weights"]
         iinp = workloads.make_inputs(iw)
         wf = PreparedWeights(iinp)
         wms, _ = time_steps(wf, 10, 3)
         wbytes = iw.B * iw.h * (iw.Lq * iw.Lk * 4 + (2 * iw.Lq + 2 * iw.Lk) * iw.d_k * 2)
-        wfl = 2 * 4 * iw.d_k * allowed_pairs(iw, iinp.valid_lens)    # two passes of scores, one of P.V
+        wfl = 8 * iw.d_k * allowed_pairs(iw, iinp.valid_lens)
         result["sdpa_weights"] = {
-            "workload": iw.description, "avg_us": round(wms * 1e3, 2),
+            "workload": iw.description, "avg_us": round(wms * 1e3, 2), "bound": "hbm",
             "GBs": round(wbytes / (wms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(wbytes / (wms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "fp32_tflops": round(wfl / (wms * 1e-3) / 1e12, 2),
-            "frac_fp32_alu_peak": round(wfl / (wms * 1e-3) / 1e12 / PEAK_F32_TFLOPS, 4)}
+            "mfma_tflops": round(wfl / (wms * 1e-3) / 1e12, 2),
+            "frac_bf16_mfma_peak": round(wfl / (wms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del wf
 
     if not args.no_cpu_baseline:

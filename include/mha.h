@@ -150,8 +150,10 @@ mha_status sdpa_decode(mha_dtype in_dt, mha_dtype out_dt,
  *   workspace : device buffer of at least sdpa_backward_workspace_bytes(B,
  *          h, Lq) bytes, 16-byte aligned; it receives each query's
  *          log-sum-exp and D_i.
- * Arithmetic is fp32 (FMA): each row's weights are recomputed from a first
- * pass over the keys, then dq is accumulated per query and dk, dv per key.
+ * Two kernels: dq accumulated per query (with each row's log-sum-exp, found
+ * in the same pass), then dk and dv per key.  MHA_BF16 inputs run on bf16
+ * MFMA with fp32 accumulation (the weights and ds rounded to bf16 for their
+ * products, as the forward rounds its weights); MHA_F32 inputs in fp32 FMA.
  * Requirements otherwise as for sdpa_forward.
  */
 size_t sdpa_backward_workspace_bytes(int B, int h, int Lq);
@@ -220,8 +222,11 @@ mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
  *             4-byte aligned, not overlapping any other argument.  It receives the normalised weights
  *             softmax_j(q_i . k_j / sqrt(d_k)) with masked keys exactly 0.
  * With p_attn == NULL and lengths per sequence this is sdpa_forward.  Else
- * it runs the inspection kernel: fp32 arithmetic, two passes over the keys
- * (slower than sdpa_forward; meant for debugging and visualisation).
+ * it runs the inspection kernel, two passes over the keys (slower than
+ * sdpa_forward; meant for debugging and visualisation): for MHA_BF16 inputs
+ * bf16 MFMA products with fp32 sums, the weights in fp32 and P.V with the
+ * weights as two bf16 terms (about 16 significant bits); for MHA_F32 inputs
+ * fp32 FMA throughout.
  */
 mha_status sdpa_forward_ex(mha_dtype in_dt, mha_dtype out_dt,
                            const void* q, mha_strides sq,

@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmha.so")
-SOURCES = ["api.hip", "sdpa_bf16_pipe.hip", "mha_fused.hip", "mha_fused_small.hip", "sdpa_decode.hip", "sdpa_weights.hip", "sdpa_backward.hip", "sdpa_backward_mfma.hip", "layer_norm.hip", "sdpa_f32.hip", "gemm.hip"]
+SOURCES = ["api.hip", "sdpa_bf16_pipe.hip", "mha_fused.hip", "mha_fused_small.hip", "sdpa_decode.hip", "sdpa_weights.hip", "sdpa_weights_mfma.hip", "sdpa_backward.hip", "sdpa_backward_mfma.hip", "layer_norm.hip", "sdpa_f32.hip", "gemm.hip"]
 
 # Packed fp32 VALU ops are disabled for every HIP translation unit.
 # -fno-honor-nans: inputs are finite, so max/min need not quiet signalling

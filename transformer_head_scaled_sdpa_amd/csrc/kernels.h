@@ -115,6 +115,8 @@ bool mha_attn_fused_small_fits(const FusedArgs& a);
 hipError_t launch_mha_attn_fused_small(const FusedArgs& a, hipStream_t s);
 hipError_t launch_sdpa_f32(const SdpaArgs& a, hipStream_t s);
 hipError_t launch_sdpa_weights(const WeightsArgs& a, hipStream_t s);
+// bf16 inputs, d = 64, on MFMA (launch_sdpa_weights dispatches to it).
+hipError_t launch_sdpa_weights_bf16(const WeightsArgs& a, hipStream_t s);
 size_t backward_workspace_bytes(int B, int H, int Lq);
 hipError_t launch_sdpa_backward(const BackwardArgs& a, hipStream_t s);
 // bf16 inputs, d = 64, on MFMA (launch_sdpa_backward dispatches to it).

@@ -1,0 +1,173 @@
+// Tile layout shared by the bf16 MFMA kernels that own 64 rows per
+// workgroup and stream the other side (the attention backward and the
+// weights-export kernel), d = 64, gfx950.
+//
+// A workgroup is 8 wave64s: two groups of 32 rows (one row per lane column
+// of the 32x32 MFMA tile) times four phases; a step streams 128 rows, 32 per
+// phase, so each wave works on its own 32x32 tile.  Products run on
+// v_mfma_f32_32x32x16_bf16: an accumulator packed to bf16 feeds the next MFMA
+// as its B operand, and transposed tiles are read from LDS with
+// ds_read_b64_tr_b16.  Streamed tiles are stored in 144-byte rows for 16-byte
+// fragment reads (conflict-free) and, where a transposed read is needed, in
+// 192-byte rows.  Row masks are key limits: keys [0, limit) are allowed.
+#pragma once
+
+#include "common.h"
+
+namespace mha {
+namespace rows64 {
+
+constexpr int kD = 64;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kGroups = 2;                   // row groups of 32 per workgroup
+constexpr int kPhases = kWaves / kGroups;    // streamed tiles per step
+constexpr int kRowsWg = 32 * kGroups;
+constexpr int kTile = 32;                    // streamed rows per phase
+constexpr int kStep = kTile * kPhases;       // streamed rows per step
+constexpr int kLdsR = kD + 8;                // 144-byte rows
+constexpr int kLdsT = kD + 32;               // 192-byte rows
+constexpr int kTileRB = kTile * kLdsR * 2;   // bytes
+constexpr int kTileTB = kTile * kLdsT * 2;
+constexpr int kChunks = kStep * 8 / kThreads;  // 16-byte chunks per thread per streamed operand
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ bf16x8 frag(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// A 32-row tile (144-byte rows) times 32 register rows: element v of the
+// result is tile row (v/4)*8 + hb*4 + v%4 against register row lane % 32.
+__device__ __forceinline__ f32x16 tile_dot(const bf16_t* t, const bf16x8 (&f)[4], int l32, int hb) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = mfma32x32x16(frag(t + l32 * kLdsR + kk * 16 + hb * 8), f[kk], acc);
+    return acc;
+}
+
+// Transposed fragment of a row-major [32 rows][64 features] LDS tile (192 B
+// rows): the A operand [32 features x 16 rows] for features tb*32 + lane%32
+// and the tile rows of slice kb in the order the packed B operands use
+// (kb*16 + hb*4 + 0..3, then + 8..11).
+__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* ts, int kb, int tb, int hb, int lane) {
+    const int g = lane >> 4, r = lane & 15;
+    const int row = kb * 16 + hb * 4 + (r >> 2);
+    const int col = tb * 32 + (g & 1) * 16 + (r & 3) * 4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ts + row * kLdsT + col));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ts + (row + 8) * kLdsT + col));
+    const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, both);
+}
+
+// Pack a 32-row accumulator (element v: row (v/4)*8 + hb*4 + v%4) as two B
+// operands: slice kb holds rows kb*16 + {hb*4 + 0..3, hb*4 + 8..11}.
+__device__ __forceinline__ void pack_b(const f32x16& x, u32x4 (&w)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pp = {static_cast<__bf16>(x[kb * 8 + e]), static_cast<__bf16>(x[kb * 8 + e + 1])};
+            w[kb][e >> 1] = __builtin_bit_cast(uint32_t, pp);
+        }
+}
+
+// Row offset of accumulator element v within its 32-row tile, less hb*4.
+__device__ __forceinline__ constexpr int acc_row(int v) { return (v >> 2) * 8 + (v & 3); }
+
+// One step of a [L, 64] bf16 operand: rows r0 .. r0+127 as 1024 chunks of 16
+// bytes (chunk n: row n / 8, features (n % 8) * 8 ..), kChunks per thread;
+// rows at or past L read as zero.
+struct Chunks {
+    uint4 c[kChunks];
+};
+__device__ __forceinline__ Chunks load_step(const bf16_t* x, long long ld, int r0, int L, int tid) {
+    Chunks t;
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n) {
+        const int ch = tid + n * kThreads, r = ch >> 3, col = (ch & 7) * 8;
+        t.c[n] = r0 + r < L ? *reinterpret_cast<const uint4*>(x + (long long)(r0 + r) * ld + col)
+                            : make_uint4(0, 0, 0, 0);
+    }
+    return t;
+}
+// Store a step into the per-phase tiles: row r goes to phase r / 32, in
+// 144-byte rows at byte offset offR of the phase area (if offR >= 0) and in
+// 192-byte rows at offT (if offT >= 0).
+__device__ __forceinline__ void store_step(const Chunks& t, char* smem, int phase_bytes, int offR, int offT, int tid) {
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n) {
+        const int ch = tid + n * kThreads, r = ch >> 3, col = (ch & 7) * 8;
+        char* base = smem + (r >> 5) * phase_bytes;
+        const int lr = r & 31;
+        if (offR >= 0) *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(base + offR) + lr * kLdsR + col) = t.c[n];
+        if (offT >= 0) *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(base + offT) + lr * kLdsT + col) = t.c[n];
+    }
+}
+
+template <typename Args>
+__device__ __forceinline__ int row_len(const Args& a, int b, int i) {
+    if (a.vl_rank == 1) return a.valid_lens[b];
+    if (a.vl_rank == 2) return a.valid_lens[(long long)b * a.Lq + i];
+    return a.Lk;
+}
+
+// Keys [0, klim) are allowed for query i; a row with no allowed key (lengths
+// given, length <= 0) allows all Lk keys with equal scores (`none`).
+template <bool kCausal, typename Args>
+__device__ __forceinline__ int key_limit(const Args& a, int b, int i, bool& none) {
+    const int len = row_len(a, b, i);
+    none = a.vl_rank != 0 && len <= 0;
+    if (none) return a.Lk;
+    const int lim = min(len, a.Lk);
+    return kCausal ? min(lim, i + 1) : lim;
+}
+
+// Sum the per-phase partials of a 32-row accumulator pair through LDS: the
+// waves of phases 1..3 write theirs, the phase-0 wave of the group adds them.
+// Leaves the result in `acc` of the phase-0 waves.  `red` holds 6 slots of
+// 8 KiB; the caller brackets the calls with barriers.
+__device__ __forceinline__ void reduce_write(float* red, const f32x16 (&acc)[2], int grp, int ph, int lane) {
+    if (ph == 0) return;
+    float* slot = red + (grp * (kPhases - 1) + ph - 1) * 32 * 64;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) slot[(tb * 16 + v) * 64 + lane] = acc[tb][v];
+}
+__device__ __forceinline__ void reduce_read(const float* red, f32x16 (&acc)[2], int grp, int ph, int lane) {
+    if (ph != 0) return;
+#pragma unroll
+    for (int p = 1; p < kPhases; ++p) {
+        const float* slot = red + (grp * (kPhases - 1) + p - 1) * 32 * 64;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[tb][v] += slot[(tb * 16 + v) * 64 + lane];
+    }
+}
+
+// Store a transposed accumulator pair (element v of block tb: feature
+// tb*32 + (v/4)*8 + hb*4 + v%4, row = the lane's row) times `scale`.
+__device__ __forceinline__ void store_rowT(void* base, long long off, bool out_f32, const f32x16 (&acc)[2], float scale,
+                                           int hb) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int t = tb * 32 + g4 * 8 + hb * 4;
+            const float y0 = acc[tb][g4 * 4] * scale, y1 = acc[tb][g4 * 4 + 1] * scale,
+                        y2 = acc[tb][g4 * 4 + 2] * scale, y3 = acc[tb][g4 * 4 + 3] * scale;
+            if (out_f32)
+                *reinterpret_cast<float4*>(static_cast<float*>(base) + off + t) = make_float4(y0, y1, y2, y3);
+            else
+                *reinterpret_cast<uint2*>(static_cast<bf16_t*>(base) + off + t) =
+                    make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+        }
+}
+
+
+}  // namespace rows64
+}  // namespace mha

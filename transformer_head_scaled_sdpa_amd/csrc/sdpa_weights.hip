@@ -1,6 +1,7 @@
-// Attention with the inspection extras, in fp32 arithmetic (FMA only),
-// d_k = d_v = 64: key-padding lengths per sequence [B] or per query [B, Lq],
-// the causal rule, and optionally the attention weights themselves.
+// Attention with the inspection extras for fp32 inputs, in fp32 arithmetic
+// (FMA only), d_k = d_v = 64: key-padding lengths per sequence [B] or per
+// query [B, Lq], the causal rule, and optionally the attention weights
+// themselves.  bf16 inputs take the MFMA kernel in sdpa_weights_mfma.hip.
 //
 // What it computes (The Annotated Transformer, "Attention" section: the
 // attention function returns the weights p_attn beside the output, which the
@@ -31,11 +32,6 @@ constexpr int kBQ = 64;   // queries per workgroup (one per lane)
 constexpr int kBK = 32;   // keys per tile
 
 __device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ float4 load4(const bf16_t* p) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
-    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
-                       __uint_as_float(w.y & 0xffff0000u));
-}
 
 template <typename T, bool kCausal>
 __global__ __launch_bounds__(64) void sdpa_weights_d64(WeightsArgs a, int n_qtiles, float c_log2) {
@@ -189,9 +185,10 @@ hipError_t launch_variant(const WeightsArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// fp32 inputs run here; bf16 inputs take the MFMA kernel.
 hipError_t launch_sdpa_weights(const WeightsArgs& a, hipStream_t s) {
     if (a.in_f32) return a.causal ? launch_variant<float, true>(a, s) : launch_variant<float, false>(a, s);
-    return a.causal ? launch_variant<bf16_t, true>(a, s) : launch_variant<bf16_t, false>(a, s);
+    return launch_sdpa_weights_bf16(a, s);
 }
 
 }  // namespace mha
