@@ -220,8 +220,16 @@ hipError_t launch_bf16(const GemmArgs& g, bool out_f32, hipStream_t s, bool shar
     return hipGetLastError();
 }
 
-// fp32: 64 x 64 tile, K in steps of 16, each of 256 threads owns 4 x 4 outputs.
-constexpr int kFT = 64, kFK = 16;
+// fp32: 64 x 64 tile, each of 256 threads owns 4 x 4 outputs.  K in steps of
+// 64: every thread loads four 16-byte pieces of each operand per step, and
+// the next step's pieces are loaded while the current step computes (the
+// small-M projections of short sequences are latency-bound: few workgroups,
+// so each step's load latency is the cost).
+constexpr int kFT = 64, kFK = 64;
+
+struct F32Step {
+    float4 a[4], w[4];
+};
 
 __global__ __launch_bounds__(256) void gemm_f32_nt(GemmArgs g, int tiles_n) {
     __shared__ float as[kFK][kFT + 4];
@@ -234,7 +242,9 @@ __global__ __launch_bounds__(256) void gemm_f32_nt(GemmArgs g, int tiles_n) {
         id -= tiles;
     }
     if (prob < 0) return;
-    const GemmProblem& P = g.p[prob];
+    // Constant indices only: a runtime index into the argument array would
+    // copy it to scratch memory.
+    const GemmProblem P = prob == 0 ? g.p[0] : (prob == 1 ? g.p[1] : g.p[2]);
     const int M = P.M, N = g.N, K = g.K;
     const int m0 = tm * kFT, n0 = tn * kFT;
     const float* A = static_cast<const float*>(P.a);
@@ -242,18 +252,33 @@ __global__ __launch_bounds__(256) void gemm_f32_nt(GemmArgs g, int tiles_n) {
 
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;     // outputs rows ty*4.., cols tx*4..
-    float acc[4][4] = {};
-    for (int k0 = 0; k0 < K; k0 += kFK) {
-        __syncthreads();
-        // 64 rows x 16 k per operand = 1024 floats: 4 per thread, stored k-major.
+    // Piece n of a step: row (tid + 256 n) / 16, k (tid % 16) * 4 .. +3 (K is
+    // a multiple of 64, so a piece is whole or past K).
+    auto load = [&](int k0) {
+        F32Step st;
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             const int c = tid + n * 256;
-            const int r = c >> 4, kq = c & 15;
-            const int k = k0 + kq;
-            as[kq][r] = (m0 + r < M && k < K) ? A[(long long)(m0 + r) * K + k] : 0.0f;
-            ws[kq][r] = (n0 + r < N && k < K) ? W[(long long)(n0 + r) * K + k] : 0.0f;
+            const int r = c >> 4, k = k0 + (c & 15) * 4;
+            st.a[n] = make_float4(0.f, 0.f, 0.f, 0.f);
+            st.w[n] = st.a[n];
+            if (m0 + r < M && k < K) st.a[n] = *reinterpret_cast<const float4*>(A + (long long)(m0 + r) * K + k);
+            if (n0 + r < N && k < K) st.w[n] = *reinterpret_cast<const float4*>(W + (long long)(n0 + r) * K + k);
         }
+        return st;
+    };
+    float acc[4][4] = {};
+    F32Step nxt = load(0);
+    for (int k0 = 0; k0 < K; k0 += kFK) {
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int c = tid + n * 256;
+            const int r = c >> 4, kq = (c & 15) * 4;
+            as[kq][r] = nxt.a[n].x; as[kq + 1][r] = nxt.a[n].y; as[kq + 2][r] = nxt.a[n].z; as[kq + 3][r] = nxt.a[n].w;
+            ws[kq][r] = nxt.w[n].x; ws[kq + 1][r] = nxt.w[n].y; ws[kq + 2][r] = nxt.w[n].z; ws[kq + 3][r] = nxt.w[n].w;
+        }
+        if (k0 + kFK < K) nxt = load(k0 + kFK);
         __syncthreads();
 #pragma unroll
         for (int kq = 0; kq < kFK; ++kq) {
@@ -301,6 +326,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool out_f32, hipStream_t s) {
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s) {
+    if (g.K % 4 != 0) return hipErrorInvalidValue;   // 16-byte operand pieces along K
     const int tiles_n = (g.N + kFT - 1) / kFT;
     long long tiles = 0;
     for (int p = 0; p < g.nprob; ++p) tiles += (long long)((g.p[p].M + kFT - 1) / kFT) * tiles_n;

@@ -6,7 +6,7 @@
 //
 // One wave64 per 64 queries of one (batch, head); each lane owns one query,
 // its 64 query features and 64 output accumulators in registers.  Key/value
-// tiles of 32 rows are staged in LDS and read as broadcasts (every lane reads
+// tiles of 16 rows are staged in LDS and read as broadcasts (every lane reads
 // the same address), so there are no bank conflicts.  Online softmax in fp32.
 #include "common.h"
 #include "kernels.h"
@@ -17,7 +17,7 @@ namespace {
 
 constexpr int kD = 64;
 constexpr int kBQ = 64;   // queries per workgroup (one per lane)
-constexpr int kBK = 32;   // keys per tile
+constexpr int kBK = 16;   // keys per tile (short sequences waste at most 15 masked keys)
 
 template <bool kCausal, bool kHasVl>
 __global__ __launch_bounds__(64) void sdpa_fwd_f32_d64(SdpaArgs a, int n_qtiles, float c_log2) {
@@ -56,9 +56,9 @@ __global__ __launch_bounds__(64) void sdpa_fwd_f32_d64(SdpaArgs a, int n_qtiles,
 
     for (int kv0 = 0; kv0 < kv_end; kv0 += kBK) {
         __syncthreads();
-        // 32 rows x 16 float4 per tensor: 8 float4 per lane each.
+        // kBK rows x 16 float4 per tensor: kBK / 4 float4 per lane each.
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
+        for (int n = 0; n < kBK / 4; ++n) {
             const int c = lane + n * 64;
             const int r = c >> 4, col = (c & 15) * 4;
             const int key = kv0 + r;
