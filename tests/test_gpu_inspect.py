@@ -147,3 +147,31 @@ def test_inspect_weights_workload_full_size():
     ro, rp = oracle.sdpa(q, k, v, valid_lens=inp.valid_lens, return_weights=True)
     print("weights", assert_fp32(to_host(p), rp, "inspect_weights weights"))
     print("output", assert_bf16(to_host(o), ro, "inspect_weights output (bf16, as benchmarked)"))
+
+
+@pytest.mark.parametrize("B,h,L,causal,kind", [
+    (2, 2, 200, True, None),      # causal without lengths: keys past each block's triangle are zero-filled
+    (1, 2, 70, True, None),       # rows of 70 weights: the last 16-byte piece of a row is partial
+    (2, 3, 150, False, "1d"),
+    (2, 2, 99, True, "2d"),
+])
+def test_weights_overwrite_every_entry(B, h, L, causal, kind):
+    """bf16 inputs (MFMA inspection kernel) into a weights buffer pre-filled
+    with NaN: every entry must be written, masked ones as exact zeros."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    rng = np.random.Generator(np.random.PCG64(B * 31 + L))
+    q, k, v = (workloads._finish(rng.standard_normal((B, h, L, 64)), "bf16") for _ in range(3))
+    vl = _lengths(kind, rng, B, L, L)
+    tq, tk, tv = (to_device(x, torch.bfloat16) for x in (q, k, v))
+    buf = torch.full((B, h, L, L), float("nan"), dtype=torch.float32, device="cuda")
+    o, p = mha.sdpa_forward(tq, tk, tv, valid_lens=vl, causal=causal, out_dtype=torch.float32,
+                            return_weights=True, weights=buf)
+    torch.cuda.synchronize()
+    assert p.data_ptr() == buf.data_ptr()
+    g = to_host(p)
+    assert not np.isnan(g).any(), "weights left unwritten"
+    ro, rp = oracle.sdpa(q, k, v, valid_lens=vl, causal=causal, return_weights=True)
+    assert_fp32(g, rp, "weights")
+    assert np.all(g[rp == 0.0] == 0.0)
+    assert_fp32(to_host(o), ro, "output")

@@ -90,11 +90,13 @@ def _raise(status, what):
         raise MhaError(status, what)
 
 
-def sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None, out=None, return_weights=False):
+def sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None, out=None, return_weights=False,
+                 weights=None):
     """softmax(q k^T / sqrt(d_k)) v per (batch, head) with key-padding
     ``valid_lens`` ([B] or [B, Lq]) and/or the causal mask; returns
     o [B, h, Lq, d_v], and the weights [B, h, Lq, Lk] (fp32) when
-    ``return_weights``."""
+    ``return_weights`` (written into ``weights`` if given: an fp32 tensor of
+    that shape whose last axis is contiguous)."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check_gpu(n, t)
@@ -113,7 +115,15 @@ def sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None, out=Non
     if not return_weights and (vl is None or vl.dim() == 1):
         _raise(lib.sdpa_forward(*head, int(bool(causal)), _stream()), "sdpa_forward")
         return out
-    p = torch.empty((B, h, Lq, Lk), dtype=torch.float32, device=q.device) if return_weights else None
+    p = None
+    if return_weights:
+        if weights is None:
+            p = torch.empty((B, h, Lq, Lk), dtype=torch.float32, device=q.device)
+        else:
+            _check_gpu("weights", weights)
+            if weights.dtype != torch.float32 or tuple(weights.shape) != (B, h, Lq, Lk) or weights.stride(3) != 1:
+                raise ValueError(f"weights must be fp32 [{B}, {h}, {Lq}, {Lk}] with a contiguous last axis")
+            p = weights
     sp = _strides4(p) if p is not None else Strides(0, 0, 0)
     st = lib.sdpa_forward_ex(*head, 1 if vl is None else vl.dim(), int(bool(causal)), _ptr(p), sp, _stream())
     _raise(st, "sdpa_forward_ex")
