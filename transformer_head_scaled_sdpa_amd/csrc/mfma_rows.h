@@ -78,18 +78,45 @@ __device__ __forceinline__ void pack_b(const f32x16& x, u32x4 (&w)[2]) {
 __device__ __forceinline__ constexpr int acc_row(int v) { return (v >> 2) * 8 + (v & 3); }
 
 // One step of a [L, 64] bf16 operand: rows r0 .. r0+127 as 1024 chunks of 16
-// bytes (chunk n: row n / 8, features (n % 8) * 8 ..), kChunks per thread;
-// rows at or past L read as zero.
+// bytes (chunk n: row n / 8, features (n % 8) * 8 ..), kChunks per thread.
+// The operand is read through a buffer resource whose range ends with row
+// L - 1, so rows at or past L read as zero in hardware; each thread's chunk
+// offsets within a step are fixed and the step's row offset is a scalar.
 struct Chunks {
     uint4 c[kChunks];
 };
-__device__ __forceinline__ Chunks load_step(const bf16_t* x, long long ld, int r0, int L, int tid) {
-    Chunks t;
+struct StepSrc {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t voff[kChunks];   // byte offsets of this thread's chunks within a step
+    uint32_t row_bytes;       // row stride in bytes
+};
+// Raw buffer (stride 0, range in bytes) with 32-bit data format: the gfx9
+// descriptor word 3.
+constexpr int kBufWord3 = 0x00020000;
+// Whether an [L, 64] view with row stride ld fits one buffer range (32-bit
+// byte offsets); launchers refuse views that do not.
+inline bool fits_buffer(long long ld, int L) { return L <= 0 || (long long)(L - 1) * ld * 2 + kD * 2 < (1ll << 31); }
+
+__device__ __forceinline__ StepSrc step_src(const bf16_t* x, long long ld, int L, int tid) {
+    StepSrc s;
+    s.row_bytes = (uint32_t)(ld * 2);
+    const uint32_t range = L > 0 ? (uint32_t)((long long)(L - 1) * ld * 2 + kD * 2) : 0u;
+    s.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(x), (short)0, (int)range, kBufWord3);
 #pragma unroll
     for (int n = 0; n < kChunks; ++n) {
-        const int ch = tid + n * kThreads, r = ch >> 3, col = (ch & 7) * 8;
-        t.c[n] = r0 + r < L ? *reinterpret_cast<const uint4*>(x + (long long)(r0 + r) * ld + col)
-                            : make_uint4(0, 0, 0, 0);
+        const int ch = tid + n * kThreads;
+        s.voff[n] = (uint32_t)(ch >> 3) * s.row_bytes + (uint32_t)(ch & 7) * 16u;
+    }
+    return s;
+}
+__device__ __forceinline__ Chunks load_step(const StepSrc& s, int r0) {
+    Chunks t;
+    const uint32_t soff = (uint32_t)r0 * s.row_bytes;
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n) {
+        typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+        const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, s.voff[n], soff, 0);
+        t.c[n] = make_uint4(v[0], v[1], v[2], v[3]);
     }
     return t;
 }

@@ -85,7 +85,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
     const bf16_t* kp = static_cast<const bf16_t*>(a.k) + b * a.sk[0] + hd * a.sk[1];
     const bf16_t* vp = static_cast<const bf16_t*>(a.v) + b * a.sv[0] + hd * a.sv[1];
 
-    Chunks nk = load_step(kp, a.sk[2], 0, Lk, tid);
+    const StepSrc ksrc = step_src(kp, a.sk[2], Lk, tid), vsrc = step_src(vp, a.sv[2], Lk, tid);
+    Chunks nk = load_step(ksrc, 0);
 
     // Q and dO fragments (B operands: query lane%32, features kk*16 + hb*8 ..).
     bf16x8 qf[4], gf[4];
@@ -117,39 +118,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
     const float ddm = dsum * dm;
     float m = -INFINITY, l = 0.0f;
     f32x16 dq[2] = {};
-    Chunks nv = load_step(vp, a.sv[2], 0, Lk, tid);
+    Chunks nv = load_step(vsrc, 0);
     for (int st = 0; st < n_steps; ++st) {
         __syncthreads();
         store_step(nk, smem, kRowsPhase, kRowsKR, kRowsKT, tid);
         store_step(nv, smem, kRowsPhase, kRowsVR, -1, tid);
         if (st + 1 < n_steps) {
-            nk = load_step(kp, a.sk[2], (st + 1) * kStep, Lk, tid);
-            nv = load_step(vp, a.sv[2], (st + 1) * kStep, Lk, tid);
+            nk = load_step(ksrc, (st + 1) * kStep);
+            nv = load_step(vsrc, (st + 1) * kStep);
         }
         __syncthreads();
         const int t0 = st * kStep + ph * kTile;   // this wave's keys t0 .. t0+31
         const char* area = smem + ph * kRowsPhase;
-        f32x16 s = tile_dot(reinterpret_cast<const bf16_t*>(area + kRowsKR), qf, l32, hb);
+        const f32x16 s = tile_dot(reinterpret_cast<const bf16_t*>(area + kRowsKR), qf, l32, hb);
         f32x16 ds = tile_dot(reinterpret_cast<const bf16_t*>(area + kRowsVR), gf, l32, hb);
-        // Scores in log2 units (masked: -inf) and the tile's row max.
-        float mt;
-        if (t0 + kTile <= kmin) {
-            float mx = s[0];
+        // The tile's row max in log2 units (raw scores times cs >= 0; masked
+        // keys excluded), then the weights exp2(s * cs - m) (masked: 0).
+        const bool full = t0 + kTile <= kmin;
+        const int rel = klim - (t0 + hb * 4);
+        float mx = -INFINITY;
+        if (full) {
 #pragma unroll
-            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) s[v] *= cs;
-            mt = mx * cs;
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
         } else {
-            const int rel = klim - (t0 + hb * 4);
-            float mx = -INFINITY;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                s[v] = acc_row(v) < rel ? s[v] * cs : -INFINITY;
-                mx = fmaxf(mx, s[v]);
-            }
-            mt = mx;
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, acc_row(v) < rel ? s[v] : -INFINITY);
         }
+        float mt = mx == -INFINITY ? -INFINITY : mx * cs;
         mt = pair_max(mt);
         if (__any(mt > m + kLazy)) {
             const float m_new = mt > m + kLazy ? mt : m;
@@ -164,11 +159,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
         }
         const float m_use = m == -INFINITY ? 0.0f : m;   // no allowed key yet: every weight is 0
         float rs = 0.0f;
+        if (full) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float p = __builtin_amdgcn_exp2f(s[v] - m_use);
-            rs += p;
-            ds[v] = p * fmaf(ds[v], dm, -ddm);
+            for (int v = 0; v < 16; ++v) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[v], cs, -m_use));
+                rs += p;
+                ds[v] = p * fmaf(ds[v], dm, -ddm);
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(s[v], cs, -m_use));
+                const float p = acc_row(v) < rel ? e : 0.0f;
+                rs += p;
+                ds[v] = p * fmaf(ds[v], dm, -ddm);
+            }
         }
         l += rs;
         u32x4 w[2];
@@ -253,8 +258,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, flo
     // weight none of its keys.
     const int i_begin = (kCausal && a.vl_rank == 0) ? k_wg : 0;
     const int n_steps = (Lq - i_begin + kStep - 1) / kStep;
-    Chunks nq = load_step(qp, a.sq[2], i_begin, Lq, tid);
-    Chunks ng = load_step(gp, a.sdo[2], i_begin, Lq, tid);
+    const StepSrc qsrc = step_src(qp, a.sq[2], Lq, tid), gsrc = step_src(gp, a.sdo[2], Lq, tid);
+    Chunks nq = load_step(qsrc, i_begin);
+    Chunks ng = load_step(gsrc, i_begin);
 
     // K and V fragments (B operands: key lane%32, features kk*16 + hb*8 ..).
     bf16x8 kf[4], vf[4];
@@ -303,8 +309,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, flo
             if ((tid & 31) == 0) tmin_s[tid >> 5] = mn;
         }
         if (st + 1 < n_steps) {
-            nq = load_step(qp, a.sq[2], i0 + kStep, Lq, tid);
-            ng = load_step(gp, a.sdo[2], i0 + kStep, Lq, tid);
+            nq = load_step(qsrc, i0 + kStep);
+            ng = load_step(gsrc, i0 + kStep);
             nr = fetch_rows(i0 + kStep);
         }
         __syncthreads();
@@ -380,6 +386,9 @@ hipError_t launch_variant(const BackwardArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_sdpa_backward_bf16(const BackwardArgs& a, hipStream_t s) {
+    if (!fits_buffer(a.sq[2], a.Lq) || !fits_buffer(a.sdo[2], a.Lq) || !fits_buffer(a.sk[2], a.Lk) ||
+        !fits_buffer(a.sv[2], a.Lk))
+        return hipErrorInvalidValue;
     return a.causal ? launch_variant<true>(a, s) : launch_variant<false>(a, s);
 }
 

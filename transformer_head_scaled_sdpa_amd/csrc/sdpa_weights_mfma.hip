@@ -83,7 +83,8 @@ __global__ __launch_bounds__(kThreads, 1) void weights_mfma(WeightsArgs a, float
     const bf16_t* kp = static_cast<const bf16_t*>(a.k) + b * a.sk[0] + hd * a.sk[1];
     const bf16_t* vp = static_cast<const bf16_t*>(a.v) + b * a.sv[0] + hd * a.sv[1];
 
-    Chunks nk = load_step(kp, a.sk[2], 0, Lk, tid);
+    const StepSrc ksrc = step_src(kp, a.sk[2], Lk, tid), vsrc = step_src(vp, a.sv[2], Lk, tid);
+    Chunks nk = load_step(ksrc, 0);
     bf16x8 qf[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 1) void weights_mfma(WeightsArgs a, float
     for (int st = 0; st < n_steps; ++st) {
         __syncthreads();
         store_step(nk, smem, kPhaseB, kKR, -1, tid);
-        if (st + 1 < n_steps) nk = load_step(kp, a.sk[2], (st + 1) * kStep, Lk, tid);
+        if (st + 1 < n_steps) nk = load_step(ksrc, (st + 1) * kStep);
         __syncthreads();
         const f32x16 s = scores(st * kStep + ph * kTile);
         float mx = -INFINITY;
@@ -146,15 +147,15 @@ __global__ __launch_bounds__(kThreads, 1) void weights_mfma(WeightsArgs a, float
     // ---- pass 2: weights and output ----
     float* prow = (a.p && live) ? a.p + b * a.sp[0] + hd * a.sp[1] + (long long)i * a.sp[2] : nullptr;
     f32x16 o[2] = {};
-    nk = load_step(kp, a.sk[2], 0, Lk, tid);
-    Chunks nv = load_step(vp, a.sv[2], 0, Lk, tid);
+    nk = load_step(ksrc, 0);
+    Chunks nv = load_step(vsrc, 0);
     for (int st = 0; st < n_steps; ++st) {
         __syncthreads();
         store_step(nk, smem, kPhaseB, kKR, -1, tid);
         store_step(nv, smem, kPhaseB, -1, kVT, tid);
         if (st + 1 < n_steps) {
-            nk = load_step(kp, a.sk[2], (st + 1) * kStep, Lk, tid);
-            nv = load_step(vp, a.sv[2], (st + 1) * kStep, Lk, tid);
+            nk = load_step(ksrc, (st + 1) * kStep);
+            nv = load_step(vsrc, (st + 1) * kStep);
         }
         __syncthreads();
         const int t0 = st * kStep + ph * kTile;
@@ -213,6 +214,7 @@ __global__ __launch_bounds__(kThreads, 1) void weights_mfma(WeightsArgs a, float
 }  // namespace
 
 hipError_t launch_sdpa_weights_bf16(const WeightsArgs& a, hipStream_t s) {
+    if (!fits_buffer(a.sk[2], a.Lk) || !fits_buffer(a.sv[2], a.Lk)) return hipErrorInvalidValue;
     const long long grid = (long long)a.B * a.H * ((a.Lq + kRowsWg - 1) / kRowsWg);
     if (grid == 0) return hipSuccess;
     const float c = kLog2e / 8.0f;   // log2(e) / sqrt(64)
