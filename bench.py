@@ -417,9 +417,16 @@ def cpu_baseline(w, inp, budget_s=20.0):
     fit = int(min(w.B, max(1, budget_s // max(dt, 1e-6))))
     if fit > 1:
         nb, dt = fit, run(fit)
+    # When the whole workload takes well under the budget, repeat it (about
+    # half the budget in total) and report the mean.
+    reps = 1
+    if nb == w.B and dt < budget_s / 4:
+        reps = int(max(1, (budget_s / 2) // max(dt, 1e-6)))
+        dt = sum(run(nb) for _ in range(reps)) / reps
     flops = 4 * nb * w.h * w.Lq * w.Lk * w.d_k
+    rep_txt = f", mean of {reps} runs" if reps > 1 else ""
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": n_threads, "kind": "oracle",
-            "sample": f"{nb} of {w.B} batches, full MHA forward (projections included); {dt:.2f} s"}
+            "sample": f"{nb} of {w.B} batches, full MHA forward (projections included); {dt:.2f} s per run{rep_txt}"}
 
 
 def main():
