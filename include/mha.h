@@ -154,7 +154,9 @@ mha_status sdpa_decode(mha_dtype in_dt, mha_dtype out_dt,
  * in the same pass), then dk and dv per key.  MHA_BF16 inputs run on bf16
  * MFMA with fp32 accumulation (the weights and ds rounded to bf16 for their
  * products, as the forward rounds its weights); MHA_F32 inputs in fp32 FMA.
- * Requirements otherwise as for sdpa_forward.
+ * Requirements otherwise as for sdpa_forward; for MHA_BF16 inputs each
+ * (batch, head)'s rows of q, k, v and dout must span less than 2 GiB
+ * (MHA_ENOTSUP otherwise).
  */
 size_t sdpa_backward_workspace_bytes(int B, int h, int Lq);
 
@@ -226,7 +228,8 @@ mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
  * sdpa_forward; meant for debugging and visualisation): for MHA_BF16 inputs
  * bf16 MFMA products with fp32 sums, the weights in fp32 and P.V with the
  * weights as two bf16 terms (about 16 significant bits); for MHA_F32 inputs
- * fp32 FMA throughout.
+ * fp32 FMA throughout.  With MHA_BF16 inputs each (batch, head)'s rows of k
+ * and v must span less than 2 GiB (MHA_ENOTSUP otherwise).
  */
 mha_status sdpa_forward_ex(mha_dtype in_dt, mha_dtype out_dt,
                            const void* q, mha_strides sq,

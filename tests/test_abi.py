@@ -220,9 +220,9 @@ def test_mha_ex_validation(lib):
 
 def bwd(lib, **kw):
     a = dict(in_dt=BF16, out_dt=F32, B=2, h=4, Lq=64, Lk=64, dk=64, dv=64, vl=None, vl_rank=1, causal=0,
-             ws=ALIGNED[8], wsb=None, dq=ALIGNED[5], dk_=ALIGNED[6], dv_=ALIGNED[7])
+             ws=ALIGNED[8], wsb=None, dq=ALIGNED[5], dk_=ALIGNED[6], dv_=ALIGNED[7], st=None)
     a.update(kw)
-    st = S(4 * 64 * 64, 64 * 64, 64)
+    st = S(4 * 64 * 64, 64 * 64, 64) if a["st"] is None else a["st"]
     need = lib.sdpa_backward_workspace_bytes(a["B"], a["h"], a["Lq"])
     wsb = need if a["wsb"] is None else a["wsb"]
     return lib.sdpa_backward(a["in_dt"], a["out_dt"], ALIGNED[0], st, ALIGNED[1], st, ALIGNED[2], st, ALIGNED[3], st,
@@ -245,6 +245,8 @@ def test_backward_workspace_and_validation(lib):
     assert bwd(lib, dv_=ALIGNED[6]) == EINVAL       # dv overlaps dk
     assert bwd(lib, ws=ALIGNED[5]) == EINVAL        # workspace overlaps dq
     assert bwd(lib, dk_=ctypes.c_void_p(P + 0x600000 + 8)) == EINVAL
+    # bf16 rows of one (batch, head) spanning 2 GiB or more: not supported
+    assert bwd(lib, st=S(0, 0, 1 << 24), Lq=128, Lk=128) == ENOTSUP
 
 
 def sub(lib, **kw):

@@ -35,6 +35,12 @@ Range view_range(const void* p, mha_strides s, int B, int h, int L, int d, size_
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// The bf16 MFMA backward and inspection kernels address one (batch, head)'s
+// rows through a buffer resource with 31-bit byte offsets.
+bool rows_fit_buffer(long long row_stride, int L, size_t elem) {
+    return L <= 0 || (long long)(L - 1) * row_stride * (long long)elem + kHeadDim * (long long)elem < (1ll << 31);
+}
+
 // ---------------------------------------------------------------------------
 // kernel timing: a fixed pool of HIP event pairs recorded around launches
 // ---------------------------------------------------------------------------
@@ -119,6 +125,7 @@ mha_status sdpa_impl(mha_dtype in_dt, mha_dtype out_dt,
     if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv)) return MHA_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (p_attn || (valid_lens && vl_rank == 2)) {
+        if (in_dt == MHA_BF16 && (!rows_fit_buffer(sk.l, Lk, ie) || !rows_fit_buffer(sv.l, Lk, ie))) return MHA_ENOTSUP;
         if (p_attn) {
             if (reinterpret_cast<uintptr_t>(p_attn) & 3u) return MHA_EINVAL;
             if (sp.b < 0 || sp.h < 0 || sp.l < 0) return MHA_EINVAL;
@@ -219,6 +226,9 @@ mha_status sdpa_backward(mha_dtype in_dt, mha_dtype out_dt,
     for (const mha_strides& st : out_s)
         if (st.b < 0 || st.h < 0 || st.l < 0 || st.b % omult || st.h % omult || st.l % omult) return MHA_EINVAL;
     const size_t ie = elem_size(in_dt), oe = elem_size(out_dt);
+    if (in_dt == MHA_BF16 && (!rows_fit_buffer(sq.l, Lq, ie) || !rows_fit_buffer(sdo.l, Lq, ie) ||
+                              !rows_fit_buffer(sk.l, Lk, ie) || !rows_fit_buffer(sv.l, Lk, ie)))
+        return MHA_ENOTSUP;
     const uintptr_t wb = reinterpret_cast<uintptr_t>(workspace);
     const Range ins[] = {view_range(q, sq, B, h, Lq, d_k, ie), view_range(k, sk, B, h, Lk, d_k, ie),
                          view_range(v, sv, B, h, Lk, d_v, ie), view_range(o, so, B, h, Lq, d_v, ie),
