@@ -519,6 +519,20 @@ def main():
         "cold_cache": {"ms_per_step": round(cold_ms, 6), "value": round(attn_flops / (cold_ms * 1e-3) / 1e12, 3),
                        "note": "512 MiB streamed before each of 20 steps; events bracket the step only"},
     }
+    # Beside the literal formula: the attention flops the masks allow
+    # (4 * d_k per allowed pair) and, for the multi-head layer, the whole
+    # step's work with the projections (Q over all queries, K and V over the
+    # keys, W_O over all queries).
+    alg_attn = 4 * w.d_k * allowed_pairs(w, inp.valid_lens)
+    result["attention_alg"] = {"flops_per_step": int(alg_attn),
+                               "tflops": round(alg_attn / (ms * 1e-3) / 1e12, 3),
+                               "frac_bf16_peak": round(alg_attn / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    if w.kind == "mha":
+        proj = 2 * w.d_model * w.d_model * w.B * (2 * w.Lq + 2 * w.Lk)
+        result["mha_total"] = {"flops_per_step": int(proj + alg_attn),
+                               "tflops": round((proj + alg_attn) / (ms * 1e-3) / 1e12, 3),
+                               "frac_peak": round((proj + alg_attn) / (ms * 1e-3) / 1e12 / mfma_peak, 4),
+                               "note": "projections Q, K, V, W_O (dense) plus the allowed attention pairs"}
 
     if not args.no_long_sdpa and w.name != "sdpa_long_causal":
         lw = workloads.BY_NAME["sdpa_long_causal"]
