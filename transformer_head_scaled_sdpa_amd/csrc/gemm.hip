@@ -310,6 +310,76 @@ __global__ __launch_bounds__(256) void gemm_f32_nt(GemmArgs g, int tiles_n) {
     }
 }
 
+// fp32 with few rows (M <= 64, the projections of short sequences): a tile is
+// 8 rows x 64 columns, one column per lane, and the four waves of a
+// workgroup split K; the 8 A rows (all of K) sit in LDS and are read as
+// broadcasts, each lane streams its own W row.  The four partial sums are
+// added through LDS.  Small tiles give more workgroups and short loops (few
+// waves run cold here, so instruction fetch matters as much as arithmetic).
+constexpr int kSM = 8, kSN = 64, kSW = 4;
+
+__global__ __launch_bounds__(64 * kSW) void gemm_f32_smallm(GemmArgs g, int tiles_n) {
+    extern __shared__ float sm[];                       // A tile [kSM][K], then partials [kSW][kSM][kSN]
+    int id = blockIdx.x, prob = -1, tm = 0, tn = 0;
+    for (int p = 0; p < g.nprob; ++p) {
+        const int tiles = ((g.p[p].M + kSM - 1) / kSM) * tiles_n;
+        if (id < tiles) { prob = p; tm = id / tiles_n; tn = id % tiles_n; break; }
+        id -= tiles;
+    }
+    if (prob < 0) return;
+    // Constant indices only: a runtime index into the argument array would
+    // copy it to scratch memory.
+    const GemmProblem P = prob == 0 ? g.p[0] : (prob == 1 ? g.p[1] : g.p[2]);
+    const int M = P.M, N = g.N, K = g.K;
+    const int m0 = tm * kSM, n0 = tn * kSN;
+    const float* A = static_cast<const float*>(P.a);
+    const float* W = static_cast<const float*>(P.w);
+    float* as = sm;
+    float* red = sm + kSM * K;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // A rows m0 .. m0+7, all of K (rows past M read as zero), 16 bytes a piece.
+    for (int c = tid; c < kSM * K / 4; c += 64 * kSW) {
+        const int r = (c * 4) / K, k = (c * 4) % K;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (m0 + r < M) x = *reinterpret_cast<const float4*>(A + (long long)(m0 + r) * K + k);
+        *reinterpret_cast<float4*>(as + r * K + k) = x;
+    }
+    __syncthreads();
+    const int n = n0 + lane;
+    const int kq = K / kSW, k0 = wave * kq;
+    const float* wr = W + (long long)min(n, N - 1) * K;   // rows past N compute a discarded copy
+    float acc[kSM] = {};
+    for (int k = k0; k < k0 + kq; k += 4) {
+        const float4 wv = *reinterpret_cast<const float4*>(wr + k);
+#pragma unroll
+        for (int r = 0; r < kSM; ++r) {
+            const float4 av = *reinterpret_cast<const float4*>(as + r * K + k);
+            acc[r] = fmaf(av.x, wv.x, acc[r]);
+            acc[r] = fmaf(av.y, wv.y, acc[r]);
+            acc[r] = fmaf(av.z, wv.z, acc[r]);
+            acc[r] = fmaf(av.w, wv.w, acc[r]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kSM; ++r) red[(wave * kSM + r) * kSN + lane] = acc[r];
+    __syncthreads();
+    // Wave w adds the partials of rows 2w and 2w + 1 and stores them.
+    const float* bias = static_cast<const float*>(P.bias);
+    float* C = static_cast<float*>(P.c);
+#pragma unroll
+    for (int rr = 0; rr < kSM / kSW; ++rr) {
+        const int r = wave * (kSM / kSW) + rr;
+        const int m = m0 + r;
+        if (m >= M || n >= N) continue;
+        float y = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kSW; ++w) y += red[(w * kSM + r) * kSN + lane];
+        const float res = P.res ? static_cast<const float*>(P.res)[(long long)m * N + n] : 0.0f;
+        C[(long long)m * N + n] = y + (bias ? bias[n] : 0.0f) + res;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, bool out_f32, hipStream_t s) {
@@ -327,6 +397,17 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, bool out_f32, hipStream_t s) {
 
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s) {
     if (g.K % 4 != 0) return hipErrorInvalidValue;   // 16-byte operand pieces along K
+    int max_m = 0;
+    for (int p = 0; p < g.nprob; ++p) max_m = max(max_m, g.p[p].M);
+    const size_t small_lds = (size_t)(kSM * g.K + kSW * kSM * kSN) * sizeof(float);
+    if (max_m <= 64 && g.K % (4 * kSW) == 0 && small_lds <= 64 * 1024) {
+        const int tiles_n = (g.N + kSN - 1) / kSN;
+        long long tiles = 0;
+        for (int p = 0; p < g.nprob; ++p) tiles += (long long)((g.p[p].M + kSM - 1) / kSM) * tiles_n;
+        if (tiles == 0) return hipSuccess;
+        hipLaunchKernelGGL(gemm_f32_smallm, dim3((unsigned)tiles), dim3(64 * kSW), small_lds, s, g, tiles_n);
+        return hipGetLastError();
+    }
     const int tiles_n = (g.N + kFT - 1) / kFT;
     long long tiles = 0;
     for (int p = 0; p < g.nprob; ++p) tiles += (long long)((g.p[p].M + kFT - 1) / kFT) * tiles_n;

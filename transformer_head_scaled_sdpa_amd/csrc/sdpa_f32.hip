@@ -5,9 +5,13 @@
 // row that has no allowed key weighting all Lk keys uniformly.
 //
 // One wave64 per 64 queries of one (batch, head); each lane owns one query,
-// its 64 query features and 64 output accumulators in registers.  Key/value
-// tiles of 16 rows are staged in LDS and read as broadcasts (every lane reads
-// the same address), so there are no bank conflicts.  Online softmax in fp32.
+// its 64 query features and 64 output accumulators in registers.  The keys
+// are walked one at a time in a loop (not unrolled over keys), with every
+// lane reading the same key and value row, so the row loads are uniform
+// (scalar loads) and the code stays small: the fp32 path serves short
+// sequences, where a few waves run cold and instruction fetch, not
+// arithmetic, sets the time of a long unrolled body.  Two passes over the
+// keys: the row max, then the weights, their sum and the output.
 #include "common.h"
 #include "kernels.h"
 
@@ -17,13 +21,22 @@ namespace {
 
 constexpr int kD = 64;
 constexpr int kBQ = 64;   // queries per workgroup (one per lane)
-constexpr int kBK = 16;   // keys per tile (short sequences waste at most 15 masked keys)
+
+__device__ __forceinline__ float row_dot(const float (&q)[kD], const float* kr) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int t4 = 0; t4 < kD / 4; ++t4) {
+        const float4 kx = *reinterpret_cast<const float4*>(kr + t4 * 4);
+        acc = fmaf(q[t4 * 4], kx.x, acc);
+        acc = fmaf(q[t4 * 4 + 1], kx.y, acc);
+        acc = fmaf(q[t4 * 4 + 2], kx.z, acc);
+        acc = fmaf(q[t4 * 4 + 3], kx.w, acc);
+    }
+    return acc;
+}
 
 template <bool kCausal, bool kHasVl>
 __global__ __launch_bounds__(64) void sdpa_fwd_f32_d64(SdpaArgs a, int n_qtiles, float c_log2) {
-    __shared__ float4 ks[kBK * kD / 4];
-    __shared__ float4 vs[kBK * kD / 4];
-
     const int lane = threadIdx.x;
     const int BH = a.B * a.H;
     const int bh = blockIdx.x % BH;
@@ -35,10 +48,11 @@ __global__ __launch_bounds__(64) void sdpa_fwd_f32_d64(SdpaArgs a, int n_qtiles,
 
     const int Lk = a.Lk;
     const int vlen = kHasVl ? a.valid_lens[b] : Lk;
-    const bool none = vlen <= 0;
+    const bool none = vlen <= 0;                  // every key masked -> uniform weights
     const int kv_lim = none ? Lk : min(vlen, Lk);
-    int kv_end = kv_lim;
+    int kv_end = kv_lim;                          // keys the wave visits (uniform)
     if (kCausal && !none) kv_end = min(kv_end, q_wg + kBQ);
+    const int key_lim = none ? Lk : (kCausal ? min(kv_lim, i + 1) : kv_lim);   // this lane's keys [0, key_lim)
 
     const float* qb = static_cast<const float*>(a.q) + b * a.sq[0] + hd * a.sq[1];
     const float* kb = static_cast<const float*>(a.k) + b * a.sk[0] + hd * a.sk[1];
@@ -52,80 +66,33 @@ __global__ __launch_bounds__(64) void sdpa_fwd_f32_d64(SdpaArgs a, int n_qtiles,
         q[t] = x.x; q[t + 1] = x.y; q[t + 2] = x.z; q[t + 3] = x.w;
         o[t] = o[t + 1] = o[t + 2] = o[t + 3] = 0.0f;
     }
-    float m_run = -INFINITY, l_run = 0.0f;
 
-    for (int kv0 = 0; kv0 < kv_end; kv0 += kBK) {
-        __syncthreads();
-        // kBK rows x 16 float4 per tensor: kBK / 4 float4 per lane each.
+    // ---- pass 1: row max over the allowed keys (scores in raw units) ----
+    float m = -INFINITY;
+    for (int j = 0; j < kv_end; ++j) {
+        const float sj = none ? 0.0f : row_dot(q, kb + (long long)j * a.sk[2]);
+        if (j < key_lim) m = fmaxf(m, sj);
+    }
+    // ---- pass 2: weights, their sum and the output ----
+    const float mc = m * c_log2;
+    float l = 0.0f;
+    for (int j = 0; j < kv_end; ++j) {
+        const float sj = none ? 0.0f : row_dot(q, kb + (long long)j * a.sk[2]);
+        const float p = j < key_lim ? __builtin_amdgcn_exp2f(fmaf(sj, c_log2, -mc)) : 0.0f;
+        l += p;
+        const float* vr = vb + (long long)j * a.sv[2];
 #pragma unroll
-        for (int n = 0; n < kBK / 4; ++n) {
-            const int c = lane + n * 64;
-            const int r = c >> 4, col = (c & 15) * 4;
-            const int key = kv0 + r;
-            float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
-            if (key < Lk) {
-                kx = *reinterpret_cast<const float4*>(kb + key * a.sk[2] + col);
-                vx = *reinterpret_cast<const float4*>(vb + key * a.sv[2] + col);
-            }
-            ks[c] = kx;
-            vs[c] = vx;
-        }
-        __syncthreads();
-
-        float s[kBK];
-#pragma unroll
-        for (int j = 0; j < kBK; ++j) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int t4 = 0; t4 < kD / 4; ++t4) {
-                const float4 kx = ks[j * (kD / 4) + t4];
-                acc = fmaf(q[t4 * 4], kx.x, acc);
-                acc = fmaf(q[t4 * 4 + 1], kx.y, acc);
-                acc = fmaf(q[t4 * 4 + 2], kx.z, acc);
-                acc = fmaf(q[t4 * 4 + 3], kx.w, acc);
-            }
-            const int key = kv0 + j;
-            bool ok;
-            if (none) {
-                ok = key < Lk;
-                acc = 0.0f;
-            } else {
-                ok = key < kv_lim && (!kCausal || key <= i);
-            }
-            s[j] = ok ? acc : -INFINITY;
-        }
-        float mt = s[0];
-#pragma unroll
-        for (int j = 1; j < kBK; ++j) mt = fmaxf(mt, s[j]);
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c_log2);
-        const float mc = m_use * c_log2;
-        float rs = 0.0f;
-#pragma unroll
-        for (int j = 0; j < kBK; ++j) {
-            s[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c_log2, -mc));
-            rs += s[j];
-        }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-#pragma unroll
-        for (int t = 0; t < kD; ++t) o[t] *= alpha;
-#pragma unroll
-        for (int j = 0; j < kBK; ++j) {
-#pragma unroll
-            for (int t4 = 0; t4 < kD / 4; ++t4) {
-                const float4 vx = vs[j * (kD / 4) + t4];
-                o[t4 * 4] = fmaf(s[j], vx.x, o[t4 * 4]);
-                o[t4 * 4 + 1] = fmaf(s[j], vx.y, o[t4 * 4 + 1]);
-                o[t4 * 4 + 2] = fmaf(s[j], vx.z, o[t4 * 4 + 2]);
-                o[t4 * 4 + 3] = fmaf(s[j], vx.w, o[t4 * 4 + 3]);
-            }
+        for (int t4 = 0; t4 < kD / 4; ++t4) {
+            const float4 vx = *reinterpret_cast<const float4*>(vr + t4 * 4);
+            o[t4 * 4] = fmaf(p, vx.x, o[t4 * 4]);
+            o[t4 * 4 + 1] = fmaf(p, vx.y, o[t4 * 4 + 1]);
+            o[t4 * 4 + 2] = fmaf(p, vx.z, o[t4 * 4 + 2]);
+            o[t4 * 4 + 3] = fmaf(p, vx.w, o[t4 * 4 + 3]);
         }
     }
 
     if (i >= a.Lq) return;
-    const float inv = 1.0f / l_run;
+    const float inv = 1.0f / l;
     float* ob = static_cast<float*>(a.o) + b * a.so[0] + hd * a.so[1] + i * a.so[2];
 #pragma unroll
     for (int t = 0; t < kD; t += 4)
