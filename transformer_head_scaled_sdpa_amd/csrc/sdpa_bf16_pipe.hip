@@ -14,7 +14,8 @@
 //    queries of one (batch, head); each wave owns 32 queries and keeps their
 //    Q fragments in registers.  Keys/values stream through LDS in tiles of
 //    64 keys, copied with one 16-byte coalesced load per thread per tensor,
-//    staged in registers one tile ahead.
+//    loaded into registers two stages before they are stored to LDS (two
+//    register sets, one for even and one for odd stages).
 //  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
 //    so every lane owns ONE query (lane % 32) and 32 keys of a tile; row sums
 //    are in-lane plus one v_permlane32_swap.  O^T += V^T P^T takes P straight
@@ -233,10 +234,10 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
     auto load_k = [&](int t) { return load_chunk(kp + t * ktile, koff, Lk - t * kBN, tid); };
     auto load_v = [&](int t) { return load_chunk(vp + t * vtile, voff, Lk - t * kBN, tid); };
 
-    // Prologue: K tiles 0 and 1 into LDS, scores of tile 0; K(2) and V(0)
-    // wait in registers for stage 0.
-    uint4 nk = load_k(0);
-    uint4 nv = n_tiles > 1 ? load_k(1) : make_uint4(0, 0, 0, 0);
+    // Prologue: K tiles 0 and 1 into LDS, scores of tile 0; K(2), K(3), V(0)
+    // and V(1) wait in registers for stages 0 and 1.
+    uint4 nk_e = load_k(0);
+    uint4 nk_o = n_tiles > 1 ? load_k(1) : make_uint4(0, 0, 0, 0);
     bf16x8 qf[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -244,10 +245,12 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
         if (i < a.Lq) raw = *reinterpret_cast<const uint4*>(qp + (long long)i * a.sq[2] + kk * 16 + hb * 8);
         qf[kk] = __builtin_bit_cast(bf16x8, raw);
     }
-    store_chunk<kLdsK>(nk, kbuf, tid);
-    if (n_tiles > 1) store_chunk<kLdsK>(nv, kbuf + kTileK, tid);
-    nk = n_tiles > 2 ? load_k(2) : make_uint4(0, 0, 0, 0);
-    nv = load_v(0);
+    store_chunk<kLdsK>(nk_e, kbuf, tid);
+    if (n_tiles > 1) store_chunk<kLdsK>(nk_o, kbuf + kTileK, tid);
+    nk_e = n_tiles > 2 ? load_k(2) : make_uint4(0, 0, 0, 0);
+    nk_o = n_tiles > 3 ? load_k(3) : make_uint4(0, 0, 0, 0);
+    uint4 nv_e = load_v(0);
+    uint4 nv_o = n_tiles > 1 ? load_v(1) : make_uint4(0, 0, 0, 0);
     __syncthreads();
     f32x16 sc[2];                 // scores of the tile whose softmax runs next
     tile_scores(sc, kbuf, qf, l32, hb);
@@ -261,15 +264,17 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
 
     // Stage s reads K(s+1) and V(s-1) and fills the other buffers with K(s+2)
     // and V(s); every wave finished with those at the last barrier.
-    auto copy_tiles = [&](int s) {
+    // Stage s stores K(s+2) and V(s), loaded two stages earlier, and loads
+    // K(s+4) and V(s+2); even and odd stages use their own register sets.
+    auto copy_tiles = [&](int s, uint4& nk, uint4& nv) {
         if (s + 2 < n_tiles) store_chunk<kLdsK>(nk, kbuf + (s & 1) * kTileK, tid);
         if (s < n_tiles) store_chunk<kLdsV>(nv, vbuf + (s & 1) * kTileV, tid);
-        if (s + 3 < n_tiles) nk = load_k(s + 3);
-        if (s + 1 < n_tiles) nv = load_v(s + 1);
+        if (s + 4 < n_tiles) nk = load_k(s + 4);
+        if (s + 2 < n_tiles) nv = load_v(s + 2);
     };
     // Unmasked steady state: softmax(s), scores(s+1) and P.V(s-1), independent.
-    auto fast_stage = [&](int s, f32x16 (&cur)[2], f32x16 (&nxt)[2], const u32x4 (&prev)[4], u32x4 (&pcur)[4]) {
-        copy_tiles(s);
+    auto fast_stage = [&](int s, f32x16 (&cur)[2], f32x16 (&nxt)[2], const u32x4 (&prev)[4], u32x4 (&pcur)[4], uint4& nk, uint4& nv) {
+        copy_tiles(s, nk, nv);
         const bf16_t* ks = kbuf + ((s + 1) & 1) * kTileK;
         const bf16_t* vs = vbuf + ((s + 1) & 1) * kTileV;
         float r = weights(cur, m, c, pcur);
@@ -283,8 +288,8 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
         __syncthreads();
     };
     // Pipeline edges, masked tiles and fully masked rows.
-    auto slow_stage = [&](int s, f32x16 (&cur)[2], f32x16 (&nxt)[2], const u32x4 (&prev)[4], u32x4 (&pcur)[4]) {
-        copy_tiles(s);
+    auto slow_stage = [&](int s, f32x16 (&cur)[2], f32x16 (&nxt)[2], const u32x4 (&prev)[4], u32x4 (&pcur)[4], uint4& nk, uint4& nv) {
+        copy_tiles(s, nk, nv);
         const bf16_t* ks = kbuf + ((s + 1) & 1) * kTileK;
         const bf16_t* vs = vbuf + ((s + 1) & 1) * kTileV;
         if (s >= 1 && s - 1 < n_w) tile_pv(o, vs, prev, hb, lane);
@@ -304,17 +309,17 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
     // Stage 0, then unmasked stages in pairs from stage 1, then the rest.
     // Even stages keep the current scores in sc and their weights in pa, odd
     // stages in sn and pb, so no registers are copied between stages.
-    slow_stage(0, sc, sn, pb, pa);
+    slow_stage(0, sc, sn, pb, pa, nk_e, nv_e);
     const int fast_last = 1 + 2 * max(0, (min(n_w - 1, t_mask) - 1) / 2);   // fast stages [1, fast_last)
     int s = 1;
     for (; s < fast_last; s += 2) {
-        fast_stage(s, sn, sc, pa, pb);
-        fast_stage(s + 1, sc, sn, pb, pa);
+        fast_stage(s, sn, sc, pa, pb, nk_o, nv_o);
+        fast_stage(s + 1, sc, sn, pb, pa, nk_e, nv_e);
     }
     for (; s <= n_tiles; s += 2) {
-        slow_stage(s, sn, sc, pa, pb);
+        slow_stage(s, sn, sc, pa, pb, nk_o, nv_o);
         if (s + 1 > n_tiles) break;
-        slow_stage(s + 1, sc, sn, pb, pa);
+        slow_stage(s + 1, sc, sn, pb, pa, nk_e, nv_e);
     }
 
     if (i >= a.Lq) return;
