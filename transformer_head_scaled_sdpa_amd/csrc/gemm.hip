@@ -75,6 +75,24 @@ __device__ __forceinline__ TileMap map_tile(const GemmArgs& g, int t, int tiles_
     return r;
 }
 
+// y[e] += x[e] for kW (4 or 8) consecutive bf16 values x.
+template <int kW>
+__device__ __forceinline__ void add_bf16_row(float* y, const bf16_t* x) {
+    uint32_t w[kW / 2];
+    if constexpr (kW == 8) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(x);
+        w[0] = raw.x, w[1] = raw.y, w[2] = raw.z, w[3] = raw.w;
+    } else {
+        const uint2 raw = *reinterpret_cast<const uint2*>(x);
+        w[0] = raw.x, w[1] = raw.y;
+    }
+#pragma unroll
+    for (int e = 0; e < kW / 2; ++e) {
+        y[2 * e] += __uint_as_float(w[e] << 16);
+        y[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+
 template <int kTN, bool kOutF32>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, int tiles_total, int per_xcd,
                                                        int shared_a) {
@@ -161,40 +179,29 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, 
                     make_float4(y[g4 * 4], y[g4 * 4 + 1], y[g4 * 4 + 2], y[g4 * 4 + 3]);
         }
     __syncthreads();
+    // Each lane stores 16 bytes: 4 fp32 or 8 bf16 columns; consecutive lanes
+    // cover a tile row left to right, so a row's output is one contiguous run.
     const bf16_t* bias = static_cast<const bf16_t*>(P.bias);
-    constexpr int kChunks = kTN / 8;               // 8-column chunks per row
+    const bf16_t* res = static_cast<const bf16_t*>(P.res);   // residual (pre-norm sublayer: x + attention(norm(x)))
+    constexpr int kW = kOutF32 ? 4 : 8;            // columns per lane
+    constexpr int kChunks = kTN / kW;              // lanes per tile row
 #pragma unroll
     for (int j = 0; j < kTM * kChunks / 256; ++j) {
         const int q = tid + 256 * j;
-        const int r = q / kChunks, c8 = (q % kChunks) * 8;
-        const int m = m0 + r, n = n0 + c8;
+        const int r = q / kChunks, c = (q % kChunks) * kW;
+        const int m = m0 + r, n = n0 + c;
         if (m >= M || n >= N) continue;
-        const float4 lo4 = *reinterpret_cast<const float4*>(st + r * kPitch + c8);
-        const float4 hi4 = *reinterpret_cast<const float4*>(st + r * kPitch + c8 + 4);
-        float y[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
-        if (bias) {
-            const uint4 braw = *reinterpret_cast<const uint4*>(bias + n);
-            const uint32_t bw[4] = {braw.x, braw.y, braw.z, braw.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                y[2 * e] += __uint_as_float(bw[e] << 16);
-                y[2 * e + 1] += __uint_as_float(bw[e] & 0xffff0000u);
-            }
-        }
         const long long o = (long long)m * N + n;
-        if (P.res) {   // residual (pre-norm sublayer: x + attention(norm(x)))
-            const uint4 rraw = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(P.res) + o);
-            const uint32_t rw[4] = {rraw.x, rraw.y, rraw.z, rraw.w};
+        float y[kW];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                y[2 * e] += __uint_as_float(rw[e] << 16);
-                y[2 * e + 1] += __uint_as_float(rw[e] & 0xffff0000u);
-            }
+        for (int e = 0; e < kW; e += 4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(st + r * kPitch + c + e);
+            y[e] = v4.x, y[e + 1] = v4.y, y[e + 2] = v4.z, y[e + 3] = v4.w;
         }
-        if (kOutF32) {
-            float* C = static_cast<float*>(P.c) + o;
-            *reinterpret_cast<float4*>(C) = make_float4(y[0], y[1], y[2], y[3]);
-            *reinterpret_cast<float4*>(C + 4) = make_float4(y[4], y[5], y[6], y[7]);
+        if (bias) add_bf16_row<kW>(y, bias + n);
+        if (res) add_bf16_row<kW>(y, res + o);
+        if constexpr (kOutF32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(P.c) + o) = make_float4(y[0], y[1], y[2], y[3]);
         } else {
             *reinterpret_cast<uint4*>(static_cast<bf16_t*>(P.c) + o) =
                 make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
