@@ -19,8 +19,9 @@ constexpr int kTileRowBytes = kTileLdsRow * 2;
 // wave-uniform base, so one wave instruction fills 1 KB of LDS and the
 // per-lane source address decides the layout.  Wave load i (i = wave +
 // kWaves*j) fills LDS bytes [1024 i, 1024 i + 1024): lane -> row x / 144,
-// 16-byte chunk (x % 144) / 16 of that row.  Chunk 8 is row padding and
-// re-reads chunk 0; rows at or past `limit` re-read row limit - 1 (their
+// 16-byte chunk (x % 144) / 16 of that row.  Chunk 8 is row padding: its
+// lanes are switched off, so those LDS bytes keep stale data and must never
+// be read; rows at or past `limit` re-read row limit - 1 (their
 // products are never stored).  With skip_dead, a wave load whose rows all lie
 // at or past `limit` is not issued at all: those LDS rows keep stale data of
 // any value, so only callers whose rows never mix with other rows' results
@@ -33,6 +34,7 @@ struct LdsTileLoader {
     static_assert(kRows % 64 == 0, "tile rows must be a multiple of 64");
     uint32_t off[kPerWave];   // element offsets from the matrix base, before the slice offset
     uint32_t live = 0;        // bit j: wave load j has a row below the limit (wave-uniform)
+    uint32_t pad = 0;         // bit j: this lane's chunk of wave load j is row padding
 
     // Rows r0 .. r0 + kRows - 1 of a row-major matrix with `ld` elements per row.
     __device__ __forceinline__ void init(int wave, int lane, int r0, int limit, int ld, bool skip_dead = false) {
@@ -41,7 +43,10 @@ struct LdsTileLoader {
             const int x = (wave + kWaves * j) * 1024 + lane * 16;
             const int r = x / kTileRowBytes;
             int c = (x % kTileRowBytes) / 16;
-            if (c == 8) c = 0;
+            if (c == 8) {
+                c = 0;
+                pad |= 1u << j;
+            }
             off[j] = (uint32_t)(min(r0 + r, limit - 1) * ld + c * 8);
             const int first = (wave + kWaves * j) * 1024 / kTileRowBytes;   // first row of the load
             if (!skip_dead || r0 + first < limit) live |= 1u << j;
@@ -53,7 +58,7 @@ struct LdsTileLoader {
 #pragma unroll
         for (int j = 0; j < kPerWave; ++j) {
             const int i = wave + kWaves * j;
-            if (i < kLoads && (live >> j & 1u))
+            if (i < kLoads && (live >> j & 1u) && !(pad >> j & 1u))
                 __builtin_amdgcn_global_load_lds((global_cvoid*)(src + off[j]), (lds_void*)(lds + i * 1024), 16, 0, 0);
         }
     }
