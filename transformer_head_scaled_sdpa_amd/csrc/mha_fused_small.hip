@@ -363,28 +363,40 @@ __global__ __launch_bounds__(kThreads, 1) void mha_attn_fused_small_bf16(FusedAr
         part[(qb * kPart + 33) * 64 + lane] = l;
     }
     __syncthreads();
-    if (!qwave || i >= L) return;
-    const float m1 = part[(qb * kPart + 32) * 64 + lane];
-    const float l1 = part[(qb * kPart + 33) * 64 + lane];
-    // The first half always holds an allowed key of every row (key 0).
-    const float mx = fmaxf(m, m1);
-    const float a0 = __builtin_amdgcn_exp2f(m - mx);
-    const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mx);
-    const float inv = 1.0f / pair_sum(a0 * l + a1 * l1);
-    bf16_t* ob = static_cast<bf16_t*>(a.o) + ((long long)b * L + i) * D + hd * kHd;
+    // Waves 0-3 merge and normalise; the bf16 result goes to LDS (K's bytes,
+    // free since the attention) and then out as whole 128-byte head rows.
+    bf16_t* o_s = reinterpret_cast<bf16_t*>(smem + kKhOff);
+    if (qwave) {
+        const float m1 = part[(qb * kPart + 32) * 64 + lane];
+        const float l1 = part[(qb * kPart + 33) * 64 + lane];
+        // The first half always holds an allowed key of every row (key 0).
+        const float mx = fmaxf(m, m1);
+        const float a0 = __builtin_amdgcn_exp2f(m - mx);
+        const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mx);
+        const float inv = 1.0f / pair_sum(a0 * l + a1 * l1);
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+        for (int tb = 0; tb < 2; ++tb) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            float y[4];
+            for (int g4 = 0; g4 < 4; ++g4) {
+                float y[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int v = g4 * 4 + e;
-                y[e] = (a0 * o[tb][v] + a1 * part[(qb * kPart + tb * 16 + v) * 64 + lane]) * inv;
+                for (int e = 0; e < 4; ++e) {
+                    const int v = g4 * 4 + e;
+                    y[e] = (a0 * o[tb][v] + a1 * part[(qb * kPart + tb * 16 + v) * 64 + lane]) * inv;
+                }
+                *reinterpret_cast<uint2*>(o_s + i * kTileLdsRow + tb * 32 + g4 * 8 + hb * 4) =
+                    make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
             }
-            *reinterpret_cast<uint2*>(ob + tb * 32 + g4 * 8 + hb * 4) =
-                make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
         }
+    }
+    __syncthreads();
+    // 8 lanes per row, 16 bytes each; rows past L are not stored.
+#pragma unroll
+    for (int pass = 0; pass < kL * 8 / kThreads; ++pass) {
+        const int r = pass * (kThreads / 8) + (tid >> 3), c8 = (tid & 7) * 8;
+        if (r < L)
+            *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.o) + ((long long)b * L + r) * D + hd * kHd + c8) =
+                *reinterpret_cast<const uint4*>(o_s + r * kTileLdsRow + c8);
     }
 }
 
