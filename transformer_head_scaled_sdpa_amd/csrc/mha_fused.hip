@@ -398,19 +398,33 @@ __global__ __launch_bounds__(kThreads, 1) void mha_attn_fused_bf16(FusedArgs a, 
         }
     }
 
-    if (!active || i >= Lq) return;
+    if (!active) return;
     const float inv = 1.0f / pair_sum(l);
     // O^T element v of block tb: feature tb*32 + (v/4)*8 + hb*4 + v%4, query i.
-    bf16_t* ob = static_cast<bf16_t*>(a.o) + ((long long)b * Lq + i) * D + hd * kHd;
+    // The wave stages its 32 x 64 bf16 result in its own slice of the
+    // projection stages (no wave reads them once the last chunk is
+    // projected) and stores whole 128-byte head rows.
+    bf16_t* o_s = reinterpret_cast<bf16_t*>(smem + wave * 32 * kTileRowBytes);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const int tt = tb * 32 + g4 * 8 + hb * 4;
-            *reinterpret_cast<uint2*>(ob + tt) =
+            *reinterpret_cast<uint2*>(o_s + l32 * kTileLdsRow + tt) =
                 make_uint2(pack_bf16x2(o[tb][g4 * 4] * inv, o[tb][g4 * 4 + 1] * inv),
                            pack_bf16x2(o[tb][g4 * 4 + 2] * inv, o[tb][g4 * 4 + 3] * inv));
         }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 8 lanes per row, 16 bytes each; rows past Lq are not stored.
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int r = pass * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+        if (q0 + r < Lq)
+            *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.o) + ((long long)b * Lq + q0 + r) * D + hd * kHd + c8) =
+                *reinterpret_cast<const uint4*>(o_s + r * kTileLdsRow + c8);
     }
 }
 
