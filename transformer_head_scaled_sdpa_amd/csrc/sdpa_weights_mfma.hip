@@ -36,6 +36,7 @@ constexpr int kVT = kTileRB;              // V, 192-byte rows (transposed reads)
 constexpr int kPhaseB = kTileRB + kTileTB;
 constexpr int kRedB = kGroups * (kPhases - 1) * 32 * 64 * 4;   // reduction slots (reuse the tiles)
 constexpr int kSmemB = kPhases * kPhaseB > kRedB ? kPhases * kPhaseB : kRedB;
+constexpr int kWstPitch = kTile + 4;      // fp32 per staged weight row (144 bytes)
 
 // Write this lane's four weights of keys t .. t+3 (row prow), as one 16-byte
 // store when aligned and whole, else element by element inside the row.
@@ -54,6 +55,7 @@ template <bool kCausal>
 __global__ __launch_bounds__(kThreads, 1) void weights_mfma(WeightsArgs a, float c, bool vec4) {
     __shared__ __attribute__((aligned(16))) char smem[kSmemB];
     __shared__ float2 stat_s[kGroups][kPhases][2][32];
+    __shared__ __attribute__((aligned(16))) float wst_s[kWaves][kTile * kWstPitch];   // per-wave weight tile
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -145,7 +147,11 @@ __global__ __launch_bounds__(kThreads, 1) void weights_mfma(WeightsArgs a, float
     const float lse = L > 0.0f ? M + __builtin_amdgcn_logf(L) : 0.0f;
 
     // ---- pass 2: weights and output ----
-    float* prow = (a.p && live) ? a.p + b * a.sp[0] + hd * a.sp[1] + (long long)i * a.sp[2] : nullptr;
+    // The wave's 32 x 32 weight tile goes through its own LDS slice so that
+    // each store instruction writes whole 128-byte runs of 8 weight rows.
+    float* const pq = a.p ? a.p + b * a.sp[0] + hd * a.sp[1] : nullptr;
+    const int q_w = q_wg + grp * 32;           // first query of this wave's tile
+    float* const wst = wst_s[wave];
     f32x16 o[2] = {};
     nk = load_step(ksrc, 0);
     Chunks nv = load_step(vsrc, 0);
@@ -162,10 +168,24 @@ __global__ __launch_bounds__(kThreads, 1) void weights_mfma(WeightsArgs a, float
         f32x16 p = scores(t0);
 #pragma unroll
         for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(p[v] - lse);   // masked: exp2(-inf) = 0
-        if (prow) {
+        if (pq) {
+            // Lane (query l32, half hb) holds keys t0 + g4*8 + hb*4 + 0..3.
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4)
-                put4(prow, t0 + g4 * 8 + hb * 4, Lk, vec4, p[g4 * 4], p[g4 * 4 + 1], p[g4 * 4 + 2], p[g4 * 4 + 3]);
+                *reinterpret_cast<float4*>(wst + l32 * kWstPitch + g4 * 8 + hb * 4) =
+                    make_float4(p[g4 * 4], p[g4 * 4 + 1], p[g4 * 4 + 2], p[g4 * 4 + 3]);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // 8 lanes per row, keys t0 + c4 .. c4+3; rows past Lq are not stored.
+#pragma unroll
+            for (int pass = 0; pass < kTile / 8; ++pass) {
+                const int r = pass * 8 + (lane >> 3), c4 = (lane & 7) * 4;
+                if (q_w + r < Lq) {
+                    const float4 w4 = *reinterpret_cast<const float4*>(wst + r * kWstPitch + c4);
+                    put4(pq + (long long)(q_w + r) * a.sp[2], t0 + c4, Lk, vec4, w4.x, w4.y, w4.z, w4.w);
+                }
+            }
         }
         // P = hi + lo in bf16; O^T += V^T (hi + lo)^T.
         u32x4 ph_w[2], pl_w[2];
