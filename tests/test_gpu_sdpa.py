@@ -69,6 +69,48 @@ def test_sdpa_bf16_sharp_softmax_and_strided_layout():
     assert_bf16(to_host(o), ref, "sharp softmax, strided")
 
 
+@pytest.mark.parametrize("out_f32,row", [(False, 64), (False, 72), (False, 136), (True, 64), (True, 68)])
+def test_sdpa_bf16_output_views(out_f32, row):
+    """The output written through a view whose rows are padded (row stride
+    `row` elements): the values match the oracle and nothing outside the view
+    is touched."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    B, h, L = 2, 2, 300
+    inp = workloads.make_sdpa_inputs(B, h, L, L, 64, "bf16", seed=row, causal=True)
+    q, k, v = (inp.tensors[n] for n in ("q", "k", "v"))
+    vls = np.array([300, 100], dtype=np.int32)
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    n = B * h * L * row
+    buf = torch.full((n,), float("nan"), dtype=dt, device="cuda")
+    out = buf.view(B, h, L, row)[..., :64]
+    mha.sdpa_forward(to_device(q, torch.bfloat16), to_device(k, torch.bfloat16), to_device(v, torch.bfloat16),
+                     valid_lens=vls, causal=True, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa(q, k, v, valid_lens=vls, causal=True)
+    assert_bf16(to_host(out), ref, f"output view row {row} f32 {out_f32}")
+    assert torch.isnan(buf.view(B, h, L, row)[..., 64:]).all(), "a store landed outside the output view"
+
+
+@pytest.mark.parametrize("out_f32,row,offset", [(False, 68, 0), (False, 64, 1), (True, 66, 0)])
+def test_sdpa_rejects_misaligned_output(out_f32, row, offset):
+    """Output rows that would not start 16-byte aligned are refused before
+    anything is enqueued, and the buffer is left as it was."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    from transformer_head_scaled_sdpa_amd._lib import MhaError
+    B, h, L = 1, 2, 40
+    x = torch.zeros((B, h, L, 64), dtype=torch.bfloat16, device="cuda")
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    n = B * h * L * row
+    buf = torch.full((n + 8,), float("nan"), dtype=dt, device="cuda")
+    out = buf[offset:offset + n].view(B, h, L, row)[..., :64]
+    with pytest.raises(MhaError, match="MHA_EINVAL"):
+        mha.sdpa_forward(x, x, x, causal=True, out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf).all()
+
+
 F32_CASES = [
     (2, 8, 10, 10, False, "random"),
     (1, 1, 1, 1, False, None),

@@ -42,6 +42,9 @@
 //    are evaluated only on the tiles that cross the diagonal or the valid
 //    length.  Workgroups are issued heaviest-first, and consecutive
 //    workgroup ids take different (batch, head) pairs.
+//  * The normalised output goes through LDS once the keys are done, so each
+//    row of 64 features leaves as whole 128-byte runs instead of 8- or
+//    16-byte pieces per lane.
 #include "common.h"
 #include "kernels.h"
 
@@ -322,25 +325,48 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
         slow_stage(s + 1, sc, sn, pb, pa, nk_e, nv_e);
     }
 
-    if (i >= a.Lq) return;
     const float inv = 1.0f / pair_sum(l);
-    // O^T element v of block tb: feature tb*32 + (v/4)*8 + hb*4 + v%4, query i.
-    char* ob = static_cast<char*>(a.o);
-    const long long orow = b * a.so[0] + hd * a.so[1] + (long long)i * a.so[2];
+    // O^T element v of block tb: feature tb*32 + (v/4)*8 + hb*4 + v%4, query
+    // i.  Every wave is past the last barrier, so the K/V buffers are idle:
+    // each wave stages 32 rows x 128 bytes of its output in its own slice
+    // (144-byte rows) and stores each row's 128 bytes as one run, 8 lanes per
+    // row; fp32 rows take two such rounds.  Output rows start 16-byte aligned
+    // (the entry points reject other pointers and strides).
+    constexpr int kEl = kOutF32 ? 4 : 2;           // bytes per output element
+    constexpr int kRounds = kOutF32 ? 2 : 1;
+    char* const o_s = reinterpret_cast<char*>(wave < 4 ? vbuf + wave * 32 * kLdsK : kbuf + (wave - 4) * 32 * kLdsK);
+    char* const orow0 = static_cast<char*>(a.o) + (b * a.so[0] + hd * a.so[1] + (long long)q0 * a.so[2]) * kEl;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+    for (int rd = 0; rd < kRounds; ++rd) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const int tt = tb * 32 + g4 * 8 + hb * 4;
-            float y[4];
+        for (int tb = 0; tb < 2; ++tb) {
+            if (kOutF32 && tb != rd) continue;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] = o[tb][g4 * 4 + e] * inv;
-            if (kOutF32) {
-                *reinterpret_cast<float4*>(ob + (orow + tt) * 4) = make_float4(y[0], y[1], y[2], y[3]);
-            } else {
-                *reinterpret_cast<uint2*>(ob + (orow + tt) * 2) =
-                    make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+            for (int g4 = 0; g4 < 4; ++g4) {
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = o[tb][g4 * 4 + e] * inv;
+                char* dst = o_s + l32 * kLdsK * 2 + (tb * 32 + g4 * 8 + hb * 4) * kEl - rd * 128;
+                if (kOutF32)
+                    *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+                else
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
             }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int r = pass * 8 + (lane >> 3), cb = (lane & 7) * 16;
+            if (q0 + r < a.Lq)
+                *reinterpret_cast<uint4*>(orow0 + (long long)r * a.so[2] * kEl + rd * 128 + cb) =
+                    *reinterpret_cast<const uint4*>(o_s + r * kLdsK * 2 + cb);
+        }
+        if (rd + 1 < kRounds) {   // the next round overwrites the slice
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
 }
