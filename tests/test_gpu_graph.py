@@ -106,3 +106,59 @@ def test_graph_sdpa_backward():
 
     _graph_check(make, lambda t: mha.sdpa_backward(t[0], t[1], t[2], t[3], t[4], causal=True,
                                                    out_dtype=torch.float32))
+
+
+def test_graph_sdpa_weights_per_query_lengths():
+    """The inspection path (weights exported) with one length per query."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    B, h, L = 2, 3, 150
+
+    def make(r):
+        qkv = [_rand((B, h, L, 64), 400 * r + i, torch.bfloat16) for i in range(3)]
+        rng = np.random.Generator(np.random.PCG64(40 + r))
+        vl = torch.from_numpy(rng.integers(0, L, size=(B, L), endpoint=True).astype(np.int32)).cuda()
+        return qkv + [vl]
+
+    _graph_check(make, lambda t: mha.sdpa_forward(t[0], t[1], t[2], valid_lens=t[3], return_weights=True))
+
+
+def test_graph_mha_forward_with_weights():
+    """mha_forward exporting the attention weights (projections to fp32 Q, K, V in the workspace)."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    B, L, D, h = 2, 96, 256, 4
+
+    def make(r):
+        x = _rand((B, L, D), 50 * r + 1, torch.bfloat16)
+        ws = [_rand((D, D), 50 * r + 2 + i, torch.bfloat16, D ** -0.5) for i in range(4)]
+        vl = torch.tensor([96, 40], dtype=torch.int32).roll(r).cuda()
+        return [x] + ws + [vl]
+
+    def call(t):
+        x, wq, wk, wv, wo, vl = t
+        return mha.mha_forward(x, x, wq, wk, wv, wo, h=h, valid_lens=vl, return_weights=True)
+
+    _graph_check(make, call)
+
+
+def test_graph_mha_sublayer():
+    """The pre-norm sublayer x + MHA(LayerNorm(x)): layer norm, attention and the
+    output projection with the residual."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    B, L, D, h = 4, 128, 512, 8
+
+    def make(r):
+        x = _rand((B, L, D), 60 * r + 1, torch.bfloat16)
+        ws = [_rand((D, D), 60 * r + 2 + i, torch.bfloat16, D ** -0.5) for i in range(4)]
+        g = _rand((D,), 60 * r + 7, torch.bfloat16, 0.1) + 1.0
+        bb = _rand((D,), 60 * r + 8, torch.bfloat16, 0.1)
+        vl = torch.tensor([128, 64, 1, 100], dtype=torch.int32).roll(r).cuda()
+        return [x] + ws + [g, bb, vl]
+
+    def call(t):
+        x, wq, wk, wv, wo, g, bb, vl = t
+        return mha.mha_sublayer_forward(x, wq, wk, wv, wo, h=h, ln_gain=g, ln_bias=bb, valid_lens=vl)
+
+    _graph_check(make, call)
