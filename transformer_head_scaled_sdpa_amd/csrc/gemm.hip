@@ -8,22 +8,24 @@
 // projection of self-attention is three problems over the same A.
 //
 // bf16 kernel: 128 x BN output tile per workgroup (BN = 128, or 64 when
-// 128-wide tiles would leave CUs without a tile), four wave64s in a 2 x 2 grid each
-// owning 64 x BN/2 through v_mfma_f32_32x32x16_bf16 with fp32 accumulators;
-// K in steps of 64.
+// 128-wide tiles would leave CUs without a tile), eight wave64s in a 4 x 2
+// grid each owning 32 x BN/2 through v_mfma_f32_32x32x16_bf16 with fp32
+// accumulators; K in steps of 64.
 //  * Operand tiles go from global memory straight into LDS
 //    (global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS, lane
 //    i at byte 16*i, so the per-lane source address decides the layout) in
 //    144-byte rows, the stride at which the 16-byte fragment reads are
 //    conflict-free; two LDS stages, one barrier per K step, the next step's
-//    loads in flight during the current step's MFMAs; two workgroups per CU.
+//    loads in flight during the current step's MFMAs; two workgroups per CU
+//    when the grid has more tiles than CUs, and two waves per SIMD even when
+//    it has fewer.
 //  * The MFMA computes the transposed block C^T = W A^T, so each lane ends up
 //    owning one output row and runs of four consecutive columns; the
 //    epilogue stages the fp32 tile in LDS with 16-byte writes and stores
 //    whole output rows with 16-byte coalesced stores.
-//  * Every wave keeps eight independent accumulators (its output blocks
-//    times a split of the K steps, summed at the end): an MFMA whose
-//    accumulator was written fewer than eight MFMAs earlier issues slower.
+//  * Every wave keeps four independent accumulators (its output blocks
+//    times a split of the K steps, summed at the end); with two or more
+//    waves per SIMD that re-use distance costs little.
 //  * Bias (and, for a residual sublayer, the residual input) is added in the
 //    epilogue.
 //
@@ -39,6 +41,7 @@ namespace mha {
 namespace {
 
 constexpr int kTM = 128, kTK = 64;
+constexpr int kGemmWaves = 8;                  // waves per workgroup of the bf16 GEMM
 constexpr int kLds = kTileLdsRow;              // bf16 per LDS row (144 B)
 constexpr int kRowBytes = kTileRowBytes;
 
@@ -93,13 +96,19 @@ __device__ __forceinline__ void add_bf16_row(float* y, const bf16_t* x) {
     }
 }
 
+// 8 waves per workgroup in a 4 x 2 grid over the tile: at most ~110 VGPRs,
+// so two workgroups (four waves per SIMD) share a CU when the grid has more
+// tiles than CUs, and a single workgroup still keeps two waves per SIMD.
 template <int kTN, bool kOutF32>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, int tiles_total, int per_xcd,
-                                                       int shared_a) {
+__global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, int tiles_total,
+                                                                   int per_xcd, int shared_a) {
+    constexpr int kWv = kGemmWaves, kThr = 64 * kWv;
+    constexpr int kRowsW = kTM / (kWv / 2);        // A rows per wave
+    constexpr int kMI = kRowsW / 32;               // 32-row blocks per wave
     constexpr int kABytes = kTM * kRowBytes, kWBytes = kTN * kRowBytes;
     constexpr int kStage = kABytes + kWBytes;
     constexpr int kNB = kTN / 64;                  // 32-wide column blocks per wave (2 or 1)
-    constexpr int kSplit = 4 / kNB;                // K-step split: 2 x kNB x kSplit = 8 accumulators
+    constexpr int kSplit = 4 / kNB;                // K-step split of the accumulators
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
 
     // XCD-aware order: ids x, x+8, x+16, ... run on XCD x; give them a
@@ -119,8 +128,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, 
 
     const bf16_t* A = static_cast<const bf16_t*>(P.a);
     const bf16_t* W = static_cast<const bf16_t*>(P.w);
-    LdsTileLoader<kTM, 4> la;
-    LdsTileLoader<kTN, 4> lw;
+    LdsTileLoader<kTM, kWv> la;
+    LdsTileLoader<kTN, kWv> lw;
     la.init(wave, lane, m0, M, K);
     lw.init(wave, lane, n0, N, K);
     auto issue = [&](int stage, int k0) {
@@ -129,8 +138,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, 
         lw.issue(W + k0, base + kABytes, wave);
     };
 
-    // acc[mi][ni][p]: A rows wm*64 + mi*32 .., W rows wn*kTN/2 + ni*32 .., K split p.
-    f32x16 acc[2][kNB][kSplit] = {};
+    // acc[mi][ni][p]: A rows wm*kRowsW + mi*32 .., W rows wn*kTN/2 + ni*32 .., K split p.
+    f32x16 acc[kMI][kNB][kSplit] = {};
     const int nk = K / kTK;
     issue(0, 0);
     for (int kt = 0; kt < nk; ++kt) {
@@ -143,22 +152,22 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, 
         const bf16_t* ws = reinterpret_cast<const bf16_t*>(smem + (kt & 1) * kStage + kABytes);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            bf16x8 fa[2], fw[kNB];
+            bf16x8 fa[kMI], fw[kNB];
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
-                fa[x] = *reinterpret_cast<const bf16x8*>(as + (wm * 64 + x * 32 + l32) * kLds + kk * 16 + hb * 8);
+            for (int x = 0; x < kMI; ++x)
+                fa[x] = *reinterpret_cast<const bf16x8*>(as + (wm * kRowsW + x * 32 + l32) * kLds + kk * 16 + hb * 8);
 #pragma unroll
             for (int x = 0; x < kNB; ++x)
                 fw[x] = *reinterpret_cast<const bf16x8*>(ws + (wn * (kTN / 2) + x * 32 + l32) * kLds + kk * 16 + hb * 8);
             const int p = kk % kSplit;
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
+            for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < kNB; ++ni) acc[mi][ni][p] = mfma32x32x16(fw[ni], fa[mi], acc[mi][ni][p]);
         }
     }
 
-    // Epilogue.  Block (mi, ni) element v is output row wm*64 + mi*32 + l32,
+    // Epilogue.  Block (mi, ni) element v is output row wm*kRowsW + mi*32 + l32,
     // column wn*kTN/2 + ni*32 + (v/4)*8 + hb*4 + v%4 of the tile: stage the
     // fp32 tile in LDS four columns at a time, then write whole rows with
     // 16-byte stores.
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, 
     __syncthreads();
     float* st = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < kNB; ++ni) {
             f32x16 y = acc[mi][ni][0];
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, 
             for (int p = 1; p < kSplit; ++p) y += acc[mi][ni][p];
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4)
-                *reinterpret_cast<float4*>(st + (wm * 64 + mi * 32 + l32) * kPitch + wn * (kTN / 2) + ni * 32 +
+                *reinterpret_cast<float4*>(st + (wm * kRowsW + mi * 32 + l32) * kPitch + wn * (kTN / 2) + ni * 32 +
                                            g4 * 8 + hb * 4) =
                     make_float4(y[g4 * 4], y[g4 * 4 + 1], y[g4 * 4 + 2], y[g4 * 4 + 3]);
         }
@@ -186,8 +195,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_nt(GemmArgs g, int tiles_n, 
     constexpr int kW = kOutF32 ? 4 : 8;            // columns per lane
     constexpr int kChunks = kTN / kW;              // lanes per tile row
 #pragma unroll
-    for (int j = 0; j < kTM * kChunks / 256; ++j) {
-        const int q = tid + 256 * j;
+    for (int j = 0; j < kTM * kChunks / kThr; ++j) {
+        const int q = tid + kThr * j;
         const int r = q / kChunks, c = (q % kChunks) * kW;
         const int m = m0 + r, n = n0 + c;
         if (m >= M || n >= N) continue;
@@ -217,12 +226,12 @@ hipError_t launch_bf16(const GemmArgs& g, bool out_f32, hipStream_t s, bool shar
     for (int p = 0; p < g.nprob; ++p) tiles += (long long)((g.p[p].M + kTM - 1) / kTM) * tiles_n;
     if (tiles == 0) return hipSuccess;
     const int per_xcd = (int)((tiles + 7) / 8);
-    const dim3 grid(8u * per_xcd);
+    const dim3 grid(8u * per_xcd), block(64 * kGemmWaves);
     if (out_f32)
-        hipLaunchKernelGGL((gemm_bf16_nt<kTN, true>), grid, dim3(256), 0, s, g, tiles_n, (int)tiles, per_xcd,
+        hipLaunchKernelGGL((gemm_bf16_nt<kTN, true>), grid, block, 0, s, g, tiles_n, (int)tiles, per_xcd,
                            (int)shared_a);
     else
-        hipLaunchKernelGGL((gemm_bf16_nt<kTN, false>), grid, dim3(256), 0, s, g, tiles_n, (int)tiles, per_xcd,
+        hipLaunchKernelGGL((gemm_bf16_nt<kTN, false>), grid, block, 0, s, g, tiles_n, (int)tiles, per_xcd,
                            (int)shared_a);
     return hipGetLastError();
 }
