@@ -1,14 +1,16 @@
-"""Benchmark: multi-head attention forward on one MI355X.
+"""Benchmark: scaled dot-product attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one full multi-head attention forward (Q/K/V projections, head
-split, masked softmax attention, head merge, output projection) over one
-batch of seeded synthetic input already resident in HBM.  Prints ONE JSON
-line: the attention throughput 4*B*h*Lq*Lk*d_k per step / step time, the
-roofline of the step's dominant kernel (duration from HIP events the library
-records on its launch stream), the fp64 CPU oracle timed on the host's cores,
-and the fused attention kernel on the long causal workload.
+The headline workload is the long causal attention core (B=4 h=16 L=4096
+d_k=64, bf16, Q/K/V given): a step is one sdpa_forward over it with inputs
+resident in HBM.  `value` is the algorithmic attention throughput (4*d_k
+flops per mask-allowed pair / step time); the literal 4*B*h*Lq*Lk*d_k rate is
+reported beside it as the dense equivalent.  Prints ONE JSON line with the
+dominant kernel's roofline (its duration from HIP events on the launch
+stream), the other four configurations (the MHA forward steps, each with its
+own dominant kernel's roofline), the NEXT-row paths, and the fp64 CPU oracle
+timed on the host's cores on a bounded sample of the headline workload.
 """
 import argparse
 import ctypes
@@ -391,19 +393,40 @@ def measured_traffic(kernel, workload):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle, untuned, on a bounded sample of the workload
 # ---------------------------------------------------------------------------
-def cpu_baseline(w, inp, budget_s=20.0):
+def sampled_alg_flops(w, valid_lens, rows):
+    """Algorithmic flops (4*d_k per allowed pair) of the given query rows of
+    every (batch, head)."""
+    vl = np.full(w.B, w.Lk) if valid_lens is None else np.asarray(valid_lens, dtype=np.int64)
+    pairs = 0
+    for v in vl:
+        lim = w.Lk if v <= 0 else min(int(v), w.Lk)
+        for i in rows:
+            pairs += w.Lk if v <= 0 else (min(int(i) + 1, lim) if w.causal else lim)
+    return 4 * w.d_k * w.h * pairs
+
+
+def cpu_baseline(w, inp, budget_s=15.0):
     import oracle
     t = inp.tensors
     n_threads = oracle.num_threads()
     if w.kind in ("sdpa", "decode"):
-        # sample query rows; every (batch, head) pair, all keys
-        rows = np.unique(np.linspace(0, w.Lq - 1, 16).astype(np.int32))
-        t0 = time.perf_counter()
-        oracle.sdpa(t["q"], t["k"], t["v"], valid_lens=inp.valid_lens, causal=w.causal, rows=rows)
-        dt = time.perf_counter() - t0
-        flops = 4 * w.B * w.h * len(rows) * w.Lk * w.d_k
+        # Query rows evenly spread over the sequence, every (batch, head),
+        # every key (the oracle computes every score as defined).  A first
+        # call on 16 rows sizes the sample to about the time budget.
+        def run(n):
+            rows = np.unique(np.linspace(0, w.Lq - 1, n).astype(np.int32))
+            t0 = time.perf_counter()
+            oracle.sdpa(t["q"], t["k"], t["v"], valid_lens=inp.valid_lens, causal=w.causal, rows=rows)
+            return rows, time.perf_counter() - t0
+        rows, dt = run(min(16, w.Lq))
+        n = int(min(w.Lq, max(16, 16 * budget_s / max(dt, 1e-6))))
+        if n > len(rows):
+            rows, dt = run(n)
+        flops = sampled_alg_flops(w, inp.valid_lens, rows)
         return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": n_threads, "kind": "oracle",
-                "sample": f"{len(rows)} query rows of every (batch, head), all {w.Lk} keys; {dt:.2f} s"}
+                "sample": f"{len(rows)} of {w.Lq} query rows (evenly spaced) of every (batch, head), all {w.Lk} "
+                          f"keys; {dt:.2f} s; rate counts the {flops / 1e9:.2f} GFLOP of mask-allowed pairs "
+                          f"in the sample (4*d_k per pair), as the GPU value does"}
     # MHA: whole batches, all rows.  Time one batch, then as many batches as
     # fit the budget (at most the whole workload).
     def run(nb):
@@ -417,61 +440,32 @@ def cpu_baseline(w, inp, budget_s=20.0):
     fit = int(min(w.B, max(1, budget_s // max(dt, 1e-6))))
     if fit > 1:
         nb, dt = fit, run(fit)
-    # When the whole workload takes well under the budget, repeat it (about
-    # half the budget in total) and report the mean.
     reps = 1
     if nb == w.B and dt < budget_s / 4:
         reps = int(max(1, (budget_s / 2) // max(dt, 1e-6)))
         dt = sum(run(nb) for _ in range(reps)) / reps
-    flops = 4 * nb * w.h * w.Lq * w.Lk * w.d_k
+    vl = None if inp.valid_lens is None else inp.valid_lens[:nb]
+    sub = workloads.Workload(w.name, w.kind, w.dtype, nb, w.Lq, w.Lk, w.h, w.d_k, w.causal, w.vl_range)
+    flops = 4 * w.d_k * allowed_pairs(sub, vl)
     rep_txt = f", mean of {reps} runs" if reps > 1 else ""
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": n_threads, "kind": "oracle",
-            "sample": f"{nb} of {w.B} batches, full MHA forward (projections included); {dt:.2f} s per run{rep_txt}"}
+            "sample": f"{nb} of {w.B} batches, full MHA forward (projections included); {dt:.2f} s per run"
+                      f"{rep_txt}; rate counts the mask-allowed attention pairs (4*d_k each)"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="encoder_self", choices=sorted(workloads.BY_NAME))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-long-sdpa", action="store_true", help="skip the long causal attention kernel line")
-    ap.add_argument("--repeat", type=int, default=10,
-                    help="back-to-back launches per event pair when timing kernels (default 10)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run 1 GiB copy kernels (for scaling memory counters)")
-    args = ap.parse_args()
+HEADLINE = "sdpa_long_causal"
+CONFIGS = ["mha_f32_tiny", "encoder_self", "decoder_causal", "enc_dec_source", "sdpa_long_causal"]
 
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
-              file=sys.stderr)
-        sys.exit(2)
 
-    import torch
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    torch.cuda.set_device(0)
-
-    if args.copy_calibration:
-        copy_calibration()
-
-    w = workloads.BY_NAME[args.workload]
-    inp = workloads.make_inputs(w)
+def measure_workload(w, inp, steps, warmup, repeat, cold=True):
+    """Time one workload's step and its kernels; returns a dict with the step
+    time, algorithmic rates and each kernel's roofline (the dominant one with
+    the measured HBM traffic when the profiled sources still match)."""
     in_b = 2 if w.dtype == "bf16" else 4
     mfma_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    log(f"workload {w.name}: {w.description}")
-
     fn = {"mha": PreparedMha, "sdpa": PreparedSdpa, "decode": PreparedDecode}[w.kind](inp)
-    ms, wall_ms = time_steps(fn, args.steps, args.warmup)
-    cold_ms = time_steps_cold(fn, 20)
-    attn_flops = w.attention_flops()
-    value = attn_flops / (ms * 1e-3) / 1e12
-    log(f"step {ms * 1e3:.2f} us (wall {wall_ms * 1e3:.2f} us)")
-
-    # per-kernel durations and the dominant kernel's roofline
-    kt = kernel_times(fn, max(1, args.steps // args.repeat), args.repeat)
+    ms, wall_ms = time_steps(fn, steps, warmup)
+    kt = kernel_times(fn, max(1, steps // repeat), repeat)
     kernels = {}
     M_q, M_kv = w.B * w.Lq, w.B * w.Lk
     for name, kms in kt.items():
@@ -490,119 +484,171 @@ def main():
         kernels[name] = {"avg_us": round(kms * 1e3, 3), "alg_flops": f, "alg_bytes": b,
                          "roofline": roofline(f, b, kms, mfma_peak)}
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
+    alg_attn = 4 * w.d_k * allowed_pairs(w, inp.valid_lens)
+    out = {"workload": w.description, "name": w.name, "dtype": w.dtype, "ms_per_step": round(ms, 6),
+           "wall_ms_per_step": round(wall_ms, 6),
+           "attention_alg_tflops": round(alg_attn / (ms * 1e-3) / 1e12, 3),
+           "attention_dense_equiv_tflops": round(w.attention_flops() / (ms * 1e-3) / 1e12, 3),
+           "kernels": {n: {"avg_us": k["avg_us"], "roofline_frac": k["roofline"]["frac"],
+                           "bound": k["roofline"]["bound"]} for n, k in kernels.items()}}
     rl = dict(kernels[dom]["roofline"])
     rl["kernel"] = dom
     rl["traffic"] = measured_traffic(dom, w.name)
     rl["alg_per_launch"] = {"flops": kernels[dom]["alg_flops"], "bytes": kernels[dom]["alg_bytes"]}
+    out["roofline"] = rl
+    if w.kind == "mha":
+        proj = 2 * w.d_model * w.d_model * w.B * (2 * w.Lq + 2 * w.Lk)
+        out["mha_total"] = {"flops_per_step": int(proj + alg_attn),
+                            "tflops": round((proj + alg_attn) / (ms * 1e-3) / 1e12, 3),
+                            "frac_peak": round((proj + alg_attn) / (ms * 1e-3) / 1e12 / mfma_peak, 4),
+                            "note": "projections Q, K, V, W_O (dense) plus the allowed attention pairs"}
+    if cold:
+        cold_ms = time_steps_cold(fn, 20)
+        out["cold_cache_ms_per_step"] = round(cold_ms, 6)
+    del fn
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(workloads.BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline workload (no other configs, no NEXT-row lines)")
+    ap.add_argument("--repeat", type=int, default=10,
+                    help="back-to-back launches per event pair when timing kernels (default 10)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run 1 GiB copy kernels (for scaling memory counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        copy_calibration()
+
+    w = workloads.BY_NAME[args.workload]
+    inp = workloads.make_inputs(w)
+    mfma_peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    log(f"workload {w.name}: {w.description}")
+    head = measure_workload(w, inp, args.steps, args.warmup, args.repeat)
+    ms = head["ms_per_step"]
+    alg_attn = 4 * w.d_k * allowed_pairs(w, inp.valid_lens)
+    value = alg_attn / (ms * 1e-3) / 1e12
+    log(f"step {ms * 1e3:.2f} us: {value:.1f} TFLOP/s algorithmic ({100 * value / mfma_peak:.1f}% of peak)")
 
     result = {
-        "metric": "attention TFLOP/s (4*B*h*Lq*Lk*d_k per step / step time) and % of MI355X bf16 MFMA peak",
+        "metric": "attention TFLOP/s (4*B*h*Lq*Lk*d_k) and % of MI355X bf16 MFMA peak",
         "value": round(value, 3),
         "unit": "TFLOP/s",
+        "value_basis": "algorithmic: 4*d_k flops per mask-allowed (batch, head, query, key) pair per step / "
+                       "step time (the literal 4*B*h*Lq*Lk*d_k count is reported as dense_equivalent)",
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
+        "dense_equivalent": {"flops_per_step": w.attention_flops(),
+                             "tflops": head["attention_dense_equiv_tflops"],
+                             "pct_bf16_peak": round(100 * head["attention_dense_equiv_tflops"] / PEAK_BF16_TFLOPS, 3)},
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 6),
+        "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded numpy PCG64; Xavier-uniform weights, zero bias)",
+        "data": "synthetic (seeded numpy PCG64; N(0,1) inputs, Xavier-uniform weights, zero bias)",
         "config": {"workload": w.description, "name": w.name, "B": w.B, "Lq": w.Lq, "Lk": w.Lk,
                    "d_model": w.d_model, "h": w.h, "d_k": w.d_k, "causal": w.causal,
                    "valid_lens": None if w.vl_range is None else f"U{{{w.vl_range[0]}..{w.vl_range[1]}}}",
-                   "attention_flops_per_step": attn_flops},
-        "kernels": {n: {"avg_us": k["avg_us"], "roofline_frac": k["roofline"]["frac"],
-                        "bound": k["roofline"]["bound"]} for n, k in kernels.items()},
-        "roofline": rl,
-        "cold_cache": {"ms_per_step": round(cold_ms, 6), "value": round(attn_flops / (cold_ms * 1e-3) / 1e12, 3),
+                   "attention_alg_flops_per_step": int(alg_attn)},
+        "kernels": head["kernels"],
+        "roofline": head["roofline"],
+        "cold_cache": {"ms_per_step": head["cold_cache_ms_per_step"],
                        "note": "512 MiB streamed before each of 20 steps; events bracket the step only"},
     }
-    # Beside the literal formula: the attention flops the masks allow
-    # (4 * d_k per allowed pair) and, for the multi-head layer, the whole
-    # step's work with the projections (Q over all queries, K and V over the
-    # keys, W_O over all queries).
-    alg_attn = 4 * w.d_k * allowed_pairs(w, inp.valid_lens)
-    result["attention_alg"] = {"flops_per_step": int(alg_attn),
-                               "tflops": round(alg_attn / (ms * 1e-3) / 1e12, 3),
-                               "frac_bf16_peak": round(alg_attn / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    if w.kind == "mha":
-        proj = 2 * w.d_model * w.d_model * w.B * (2 * w.Lq + 2 * w.Lk)
-        result["mha_total"] = {"flops_per_step": int(proj + alg_attn),
-                               "tflops": round((proj + alg_attn) / (ms * 1e-3) / 1e12, 3),
-                               "frac_peak": round((proj + alg_attn) / (ms * 1e-3) / 1e12 / mfma_peak, 4),
-                               "note": "projections Q, K, V, W_O (dense) plus the allowed attention pairs"}
+    if "mha_total" in head:
+        result["mha_total"] = head["mha_total"]
 
-    if not args.no_long_sdpa and w.name != "sdpa_long_causal":
-        lw = workloads.BY_NAME["sdpa_long_causal"]
-        linp = workloads.make_inputs(lw)
-        sf = PreparedSdpa(linp)
-        sms, _ = time_steps(sf, 50, 20)
-        f, b = sdpa_alg(lw, None, 2, 2)
-        result["sdpa_long_causal"] = {
-            "workload": lw.description, "avg_us": round(sms * 1e3, 2),
-            "alg_tflops": round(f / (sms * 1e-3) / 1e12, 2),
-            "dense_equiv_tflops": round(lw.attention_flops() / (sms * 1e-3) / 1e12, 2),
-            "frac_bf16_peak_alg": round(f / (sms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        del sf
-
-    if not args.no_long_sdpa and w.name != "decode_step":
-        dw = workloads.BY_NAME["decode_step"]
-        dinp = workloads.make_inputs(dw)
-        df = PreparedDecode(dinp)
-        dms, _ = time_steps(df, 200, 20)
-        f, b = decode_alg(dw, dinp.valid_lens)
-        result["decode_step"] = {
-            "workload": dw.description, "avg_us": round(dms * 1e3, 2),
-            "alg_GBs": round(b / (dms * 1e-3) / 1e9, 1),
-            "frac_hbm_peak": round(b / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        del df
-
-    if not args.no_long_sdpa and w.kind == "mha" and w.dtype == "bf16" and w.self_attn:
-        sf = PreparedSublayer(inp)
-        sms, _ = time_steps(sf, args.steps, args.warmup)
-        result["mha_sublayer"] = {
-            "workload": w.description + ", as the pre-norm residual sublayer x + MHA(LayerNorm(x))",
-            "ms_per_step": round(sms, 6), "value": round(attn_flops / (sms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
-            "vs_plain_step": round(sms / ms, 3)}
-        del sf
-
-    if not args.no_long_sdpa:
-        # backward: algorithmic 8*d_k flops per allowed pair (the four
-        # gradient products dv, dp, dq, dk; the recomputed scores not counted)
-        bw = workloads.BY_NAME["backward_causal"]
-        binp = workloads.make_inputs(bw)
-        bf = PreparedBackward(binp)
-        bms, _ = time_steps(bf, 10, 3)
-        pairs = allowed_pairs(bw, binp.valid_lens)
-        bfl = 8 * bw.d_k * pairs
-        result["sdpa_backward"] = {
-            "workload": bw.description, "avg_us": round(bms * 1e3, 2),
-            "alg_tflops": round(bfl / (bms * 1e-3) / 1e12, 2),
-            "frac_bf16_mfma_peak": round(bfl / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "bound": "mfma"}
-        del bf
-        # inspection path: the weights written (fp32) plus q, k, v read and o
-        # written; on bf16 MFMA the scores run twice (2 * 2 * d_k flops per
-        # allowed pair) and P.V once with P as two bf16 terms (2 * 2 * d_k)
-        iw = workloads.BY_NAME["inspect_weights"]
-        iinp = workloads.make_inputs(iw)
-        wf = PreparedWeights(iinp)
-        wms, _ = time_steps(wf, 10, 3)
-        wbytes = iw.B * iw.h * (iw.Lq * iw.Lk * 4 + (2 * iw.Lq + 2 * iw.Lk) * iw.d_k * 2)
-        wfl = 8 * iw.d_k * allowed_pairs(iw, iinp.valid_lens)
-        result["sdpa_weights"] = {
-            "workload": iw.description, "avg_us": round(wms * 1e3, 2), "bound": "hbm",
-            "GBs": round(wbytes / (wms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(wbytes / (wms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "mfma_tflops": round(wfl / (wms * 1e-3) / 1e12, 2),
-            "frac_bf16_mfma_peak": round(wfl / (wms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        del wf
+    if not args.no_extras:
+        # The other configurations, each with its own dominant kernel's roofline.
+        result["configs"] = {}
+        for name in CONFIGS:
+            if name == w.name:
+                continue
+            cw = workloads.BY_NAME[name]
+            log(f"config {name} ...")
+            result["configs"][name] = measure_workload(cw, workloads.make_inputs(cw), 50, 10, args.repeat,
+                                                       cold=False)
+        extras(result, args, w)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(w, inp)
 
     print(json.dumps(result), flush=True)
+
+
+def extras(result, args, w):
+    """The NEXT rows: decoding step, backward, inspection path, sublayer."""
+    dw = workloads.BY_NAME["decode_step"]
+    dinp = workloads.make_inputs(dw)
+    df = PreparedDecode(dinp)
+    dms, _ = time_steps(df, 200, 20)
+    f, b = decode_alg(dw, dinp.valid_lens)
+    result["decode_step"] = {
+        "workload": dw.description, "avg_us": round(dms * 1e3, 2),
+        "alg_GBs": round(b / (dms * 1e-3) / 1e9, 1),
+        "frac_hbm_peak": round(b / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del df
+
+    ew = workloads.BY_NAME["encoder_self"]
+    einp = workloads.make_inputs(ew)
+    sf = PreparedSublayer(einp)
+    sms, _ = time_steps(sf, 100, 10)
+    result["mha_sublayer"] = {
+        "workload": ew.description + ", as the pre-norm residual sublayer x + MHA(LayerNorm(x))",
+        "ms_per_step": round(sms, 6)}
+    del sf
+
+    # backward: algorithmic 8*d_k flops per allowed pair (the four gradient
+    # products dv, dp, dq, dk; the recomputed scores not counted)
+    bw = workloads.BY_NAME["backward_causal"]
+    binp = workloads.make_inputs(bw)
+    bf = PreparedBackward(binp)
+    bms, _ = time_steps(bf, 20, 5)
+    pairs = allowed_pairs(bw, binp.valid_lens)
+    bfl = 8 * bw.d_k * pairs
+    result["sdpa_backward"] = {
+        "workload": bw.description, "avg_us": round(bms * 1e3, 2),
+        "alg_tflops": round(bfl / (bms * 1e-3) / 1e12, 2),
+        "frac_bf16_mfma_peak": round(bfl / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "bound": "mfma",
+        "note": "8*d_k flops per allowed pair (dV, dP, dQ, dK products); recomputed scores not counted"}
+    del bf
+
+    # inspection path: HBM-bound on the fp32 weights it writes; its matrix
+    # work counted as the forward's algorithmic 4*d_k per allowed pair
+    iw = workloads.BY_NAME["inspect_weights"]
+    iinp = workloads.make_inputs(iw)
+    wf = PreparedWeights(iinp)
+    wms, _ = time_steps(wf, 20, 5)
+    wbytes = iw.B * iw.h * (iw.Lq * iw.Lk * 4 + (2 * iw.Lq + 2 * iw.Lk) * iw.d_k * 2)
+    wfl = 4 * iw.d_k * allowed_pairs(iw, iinp.valid_lens)
+    result["sdpa_weights"] = {
+        "workload": iw.description, "avg_us": round(wms * 1e3, 2), "bound": "hbm",
+        "GBs": round(wbytes / (wms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(wbytes / (wms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "alg_tflops": round(wfl / (wms * 1e-3) / 1e12, 2),
+        "note": "bytes: fp32 weights written plus q, k, v read and o written; tflops: 4*d_k per allowed pair"}
+    del wf
 
 
 if __name__ == "__main__":

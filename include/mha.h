@@ -34,7 +34,12 @@
  *   - Errors: MHA_EINVAL (null required pointer, negative or inconsistent
  *     sizes, d_model != h * d_k, causal with Lq != Lk, misaligned pointers or
  *     strides, output aliasing an input); MHA_ENOTSUP (d_k or d_v other than
- *     64, an unsupported dtype pair); MHA_EWORKSPACE (workspace too small);
+ *     64, an unsupported dtype pair, or sizes past the kernels' 32-bit
+ *     offsets: an activation operand of mha_forward / mha_forward_ex /
+ *     mha_sublayer_forward with B * L * d_model >= 2^31 elements, a row
+ *     stride of sdpa_forward with 128 rows >= 2^31 bytes, or, on the bf16
+ *     backward and weights paths, one (batch, head)'s rows spanning >= 2^31
+ *     bytes); MHA_EWORKSPACE (workspace too small);
  *     MHA_EHIP (the HIP runtime reported an error when enqueuing).  Faults of
  *     the device itself surface when the caller synchronises the stream.
  *   - dtypes: MHA_F32 computes in fp32 throughout (FMA, no reduced
@@ -309,18 +314,23 @@ mha_status mha_sublayer_forward(mha_dtype in_dt, mha_dtype out_dt,
 const char* mha_status_string(mha_status s);
 
 /*
- * Kernel timing (observability).  mha_timing_enable(repeat) with repeat in
- * 1..1000 turns it on: every kernel the library enqueues is then launched
- * `repeat` times in a row, bracketed by one pair of HIP events recorded on the
- * same stream (each kernel is a pure function of its inputs, so the results
- * are unchanged; repeat > 1 amortises the gaps the events themselves add).
- * repeat = 0 turns it off; other values return MHA_EINVAL.
- * mha_timing_read() waits for the recorded events, adds their elapsed times
- * per kernel name into `total_ms` and the number of launches into `count`
- * (up to `max` entries, names are static strings) and returns the number of
- * entries written; it also clears the record.  Returns -1 on a HIP error.
- * Event pairs beyond the library's fixed pool (4096 pairs) are not recorded.
- * Not thread-safe.
+ * Kernel timing (a profiling instrument; not part of the attention path).
+ * It is the one piece of library state, and it exists only on a thread that
+ * turns it on: mha_timing_enable(repeat) with repeat in 1..1000 creates that
+ * thread's own pool of 4096 HIP event pairs (on its first call) and turns
+ * timing on for calls made from that thread only.  Every kernel such a call
+ * enqueues is then launched `repeat` times in a row, bracketed by one pair of
+ * events recorded on the same stream (each kernel is a pure function of its
+ * inputs, so results are unchanged; repeat > 1 amortises the gaps the events
+ * themselves add).  repeat = 0 turns it off for the thread; other values
+ * return MHA_EINVAL; MHA_EHIP if the events cannot be created.
+ * mha_timing_read() waits for the thread's recorded events, adds their
+ * elapsed times per kernel name into `total_ms` and the number of launches
+ * into `count` (up to `max` entries, names are static strings), returns the
+ * number of entries written and clears the record; -1 on a HIP error.
+ * Event pairs beyond the pool are not recorded.  With timing off (the
+ * default) the entry points keep no state and may be called from any number
+ * of threads at once.  The pool lives until the process ends.
  */
 mha_status mha_timing_enable(int repeat);
 int mha_timing_read(const char** names, double* total_ms, int* count, int max);

@@ -17,8 +17,8 @@
  *       (same section: view to [B, L, h, d_k] then transpose to [B, h, L, d_k])
  *   s_ij = (q_i . k_j) / sqrt(d_k)          (The Annotated Transformer,
  *       "Attention" section; d_k is the per-head width of the query)
- *   masked entries are REPLACED by -1e9 after scaling (same section:
- *       masked_fill(mask == 0, -1e9))
+ *   the score of a masked pair is REPLACED by -1e9 after scaling (same
+ *       section: the mask fills the scaled scores with that constant)
  *   p_i = softmax over the key axis, o_i = sum_j p_ij v_j   (same section)
  *   merge heads back to [B, L, h*d_v], then out = Ocat Wo^T + bo
  *       ("Transformer" study notes, multi-head attention: Concat(head_1..h) W^O)

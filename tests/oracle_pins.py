@@ -379,19 +379,20 @@ def pin_backward_matches_finite_differences():
 
 
 def pin_backward_matches_torch_float64_autograd():
-    """torch's float64 CPU autograd through the pages' printed attention
-    (scores, masked_fill with -1e9, softmax, product with V)."""
+    """torch's float64 CPU autograd through its own fused attention
+    (scaled_dot_product_attention, default 1/sqrt(d) scale) with a boolean
+    key mask.  Every row here keeps at least one allowed key, where excluding
+    a key and filling its score with -1e9 give the same weights."""
     import torch
+    import torch.nn.functional as F
     r = _rng(52)
     B, h, Lq, Lk, d = 2, 3, 5, 6, 4
     q, k, v = (r.standard_normal(s) for s in ((B, h, Lq, d), (B, h, Lk, d), (B, h, Lk, d)))
     g = r.standard_normal((B, h, Lq, d))
     vl = np.array([4, 6], np.int32)
     tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
-    sc = torch.matmul(tq, tk.transpose(-2, -1)) / math.sqrt(d)
-    allowed = torch.arange(Lk)[None, None, None, :] < torch.tensor(vl)[:, None, None, None]
-    sc = sc.masked_fill(~allowed, -1e9)
-    o = torch.matmul(torch.softmax(sc, dim=-1), tv)
+    keep = torch.arange(Lk)[None, None, None, :] < torch.tensor(vl)[:, None, None, None]
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=keep.expand(B, h, Lq, Lk))
     (o * torch.tensor(g)).sum().backward()
     for a, b in zip(oracle.sdpa_backward(q, k, v, g, valid_lens=vl), (tq.grad, tk.grad, tv.grad)):
         _close(a, b.numpy(), 1e-12)

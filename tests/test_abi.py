@@ -75,6 +75,20 @@ def test_sdpa_validation(lib):
     assert sdpa(lib, q=ctypes.c_void_p(P + 8)) == EINVAL         # misaligned pointer
     assert sdpa(lib, sq=S(4 * 128 * 64, 128 * 64, 60)) == EINVAL  # stride not a multiple of 8
     assert sdpa(lib, o=ALIGNED[0]) == EINVAL         # output overlaps q
+    # 128 rows of a row stride must span fewer than 2^31 bytes (32-bit
+    # per-lane tile offsets): 2^23 bf16 elements is the first that does not.
+    assert sdpa(lib, sq=S(0, 0, 1 << 23)) == ENOTSUP
+    assert sdpa(lib, so=S(0, 0, 1 << 23)) == ENOTSUP
+
+
+def test_mha_size_limit(lib):
+    # Activations of 2^31 elements or more are refused before any pointer is
+    # used (32-bit element offsets inside the kernels' tiles).
+    # 2 * 2^20 * 512 = 2^30 elements fit; the fake buffers 1 MiB apart then
+    # overlap, which is the error reported.
+    assert mha(lib, B=2, Lq=1 << 20, Lk=16) == EINVAL
+    assert mha(lib, B=4, Lq=1 << 20, Lk=16) == ENOTSUP     # 2^31 elements
+    assert mha(lib, B=4, Lq=16, Lk=1 << 20) == ENOTSUP
 
 
 def mha(lib, **kw):

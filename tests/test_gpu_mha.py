@@ -67,6 +67,27 @@ def test_mha_bf16_vs_oracle(B, Lq, Lk, D, h, causal, vlr, bias, self_attn, out_f
     print("vs fp64 oracle", e, "vs bf16-storage oracle", errors(g, run_oracle(inp, bf16_stages=True)))
 
 
+# More than one 256-query block without the causal rule, and more than four
+# 128-key chunks, with ragged key lengths that include 0 (a fully masked
+# sequence) and the full length.
+MULTI_BLOCK_CASES = [
+    # B, Lq, Lk, D, h, self_attn, lengths
+    (3, 600, 600, 128, 2, True, [0, 600, 333]),
+    (3, 300, 700, 256, 4, False, [700, 0, 517]),
+    (2, 513, 513, 192, 3, True, [513, 257]),
+]
+
+
+@pytest.mark.parametrize("B,Lq,Lk,D,h,self_attn,lens", MULTI_BLOCK_CASES)
+def test_mha_bf16_multi_block_ragged(B, Lq, Lk, D, h, self_attn, lens):
+    inp = workloads.make_mha_inputs(B, Lq, Lk, D, h, "bf16", seed=7000 + Lq + Lk, vl_range=(1, Lk),
+                                    causal=False, self_attn=self_attn, bias=True)
+    inp.valid_lens = np.array(lens, dtype=np.int32)
+    g = run_gpu(inp, True)
+    e = assert_bf16(g, run_oracle(inp, bf16_stages=False), f"mha bf16 B{B} Lq{Lq} Lk{Lk} lengths {lens}")
+    print("vs fp64 oracle", e)
+
+
 MHA_F32_CASES = [
     (2, 10, 10, 512, 8, False, (3, 10), False, True),
     (2, 33, 45, 256, 4, False, (0, 45), True, False),

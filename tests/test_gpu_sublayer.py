@@ -1,7 +1,8 @@
 """GPU parity of mha_sublayer_forward, the pre-norm residual sublayer
-x + MHA(norm(x), ...), against the fp64 oracle (both printed LayerNorm
-forms; the normalisation fused into the attention kernel for bf16
-self-attention with L <= 128, a row-wise kernel otherwise)."""
+x + MHA(norm(x), ...), against the fp64 oracle, in both printed LayerNorm
+forms.  The normalisation is a row-wise kernel that writes norm(x) to the
+workspace before the attention layer runs on it; the residual add is fused
+into the output projection's epilogue."""
 import numpy as np
 import pytest
 

@@ -1,34 +1,67 @@
-"""Build libmha.so (the gfx950 HIP attention library) in-tree with hipcc."""
+"""Build libmha.so (the gfx950 HIP attention library) in-tree with hipcc.
+
+Each translation unit is compiled to an object in parallel (``_build/``),
+then the objects are linked into one shared library.
+"""
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmha.so")
-SOURCES = ["api.hip", "sdpa_bf16_pipe.hip", "mha_fused.hip", "mha_fused_small.hip", "sdpa_decode.hip", "sdpa_weights.hip", "sdpa_weights_mfma.hip", "sdpa_backward.hip", "sdpa_backward_mfma.hip", "layer_norm.hip", "sdpa_f32.hip", "gemm.hip"]
+SOURCES = ["api.hip", "sdpa_bf16_pipe.hip", "mha_fused.hip", "mha_fused_small.hip", "sdpa_decode.hip",
+           "sdpa_weights.hip", "sdpa_weights_mfma.hip", "sdpa_backward.hip", "sdpa_backward_mfma.hip",
+           "layer_norm.hip", "sdpa_f32.hip", "gemm.hip"]
 
 # Packed fp32 VALU ops are disabled for every HIP translation unit.
 # -fno-honor-nans: inputs are finite, so max/min need not quiet signalling
 # NaNs (otherwise every fmaxf operand gets an extra canonicalising v_max);
 # infinities keep their meaning (masked scores are -inf).
-HIP_FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+HIP_FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-fno-honor-nans", "-Wall", "-Wno-unused-function"]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = ["hipcc"] + HIP_FLAGS + srcs + ["-o", LIB + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # hipcc's host pass does not know the packed-fp32 feature name and says so; drop that line.
     out = "\n".join(l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l)
+    return proc.returncode, out
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
+    cmds = []
+    for s in SOURCES:
+        obj = os.path.join(OBJ, s.replace(".hip", ".o"))
+        cmds.append(["hipcc"] + HIP_FLAGS + ["-c", os.path.join(CSRC, s), "-o", obj])
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_run, cmds))
+    failed = False
+    for (rc, out), c in zip(results, cmds):
+        if out.strip():
+            print(out, file=sys.stderr)
+        if rc != 0:
+            failed = True
+            print(f"hipcc failed ({rc}): {' '.join(c)}", file=sys.stderr)
+    if failed:
+        raise RuntimeError("hipcc failed")
+    link = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC"] + [c[c.index("-o") + 1] for c in cmds] + \
+           ["-o", LIB + ".tmp"]
+    if verbose:
+        print(" ".join(link), flush=True)
+    rc, out = _run(link)
     if out.strip():
         print(out, file=sys.stderr)
-    if proc.returncode != 0:
-        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
+    if rc != 0:
+        raise RuntimeError(f"hipcc link failed with exit code {rc}")
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

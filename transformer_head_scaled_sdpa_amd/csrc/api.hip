@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <new>
+
 #include "../../include/mha.h"
 #include "common.h"
 #include "kernels.h"
@@ -41,35 +43,48 @@ bool rows_fit_buffer(long long row_stride, int L, size_t elem) {
     return L <= 0 || (long long)(L - 1) * row_stride * (long long)elem + kHeadDim * (long long)elem < (1ll << 31);
 }
 
+// The split-head kernels add 32-bit per-lane byte offsets of up to 128 rows
+// to a tile's base address.
+bool tile_rows_fit(long long row_stride, size_t elem) { return row_stride * 128 * (long long)elem < (1ll << 31); }
+
+// The multi-head kernels index the [rows, d_model] activations with 32-bit
+// element offsets inside a tile and compute row indices as int: each operand
+// must hold fewer than 2^31 elements.
+bool mha_rows_fit(int B, int L, int d_model) { return (long long)B * L * d_model < (1ll << 31); }
+
 // ---------------------------------------------------------------------------
-// kernel timing: a fixed pool of HIP event pairs recorded around launches
+// kernel timing (a profiling instrument, off unless the calling thread turns
+// it on): a pool of HIP event pairs recorded around launches.  The state is
+// per thread and created only by mha_timing_enable, so with timing off an
+// entry point reads one null thread-local pointer and keeps no state, and
+// threads never share a pool.
 // ---------------------------------------------------------------------------
 constexpr int kPool = 4096;
 struct TimingState {
     bool on = false;
     int repeat = 1;      // launches of the kernel inside one event pair
     int used = 0;
-    bool created = false;
     hipEvent_t ev[2 * kPool];
     const char* name[kPool];
 };
-TimingState g_timing;
+thread_local TimingState* t_timing = nullptr;
 
 template <typename F>
 hipError_t timed(const char* name, hipStream_t s, F&& launch) {
-    if (!g_timing.on || g_timing.used >= kPool) return launch();
-    const int k = g_timing.used++;
-    g_timing.name[k] = name;
-    hipError_t e = hipEventRecord(g_timing.ev[2 * k], s);
+    TimingState* t = t_timing;
+    if (!t || !t->on || t->used >= kPool) return launch();
+    const int k = t->used++;
+    t->name[k] = name;
+    hipError_t e = hipEventRecord(t->ev[2 * k], s);
     if (e != hipSuccess) return e;
     // Every kernel here is a pure function of its inputs, so repeating it
     // leaves the result unchanged; the pair then times `repeat` back-to-back
     // launches and the per-launch average excludes the events' own gaps.
-    for (int r = 0; r < g_timing.repeat; ++r) {
+    for (int r = 0; r < t->repeat; ++r) {
         e = launch();
         if (e != hipSuccess) return e;
     }
-    return hipEventRecord(g_timing.ev[2 * k + 1], s);
+    return hipEventRecord(t->ev[2 * k + 1], s);
 }
 
 mha_status hip_status(hipError_t e) { return e == hipSuccess ? MHA_OK : MHA_EHIP; }
@@ -119,6 +134,8 @@ mha_status sdpa_impl(mha_dtype in_dt, mha_dtype out_dt,
         if (s.b < 0 || s.h < 0 || s.l < 0 || s.b % mult || s.h % mult || s.l % mult) return MHA_EINVAL;
     if (so.b < 0 || so.h < 0 || so.l < 0 || so.b % omult || so.h % omult || so.l % omult) return MHA_EINVAL;
     const size_t ie = elem_size(in_dt), oe = elem_size(out_dt);
+    if (!tile_rows_fit(sq.l, ie) || !tile_rows_fit(sk.l, ie) || !tile_rows_fit(sv.l, ie) || !tile_rows_fit(so.l, oe))
+        return MHA_ENOTSUP;
     const Range ro = view_range(o, so, B, h, Lq, d_v, oe);
     const Range rq = view_range(q, sq, B, h, Lq, d_k, ie), rk = view_range(k, sk, B, h, Lk, d_k, ie),
                 rv = view_range(v, sv, B, h, Lk, d_v, ie);
@@ -357,6 +374,7 @@ mha_status mha_impl(mha_dtype in_dt, mha_dtype out_dt,
     if (d_k != kHeadDim) return MHA_ENOTSUP;
     if (in_dt == MHA_F32 && out_dt != MHA_F32) return MHA_ENOTSUP;
     if (B == 0 || Lq == 0) return MHA_OK;
+    if (!mha_rows_fit(B, Lq, d_model) || !mha_rows_fit(B, Lk, d_model)) return MHA_ENOTSUP;
     if (!x_q || !x_kv || !w_q || !w_k || !w_v || !w_o || !out || !workspace) return MHA_EINVAL;
     const void* ptrs[] = {x_q, x_kv, w_q, w_k, w_v, w_o, out, workspace, b_q, b_k, b_v, b_o};
     for (const void* p : ptrs)
@@ -550,6 +568,7 @@ mha_status mha_sublayer_forward(mha_dtype in_dt, mha_dtype out_dt,
     if (d_k != kHeadDim) return MHA_ENOTSUP;
     if (in_dt == MHA_F32 && out_dt != MHA_F32) return MHA_ENOTSUP;
     if (B == 0 || L == 0) return MHA_OK;
+    if (!mha_rows_fit(B, L, d_model) || !mha_rows_fit(B, Lk, d_model)) return MHA_ENOTSUP;
     if (!x || !out || !workspace) return MHA_EINVAL;
     const void* ptrs[] = {x, memory, ln_gain, ln_bias, workspace};
     for (const void* p : ptrs)
@@ -589,37 +608,50 @@ mha_status mha_sublayer_forward(mha_dtype in_dt, mha_dtype out_dt,
 
 mha_status mha_timing_enable(int repeat) {
     if (repeat < 0 || repeat > 1000) return MHA_EINVAL;
-    const bool on = repeat > 0;
-    if (on && !g_timing.created) {
-        for (int n = 0; n < 2 * kPool; ++n)
-            if (hipEventCreate(&g_timing.ev[n]) != hipSuccess) return MHA_EHIP;
-        g_timing.created = true;
+    TimingState* t = t_timing;
+    if (repeat == 0) {
+        if (t) t->on = false;
+        return MHA_OK;
     }
-    g_timing.on = on;
-    g_timing.repeat = on ? repeat : 1;
+    if (!t) {
+        t = new (std::nothrow) TimingState();
+        if (!t) return MHA_EHIP;
+        for (int n = 0; n < 2 * kPool; ++n) {
+            if (hipEventCreate(&t->ev[n]) != hipSuccess) {
+                for (int x = 0; x < n; ++x) (void)hipEventDestroy(t->ev[x]);
+                delete t;
+                return MHA_EHIP;
+            }
+        }
+        t_timing = t;
+    }
+    t->on = true;
+    t->repeat = repeat;
     return MHA_OK;
 }
 
 int mha_timing_read(const char** names, double* total_ms, int* count, int max) {
+    TimingState* t = t_timing;
+    if (!t) return 0;
     int n_out = 0;
-    for (int k = 0; k < g_timing.used; ++k) {
-        if (hipEventSynchronize(g_timing.ev[2 * k + 1]) != hipSuccess) return -1;
+    for (int k = 0; k < t->used; ++k) {
+        if (hipEventSynchronize(t->ev[2 * k + 1]) != hipSuccess) return -1;
         float ms = 0.0f;
-        if (hipEventElapsedTime(&ms, g_timing.ev[2 * k], g_timing.ev[2 * k + 1]) != hipSuccess) return -1;
+        if (hipEventElapsedTime(&ms, t->ev[2 * k], t->ev[2 * k + 1]) != hipSuccess) return -1;
         int slot = -1;
         for (int x = 0; x < n_out; ++x)
-            if (strcmp(names[x], g_timing.name[k]) == 0) slot = x;
+            if (strcmp(names[x], t->name[k]) == 0) slot = x;
         if (slot < 0) {
             if (n_out >= max) continue;
             slot = n_out++;
-            names[slot] = g_timing.name[k];
+            names[slot] = t->name[k];
             total_ms[slot] = 0.0;
             count[slot] = 0;
         }
         total_ms[slot] += ms;
-        count[slot] += g_timing.repeat;
+        count[slot] += t->repeat;
     }
-    g_timing.used = 0;
+    t->used = 0;
     return n_out;
 }
 

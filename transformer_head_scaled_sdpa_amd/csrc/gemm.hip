@@ -130,12 +130,12 @@ __global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_nt(GemmArgs g, i
     const bf16_t* W = static_cast<const bf16_t*>(P.w);
     LdsTileLoader<kTM, kWv> la;
     LdsTileLoader<kTN, kWv> lw;
-    la.init(wave, lane, m0, M, K);
-    lw.init(wave, lane, n0, N, K);
+    la.init(wave, lane, A, m0, M, K);
+    lw.init(wave, lane, W, n0, N, K);
     auto issue = [&](int stage, int k0) {
         unsigned char* base = smem + stage * kStage;
-        la.issue(A + k0, base, wave);
-        lw.issue(W + k0, base + kABytes, wave);
+        la.issue(k0, base, wave);
+        lw.issue(k0, base + kABytes, wave);
     };
 
     // acc[mi][ni][p]: A rows wm*kRowsW + mi*32 .., W rows wn*kTN/2 + ni*32 .., K split p.

@@ -26,18 +26,26 @@ constexpr int kTileRowBytes = kTileLdsRow * 2;
 // at or past `limit` is not issued at all: those LDS rows keep stale data of
 // any value, so only callers whose rows never mix with other rows' results
 // (each output row depends on its own input row only) may ask for it.
-// kRows must be a multiple of 64.
+// Per-lane offsets are relative to the tile's first row (held as a 64-bit,
+// wave-uniform pointer), so they stay below kRows * ld whatever the size of
+// the whole matrix.  kRows must be a multiple of 64.
 template <int kRows, int kWaves>
 struct LdsTileLoader {
     static constexpr int kLoads = kRows * kTileRowBytes / 1024;
     static constexpr int kPerWave = (kLoads + kWaves - 1) / kWaves;
     static_assert(kRows % 64 == 0, "tile rows must be a multiple of 64");
-    uint32_t off[kPerWave];   // element offsets from the matrix base, before the slice offset
+    const bf16_t* rows = nullptr;   // row r0 of the matrix
+    uint32_t off[kPerWave];   // element offsets from row r0, before the slice offset
     uint32_t live = 0;        // bit j: wave load j has a row below the limit (wave-uniform)
     uint32_t pad = 0;         // bit j: this lane's chunk of wave load j is row padding
 
-    // Rows r0 .. r0 + kRows - 1 of a row-major matrix with `ld` elements per row.
-    __device__ __forceinline__ void init(int wave, int lane, int r0, int limit, int ld, bool skip_dead = false) {
+    // Rows r0 .. r0 + kRows - 1 of the row-major matrix `m` with `ld`
+    // elements per row.
+    __device__ __forceinline__ void init(int wave, int lane, const bf16_t* m, int r0, int limit, int ld,
+                                         bool skip_dead = false) {
+        rows = m + (long long)r0 * ld;
+        live = 0;
+        pad = 0;
 #pragma unroll
         for (int j = 0; j < kPerWave; ++j) {
             const int x = (wave + kWaves * j) * 1024 + lane * 16;
@@ -47,14 +55,17 @@ struct LdsTileLoader {
                 c = 0;
                 pad |= 1u << j;
             }
-            off[j] = (uint32_t)(min(r0 + r, limit - 1) * ld + c * 8);
+            // A tile that starts at or past the limit has no row to read.
+            const int rr = min(r0 + r, limit - 1) - r0;
+            off[j] = rr >= 0 ? (uint32_t)(rr * ld + c * 8) : 0u;
             const int first = (wave + kWaves * j) * 1024 / kTileRowBytes;   // first row of the load
-            if (!skip_dead || r0 + first < limit) live |= 1u << j;
+            if (r0 < limit && (!skip_dead || r0 + first < limit)) live |= 1u << j;
         }
     }
 
-    // Copy the slice starting at element column `src - base` (src = base + k0).
-    __device__ __forceinline__ void issue(const bf16_t* src, unsigned char* lds, int wave) const {
+    // Copy the 64-wide slice starting at element column d0.
+    __device__ __forceinline__ void issue(int d0, unsigned char* lds, int wave) const {
+        const bf16_t* src = rows + d0;
 #pragma unroll
         for (int j = 0; j < kPerWave; ++j) {
             const int i = wave + kWaves * j;

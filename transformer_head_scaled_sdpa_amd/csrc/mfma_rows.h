@@ -79,14 +79,18 @@ __device__ __forceinline__ constexpr int acc_row(int v) { return (v >> 2) * 8 + 
 
 // One step of a [L, 64] bf16 operand: rows r0 .. r0+127 as 1024 chunks of 16
 // bytes (chunk n: row n / 8, features (n % 8) * 8 ..), kChunks per thread.
-// The operand is read through a buffer resource whose range ends with row
-// L - 1, so rows at or past L read as zero in hardware; each thread's chunk
-// offsets within a step are fixed and the step's row offset is a scalar.
+// Each step reads through a buffer resource based at row r0 whose range ends
+// with row L - 1, so rows at or past L read as zero in hardware (the range
+// check covers the per-lane offset only, which is why the step's row offset
+// goes into the resource's base and range rather than into soffset).  Each
+// thread's chunk offsets within a step are fixed; the per-step resource is
+// scalar arithmetic.
 struct Chunks {
     uint4 c[kChunks];
 };
 struct StepSrc {
-    __amdgpu_buffer_rsrc_t rsrc;
+    const char* base;         // row 0 of the operand
+    uint32_t range;           // bytes from row 0 to the end of row L - 1
     uint32_t voff[kChunks];   // byte offsets of this thread's chunks within a step
     uint32_t row_bytes;       // row stride in bytes
 };
@@ -99,9 +103,9 @@ inline bool fits_buffer(long long ld, int L) { return L <= 0 || (long long)(L - 
 
 __device__ __forceinline__ StepSrc step_src(const bf16_t* x, long long ld, int L, int tid) {
     StepSrc s;
+    s.base = reinterpret_cast<const char*>(x);
     s.row_bytes = (uint32_t)(ld * 2);
-    const uint32_t range = L > 0 ? (uint32_t)((long long)(L - 1) * ld * 2 + kD * 2) : 0u;
-    s.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(x), (short)0, (int)range, kBufWord3);
+    s.range = L > 0 ? (uint32_t)((long long)(L - 1) * ld * 2 + kD * 2) : 0u;
 #pragma unroll
     for (int n = 0; n < kChunks; ++n) {
         const int ch = tid + n * kThreads;
@@ -111,11 +115,16 @@ __device__ __forceinline__ StepSrc step_src(const bf16_t* x, long long ld, int L
 }
 __device__ __forceinline__ Chunks load_step(const StepSrc& s, int r0) {
     Chunks t;
-    const uint32_t soff = (uint32_t)r0 * s.row_bytes;
+    // A step wholly past row L - 1 gets an empty range (every load reads zero).
+    const unsigned long long skip = (unsigned long long)(uint32_t)r0 * s.row_bytes;
+    const bool any = skip < s.range;
+    const uint32_t left = any ? s.range - (uint32_t)skip : 0u;   // bytes of rows r0 .. L-1
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(s.base + (any ? skip : 0ull)), (short)0, (int)left, kBufWord3);
 #pragma unroll
     for (int n = 0; n < kChunks; ++n) {
         typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-        const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, s.voff[n], soff, 0);
+        const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, s.voff[n], 0, 0);
         t.c[n] = make_uint4(v[0], v[1], v[2], v[3]);
     }
     return t;

@@ -197,13 +197,15 @@ __global__ __launch_bounds__(kThreads, 1) void mha_attn_fused_bf16(FusedArgs a, 
     int gstep = 0;
     LdsTileLoader<kKC, kW> lkx;       // X_kv rows of the current key chunk
     LdsTileLoader<kHd, kW> lkw;       // W_K[h] and W_V[h] rows 0..63 each
-    lkw.init(wave, lane, 0, kHd, D);
-    lkx.init(wave, lane, 0, Lk, D);
+    LdsTileLoader<kHd, kW> lvw;
+    lkw.init(wave, lane, wk, 0, kHd, D);
+    lvw.init(wave, lane, wv, 0, kHd, D);
+    lkx.init(wave, lane, xkv, 0, Lk, D);
     auto kv_issue = [&](int stage, int d0) {
         unsigned char* base = smem + stage * kStageBytes;
-        lkx.issue(xkv + d0, base, wave);
-        lkw.issue(wk + d0, base + kKC * kTileRowBytes, wave);
-        lkw.issue(wv + d0, base + (kKC + kHd) * kTileRowBytes, wave);
+        lkx.issue(d0, base, wave);
+        lkw.issue(d0, base + kKC * kTileRowBytes, wave);
+        lvw.issue(d0, base + (kKC + kHd) * kTileRowBytes, wave);
     };
 
     // ---------------- Q projection: Q^T (64 x 256) = W_Q[h] X_q^T -------------
@@ -212,12 +214,12 @@ __global__ __launch_bounds__(kThreads, 1) void mha_attn_fused_bf16(FusedArgs a, 
         LdsTileLoader<kBQ, kW> lx;
         LdsTileLoader<kHd, kW> lw;
         // Query rows past Lq only feed their own (never stored) outputs.
-        lx.init(wave, lane, q_wg, Lq, D, true);
-        lw.init(wave, lane, 0, kHd, D);
+        lx.init(wave, lane, xq, q_wg, Lq, D, true);
+        lw.init(wave, lane, wq, 0, kHd, D);
         auto issue = [&](int stage, int d0) {
             unsigned char* base = smem + stage * kStageBytes;
-            lx.issue(xq + d0, base, wave);
-            lw.issue(wq + d0, base + kBQ * kTileRowBytes, wave);
+            lx.issue(d0, base, wave);
+            lw.issue(d0, base + kBQ * kTileRowBytes, wave);
         };
         f32x16 acc[2] = {};
         issue(0, 0);
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void mha_attn_fused_bf16(FusedArgs a, 
             if (dt + 1 < nd) {
                 kv_issue((gstep + 1) & 1, (dt + 1) * 64);
             } else if (k0 + kKC < kv_end) {
-                lkx.init(wave, lane, k0 + kKC, Lk, D);
+                lkx.init(wave, lane, xkv, k0 + kKC, Lk, D);
                 kv_issue((gstep + 1) & 1, 0);
             }
             const bf16_t* xs = reinterpret_cast<const bf16_t*>(smem + (gstep & 1) * kStageBytes);

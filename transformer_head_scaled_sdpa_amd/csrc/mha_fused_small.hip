@@ -164,15 +164,17 @@ __global__ __launch_bounds__(kThreads, 1) void mha_attn_fused_small_bf16(FusedAr
 
     // ---------------- Q, K, V projections: one pass over d_model ------------
     LdsTileLoader<kL, kW> lx;         // X rows 0..127 (rows past L re-read row L-1)
-    LdsTileLoader<kHd, kW> lw;        // 64 rows of one weight slice
-    lx.init(wave, lane, 0, L, D);
-    lw.init(wave, lane, 0, kHd, D);
+    LdsTileLoader<kHd, kW> lwq, lwk, lwv;   // 64 rows of one weight slice each
+    lx.init(wave, lane, x, 0, L, D);
+    lwq.init(wave, lane, wq, 0, kHd, D);
+    lwk.init(wave, lane, wk, 0, kHd, D);
+    lwv.init(wave, lane, wv, 0, kHd, D);
     auto issue = [&](int stage, int d0) {
         unsigned char* base = smem + stage * kStageBytes;
-        lx.issue(x + d0, base, wave);
-        lw.issue(wq + d0, base + kL * kTileRowBytes, wave);
-        lw.issue(wk + d0, base + (kL + kHd) * kTileRowBytes, wave);
-        lw.issue(wv + d0, base + (kL + 2 * kHd) * kTileRowBytes, wave);
+        lx.issue(d0, base, wave);
+        lwq.issue(d0, base + kL * kTileRowBytes, wave);
+        lwk.issue(d0, base + (kL + kHd) * kTileRowBytes, wave);
+        lwv.issue(d0, base + (kL + 2 * kHd) * kTileRowBytes, wave);
     };
     // Feature blocks 0..5 are Q0, Q1, K0, K1, V0, V1 (weight rows 32*f ..);
     // wave w owns rows rb = w % 4 and feature blocks 3*(w/4) + j in acc[j].
