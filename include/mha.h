@@ -178,6 +178,28 @@ mha_status sdpa_backward(mha_dtype in_dt, mha_dtype out_dt,
                          const int* valid_lens, int vl_rank, int causal,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sdpa_decode_noalloc -- sdpa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, results and errors as sdpa_decode, minus
+ * the workspace: the per-split partials live in a 16 MiB array inside the
+ * library that each GPU holds from the library's load until the process ends
+ * (found on a device's first call with hipGetSymbolAddress; the call neither
+ * allocates nor frees).  A step needs round_up(sdpa_decode_workspace_bytes(
+ * B, h, L), 256) bytes of it; larger steps (B * h * ceil(L / 256) above about
+ * 63,500) return MHA_EWORKSPACE before anything is enqueued.  Every call on
+ * one GPU shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two threads) race on it and must be serialised by the caller.
+ * Nothing in the array needs to start at zero.  MHA_EHIP if the array's
+ * device address cannot be found.
+ */
+mha_status sdpa_decode_noalloc(mha_dtype in_dt, mha_dtype out_dt,
+                               const void* q, mha_strides sq,
+                               const void* k, mha_strides sk,
+                               const void* v, mha_strides sv,
+                               void* o, mha_strides so,
+                               int B, int h, int L, int d_k, int d_v, const int* lens, void* stream);
+
 /* Bytes of device workspace mha_forward needs: for MHA_BF16 the merged head
  * output [B*Lq, d_model] in bf16; for MHA_F32 the projected Q, K, V and the
  * merged head output in fp32.  Each region is 256-byte aligned.  Returns 0

@@ -151,6 +151,22 @@ def decode(lib, **kw):
                            a["ws"], a["ws_bytes"], None)
 
 
+def test_decode_noalloc_validation(lib):
+    st = S(4 * 300 * 64, 300 * 64, 64)
+    s1 = S(4 * 64, 64, 0)
+
+    def call(B=2, h=4, L=300, dk=64, in_dt=BF16):
+        return lib.sdpa_decode_noalloc(in_dt, BF16, ALIGNED[0], s1, ALIGNED[1], st, ALIGNED[2], st, ALIGNED[3], s1,
+                                       B, h, L, dk, 64, ALIGNED[4], None)
+    assert call(B=0) == OK
+    assert call(dk=32) == ENOTSUP
+    assert call(in_dt=F32) == ENOTSUP
+    assert call(L=0) == EINVAL
+    # A step whose partials exceed the library's 16 MiB array is refused
+    # before any pointer is used: 64 * 8 * 256 slices of 264 bytes.
+    assert call(B=64, h=8, L=65536) == EWORK
+
+
 def test_decode_workspace_bytes(lib):
     # one partial (max, sum, 64 outputs) of fp32 per (batch, head, 256-key split), 256-byte rounded
     assert lib.sdpa_decode_workspace_bytes(2, 4, 300) == 4352          # 2*4*2*66*4 = 4224 rounded up

@@ -19,6 +19,8 @@ there is no CPU or PyTorch fallback, and a missing library raises.
         -> dq, dk, dv (gradients of sdpa_forward for the output gradient dout)
     sdpa_decode(q, k_cache, v_cache, lens)
         one decoding step: q [B,h,64] against caches [B,h,L,64]
+    sdpa_decode_noalloc(q, k_cache, v_cache, lens, out=None)
+        the same step with no workspace (for callers that cannot allocate)
 
 valid_lens is [B] (one length per sequence) or [B, Lq] (one per query).
 return_weights=True also returns the attention weights [B, h, Lq, Lk]
@@ -30,7 +32,7 @@ import ctypes
 from . import _lib
 from ._lib import MhaError, MHA_BF16, MHA_F32, MHA_OK, Strides
 
-__all__ = ["sdpa_forward", "sdpa_backward", "sdpa_decode", "mha_forward", "mha_sublayer_forward", "workspace_bytes", "kernel_timing", "MhaError", "library"]
+__all__ = ["sdpa_forward", "sdpa_backward", "sdpa_decode", "sdpa_decode_noalloc", "mha_forward", "mha_sublayer_forward", "workspace_bytes", "kernel_timing", "MhaError", "library"]
 
 
 def library():
@@ -184,6 +186,31 @@ def sdpa_decode(q, k_cache, v_cache, lens, out_dtype=None, out=None, workspace=N
                          _strides4(k_cache), _ptr(v_cache), _strides4(v_cache), _ptr(out), S3(out), B, h, L, dk, dv,
                          _ptr(ln), _ptr(workspace), workspace.numel(), _stream())
     _raise(st, "sdpa_decode")
+    return out
+
+
+def sdpa_decode_noalloc(q, k_cache, v_cache, lens, out_dtype=None, out=None):
+    """sdpa_decode whose partial results live in the library's own device
+    array (no workspace); the C entry point allocates nothing.  Pass ``out``
+    and a device int32 ``lens`` to keep the whole call allocation-free."""
+    torch = _torch()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_gpu(n, t)
+    B, h, dk = q.shape
+    L, dv = k_cache.shape[2], v_cache.shape[3]
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, h, dv), dtype=out_dtype, device=q.device)
+    ln = _valid_lens(lens, B, q.device)
+    if ln is None:
+        raise ValueError("lens is required")
+    S3 = lambda t: _lib.Strides(t.stride(0), t.stride(1), 0)
+    st = _lib.load().sdpa_decode_noalloc(_dtype_code(q.dtype), _dtype_code(out.dtype), _ptr(q), S3(q),
+                                         _ptr(k_cache), _strides4(k_cache), _ptr(v_cache), _strides4(v_cache),
+                                         _ptr(out), S3(out), B, h, L, dk, dv, _ptr(ln), _stream())
+    _raise(st, "sdpa_decode_noalloc")
     return out
 
 

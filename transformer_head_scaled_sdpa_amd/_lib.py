@@ -19,7 +19,7 @@ MHA_EHIP = 4
 
 # Every function the header declares; tests check that each is exported.
 EXPORTED = ("sdpa_forward", "sdpa_forward_ex", "sdpa_backward_workspace_bytes", "sdpa_backward",
-            "sdpa_decode_workspace_bytes", "sdpa_decode", "mha_workspace_bytes",
+            "sdpa_decode_workspace_bytes", "sdpa_decode", "sdpa_decode_noalloc", "mha_workspace_bytes",
             "mha_workspace_bytes_ex", "mha_forward", "mha_forward_ex", "mha_sublayer_workspace_bytes",
             "mha_sublayer_forward", "mha_status_string", "mha_timing_enable",
             "mha_timing_read")
@@ -63,6 +63,9 @@ def load():
     lib.sdpa_decode.restype = i
     lib.sdpa_decode.argtypes = [i, i, vp, Strides, vp, Strides, vp, Strides, vp, Strides,
                                 i, i, i, i, i, vp, vp, sz, vp]
+    lib.sdpa_decode_noalloc.restype = i
+    lib.sdpa_decode_noalloc.argtypes = [i, i, vp, Strides, vp, Strides, vp, Strides, vp, Strides,
+                                        i, i, i, i, i, vp, vp]
     lib.mha_workspace_bytes.restype = sz
     lib.mha_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.mha_forward.restype = i

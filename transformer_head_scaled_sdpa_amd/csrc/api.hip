@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "../../include/mha.h"
@@ -280,43 +282,85 @@ mha_status sdpa_backward(mha_dtype in_dt, mha_dtype out_dt,
     return hip_status(timed("sdpa_backward", s, [&] { return mha::launch_sdpa_backward(a, s); }));
 }
 
-size_t sdpa_decode_workspace_bytes(int B, int h, int L) {
-    if (B < 0 || h <= 0 || L <= 0) return 0;
-    return round_up(mha::decode_workspace_bytes(B, h, L), 256);
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// sdpa_decode and its allocation-free variant
+// ---------------------------------------------------------------------------
+// The allocation-free variant keeps the per-split partials of a decoding step
+// in this file-scope device array instead of a caller workspace.  Each GPU the
+// library runs on holds its own copy until the process ends; every call on a
+// GPU shares it (calls that overlap on one GPU race on it).  No part of it
+// has to start at zero: each launch writes every partial it later reads.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current (in host code the array's name is only a stand-in).
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+mha_status decode_scratch(void** addr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MHA_EHIP;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MHA_EHIP;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *addr = p;
+    return MHA_OK;
 }
 
-mha_status sdpa_decode(mha_dtype in_dt, mha_dtype out_dt,
+// use_scratch: the partials go to the device's `scratch` array (workspace and
+// workspace_bytes are ignored), and steps that need more than it holds are
+// refused with MHA_EWORKSPACE.
+mha_status decode_impl(mha_dtype in_dt, mha_dtype out_dt,
                        const void* q, mha_strides sq,
                        const void* k, mha_strides sk,
                        const void* v, mha_strides sv,
                        void* o, mha_strides so,
                        int B, int h, int L, int d_k, int d_v, const int* lens,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       bool use_scratch, void* workspace, size_t workspace_bytes, void* stream) {
     if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
     if (B < 0 || h <= 0 || L <= 0 || d_k <= 0 || d_v <= 0) return MHA_EINVAL;
     if (d_k != kHeadDim || d_v != kHeadDim || in_dt != MHA_BF16) return MHA_ENOTSUP;
     if (B == 0) return MHA_OK;
-    if (!q || !k || !v || !o || !lens || !workspace) return MHA_EINVAL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
+    if (!q || !k || !v || !o || !lens || (!use_scratch && !workspace)) return MHA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (!use_scratch && !aligned16(workspace)))
         return MHA_EINVAL;
     const long long omult = out_dt == MHA_F32 ? 4 : 8;
     const mha_strides in_s[3] = {sq, sk, sv};
     for (const mha_strides& s : in_s)
         if (s.b < 0 || s.h < 0 || s.l < 0 || s.b % 8 || s.h % 8 || s.l % 8) return MHA_EINVAL;
     if (so.b < 0 || so.h < 0 || so.b % omult || so.h % omult) return MHA_EINVAL;
-    const size_t need = sdpa_decode_workspace_bytes(B, h, L);
-    if (workspace_bytes < need) return MHA_EWORKSPACE;
+    const size_t need = round_up(mha::decode_workspace_bytes(B, h, L), 256);
+    if (use_scratch ? need > kDecodeScratchBytes : workspace_bytes < need) return MHA_EWORKSPACE;
     const size_t oe = elem_size(out_dt);
     const mha_strides so1{so.b, so.h, 0};
     const Range ro = view_range(o, so1, B, h, 1, d_v, oe);
-    const uintptr_t wb = reinterpret_cast<uintptr_t>(workspace);
-    const Range rw{wb, wb + need};
     const mha_strides sq1{sq.b, sq.h, 0};
     const Range ins[3] = {view_range(q, sq1, B, h, 1, d_k, 2), view_range(k, sk, B, h, L, d_k, 2),
                           view_range(v, sv, B, h, L, d_v, 2)};
     for (const Range& r : ins)
-        if (overlap(ro, r) || overlap(rw, r)) return MHA_EINVAL;
-    if (overlap(ro, rw)) return MHA_EINVAL;
+        if (overlap(ro, r)) return MHA_EINVAL;
+    if (!use_scratch) {
+        const uintptr_t wb = reinterpret_cast<uintptr_t>(workspace);
+        const Range rw{wb, wb + need};
+        for (const Range& r : ins)
+            if (overlap(rw, r)) return MHA_EINVAL;
+        if (overlap(ro, rw)) return MHA_EINVAL;
+    } else {
+        const mha_status st = decode_scratch(&workspace);
+        if (st != MHA_OK) return st;
+    }
 
     mha::DecodeArgs d;
     d.q = q; d.k = k; d.v = v; d.o = o;
@@ -330,6 +374,36 @@ mha_status sdpa_decode(mha_dtype in_dt, mha_dtype out_dt,
     return hip_status(timed("sdpa_decode", s, [&] {
         return mha::launch_sdpa_decode(d, out_dt == MHA_F32, workspace, s);
     }));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sdpa_decode_workspace_bytes(int B, int h, int L) {
+    if (B < 0 || h <= 0 || L <= 0) return 0;
+    return round_up(mha::decode_workspace_bytes(B, h, L), 256);
+}
+
+mha_status sdpa_decode(mha_dtype in_dt, mha_dtype out_dt,
+                       const void* q, mha_strides sq,
+                       const void* k, mha_strides sk,
+                       const void* v, mha_strides sv,
+                       void* o, mha_strides so,
+                       int B, int h, int L, int d_k, int d_v, const int* lens,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(in_dt, out_dt, q, sq, k, sk, v, sv, o, so, B, h, L, d_k, d_v, lens, false, workspace,
+                       workspace_bytes, stream);
+}
+
+mha_status sdpa_decode_noalloc(mha_dtype in_dt, mha_dtype out_dt,
+                               const void* q, mha_strides sq,
+                               const void* k, mha_strides sk,
+                               const void* v, mha_strides sv,
+                               void* o, mha_strides so,
+                               int B, int h, int L, int d_k, int d_v, const int* lens, void* stream) {
+    return decode_impl(in_dt, out_dt, q, sq, k, sk, v, sv, o, so, B, h, L, d_k, d_v, lens, true, nullptr, 0,
+                       stream);
 }
 
 size_t mha_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h) {
