@@ -513,7 +513,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The clock ramps up over tens of milliseconds of sustained load (the long
+    # causal kernel takes ~200 us per launch cold and ~155 us once warm), so
+    # the default warm-up runs about 100 ms of steps before timing.
+    ap.add_argument("--warmup", type=int, default=600)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(workloads.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
@@ -587,7 +590,7 @@ def main():
                 continue
             cw = workloads.BY_NAME[name]
             log(f"config {name} ...")
-            result["configs"][name] = measure_workload(cw, workloads.make_inputs(cw), 50, 10, args.repeat,
+            result["configs"][name] = measure_workload(cw, workloads.make_inputs(cw), 100, 50, args.repeat,
                                                        cold=False)
         extras(result, args, w)
 

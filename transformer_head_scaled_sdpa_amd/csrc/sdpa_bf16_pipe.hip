@@ -15,7 +15,8 @@
 //    Q fragments in registers.  Keys/values stream through LDS in tiles of
 //    64 keys, copied with one 16-byte coalesced load per thread per tensor,
 //    loaded into registers two stages before they are stored to LDS (two
-//    register sets, one for even and one for odd stages).
+//    register sets, one for even and one for odd stages) through buffer
+//    loads that zero-fill rows past Lk, so the copy is branch-free.
 //  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
 //    so every lane owns ONE query (lane % 32) and 32 keys of a tile; row sums
 //    are in-lane plus one v_permlane32_swap.  O^T += V^T P^T takes P straight
@@ -36,8 +37,10 @@
 //    2^20, in which case the tile's row max is folded into m, the
 //    accumulators are rescaled and the tile's weights recomputed.  Weights
 //    stay below 2^20 * 32 per lane and tile, far from fp32 and bf16 limits,
-//    and no per-tile max reduction runs in the common case.  The row sum
-//    adds the bf16-rounded weights that the P.V product uses.
+//    and no per-tile max reduction runs in the common case.  Row sums of
+//    the bf16 weights run on the matrix core (a 16x16x32 MFMA with a 0/1
+//    selector per 16-key slice), which idles half the time, instead of the
+//    VALU, which bounds the loop.
 //  * Causal: tiles above the diagonal are never loaded or multiplied; masks
 //    are evaluated only on the tiles that cross the diagonal or the valid
 //    length.  Workgroups are issued heaviest-first, and consecutive
@@ -63,7 +66,7 @@ constexpr int kLdsK = kD + 8;
 constexpr int kLdsV = kD + 32;
 constexpr int kTileK = kBN * kLdsK;
 constexpr int kTileV = kBN * kLdsV;
-constexpr float kSumLimit = 1048576.0f;   // 2^20
+constexpr float kSumLimit = 4194304.0f;   // 2^22: a tile's weight sum per query that triggers a rescale
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -72,12 +75,28 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // A 64 x 64 bf16 tile is 512 16-byte chunks, one per thread: chunk c holds
-// row c / 8, features (c % 8) * 8 .. +7.  The tile's base address is uniform
-// (scalar registers) and each lane adds a fixed 32-bit byte offset; only a
-// tile that runs past Lk checks rows, which then read as zero.
-__device__ __forceinline__ uint4 load_chunk(const char* tile, uint32_t lane_off, int rows_left, int tid) {
-    if (rows_left >= kBN) return *reinterpret_cast<const uint4*>(tile + lane_off);
-    return (tid >> 3) < rows_left ? *reinterpret_cast<const uint4*>(tile + lane_off) : make_uint4(0, 0, 0, 0);
+// row c / 8, features (c % 8) * 8 .. +7.  Tiles are read through a buffer
+// resource based at the tile's first row whose range ends with row Lk - 1,
+// so rows at or past Lk read as zero in hardware and the copy needs no
+// branch; straight-line loads and stores let the compiler wait for exactly
+// the loads a store needs.  Each lane adds a fixed byte offset.
+struct TileSrc {
+    const char* base;    // row 0 of the (batch, head)
+    uint32_t range;      // bytes from row 0 to the end of row Lk - 1
+    uint32_t tile_bytes; // bytes per tile of rows
+    uint32_t lane_off;   // this thread's chunk within a tile
+};
+constexpr int kBufWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 descriptor word 3)
+
+__device__ __forceinline__ uint4 load_tile(const TileSrc& src, int t) {
+    const unsigned long long skip = (unsigned long long)(uint32_t)t * src.tile_bytes;
+    const bool any = skip < src.range;
+    const uint32_t left = any ? src.range - (uint32_t)skip : 0u;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(src.base + (any ? skip : 0ull)), (short)0, (int)left, kBufWord3);
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, src.lane_off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 template <int kLds>
@@ -152,11 +171,8 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
 }
 
 // Weights exp2(s * c - m) packed as the B operand of O^T += V^T P^T: slice
-// kb covers keys kb*16 + (e/4)*8 + hb*4 + e%4 as bf16 pairs.  Returns this
-// lane's sum of the rounded weights.
-__device__ __forceinline__ float weights(const f32x16 (&s)[2], float m, float c, u32x4 (&w)[4]) {
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    float acc[2] = {0.0f, 0.0f};
+// kb covers keys kb*16 + (e/4)*8 + hb*4 + e%4 as bf16 pairs.
+__device__ __forceinline__ void weights(const f32x16 (&s)[2], float m, float c, u32x4 (&w)[4]) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
@@ -166,26 +182,54 @@ __device__ __forceinline__ float weights(const f32x16 (&s)[2], float m, float c,
             const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb >> 1][v + 1], c, -m));
             const bf16x2 pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
             w[kb][e >> 1] = __builtin_bit_cast(uint32_t, pp);
-            acc[kb & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc[kb & 1], false);
         }
     }
-    return acc[0] + acc[1];
+}
+
+// Row sums of the packed weights on the matrix core.  Read as the B operand
+// of v_mfma_f32_16x16x32_bf16, lane l holds 8 weights of query l % 32 (keys
+// of lane half l / 32), which the MFMA files under column l % 16 and k-group
+// l / 16.  The selector A has row 0 = 1 over k-groups 0 and 2 (lanes l and
+// l + 32: query l) and row 1 = 1 over k-groups 1 and 3 (query l + 16), so
+// lanes 0..15 receive the sums over the tile's 64 keys: element 0 for query
+// l, element 1 for query l + 16.  These are sums of the same bf16 weights
+// the P.V product uses, formed where the VALU (which bounds the loop) is not
+// involved.
+__device__ __forceinline__ f32x4 tile_sums(const bf16x8& sel, const u32x4 (&w)[4]) {
+    f32x4 t = {};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, __builtin_bit_cast(bf16x8, w[kb]), t, 0, 0, 0);
+    return t;
+}
+
+// The sum of query lane % 32 from tile_sums' layout (lane l < 16: element 0,
+// lane l + 16: element 1 of lane l).
+__device__ __forceinline__ float query_sum(const float (&t)[2], int l32) {
+    const int src = (l32 & 15) * 4;
+    const float lo = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, t[0])));
+    const float hi = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, t[1])));
+    return l32 < 16 ? lo : hi;
 }
 
 // A tile's weights outgrew the offset m: fold the tile's row max into m
-// (never lowering it), rescale the accumulators and recompute the weights.
-__device__ __forceinline__ float rescale(const f32x16 (&s)[2], float& m, float c, float& l, f32x16 (&o)[2],
-                                         u32x4 (&w)[4]) {
+// (never lowering it), rescale the output accumulators and the running sums
+// (lanes 0..15 hold queries l and l + 16) and recompute the tile's weights.
+__device__ __forceinline__ void rescale(const f32x16 (&s)[2], float& m, float c, float (&l)[2], f32x16 (&o)[2],
+                                        u32x4 (&w)[4], int l32) {
     const float d = fmaxf(fmaf(tile_max(s), c, -m), 0.0f);
     m += d;
     const float alpha = __builtin_amdgcn_exp2f(-d);
-    l *= alpha;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         o[0][v] *= alpha;
         o[1][v] *= alpha;
     }
-    return weights(s, m, c, w);
+    const int src = ((l32 & 15) + 16) * 4;
+    const float alpha_hi = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, alpha)));
+    l[0] *= alpha;
+    l[1] *= alpha_hi;
+    weights(s, m, c, w);
 }
 
 template <bool kCausal, bool kHasVl, bool kOutF32>
@@ -229,18 +273,19 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
     const int key_lim = none ? Lk : (kCausal ? min(kv_lim, i + 1) : kv_lim);
 
     const bf16_t* qp = static_cast<const bf16_t*>(a.q) + b * a.sq[0] + hd * a.sq[1];
-    const char* kp = reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.k) + b * a.sk[0] + hd * a.sk[1]);
-    const char* vp = reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.v) + b * a.sv[0] + hd * a.sv[1]);
-    const long long ktile = a.sk[2] * (2 * kBN), vtile = a.sv[2] * (2 * kBN);   // bytes per 64 keys
-    const uint32_t koff = (uint32_t)((tid >> 3) * a.sk[2] * 2) + (tid & 7) * 16;
-    const uint32_t voff = (uint32_t)((tid >> 3) * a.sv[2] * 2) + (tid & 7) * 16;
-    auto load_k = [&](int t) { return load_chunk(kp + t * ktile, koff, Lk - t * kBN, tid); };
-    auto load_v = [&](int t) { return load_chunk(vp + t * vtile, voff, Lk - t * kBN, tid); };
+    const TileSrc ksrc{reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.k) + b * a.sk[0] + hd * a.sk[1]),
+                       (uint32_t)((long long)(Lk - 1) * a.sk[2] * 2 + kD * 2), (uint32_t)(a.sk[2] * 2 * kBN),
+                       (uint32_t)((tid >> 3) * a.sk[2] * 2) + (tid & 7) * 16};
+    const TileSrc vsrc{reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.v) + b * a.sv[0] + hd * a.sv[1]),
+                       (uint32_t)((long long)(Lk - 1) * a.sv[2] * 2 + kD * 2), (uint32_t)(a.sv[2] * 2 * kBN),
+                       (uint32_t)((tid >> 3) * a.sv[2] * 2) + (tid & 7) * 16};
+    auto load_k = [&](int t) { return load_tile(ksrc, t); };
+    auto load_v = [&](int t) { return load_tile(vsrc, t); };
 
     // Prologue: K tiles 0 and 1 into LDS, scores of tile 0; K(2), K(3), V(0)
     // and V(1) wait in registers for stages 0 and 1.
     uint4 nk_e = load_k(0);
-    uint4 nk_o = n_tiles > 1 ? load_k(1) : make_uint4(0, 0, 0, 0);
+    uint4 nk_o = load_k(1);
     bf16x8 qf[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -249,11 +294,11 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
         qf[kk] = __builtin_bit_cast(bf16x8, raw);
     }
     store_chunk<kLdsK>(nk_e, kbuf, tid);
-    if (n_tiles > 1) store_chunk<kLdsK>(nk_o, kbuf + kTileK, tid);
-    nk_e = n_tiles > 2 ? load_k(2) : make_uint4(0, 0, 0, 0);
-    nk_o = n_tiles > 3 ? load_k(3) : make_uint4(0, 0, 0, 0);
+    store_chunk<kLdsK>(nk_o, kbuf + kTileK, tid);
+    nk_e = load_k(2);
+    nk_o = load_k(3);
     uint4 nv_e = load_v(0);
-    uint4 nv_o = n_tiles > 1 ? load_v(1) : make_uint4(0, 0, 0, 0);
+    uint4 nv_o = load_v(1);
     __syncthreads();
     f32x16 sc[2];                 // scores of the tile whose softmax runs next
     tile_scores(sc, kbuf, qf, l32, hb);
@@ -263,32 +308,51 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
     f32x16 sn[2];                 // scores being formed for the next stage
     u32x4 pa[4], pb[4];           // weights of two consecutive tiles (B operand)
     float m = 0.0f;               // exponent offset (log2 units of the scaled scores)
-    float l = 0.0f;               // this lane's share of the weight sum
+    float l[2] = {0.0f, 0.0f};    // running weight sums (elements 0, 1 of tile_sums' layout)
+    // Row selector of tile_sums (bf16 ones in lanes 0, 32 and 17, 49).
+    bf16x8 sel;
+    {
+        const __bf16 one = (lane == 0 || lane == 32 || lane == 17 || lane == 49) ? static_cast<__bf16>(1.0f)
+                                                                                : static_cast<__bf16>(0.0f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sel[e] = one;
+    }
+    auto over = [&](const f32x4& t) { return __any(fmaxf(t[0], t[1]) > kSumLimit); };
 
     // Stage s reads K(s+1) and V(s-1) and fills the other buffers with K(s+2)
-    // and V(s); every wave finished with those at the last barrier.
-    // Stage s stores K(s+2) and V(s), loaded two stages earlier, and loads
-    // K(s+4) and V(s+2); even and odd stages use their own register sets.
+    // and V(s), loaded two stages earlier (every wave finished with those
+    // buffers at the last barrier); it loads K(s+4) and V(s+2).  Even and odd
+    // stages use their own register sets.  Tiles past the last one load as
+    // zeros and land in buffers no stage reads again, so the copy is the same
+    // straight-line code every stage.
     auto copy_tiles = [&](int s, uint4& nk, uint4& nv) {
-        if (s + 2 < n_tiles) store_chunk<kLdsK>(nk, kbuf + (s & 1) * kTileK, tid);
-        if (s < n_tiles) store_chunk<kLdsV>(nv, vbuf + (s & 1) * kTileV, tid);
-        if (s + 4 < n_tiles) nk = load_k(s + 4);
-        if (s + 2 < n_tiles) nv = load_v(s + 2);
+        store_chunk<kLdsK>(nk, kbuf + (s & 1) * kTileK, tid);
+        store_chunk<kLdsV>(nv, vbuf + (s & 1) * kTileV, tid);
+        nk = load_k(s + 4);
+        nv = load_v(s + 2);
     };
     // Unmasked steady state: softmax(s), scores(s+1) and P.V(s-1), independent.
+    // Everything up to the barrier is one branch-free block, so the scheduler
+    // can spread the softmax over all the stage's MFMAs; the rare offset
+    // check runs after the barrier, while S(s) is still held (the next
+    // stage's scores overwrite it only after the check) and before P(s)
+    // enters a product.
     auto fast_stage = [&](int s, f32x16 (&cur)[2], f32x16 (&nxt)[2], const u32x4 (&prev)[4], u32x4 (&pcur)[4], uint4& nk, uint4& nv) {
         copy_tiles(s, nk, nv);
         const bf16_t* ks = kbuf + ((s + 1) & 1) * kTileK;
         const bf16_t* vs = vbuf + ((s + 1) & 1) * kTileV;
-        float r = weights(cur, m, c, pcur);
+        weights(cur, m, c, pcur);
+        f32x4 t = tile_sums(sel, pcur);
         tile_scores(nxt, ks, qf, l32, hb);
         tile_pv(o, vs, prev, hb, lane);
-        if (__any(r > kSumLimit)) [[unlikely]] {
-            asm volatile("" ::: "memory");
-            r = rescale(cur, m, c, l, o, pcur);
-        }
-        l += r;
         __syncthreads();
+        if (over(t)) [[unlikely]] {
+            asm volatile("" ::: "memory");
+            rescale(cur, m, c, l, o, pcur, l32);
+            t = tile_sums(sel, pcur);
+        }
+        l[0] += t[0];
+        l[1] += t[1];
     };
     // Pipeline edges, masked tiles and fully masked rows.
     auto slow_stage = [&](int s, f32x16 (&cur)[2], f32x16 (&nxt)[2], const u32x4 (&prev)[4], u32x4 (&pcur)[4], uint4& nk, uint4& nv) {
@@ -301,9 +365,14 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
             // The first tile sets the offset (every row has an allowed key in
             // tile 0).
             if (s == 0) m = tile_max(cur) * c;
-            float r = weights(cur, m, c, pcur);
-            if (s > 0 && __any(r > kSumLimit)) r = rescale(cur, m, c, l, o, pcur);
-            l += r;
+            weights(cur, m, c, pcur);
+            f32x4 t = tile_sums(sel, pcur);
+            if (s > 0 && over(t)) {
+                rescale(cur, m, c, l, o, pcur, l32);
+                t = tile_sums(sel, pcur);
+            }
+            l[0] += t[0];
+            l[1] += t[1];
         }
         if (s + 1 < n_w) tile_scores(nxt, ks, qf, l32, hb);
         __syncthreads();
@@ -325,7 +394,7 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
         slow_stage(s + 1, sc, sn, pb, pa, nk_e, nv_e);
     }
 
-    const float inv = 1.0f / pair_sum(l);
+    const float inv = 1.0f / query_sum(l, l32);
     // O^T element v of block tb: feature tb*32 + (v/4)*8 + hb*4 + v%4, query
     // i.  Every wave is past the last barrier, so the K/V buffers are idle:
     // each wave stages 32 rows x 128 bytes of its output in its own slice
