@@ -46,13 +46,17 @@
  *     precision).  MHA_BF16 takes bf16 inputs and weights, multiplies on bf16
  *     MFMA with fp32 accumulation, keeps the softmax state in fp32, and writes
  *     the output as bf16 or fp32 (out_dt).  With MHA_BF16, mha_forward
- *     projects each head's Q, K and V inside its attention kernel and keeps
- *     them on chip: Q (times log2(e)/sqrt(d_k)) and K as bf16 hi + lo pairs
+ *     carries Q (times log2(e)/sqrt(d_k)) and K as bf16 hi + lo pairs
  *     (hi = bf16(x), lo = bf16(x - hi)) whose scores are formed from three
  *     bf16 products (hi.hi + lo.hi + hi.lo), so large logits, such as those
  *     of embeddings scaled by sqrt(d_model), keep near-fp32 accuracy instead
  *     of moving by a bf16 rounding step; V and the merged head output are
- *     rounded to bf16.  sdpa_forward's and sdpa_decode's bf16 inputs are
+ *     rounded to bf16.  Two routes compute this: for short sequences (K and
+ *     V re-projected at most 1.5 times over the blocks of 256 queries, at
+ *     most 512 keys) each head's Q, K and V are projected inside its
+ *     attention kernel and stay on chip; otherwise one GEMM launch writes
+ *     the hi + lo projections to the workspace and the attention kernel
+ *     reads them.  sdpa_forward's and sdpa_decode's bf16 inputs are
  *     exact bf16 values and use a single product.
  */
 #ifndef MHA_H
@@ -201,9 +205,11 @@ mha_status sdpa_decode_noalloc(mha_dtype in_dt, mha_dtype out_dt,
                                int B, int h, int L, int d_k, int d_v, const int* lens, void* stream);
 
 /* Bytes of device workspace mha_forward needs: for MHA_BF16 the merged head
- * output [B*Lq, d_model] in bf16; for MHA_F32 the projected Q, K, V and the
- * merged head output in fp32.  Each region is 256-byte aligned.  Returns 0
- * for inconsistent arguments. */
+ * output [B*Lq, d_model] and the Q hi, Q lo [B*Lq, d_model] and K hi, K lo,
+ * V [B*Lk, d_model] projections, all bf16 (the projected route; the on-chip
+ * route uses only the first region); for MHA_F32 the projected Q, K, V and
+ * the merged head output in fp32.  Each region is 256-byte aligned.  Returns
+ * 0 for inconsistent arguments. */
 size_t mha_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h);
 
 /*

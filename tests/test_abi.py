@@ -119,9 +119,10 @@ def test_mha_validation(lib):
 
 
 def test_workspace_bytes(lib):
-    # bf16: the merged heads only (2 * 10 * 512 bf16 = 20480 bytes); fp32: Q,
-    # K, V and merged heads; each region rounded up to 256 bytes.
-    assert lib.mha_workspace_bytes(BF16, 2, 10, 12, 512, 8) == 20480
+    # bf16: merged heads, Q hi and lo (3 x 2 * 10 * 512 bf16 = 3 x 20480
+    # bytes), K hi and lo, V (3 x 2 * 12 * 512 bf16 = 3 x 24576); fp32: Q, K,
+    # V and merged heads; each region rounded up to 256 bytes.
+    assert lib.mha_workspace_bytes(BF16, 2, 10, 12, 512, 8) == 3 * 20480 + 3 * 24576
     assert lib.mha_workspace_bytes(F32, 2, 10, 10, 512, 8) == 4 * 40960
     assert lib.mha_workspace_bytes(F32, 2, 10, 10, 500, 8) == 0
 
@@ -292,7 +293,7 @@ def sub(lib, **kw):
 
 def test_sublayer_workspace_and_validation(lib):
     # norm(x) in in_dt, then mha_forward's workspace
-    assert lib.mha_sublayer_workspace_bytes(BF16, 2, 10, 10, 512, 8) == 20480 + 20480
+    assert lib.mha_sublayer_workspace_bytes(BF16, 2, 10, 10, 512, 8) == 20480 + 6 * 20480
     assert lib.mha_sublayer_workspace_bytes(F32, 2, 10, 10, 512, 8) == 40960 + 4 * 40960
     assert sub(lib, B=0) == OK
     assert sub(lib, kind=2) == EINVAL                  # the two printed LayerNorm forms only

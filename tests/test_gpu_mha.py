@@ -67,24 +67,42 @@ def test_mha_bf16_vs_oracle(B, Lq, Lk, D, h, causal, vlr, bias, self_attn, out_f
     print("vs fp64 oracle", e, "vs bf16-storage oracle", errors(g, run_oracle(inp, bf16_stages=True)))
 
 
-# More than one 256-query block without the causal rule, and more than four
-# 128-key chunks, with ragged key lengths that include 0 (a fully masked
-# sequence) and the full length.
+# Several 256-query blocks and more than four 128-key chunks, with ragged key
+# lengths that include 0 (a fully masked sequence) and the full length.
+# These shapes take the projected route (Q/K/V GEMM, then attention on the
+# hi + lo projections); the last two keep the single-kernel route with two
+# causal blocks.
 MULTI_BLOCK_CASES = [
-    # B, Lq, Lk, D, h, self_attn, lengths
-    (3, 600, 600, 128, 2, True, [0, 600, 333]),
-    (3, 300, 700, 256, 4, False, [700, 0, 517]),
-    (2, 513, 513, 192, 3, True, [513, 257]),
+    # B, Lq, Lk, D, h, self_attn, causal, lengths
+    (3, 600, 600, 128, 2, True, False, [0, 600, 333]),
+    (3, 300, 700, 256, 4, False, False, [700, 0, 517]),
+    (2, 513, 513, 192, 3, True, False, [513, 257]),
+    (2, 1000, 1000, 128, 2, True, True, [1000, 611]),
+    (2, 260, 900, 256, 4, False, False, [900, 1]),
+    (2, 512, 512, 128, 2, True, True, [0, 300]),
+    (2, 400, 400, 192, 3, True, True, [400, 129]),
 ]
 
 
-@pytest.mark.parametrize("B,Lq,Lk,D,h,self_attn,lens", MULTI_BLOCK_CASES)
-def test_mha_bf16_multi_block_ragged(B, Lq, Lk, D, h, self_attn, lens):
+@pytest.mark.parametrize("B,Lq,Lk,D,h,self_attn,causal,lens", MULTI_BLOCK_CASES)
+def test_mha_bf16_multi_block_ragged(B, Lq, Lk, D, h, self_attn, causal, lens):
     inp = workloads.make_mha_inputs(B, Lq, Lk, D, h, "bf16", seed=7000 + Lq + Lk, vl_range=(1, Lk),
-                                    causal=False, self_attn=self_attn, bias=True)
+                                    causal=causal, self_attn=self_attn, bias=True)
     inp.valid_lens = np.array(lens, dtype=np.int32)
     g = run_gpu(inp, True)
     e = assert_bf16(g, run_oracle(inp, bf16_stages=False), f"mha bf16 B{B} Lq{Lq} Lk{Lk} lengths {lens}")
+    print("vs fp64 oracle", e)
+
+
+def test_mha_bf16_projected_route_large_logits():
+    """The projected route on embeddings scaled by sqrt(d_model) plus the
+    positional encoding (logits with std in the hundreds, as in the encoder
+    workload) at a length that takes that route: Q and K travel as hi + lo
+    bf16 planes, so the result stays within the bar."""
+    inp = workloads.make_mha_inputs(2, 600, 600, 256, 4, "bf16", seed=4242, vl_range=(300, 600),
+                                    x_kind="embed_pe", self_attn=True, bias=True)
+    g = run_gpu(inp, True)
+    e = assert_bf16(g, run_oracle(inp, bf16_stages=False), "projected route, large logits")
     print("vs fp64 oracle", e)
 
 

@@ -69,6 +69,28 @@ def test_sdpa_bf16_sharp_softmax_and_strided_layout():
     assert_bf16(to_host(o), ref, "sharp softmax, strided")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_sdpa_bf16_later_tile_far_above_the_first(causal):
+    """Key 200 scores about 350 log2 units above every key of the first tile
+    (q in [1, ~4], k_200 = 16): its weight overflows fp32 under the first
+    tile's offset, and the kernel must move the offset and recompute rather
+    than let infinities (or NaNs from them) into the output.  Rows that see
+    key 200 put almost all their weight on it."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    rng = np.random.Generator(np.random.PCG64(2024))
+    B, h, L = 1, 2, 300
+    q = workloads.round_to_bf16((1.0 + np.abs(rng.standard_normal((B, h, L, 64)))).astype(np.float32))
+    k = workloads.round_to_bf16(rng.standard_normal((B, h, L, 64)).astype(np.float32))
+    v = workloads.round_to_bf16(rng.standard_normal((B, h, L, 64)).astype(np.float32))
+    k[:, :, 200, :] = 16.0
+    o = mha.sdpa_forward(*(to_device(x, torch.bfloat16) for x in (q, k, v)), causal=causal,
+                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa(q, k, v, causal=causal)
+    assert_bf16(to_host(o), ref, f"score jump above the first tile, causal={causal}")
+
+
 @pytest.mark.parametrize("out_f32,row", [(False, 64), (False, 72), (False, 136), (True, 64), (True, 68)])
 def test_sdpa_bf16_output_views(out_f32, row):
     """The output written through a view whose rows are padded (row stride

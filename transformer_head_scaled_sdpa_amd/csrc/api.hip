@@ -411,9 +411,11 @@ size_t mha_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, 
     const size_t es = elem_size(in_dt);
     const size_t q = round_up((size_t)B * Lq * d_model * es, 256);
     const size_t kv = round_up((size_t)B * Lk * d_model * es, 256);
-    // fp32: Q, K, V, merged heads.  bf16: the merged heads only (the
-    // projections are fused into the attention kernel).
-    return in_dt == MHA_BF16 ? q : 2 * q + 2 * kv;
+    // fp32: Q, K, V, merged heads.  bf16: merged heads, Q hi and lo, K hi and
+    // lo, V (the projected route; the single-pass route for short
+    // self-attention uses only the merged heads, but the shapes alone do not
+    // tell self- from cross-attention).
+    return in_dt == MHA_BF16 ? 3 * q + 3 * kv : 2 * q + 2 * kv;
 }
 
 size_t mha_workspace_bytes_ex(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h) {
@@ -426,6 +428,22 @@ size_t mha_workspace_bytes_ex(mha_dtype in_dt, int B, int Lq, int Lk, int d_mode
 }  // extern "C"
 
 namespace {
+
+// The bf16 multi-head layer projects K and V inside its attention kernel for
+// every block of 256 queries, so it repeats that work n = ceil(Lq / 256)
+// times without the causal rule and (n + 1) / 2 times with it (block i needs
+// keys below (i + 1) * 256).  Measured on MI355X against the projected route
+// (one GEMM launch for Q, K, V, then attention on the projections): the
+// single kernel is faster or equal up to a factor of 1.5 with at most 512
+// keys (B64 L512 causal: 174 against 188 us; B16 Lq256 Lk384: 85 against
+// 85 us); beyond that the projected route wins (B4 L1024 causal 85 against
+// 52 us; B16 L512 non-causal d_model 1024: 182 against 142 us; B8 Lq256
+// Lk768: 66 against 47 us).
+bool fused_route_pays(int Lq, int Lk, bool causal) {
+    const long long n = (Lq + 255) / 256;
+    const long long twice_factor = causal ? n + 1 : 2 * n;   // 2 x re-projection factor
+    return twice_factor <= 3 && Lk <= 512;
+}
 
 // mha_forward and mha_forward_ex (lengths per query, optional weights).
 mha_status mha_impl(mha_dtype in_dt, mha_dtype out_dt,
@@ -526,8 +544,6 @@ mha_status mha_impl(mha_dtype in_dt, mha_dtype out_dt,
         e = timed("sdpa_weights", s, [&] { return mha::launch_sdpa_weights(a, s); });
         if (e != hipSuccess) return MHA_EHIP;
     } else if (bf16) {
-        // 1-2. Q/K/V projections, head split, attention and head merge in one
-        // kernel: the merged heads [B*Lq, D] land in the workspace.
         mha::FusedArgs f;
         f.x_q = x_q; f.x_kv = x_kv;
         f.w_q = w_q; f.w_k = w_k; f.w_v = w_v;
@@ -536,8 +552,50 @@ mha_status mha_impl(mha_dtype in_dt, mha_dtype out_dt,
         f.B = B; f.H = h; f.Lq = Lq; f.Lk = Lk; f.D = d_model;
         f.valid_lens = valid_lens;
         f.causal = causal ? 1 : 0;
-        e = timed("attn_fused_bf16", s, [&] { return mha::launch_mha_attn_fused(f, s); });
-        if (e != hipSuccess) return MHA_EHIP;
+        if (mha::mha_attn_fused_small_fits(f) || fused_route_pays(Lq, Lk, causal != 0)) {
+            // 1-2. Q/K/V projections, head split, attention and head merge in
+            // one kernel (K and V projected on chip for each block of
+            // queries); the merged heads land in the workspace.
+            e = timed("attn_fused_bf16", s, [&] { return mha::launch_mha_attn_fused(f, s); });
+            if (e != hipSuccess) return MHA_EHIP;
+        } else {
+            // 1. Q/K/V projections in one launch (three problems): Q times
+            // log2(e)/sqrt(d_k) and K as bf16 hi + lo planes, V in bf16.
+            // Workspace: merged heads [B*Lq, D], Q hi, Q lo [B*Lq, D], K hi,
+            // K lo, V [B*Lk, D], all bf16.
+            const size_t qb = round_up((size_t)B * Lq * d_model * 2, 256);
+            const size_t kb = round_up((size_t)B * Lk * d_model * 2, 256);
+            char* Qh = w + qb;
+            char* Ql = Qh + qb;
+            char* Kh = Ql + qb;
+            char* Kl = Kh + kb;
+            char* V = Kl + kb;
+            mha::GemmArgs g;
+            g.nprob = 3;
+            g.N = d_model;
+            g.K = d_model;
+            g.p[0] = {x_q, w_q, b_q, Qh, B * Lq};
+            g.p[0].c_lo = Ql;
+            g.p[0].scale = mha::kLog2e / 8.0f;   // log2(e) / sqrt(64)
+            g.p[1] = {x_kv, w_k, b_k, Kh, B * Lk};
+            g.p[1].c_lo = Kl;
+            g.p[2] = {x_kv, w_v, b_v, V, B * Lk};
+            e = timed("qkv_proj_bf16", s, [&] { return mha::launch_gemm_bf16(g, false, s); });
+            if (e != hipSuccess) return MHA_EHIP;
+            // 2. Attention per head over [B*L, D] viewed as [B, L, h, d_k],
+            // scores from the three hi/lo products.
+            mha::SdpaArgs a;
+            a.q = Qh; a.q_lo = Ql; a.k = Kh; a.k_lo = Kl; a.v = V; a.o = Ocat;
+            a.sq[0] = (long long)Lq * d_model; a.sq[1] = d_k; a.sq[2] = d_model;
+            a.sk[0] = (long long)Lk * d_model; a.sk[1] = d_k; a.sk[2] = d_model;
+            a.sv[0] = (long long)Lk * d_model; a.sv[1] = d_k; a.sv[2] = d_model;
+            a.so[0] = (long long)Lq * d_model; a.so[1] = d_k; a.so[2] = d_model;
+            a.B = B; a.H = h; a.Lq = Lq; a.Lk = Lk;
+            a.valid_lens = valid_lens;
+            a.causal = causal ? 1 : 0;
+            e = timed("sdpa_hilo_bf16", s, [&] { return mha::launch_sdpa_bf16(a, false, s); });
+            if (e != hipSuccess) return MHA_EHIP;
+        }
     } else {
         // Workspace: merged heads [B*Lq, D], Q [B*Lq, D], K [B*Lk, D], V [B*Lk, D].
         const size_t qbytes = round_up((size_t)B * Lq * d_model * ie, 256);

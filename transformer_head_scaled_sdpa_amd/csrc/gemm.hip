@@ -212,6 +212,19 @@ __global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_nt(GemmArgs g, i
         if constexpr (kOutF32) {
             *reinterpret_cast<float4*>(static_cast<float*>(P.c) + o) = make_float4(y[0], y[1], y[2], y[3]);
         } else {
+            if (P.c_lo) {
+                // y * scale as a bf16 pair: hi, then the rounding remainder.
+                float lo[kW];
+#pragma unroll
+                for (int e = 0; e < kW; ++e) {
+                    const float x = y[e] * P.scale;
+                    y[e] = bf16_to_f32(static_cast<bf16_t>(pack_bf16x2(x, 0.0f) & 0xffffu));
+                    lo[e] = x - y[e];
+                }
+                *reinterpret_cast<uint4*>(static_cast<bf16_t*>(P.c_lo) + o) =
+                    make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(lo[4], lo[5]),
+                               pack_bf16x2(lo[6], lo[7]));
+            }
             *reinterpret_cast<uint4*>(static_cast<bf16_t*>(P.c) + o) =
                 make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
                            pack_bf16x2(y[6], y[7]));

@@ -16,6 +16,12 @@ struct SdpaArgs {
     int B, H, Lq, Lk;
     const int* valid_lens;  // device int32 [B] or nullptr
     int causal;
+    // Optional second bf16 planes of Q and K (same strides): when set, q and
+    // q_lo hold q * log2(e) / sqrt(d_k) as hi + lo and k, k_lo hold k as
+    // hi + lo; scores are formed from three products (hi.hi + lo.hi + hi.lo)
+    // and come out in log2 units.  Bf16 output only.
+    const void* q_lo = nullptr;
+    const void* k_lo = nullptr;
 };
 
 // C[m, n] = sum_k A[m, k] * W[n, k] + bias[n] for up to three problems that
@@ -27,6 +33,11 @@ struct GemmProblem {
     void* c;           // [M, N] row-major
     int M;
     const void* res = nullptr;  // [M, N] in the input dtype, added to c (a residual), or nullptr
+    // bf16 output only: when c_lo is set, y = (A W^T + bias) * scale is
+    // written as two bf16 planes, c = bf16(y) and c_lo = bf16(y - c), which
+    // together carry about 16 significant bits.
+    void* c_lo = nullptr;
+    float scale = 1.0f;
 };
 
 struct GemmArgs {

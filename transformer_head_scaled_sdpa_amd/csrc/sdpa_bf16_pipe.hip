@@ -136,6 +136,23 @@ __device__ __forceinline__ void tile_scores(f32x16 (&s)[2], const bf16_t* ks, co
     }
 }
 
+// Scores of one 64-key tile from hi + lo operands (q * log2(e)/sqrt(d_k)
+// and k each split as hi + lo): hi.hi + lo.hi + hi.lo, in log2 units.
+__device__ __forceinline__ void tile_scores_hilo(f32x16 (&s)[2], const bf16_t* ks, const bf16_t* ksl,
+                                                 const bf16x8 (&qf)[4], const bf16x8 (&qfl)[4], int l32, int hb) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const int off = (jb * 32 + l32) * kLdsK + kk * 16 + hb * 8;
+            const bf16x8 kf = frag(ks + off), kfl = frag(ksl + off);
+            s[jb] = mfma32x32x16(kf, qf[kk], kk == 0 ? f32x16{} : s[jb]);
+            s[jb] = mfma32x32x16(kfl, qf[kk], s[jb]);
+            s[jb] = mfma32x32x16(kf, qfl[kk], s[jb]);
+        }
+    }
+}
+
 // O^T += V^T P^T over one 64-key tile.
 __device__ __forceinline__ void tile_pv(f32x16 (&o)[2], const bf16_t* vs, const u32x4 (&p)[4], int hb, int lane) {
 #pragma unroll
@@ -190,9 +207,9 @@ __device__ __forceinline__ void weights(const f32x16 (&s)[2], float m, float c, 
 // of v_mfma_f32_16x16x32_bf16, lane l holds 8 weights of query l % 32 (keys
 // of lane half l / 32), which the MFMA files under column l % 16 and k-group
 // l / 16.  The selector A has row 0 = 1 over k-groups 0 and 2 (lanes l and
-// l + 32: query l) and row 1 = 1 over k-groups 1 and 3 (query l + 16), so
-// lanes 0..15 receive the sums over the tile's 64 keys: element 0 for query
-// l, element 1 for query l + 16.  These are sums of the same bf16 weights
+// l + 32: query l) and row 1 = 1 over k-groups 1 and 3 (query l + 16), and
+// 2^-126 elsewhere, so lanes 0..15 receive the sums over the tile's 64 keys:
+// element 0 for query l, element 1 for query l + 16.  These are sums of the same bf16 weights
 // the P.V product uses, formed where the VALU (which bounds the loop) is not
 // involved.
 __device__ __forceinline__ f32x4 tile_sums(const bf16x8& sel, const u32x4 (&w)[4]) {
@@ -232,10 +249,11 @@ __device__ __forceinline__ void rescale(const f32x16 (&s)[2], float& m, float c,
     weights(s, m, c, w);
 }
 
-template <bool kCausal, bool kHasVl, bool kOutF32>
+template <bool kCausal, bool kHasVl, bool kOutF32, bool kHiLo>
 __global__ __launch_bounds__(kThreads, 1)
 void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
-    __shared__ __attribute__((aligned(16))) bf16_t kbuf[2 * kTileK];
+    // K tiles (two buffers), then with hi + lo operands the two K lo tiles.
+    __shared__ __attribute__((aligned(16))) bf16_t kbuf[(kHiLo ? 4 : 2) * kTileK];
     __shared__ __attribute__((aligned(16))) bf16_t vbuf[2 * kTileV];
 
     const int tid = threadIdx.x;
@@ -280,28 +298,50 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
                        (uint32_t)((long long)(Lk - 1) * a.sv[2] * 2 + kD * 2), (uint32_t)(a.sv[2] * 2 * kBN),
                        (uint32_t)((tid >> 3) * a.sv[2] * 2) + (tid & 7) * 16};
     auto load_k = [&](int t) { return load_tile(ksrc, t); };
+    // K lo plane (hi + lo operands only; same strides as K).
+    const TileSrc klsrc{kHiLo ? reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.k_lo) + b * a.sk[0] + hd * a.sk[1])
+                              : ksrc.base,
+                        ksrc.range, ksrc.tile_bytes, ksrc.lane_off};
+    auto load_kl = [&](int t) { return load_tile(klsrc, t); };
+    bf16_t* const klbuf = kbuf + 2 * kTileK;
     auto load_v = [&](int t) { return load_tile(vsrc, t); };
 
     // Prologue: K tiles 0 and 1 into LDS, scores of tile 0; K(2), K(3), V(0)
     // and V(1) wait in registers for stages 0 and 1.
     uint4 nk_e = load_k(0);
     uint4 nk_o = load_k(1);
-    bf16x8 qf[4];
+    bf16x8 qf[4], qfl[4];
+    const bf16_t* qlp = kHiLo ? static_cast<const bf16_t*>(a.q_lo) + b * a.sq[0] + hd * a.sq[1] : qp;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (i < a.Lq) raw = *reinterpret_cast<const uint4*>(qp + (long long)i * a.sq[2] + kk * 16 + hb * 8);
+        uint4 raw = make_uint4(0, 0, 0, 0), rawl = make_uint4(0, 0, 0, 0);
+        if (i < a.Lq) {
+            raw = *reinterpret_cast<const uint4*>(qp + (long long)i * a.sq[2] + kk * 16 + hb * 8);
+            if (kHiLo) rawl = *reinterpret_cast<const uint4*>(qlp + (long long)i * a.sq[2] + kk * 16 + hb * 8);
+        }
         qf[kk] = __builtin_bit_cast(bf16x8, raw);
+        qfl[kk] = __builtin_bit_cast(bf16x8, rawl);
     }
     store_chunk<kLdsK>(nk_e, kbuf, tid);
     store_chunk<kLdsK>(nk_o, kbuf + kTileK, tid);
-    nk_e = load_k(2);
-    nk_o = load_k(3);
+    // With hi + lo operands the K tiles run one stage ahead (hi in nk_e, lo
+    // in nk_o, both for the same tile) to keep the register count; plain
+    // operands run two stages ahead (even and odd tiles in nk_e, nk_o).
+    if constexpr (kHiLo) {
+        store_chunk<kLdsK>(load_kl(0), klbuf, tid);
+        store_chunk<kLdsK>(load_kl(1), klbuf + kTileK, tid);
+        nk_e = load_k(2);
+        nk_o = load_kl(2);
+    } else {
+        nk_e = load_k(2);
+        nk_o = load_k(3);
+    }
     uint4 nv_e = load_v(0);
     uint4 nv_o = load_v(1);
     __syncthreads();
     f32x16 sc[2];                 // scores of the tile whose softmax runs next
-    tile_scores(sc, kbuf, qf, l32, hb);
+    if constexpr (kHiLo) tile_scores_hilo(sc, kbuf, klbuf, qf, qfl, l32, hb);
+    else tile_scores(sc, kbuf, qf, l32, hb);
     __syncthreads();              // K(0)'s buffer is refilled in stage 0
 
     f32x16 o[2] = {};             // O^T accumulators: features [0,32) and [32,64)
@@ -309,13 +349,17 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
     u32x4 pa[4], pb[4];           // weights of two consecutive tiles (B operand)
     float m = 0.0f;               // exponent offset (log2 units of the scaled scores)
     float l[2] = {0.0f, 0.0f};    // running weight sums (elements 0, 1 of tile_sums' layout)
-    // Row selector of tile_sums (bf16 ones in lanes 0, 32 and 17, 49).
+    // Row selector of tile_sums: 1 in lanes 0, 32 and 17, 49; elsewhere the
+    // smallest normal bf16, 2^-126, rather than 0, so that a weight that
+    // overflowed to infinity (a tile far above the offset) makes the sums
+    // infinite, which triggers the rescale, instead of 0 * inf = NaN.  The
+    // stray terms are below 2^-100 of any sum.
     bf16x8 sel;
     {
-        const __bf16 one = (lane == 0 || lane == 32 || lane == 17 || lane == 49) ? static_cast<__bf16>(1.0f)
-                                                                                : static_cast<__bf16>(0.0f);
+        const uint16_t bits = (lane == 0 || lane == 32 || lane == 17 || lane == 49) ? 0x3f80u : 0x0080u;
+        const __bf16 v = __builtin_bit_cast(__bf16, bits);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sel[e] = one;
+        for (int e = 0; e < 8; ++e) sel[e] = v;
     }
     auto over = [&](const f32x4& t) { return __any(fmaxf(t[0], t[1]) > kSumLimit); };
 
@@ -326,10 +370,22 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
     // zeros and land in buffers no stage reads again, so the copy is the same
     // straight-line code every stage.
     auto copy_tiles = [&](int s, uint4& nk, uint4& nv) {
-        store_chunk<kLdsK>(nk, kbuf + (s & 1) * kTileK, tid);
+        if constexpr (kHiLo) {
+            store_chunk<kLdsK>(nk_e, kbuf + (s & 1) * kTileK, tid);
+            store_chunk<kLdsK>(nk_o, klbuf + (s & 1) * kTileK, tid);
+            nk_e = load_k(s + 3);
+            nk_o = load_kl(s + 3);
+        } else {
+            store_chunk<kLdsK>(nk, kbuf + (s & 1) * kTileK, tid);
+            nk = load_k(s + 4);
+        }
         store_chunk<kLdsV>(nv, vbuf + (s & 1) * kTileV, tid);
-        nk = load_k(s + 4);
         nv = load_v(s + 2);
+    };
+    auto scores = [&](f32x16 (&nxt)[2], int s) {
+        const bf16_t* ks = kbuf + ((s + 1) & 1) * kTileK;
+        if constexpr (kHiLo) tile_scores_hilo(nxt, ks, klbuf + ((s + 1) & 1) * kTileK, qf, qfl, l32, hb);
+        else tile_scores(nxt, ks, qf, l32, hb);
     };
     // Unmasked steady state: softmax(s), scores(s+1) and P.V(s-1), independent.
     // Everything up to the barrier is one branch-free block, so the scheduler
@@ -339,11 +395,10 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
     // enters a product.
     auto fast_stage = [&](int s, f32x16 (&cur)[2], f32x16 (&nxt)[2], const u32x4 (&prev)[4], u32x4 (&pcur)[4], uint4& nk, uint4& nv) {
         copy_tiles(s, nk, nv);
-        const bf16_t* ks = kbuf + ((s + 1) & 1) * kTileK;
         const bf16_t* vs = vbuf + ((s + 1) & 1) * kTileV;
         weights(cur, m, c, pcur);
         f32x4 t = tile_sums(sel, pcur);
-        tile_scores(nxt, ks, qf, l32, hb);
+        scores(nxt, s);
         tile_pv(o, vs, prev, hb, lane);
         __syncthreads();
         if (over(t)) [[unlikely]] {
@@ -357,7 +412,6 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
     // Pipeline edges, masked tiles and fully masked rows.
     auto slow_stage = [&](int s, f32x16 (&cur)[2], f32x16 (&nxt)[2], const u32x4 (&prev)[4], u32x4 (&pcur)[4], uint4& nk, uint4& nv) {
         copy_tiles(s, nk, nv);
-        const bf16_t* ks = kbuf + ((s + 1) & 1) * kTileK;
         const bf16_t* vs = vbuf + ((s + 1) & 1) * kTileV;
         if (s >= 1 && s - 1 < n_w) tile_pv(o, vs, prev, hb, lane);
         if (s < n_w) {
@@ -374,7 +428,7 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
             l[0] += t[0];
             l[1] += t[1];
         }
-        if (s + 1 < n_w) tile_scores(nxt, ks, qf, l32, hb);
+        if (s + 1 < n_w) scores(nxt, s);
         __syncthreads();
     };
 
@@ -440,13 +494,14 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
     }
 }
 
-template <bool kCausal, bool kHasVl, bool kOutF32>
+template <bool kCausal, bool kHasVl, bool kOutF32, bool kHiLo>
 hipError_t launch_variant(const SdpaArgs& a, hipStream_t s) {
     const int n_qtiles = (a.Lq + kBM - 1) / kBM;
     const long long grid = (long long)n_qtiles * a.B * a.H;
-    const float c = kLog2e / 8.0f;   // log2(e) / sqrt(64)
-    hipLaunchKernelGGL((sdpa_fwd_bf16_pipe<kCausal, kHasVl, kOutF32>), dim3((unsigned)grid), dim3(kThreads), 0, s,
-                       a, n_qtiles, c);
+    // Exponent scale: log2(e) / sqrt(64), or 1 when q arrives pre-scaled.
+    const float c = kHiLo ? 1.0f : kLog2e / 8.0f;
+    hipLaunchKernelGGL((sdpa_fwd_bf16_pipe<kCausal, kHasVl, kOutF32, kHiLo>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       s, a, n_qtiles, c);
     return hipGetLastError();
 }
 
@@ -454,12 +509,17 @@ hipError_t launch_variant(const SdpaArgs& a, hipStream_t s) {
 
 hipError_t launch_sdpa_bf16(const SdpaArgs& a, bool out_f32, hipStream_t s) {
     const bool c = a.causal != 0, v = a.valid_lens != nullptr;
-    if (out_f32) {
-        if (c) return v ? launch_variant<true, true, true>(a, s) : launch_variant<true, false, true>(a, s);
-        return v ? launch_variant<false, true, true>(a, s) : launch_variant<false, false, true>(a, s);
+    if (a.q_lo) {   // hi + lo operands: bf16 output
+        if (out_f32 || !a.k_lo) return hipErrorInvalidValue;
+        if (c) return v ? launch_variant<true, true, false, true>(a, s) : launch_variant<true, false, false, true>(a, s);
+        return v ? launch_variant<false, true, false, true>(a, s) : launch_variant<false, false, false, true>(a, s);
     }
-    if (c) return v ? launch_variant<true, true, false>(a, s) : launch_variant<true, false, false>(a, s);
-    return v ? launch_variant<false, true, false>(a, s) : launch_variant<false, false, false>(a, s);
+    if (out_f32) {
+        if (c) return v ? launch_variant<true, true, true, false>(a, s) : launch_variant<true, false, true, false>(a, s);
+        return v ? launch_variant<false, true, true, false>(a, s) : launch_variant<false, false, true, false>(a, s);
+    }
+    if (c) return v ? launch_variant<true, true, false, false>(a, s) : launch_variant<true, false, false, false>(a, s);
+    return v ? launch_variant<false, true, false, false>(a, s) : launch_variant<false, false, false, false>(a, s);
 }
 
 }  // namespace mha
