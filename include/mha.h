@@ -164,8 +164,8 @@ mha_status sdpa_decode(mha_dtype in_dt, mha_dtype out_dt,
  * MFMA with fp32 accumulation (the weights and ds rounded to bf16 for their
  * products, as the forward rounds its weights); MHA_F32 inputs in fp32 FMA.
  * Requirements otherwise as for sdpa_forward; for MHA_BF16 inputs each
- * (batch, head)'s rows of q, k, v and dout must span less than 2 GiB
- * (MHA_ENOTSUP otherwise).
+ * (batch, head)'s rows of q, k, v, o and dout must span less than 2 GiB, as
+ * must 128 rows at each one's row stride (MHA_ENOTSUP otherwise).
  */
 size_t sdpa_backward_workspace_bytes(int B, int h, int Lq);
 

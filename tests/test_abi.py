@@ -278,6 +278,8 @@ def test_backward_workspace_and_validation(lib):
     assert bwd(lib, dk_=ctypes.c_void_p(P + 0x600000 + 8)) == EINVAL
     # bf16 rows of one (batch, head) spanning 2 GiB or more: not supported
     assert bwd(lib, st=S(0, 0, 1 << 24), Lq=128, Lk=128) == ENOTSUP
+    # two rows fit, but 128 rows at this stride span 2 GiB: not supported
+    assert bwd(lib, st=S(0, 0, 1 << 23), B=1, h=1, Lq=2, Lk=2) == ENOTSUP
 
 
 def sub(lib, **kw):

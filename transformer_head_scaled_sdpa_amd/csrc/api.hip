@@ -246,7 +246,10 @@ mha_status sdpa_backward(mha_dtype in_dt, mha_dtype out_dt,
         if (st.b < 0 || st.h < 0 || st.l < 0 || st.b % omult || st.h % omult || st.l % omult) return MHA_EINVAL;
     const size_t ie = elem_size(in_dt), oe = elem_size(out_dt);
     if (in_dt == MHA_BF16 && (!rows_fit_buffer(sq.l, Lq, ie) || !rows_fit_buffer(sdo.l, Lq, ie) ||
-                              !rows_fit_buffer(sk.l, Lk, ie) || !rows_fit_buffer(sv.l, Lk, ie)))
+                              !rows_fit_buffer(so.l, Lq, ie) || !rows_fit_buffer(sk.l, Lk, ie) ||
+                              !rows_fit_buffer(sv.l, Lk, ie) || !tile_rows_fit(sq.l, ie) ||
+                              !tile_rows_fit(sdo.l, ie) || !tile_rows_fit(so.l, ie) || !tile_rows_fit(sk.l, ie) ||
+                              !tile_rows_fit(sv.l, ie)))
         return MHA_ENOTSUP;
     const uintptr_t wb = reinterpret_cast<uintptr_t>(workspace);
     const Range ins[] = {view_range(q, sq, B, h, Lq, d_k, ie), view_range(k, sk, B, h, Lk, d_k, ie),

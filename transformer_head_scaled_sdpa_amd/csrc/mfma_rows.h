@@ -48,6 +48,15 @@ __device__ __forceinline__ f32x16 tile_dot(const bf16_t* t, const bf16x8 (&f)[4]
     return acc;
 }
 
+// The same product added to a given accumulator.
+__device__ __forceinline__ f32x16 tile_dot_from(const bf16_t* t, const bf16x8 (&f)[4], const f32x16& init, int l32,
+                                                int hb) {
+    f32x16 acc = mfma32x32x16(frag(t + l32 * kLdsR + hb * 8), f[0], init);
+#pragma unroll
+    for (int kk = 1; kk < 4; ++kk) acc = mfma32x32x16(frag(t + l32 * kLdsR + kk * 16 + hb * 8), f[kk], acc);
+    return acc;
+}
+
 // Transposed fragment of a row-major [32 rows][64 features] LDS tile (192 B
 // rows): the A operand [32 features x 16 rows] for features tb*32 + lane%32
 // and the tile rows of slice kb in the order the packed B operands use
@@ -99,7 +108,10 @@ struct StepSrc {
 constexpr int kBufWord3 = 0x00020000;
 // Whether an [L, 64] view with row stride ld fits one buffer range (32-bit
 // byte offsets); launchers refuse views that do not.
-inline bool fits_buffer(long long ld, int L) { return L <= 0 || (long long)(L - 1) * ld * 2 + kD * 2 < (1ll << 31); }
+// The per-lane offsets of a step (up to kStep rows) must not wrap either.
+inline bool fits_buffer(long long ld, int L) {
+    return ld * 2 * kStep < (1ll << 31) && (L <= 0 || (long long)(L - 1) * ld * 2 + kD * 2 < (1ll << 31));
+}
 
 __device__ __forceinline__ StepSrc step_src(const bf16_t* x, long long ld, int L, int tid) {
     StepSrc s;
@@ -132,6 +144,28 @@ __device__ __forceinline__ Chunks load_step(const StepSrc& s, int r0) {
 // Store a step into the per-phase tiles: row r goes to phase r / 32, in
 // 144-byte rows at byte offset offR of the phase area (if offR >= 0) and in
 // 192-byte rows at offT (if offT >= 0).
+// Chunk tid of the 64 rows r0 .. r0+63 (row tid / 8, features (tid % 8) * 8
+// ..), zero past row L - 1: the first chunk of a step.
+__device__ __forceinline__ uint4 load_chunk(const StepSrc& s, int r0) {
+    const unsigned long long skip = (unsigned long long)(uint32_t)r0 * s.row_bytes;
+    const bool any = skip < s.range;
+    const uint32_t left = any ? s.range - (uint32_t)skip : 0u;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(s.base + (any ? skip : 0ull)), (short)0, (int)left, kBufWord3);
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, s.voff[0], 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// 64-row staging tiles of 144-byte rows in LDS: store chunk tid of tile t,
+// read the fragment of row r, features kk*16 + hb*8 .. +7.
+constexpr int kStageB = kRowsWg * kLdsR * 2;
+__device__ __forceinline__ void stage_chunk(char* smem, int t, uint4 c, int tid) {
+    *reinterpret_cast<uint4*>(smem + t * kStageB + (tid >> 3) * (kLdsR * 2) + (tid & 7) * 16) = c;
+}
+__device__ __forceinline__ uint4 staged_frag(const char* smem, int t, int r, int kk, int hb) {
+    return *reinterpret_cast<const uint4*>(smem + t * kStageB + r * (kLdsR * 2) + kk * 32 + hb * 16);
+}
+
 __device__ __forceinline__ void store_step(const Chunks& t, char* smem, int phase_bytes, int offR, int offT, int tid) {
 #pragma unroll
     for (int n = 0; n < kChunks; ++n) {
@@ -153,12 +187,15 @@ __device__ __forceinline__ int row_len(const Args& a, int b, int i) {
 // Keys [0, klim) are allowed for query i; a row with no allowed key (lengths
 // given, length <= 0) allows all Lk keys with equal scores (`none`).
 template <bool kCausal, typename Args>
-__device__ __forceinline__ int key_limit(const Args& a, int b, int i, bool& none) {
-    const int len = row_len(a, b, i);
+__device__ __forceinline__ int limit_from_len(const Args& a, int len, int i, bool& none) {
     none = a.vl_rank != 0 && len <= 0;
     if (none) return a.Lk;
     const int lim = min(len, a.Lk);
     return kCausal ? min(lim, i + 1) : lim;
+}
+template <bool kCausal, typename Args>
+__device__ __forceinline__ int key_limit(const Args& a, int b, int i, bool& none) {
+    return limit_from_len<kCausal>(a, row_len(a, b, i), i, none);
 }
 
 // Sum the per-phase partials of a 32-row accumulator pair through LDS: the
@@ -182,6 +219,58 @@ __device__ __forceinline__ void reduce_read(const float* red, f32x16 (&acc)[2], 
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[tb][v] += slot[(tb * 16 + v) * 64 + lane];
+    }
+}
+
+// The same sum spread over all four phase waves, one quarter of the 64
+// features each.  part_write: every wave writes its partial times `scale` to
+// its own 8 KiB slot (values 4q .. 4q+3 of lane l, q = tb*4 + g4, at float
+// (q*64 + l)*4, 16-byte accesses).  After a barrier (the caller's),
+// part_sum: wave ph adds feature block tb = ph/2, groups g4 = 2*(ph%2) + n
+// (n = 0, 1) over the four slots of its group.  The slots take kRedAllB bytes.
+constexpr int kRedSlotF = 32 * 64;
+constexpr int kRedAllB = kGroups * kPhases * kRedSlotF * 4;
+__device__ __forceinline__ void part_write(float* red, const f32x16 (&acc)[2], float scale, int grp, int ph,
+                                           int lane) {
+    float* slot = red + (grp * kPhases + ph) * kRedSlotF;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<float4*>(slot + ((tb * 4 + g4) * 64 + lane) * 4) =
+                make_float4(acc[tb][g4 * 4] * scale, acc[tb][g4 * 4 + 1] * scale, acc[tb][g4 * 4 + 2] * scale,
+                            acc[tb][g4 * 4 + 3] * scale);
+}
+__device__ __forceinline__ void part_sum(const float* red, float4 (&r)[2], int grp, int ph, int lane) {
+    const int tb = ph >> 1;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int q = tb * 4 + (ph & 1) * 2 + n;
+        float4 t = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int p = 0; p < kPhases; ++p) {
+            const float4 x = *reinterpret_cast<const float4*>(red + (grp * kPhases + p) * kRedSlotF + (q * 64 + lane) * 4);
+            t.x += x.x;
+            t.y += x.y;
+            t.z += x.z;
+            t.w += x.w;
+        }
+        r[n] = t;
+    }
+}
+// Store wave ph's quarter from part_sum times `scale` (features
+// tb*32 + g4*8 + hb*4 .. +3 for its two groups g4).
+__device__ __forceinline__ void store_quarter(void* base, long long off, bool out_f32, const float4 (&r)[2],
+                                              float scale, int ph, int hb) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int t = (ph >> 1) * 32 + ((ph & 1) * 2 + n) * 8 + hb * 4;
+        const float y0 = r[n].x * scale, y1 = r[n].y * scale, y2 = r[n].z * scale, y3 = r[n].w * scale;
+        if (out_f32)
+            *reinterpret_cast<float4*>(static_cast<float*>(base) + off + t) = make_float4(y0, y1, y2, y3);
+        else
+            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(base) + off + t) =
+                make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
     }
 }
 

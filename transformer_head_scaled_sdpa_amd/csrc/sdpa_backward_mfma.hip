@@ -41,14 +41,26 @@ using namespace rows64;
 // ---------------------------------------------------------------------------
 // rows: log-sum-exp, D, dq
 // ---------------------------------------------------------------------------
-constexpr int kRowsKR = 0;                        // K, 144-byte rows
-constexpr int kRowsKT = kTileRB;                  // K, 192-byte rows
-constexpr int kRowsVR = kTileRB + kTileTB;        // V, 144-byte rows
-constexpr int kRowsPhase = 2 * kTileRB + kTileTB;
+// LDS: the K and V tiles in 144-byte rows (score products) in two slots,
+// the K tiles in 192-byte rows (transposed reads for dq) in three: step st
+// goes to K/V slot st % 2 and K^T slot st % 3.  The scores of step st + 1 are
+// computed during step st, so at step st the K/V slot of st + 1 and the K^T
+// slot of st are read while step st + 2 is written to the slots of st (K/V,
+// last read during step st - 1) and st - 1 (K^T).  The staged Q, dO and O
+// sit in K^T slot 2 before the first step, the dq partials at the start
+// after the last.
+constexpr int kRowsSlotR = kPhases * kTileRB;     // one step in 144-byte rows
+constexpr int kRowsSlotT = kPhases * kTileTB;     // one step in 192-byte rows
+constexpr int kRowsKR = 0;
+constexpr int kRowsVR = 2 * kRowsSlotR;
+constexpr int kRowsKT = 4 * kRowsSlotR;
+constexpr int kRowsStage = kRowsKT + 2 * kRowsSlotT;
+constexpr int kRowsLds = kRowsStage + 3 * kStageB;
+static_assert(kRowsKT + 3 * kRowsSlotT <= kRowsLds && kRedAllB <= kRowsLds, "tiles and partials fit");
 
 template <bool kCausal>
 __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, float c) {
-    __shared__ __attribute__((aligned(16))) char smem[kPhases * kRowsPhase];
+    __shared__ __attribute__((aligned(16))) char smem[kRowsLds];
     __shared__ float2 stat_s[kGroups][kPhases][2][32];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -68,8 +80,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
 
     bool none = false;
     const int klim = live ? key_limit<kCausal>(a, b, i, none) : Lk;
-    const float cs = none ? 0.0f : c;      // score scale (log2 units); 0: equal scores
-    const float dm = none ? 0.0f : 1.0f;   // 0: no gradient through the scores
+    // Score scale (log2 units).  A row with no allowed key weights its keys
+    // equally: its scale 2^-100 makes every finite score's exponent round to
+    // the same value while masked keys (-inf) still weigh 0.
+    const float cs = none ? 0x1p-100f : c;
     int kmin = klim;                        // smallest key limit in the wave
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) kmin = min(kmin, __shfl_xor(kmin, o));
@@ -85,22 +99,56 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
     const bf16_t* kp = static_cast<const bf16_t*>(a.k) + b * a.sk[0] + hd * a.sk[1];
     const bf16_t* vp = static_cast<const bf16_t*>(a.v) + b * a.sv[0] + hd * a.sv[1];
 
-    const StepSrc ksrc = step_src(kp, a.sk[2], Lk, tid), vsrc = step_src(vp, a.sv[2], Lk, tid);
-    Chunks nk = load_step(ksrc, 0);
+    // This workgroup's 64 rows of Q, dO and O: one range-checked 16-byte
+    // chunk per thread each (zeros past the queries), issued first and
+    // staged through LDS, so the four phase waves of a group read their
+    // fragments from there instead of each loading them.
+    const StepSrc qsrc = step_src(qp, a.sq[2], Lq, tid), gsrc = step_src(gp, a.sdo[2], Lq, tid),
+                  osrc = step_src(op, a.so[2], Lq, tid);
+    const uint4 cq = load_chunk(qsrc, q_wg), cg = load_chunk(gsrc, q_wg), co = load_chunk(osrc, q_wg);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // Q and dO fragments (B operands: query lane%32, features kk*16 + hb*8 ..).
+    // K and V steps go to LDS two steps before their scores are computed
+    // (see the slots above), from registers loaded two steps before that
+    // (even and odd steps in their own registers).  The range ends at the
+    // last key the workgroup visits, so loads past it read zeros without a
+    // memory access and every load and store is unconditional: each store
+    // waits only for its own loads.  The prologue issues them in the loop's
+    // order, so the waits the compiler derives hold on every iteration.
+    const StepSrc ksrc = step_src(kp, a.sk[2], kv_end, tid), vsrc = step_src(vp, a.sv[2], kv_end, tid);
+    Chunks nk_e = load_step(ksrc, 0), nv_e = load_step(vsrc, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    Chunks nk_o = load_step(ksrc, kStep), nv_o = load_step(vsrc, kStep);
+    __builtin_amdgcn_sched_barrier(0);
+    auto put = [&](const Chunks& nk, const Chunks& nv, int slot2, int slot3) {
+        store_step(nk, smem + kRowsKR + slot2 * kRowsSlotR, kTileRB, 0, -1, tid);
+        store_step(nv, smem + kRowsVR + slot2 * kRowsSlotR, kTileRB, 0, -1, tid);
+        store_step(nk, smem + kRowsKT + slot3 * kRowsSlotT, kTileTB, -1, 0, tid);
+    };
+    char* const stage = smem + kRowsStage;
+    stage_chunk(stage, 0, cq, tid);
+    stage_chunk(stage, 1, cg, tid);
+    stage_chunk(stage, 2, co, tid);
+    put(nk_e, nv_e, 0, 0);
+    nk_e = load_step(ksrc, 2 * kStep);
+    nv_e = load_step(vsrc, 2 * kStep);
+    put(nk_o, nv_o, 1, 1);
+    nk_o = load_step(ksrc, 3 * kStep);
+    nv_o = load_step(vsrc, 3 * kStep);
+    __syncthreads();
+
+    // Q and dO fragments (B operands: query lane%32, features kk*16 + hb*8 ..);
+    // a row with no allowed key passes no gradient through its scores, so
+    // its dO fragment is zero (with D below, dp - D is then 0).
     bf16x8 qf[4], gf[4];
     float dsum = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        uint4 rq = make_uint4(0, 0, 0, 0), rg = rq, ro = rq;
-        if (live) {
-            rq = *reinterpret_cast<const uint4*>(qp + (long long)i * a.sq[2] + kk * 16 + hb * 8);
-            rg = *reinterpret_cast<const uint4*>(gp + (long long)i * a.sdo[2] + kk * 16 + hb * 8);
-            ro = *reinterpret_cast<const uint4*>(op + (long long)i * a.so[2] + kk * 16 + hb * 8);
-        }
+        const uint4 rq = staged_frag(stage, 0, grp * 32 + l32, kk, hb);
+        const uint4 rg = staged_frag(stage, 1, grp * 32 + l32, kk, hb);
+        const uint4 ro = staged_frag(stage, 2, grp * 32 + l32, kk, hb);
         qf[kk] = __builtin_bit_cast(bf16x8, rq);
-        gf[kk] = __builtin_bit_cast(bf16x8, rg);
+        gf[kk] = __builtin_bit_cast(bf16x8, none ? make_uint4(0, 0, 0, 0) : rg);
         const uint32_t ug[4] = {rg.x, rg.y, rg.z, rg.w}, uo[4] = {ro.x, ro.y, ro.z, ro.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -108,6 +156,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
                     __uint_as_float(ug[e] & 0xffff0000u) * __uint_as_float(uo[e] & 0xffff0000u);
     }
     dsum = pair_sum(dsum);                  // D_i over both lane halves
+    // dP^T - D starts from -D in the accumulator (element v of a lane is the
+    // lane's query).
+    f32x16 neg_d;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) neg_d[v] = none ? 0.0f : -dsum;
 
     // ---- one pass: online softmax with a lazy offset ----
     // dq accumulates exp2(s - m) (dp - D) k with the offset m of this lane's
@@ -115,35 +168,37 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
     // exceeds it by more than kLazy, and then dq and the weight sum l (this
     // lane half's keys) are rescaled.  The phases merge at the end.
     constexpr float kLazy = 10.0f;
-    const float ddm = dsum * dm;
     float m = -INFINITY, l = 0.0f;
     f32x16 dq[2] = {};
-    Chunks nv = load_step(vsrc, 0);
-    for (int st = 0; st < n_steps; ++st) {
-        __syncthreads();
-        store_step(nk, smem, kRowsPhase, kRowsKR, kRowsKT, tid);
-        store_step(nv, smem, kRowsPhase, kRowsVR, -1, tid);
-        if (st + 1 < n_steps) {
-            nk = load_step(ksrc, (st + 1) * kStep);
-            nv = load_step(vsrc, (st + 1) * kStep);
-        }
-        __syncthreads();
+    // S^T = K Q^T and dP^T - D = V dO^T - D of step st from its K/V slot.
+    auto scores = [&](int st, f32x16& s, f32x16& dp) {
+        const char* kr = smem + kRowsKR + (st & 1) * kRowsSlotR + ph * kTileRB;
+        const char* vr = smem + kRowsVR + (st & 1) * kRowsSlotR + ph * kTileRB;
+        s = tile_dot(reinterpret_cast<const bf16_t*>(kr), qf, l32, hb);
+        dp = tile_dot_from(reinterpret_cast<const bf16_t*>(vr), gf, neg_d, l32, hb);
+    };
+    f32x16 s_e, dp_e, s_o, dp_o;
+    scores(0, s_e, dp_e);
+    // Step st (K^T slot t3 = st % 3): its scores (s, dp) were computed during
+    // step st - 1; compute step st + 1's into (s_n, dp_n), then the weights
+    // and dq; store step st + 2 from (nk, nv) and load step st + 4 there.
+    auto step = [&](int st, int t3, Chunks& nk, Chunks& nv, f32x16& s, f32x16& dp, f32x16& s_n, f32x16& dp_n) {
+        __syncthreads();   // step st + 1 stored; the slots of st (K/V) and st - 1 (K^T) free
+        put(nk, nv, st & 1, t3 == 0 ? 2 : t3 - 1);
+        nk = load_step(ksrc, (st + 4) * kStep);
+        nv = load_step(vsrc, (st + 4) * kStep);
+        scores(st + 1, s_n, dp_n);
         const int t0 = st * kStep + ph * kTile;   // this wave's keys t0 .. t0+31
-        const char* area = smem + ph * kRowsPhase;
-        const f32x16 s = tile_dot(reinterpret_cast<const bf16_t*>(area + kRowsKR), qf, l32, hb);
-        f32x16 ds = tile_dot(reinterpret_cast<const bf16_t*>(area + kRowsVR), gf, l32, hb);
-        // The tile's row max in log2 units (raw scores times cs >= 0; masked
-        // keys excluded), then the weights exp2(s * cs - m) (masked: 0).
-        const bool full = t0 + kTile <= kmin;
-        const int rel = klim - (t0 + hb * 4);
-        float mx = -INFINITY;
-        if (full) {
+        // Masked keys score -inf; the tile's row max in log2 units, then the
+        // weights exp2(s * cs - m) (masked: 0).
+        if (t0 + kTile > kmin) {
+            const int rel = klim - (t0 + hb * 4);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
-        } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, acc_row(v) < rel ? s[v] : -INFINITY);
+            for (int v = 0; v < 16; ++v) s[v] = acc_row(v) < rel ? s[v] : -INFINITY;
         }
+        float mx = s[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
         float mt = mx == -INFINITY ? -INFINITY : mx * cs;
         mt = pair_max(mt);
         if (__any(mt > m + kLazy)) {
@@ -158,34 +213,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
             m = m_new;
         }
         const float m_use = m == -INFINITY ? 0.0f : m;   // no allowed key yet: every weight is 0
-        float rs = 0.0f;
-        if (full) {
+        f32x16 ds;
+        float q4[4];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[v], cs, -m_use));
-                rs += p;
-                ds[v] = p * fmaf(ds[v], dm, -ddm);
-            }
-        } else {
+        for (int g = 0; g < 4; ++g) {
+            float pr[4];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(s[v], cs, -m_use));
-                const float p = acc_row(v) < rel ? e : 0.0f;
-                rs += p;
-                ds[v] = p * fmaf(ds[v], dm, -ddm);
+            for (int e = 0; e < 4; ++e) {
+                const int v = g * 4 + e;
+                pr[e] = __builtin_amdgcn_exp2f(fmaf(s[v], cs, -m_use));
+                ds[v] = pr[e] * dp[v];
             }
+            q4[g] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
         }
-        l += rs;
+        l += (q4[0] + q4[1]) + (q4[2] + q4[3]);
         u32x4 w[2];
         pack_b(ds, w);
-        const bf16_t* kt = reinterpret_cast<const bf16_t*>(area + kRowsKT);
+        const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem + kRowsKT + t3 * kRowsSlotT + ph * kTileTB);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const bf16x8 d8 = __builtin_bit_cast(bf16x8, w[kb]);
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) dq[tb] = mfma32x32x16(tr_frag(kt, kb, tb, hb, lane), d8, dq[tb]);
         }
+    };
+    // Pairs of steps, then a lone last step: no path through the loop skips
+    // a load, so every wait covers exactly the step it stores.  (The scores
+    // computed during the last step are past the keys and unused.)
+    int st = 0, t3 = 0;
+    for (; st + 1 < n_steps; st += 2) {
+        step(st, t3, nk_e, nv_e, s_e, dp_e, s_o, dp_o);
+        t3 = t3 == 2 ? 0 : t3 + 1;
+        step(st + 1, t3, nk_o, nv_o, s_o, dp_o, s_e, dp_e);
+        t3 = t3 == 2 ? 0 : t3 + 1;
     }
+    if (st < n_steps) step(st, t3, nk_e, nv_e, s_e, dp_e, s_o, dp_o);
     // Merge the phases: common offset M, total weight L, rescaled dq.
     stat_s[grp][ph][hb][l32] = make_float2(m, l);
     __syncthreads();
@@ -201,24 +263,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
             L += x.x == -INFINITY ? 0.0f : x.y * __builtin_amdgcn_exp2f(x.x - M);
         }
     const float own = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        dq[0][v] *= own;
-        dq[1][v] *= own;
-    }
     // v_log_f32 is the base-2 logarithm, matching the log2-unit scores.
     const float lse = L > 0.0f ? M + __builtin_amdgcn_logf(L) : 0.0f;
+    // The barrier above also ends every wave's reads of the last step's
+    // tiles, so the partials may overwrite them.
+    float* red = reinterpret_cast<float*>(smem);
+    part_write(red, dq, own, grp, ph, lane);
     __syncthreads();
-    reduce_write(reinterpret_cast<float*>(smem), dq, grp, ph, lane);
-    __syncthreads();
-    reduce_read(reinterpret_cast<const float*>(smem), dq, grp, ph, lane);
-    if (ph != 0 || !live) return;
-    if (hb == 0) {
+    float4 r[2];
+    part_sum(red, r, grp, ph, lane);
+    if (!live) return;
+    if (ph == 0 && hb == 0) {
         a.rows[((long long)bh * Lq + i) * 2] = lse;
         a.rows[((long long)bh * Lq + i) * 2 + 1] = dsum;
     }
-    store_rowT(a.dq, b * a.sdq[0] + hd * a.sdq[1] + (long long)i * a.sdq[2], a.out_f32, dq,
-               L > 0.0f ? 0.125f / L : 0.0f, hb);
+    store_quarter(a.dq, b * a.sdq[0] + hd * a.sdq[1] + (long long)i * a.sdq[2], a.out_f32, r,
+                  L > 0.0f ? 0.125f / L : 0.0f, ph, hb);
 }
 
 // ---------------------------------------------------------------------------
@@ -229,12 +289,18 @@ constexpr int kKeysQT = kTileRB;                  // Q, 192-byte rows
 constexpr int kKeysGR = kTileRB + kTileTB;        // dO, 144-byte rows
 constexpr int kKeysGT = 2 * kTileRB + kTileTB;    // dO, 192-byte rows
 constexpr int kKeysPhase = 2 * kTileRB + 2 * kTileTB;
+// The step tiles, reused first for the staged K and V and last for the dv
+// and dk partials.
+constexpr int kKeysLds = kPhases * kKeysPhase > 2 * kRedAllB ? kPhases * kKeysPhase : 2 * kRedAllB;
+static_assert(2 * kStageB <= kKeysLds, "staging fits");
 
 template <bool kCausal>
 __global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, float c) {
-    __shared__ __attribute__((aligned(16))) char smem[kPhases * kKeysPhase];
-    __shared__ float4 rowf_s[kStep];   // per streamed query: log-sum-exp, D, score scale, gradient factor
-    __shared__ int klim_s[kStep];      // per streamed query: key limit
+    __shared__ __attribute__((aligned(16))) char smem[kKeysLds];
+    // Per streamed query: log-sum-exp, -D, score scale and gradient factor
+    // (0 for a row with no allowed key), key limit.
+    __shared__ __attribute__((aligned(16))) float lse_s[kStep], nd_s[kStep], sc_s[kStep], gw_s[kStep];
+    __shared__ int klim_s[kStep];
     __shared__ int tmin_s[kPhases];    // per phase tile: smallest key limit (-1 if a row has none allowed)
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -258,84 +324,123 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, flo
     // weight none of its keys.
     const int i_begin = (kCausal && a.vl_rank == 0) ? k_wg : 0;
     const int n_steps = (Lq - i_begin + kStep - 1) / kStep;
-    const StepSrc qsrc = step_src(qp, a.sq[2], Lq, tid), gsrc = step_src(gp, a.sdo[2], Lq, tid);
-    Chunks nq = load_step(qsrc, i_begin);
-    Chunks ng = load_step(gsrc, i_begin);
+    // Q and dO steps are loaded two steps before they are stored (even and
+    // odd steps in their own registers), unconditionally: steps past the
+    // queries read as zeros.
+    // This workgroup's 64 rows of K and V: one range-checked 16-byte chunk
+    // per thread each (zeros past the keys), staged through LDS like the
+    // rows kernel's Q, dO and O.
+    const StepSrc ksrc = step_src(kp, a.sk[2], Lk, tid), vsrc = step_src(vp, a.sv[2], Lk, tid);
+    const uint4 ck = load_chunk(ksrc, k_wg), cv = load_chunk(vsrc, k_wg);
+    __builtin_amdgcn_sched_barrier(0);
 
+    // Per streamed query (threads below kStep keep them): log-sum-exp and D
+    // from the rows kernel and the query's length, read one step ahead by
+    // range-checked loads (zeros past the queries; the length load has an
+    // empty range unless lengths vary by query).
+    const __amdgpu_buffer_rsrc_t rows_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        a.rows + (long long)bh * Lq * 2, (short)0, Lq * 8, kBufWord3);
+    const __amdgpu_buffer_rsrc_t len_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int*>(a.vl_rank == 2 ? a.valid_lens + (long long)b * Lq : a.valid_lens), (short)0,
+        a.vl_rank == 2 ? Lq * 4 : 0, kBufWord3);
+    const int len_all = a.vl_rank == 1 ? a.valid_lens[b] : Lk;
+    struct RowRaw {
+        float lse, dsum;
+        int len;
+    };
+    auto fetch_rows = [&](int i0) {
+        typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+        const uint32_t qi = (uint32_t)(i0 + (tid & (kStep - 1)));
+        const u32x2v v = __builtin_amdgcn_raw_buffer_load_b64(rows_rsrc, qi * 8u, 0, 0);
+        const int len = (int)__builtin_amdgcn_raw_buffer_load_b32(len_rsrc, qi * 4u, 0, 0);
+        return RowRaw{__uint_as_float(v[0]), __uint_as_float(v[1]), a.vl_rank == 2 ? len : len_all};
+    };
+
+    // Q and dO steps are loaded two steps before they are stored (even and
+    // odd steps in their own registers) and the query data one step before,
+    // all unconditionally: steps past the queries read as zeros.  The
+    // prologue issues them in the loop's order, so the waits the compiler
+    // derives hold on every iteration.
+    const StepSrc qsrc = step_src(qp, a.sq[2], Lq, tid), gsrc = step_src(gp, a.sdo[2], Lq, tid);
+    __builtin_amdgcn_sched_barrier(0);
+    Chunks nq_e = load_step(qsrc, i_begin), ng_e = load_step(gsrc, i_begin);
+    __builtin_amdgcn_sched_barrier(0);
+    RowRaw nr = fetch_rows(i_begin);
+    __builtin_amdgcn_sched_barrier(0);
+    Chunks nq_o = load_step(qsrc, i_begin + kStep), ng_o = load_step(gsrc, i_begin + kStep);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_chunk(smem, 0, ck, tid);
+    stage_chunk(smem, 1, cv, tid);
+    __syncthreads();
     // K and V fragments (B operands: key lane%32, features kk*16 + hb*8 ..).
     bf16x8 kf[4], vf[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        uint4 rk = make_uint4(0, 0, 0, 0), rv = rk;
-        if (j < Lk) {
-            rk = *reinterpret_cast<const uint4*>(kp + (long long)j * a.sk[2] + kk * 16 + hb * 8);
-            rv = *reinterpret_cast<const uint4*>(vp + (long long)j * a.sv[2] + kk * 16 + hb * 8);
-        }
-        kf[kk] = __builtin_bit_cast(bf16x8, rk);
-        vf[kk] = __builtin_bit_cast(bf16x8, rv);
+        kf[kk] = __builtin_bit_cast(bf16x8, staged_frag(smem, 0, grp * 32 + l32, kk, hb));
+        vf[kk] = __builtin_bit_cast(bf16x8, staged_frag(smem, 1, grp * 32 + l32, kk, hb));
     }
 
-    // Per streamed query (threads below kStep): log-sum-exp, D and key limit,
-    // fetched one step ahead like the tiles.
-    struct RowData {
-        float lse, dsum;
-        int kl;
-        bool none;
-    };
-    auto fetch_rows = [&](int i0) {
-        RowData r = {0.0f, 0.0f, 0, false};
-        const int qi = i0 + tid;
-        if (tid < kStep && qi < Lq) {
-            r.lse = a.rows[((long long)bh * Lq + qi) * 2];
-            r.dsum = a.rows[((long long)bh * Lq + qi) * 2 + 1];
-            r.kl = key_limit<kCausal>(a, b, qi, r.none);
-        }
-        return r;
-    };
-    RowData nr = fetch_rows(i_begin);
-
     f32x16 dk[2] = {}, dv[2] = {};
-    for (int st = 0; st < n_steps; ++st) {
+    auto step = [&](int st, Chunks& nq, Chunks& ng) {
         const int i0 = i_begin + st * kStep;
         __syncthreads();
         store_step(nq, smem, kKeysPhase, kKeysQR, kKeysQT, tid);
         store_step(ng, smem, kKeysPhase, kKeysGR, kKeysGT, tid);
         if (tid < kStep) {
-            rowf_s[tid] = make_float4(nr.lse, nr.dsum, nr.none ? 0.0f : c, nr.none ? 0.0f : 1.0f);
-            klim_s[tid] = nr.kl;
-            int mn = nr.none ? -1 : nr.kl;
+            const int qi = i0 + tid;
+            bool none = false;
+            const int kl = qi < Lq ? limit_from_len<kCausal>(a, nr.len, qi, none) : 0;
+            lse_s[tid] = nr.lse;
+            nd_s[tid] = -nr.dsum;
+            sc_s[tid] = none ? 0.0f : c;
+            gw_s[tid] = none ? 0.0f : 1.0f;
+            klim_s[tid] = kl;
+            int mn = none ? -1 : kl;
 #pragma unroll
             for (int o = 16; o >= 1; o >>= 1) mn = min(mn, __shfl_xor(mn, o));
             if ((tid & 31) == 0) tmin_s[tid >> 5] = mn;
         }
-        if (st + 1 < n_steps) {
-            nq = load_step(qsrc, i0 + kStep);
-            ng = load_step(gsrc, i0 + kStep);
-            nr = fetch_rows(i0 + kStep);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        nr = fetch_rows(i0 + kStep);
+        __builtin_amdgcn_sched_barrier(0);
+        nq = load_step(qsrc, i0 + 2 * kStep);
+        ng = load_step(gsrc, i0 + 2 * kStep);
         __syncthreads();
-        // S = Q K^T and dP = dO V^T: element v is query ph*32 + acc_row(v) +
-        // hb*4 of this step, key j.
+        // S = Q K^T and dP - D = dO V^T - D: element v is query ph*32 +
+        // acc_row(v) + hb*4 of this step, key j; the dP accumulator starts
+        // from -D of its query (four consecutive queries per 16-byte read).
         const char* area = smem + ph * kKeysPhase;
-        f32x16 p = tile_dot(reinterpret_cast<const bf16_t*>(area + kKeysQR), kf, l32, hb);
-        f32x16 ds = tile_dot(reinterpret_cast<const bf16_t*>(area + kKeysGR), vf, l32, hb);
         const int rb = ph * kTile + hb * 4;
+        f32x16 nd;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 x = *reinterpret_cast<const float4*>(nd_s + rb + g * 8);
+            nd[g * 4] = x.x;
+            nd[g * 4 + 1] = x.y;
+            nd[g * 4 + 2] = x.z;
+            nd[g * 4 + 3] = x.w;
+        }
+        f32x16 p = tile_dot(reinterpret_cast<const bf16_t*>(area + kKeysQR), kf, l32, hb);
+        f32x16 ds = tile_dot_from(reinterpret_cast<const bf16_t*>(area + kKeysGR), vf, nd, l32, hb);
         if (j_last < __builtin_amdgcn_readfirstlane(tmin_s[ph])) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float4 rf = rowf_s[rb + acc_row(v)];
-                const float e = __builtin_amdgcn_exp2f(fmaf(p[v], c, -rf.x));
-                p[v] = e;
-                ds[v] = e * (ds[v] - rf.y);
+            for (int g = 0; g < 4; ++g) {
+                const float4 x = *reinterpret_cast<const float4*>(lse_s + rb + g * 8);
+                const float lse4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = g * 4 + e;
+                    p[v] = __builtin_amdgcn_exp2f(fmaf(p[v], c, -lse4[e]));
+                    ds[v] *= p[v];
+                }
             }
         } else {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float4 rf = rowf_s[rb + acc_row(v)];
-                const int kl = klim_s[rb + acc_row(v)];
-                const float e = j < kl ? __builtin_amdgcn_exp2f(fmaf(p[v], rf.z, -rf.x)) : 0.0f;
-                p[v] = e;
-                ds[v] = e * (ds[v] - rf.y) * rf.w;
+                const int r = rb + acc_row(v);
+                const float e = __builtin_amdgcn_exp2f(fmaf(p[v], sc_s[r], -lse_s[r]));
+                p[v] = j < klim_s[r] ? e : 0.0f;
+                ds[v] *= p[v] * gw_s[r];
             }
         }
         u32x4 pw[2], dw[2];
@@ -352,23 +457,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, flo
                 dk[tb] = mfma32x32x16(tr_frag(qt, kb, tb, hb, lane), d8, dk[tb]);
             }
         }
+    };
+    // Pairs of steps, then a lone last step.  The loads past the last step
+    // read past the end of Q and dO (the stream runs to the last query), so
+    // they return zeros without a memory access and cost the end nothing.
+    int st = 0;
+    for (; st + 1 < n_steps; st += 2) {
+        step(st, nq_e, ng_e);
+        step(st + 1, nq_o, ng_o);
     }
+    if (st < n_steps) step(st, nq_e, ng_e);
+    // Both sums in one round: dv's slots, then dk's.
     float* red = reinterpret_cast<float*>(smem);
     __syncthreads();
-    reduce_write(red, dv, grp, ph, lane);
+    part_write(red, dv, 1.0f, grp, ph, lane);
+    part_write(red + kRedAllB / 4, dk, 1.0f / 8.0f, grp, ph, lane);
     __syncthreads();
-    reduce_read(red, dv, grp, ph, lane);
-    __syncthreads();
-    reduce_write(red, dk, grp, ph, lane);
-    __syncthreads();
-    reduce_read(red, dk, grp, ph, lane);
-    if (ph != 0 || j >= Lk) return;
-    store_rowT(a.dk, b * a.sdk[0] + hd * a.sdk[1] + (long long)j * a.sdk[2], a.out_f32, dk, 1.0f / 8.0f, hb);
-    store_rowT(a.dv, b * a.sdv[0] + hd * a.sdv[1] + (long long)j * a.sdv[2], a.out_f32, dv, 1.0f, hb);
+    float4 rv[2], rk[2];
+    part_sum(red, rv, grp, ph, lane);
+    part_sum(red + kRedAllB / 4, rk, grp, ph, lane);
+    if (j >= Lk) return;
+    store_quarter(a.dk, b * a.sdk[0] + hd * a.sdk[1] + (long long)j * a.sdk[2], a.out_f32, rk, 1.0f, ph, hb);
+    store_quarter(a.dv, b * a.sdv[0] + hd * a.sdv[1] + (long long)j * a.sdv[2], a.out_f32, rv, 1.0f, ph, hb);
 }
-
-static_assert(kGroups * (kPhases - 1) * 32 * 64 * 4 <= kPhases * kRowsPhase, "reduction slots fit the rows tiles");
-static_assert(kGroups * (kPhases - 1) * 32 * 64 * 4 <= kPhases * kKeysPhase, "reduction slots fit the keys tiles");
 
 template <bool kCausal>
 hipError_t launch_variant(const BackwardArgs& a, hipStream_t s) {
