@@ -109,6 +109,29 @@ mha_status sdpa_forward(mha_dtype in_dt, mha_dtype out_dt,
                         const int* valid_lens, int causal, void* stream);
 
 /*
+ * sdpa_forward_lse -- sdpa_forward that also writes each query's log-sum-exp
+ * of its scaled scores, the statistic a training step keeps for the
+ * backward pass (the pages train these models: d2l Transformer digest,
+ * training; The Annotated Transformer, Part 2).  The softmax of the
+ * "Attention" section's attention() normalises by the sum of exp(s_ij) over
+ * the allowed keys j (s_ij = q_i . k_j / sqrt(d_k)); lse_i is the natural
+ * log of that sum, so the weights are exp(s_ij - lse_i).
+ *   lse : device fp32, B*h*Lq elements, 4-byte aligned, element (b, hd, i)
+ *         at (b*h + hd)*Lq + i (written); must not overlap q, k, v or o.  A
+ *         row with no allowed key (length <= 0) weighs its Lk keys equally
+ *         and gets ln(Lk).  NULL is MHA_EINVAL unless B*Lq == 0.
+ * Everything else as sdpa_forward; the kernels are sdpa_forward's, which
+ * form the statistic in their last step (log2 units, converted here).
+ */
+mha_status sdpa_forward_lse(mha_dtype in_dt, mha_dtype out_dt,
+                            const void* q, mha_strides sq,
+                            const void* k, mha_strides sk,
+                            const void* v, mha_strides sv,
+                            void* o, mha_strides so,
+                            int B, int h, int Lq, int Lk, int d_k, int d_v,
+                            const int* valid_lens, int causal, float* lse, void* stream);
+
+/*
  * sdpa_decode -- one incremental-decoding step: a single new query per
  * (batch, head) attends to that head's cached keys and values.  At
  * prediction time the pages' decoder concatenates the keys and values of all
@@ -181,6 +204,32 @@ mha_status sdpa_backward(mha_dtype in_dt, mha_dtype out_dt,
                          int B, int h, int Lq, int Lk, int d_k, int d_v,
                          const int* valid_lens, int vl_rank, int causal,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sdpa_backward_lse -- sdpa_backward given the forward's log-sum-exp `lse`
+ * (as sdpa_forward_lse writes it: device fp32 [B, h, Lq] contiguous, 4-byte
+ * aligned, not overlapping the outputs or the workspace; NULL is MHA_EINVAL
+ * unless B*Lq == 0), so the weights are recomputed as exp(s_ij - lse_i)
+ * rather than found by a pass of their own.  For MHA_BF16 inputs a small
+ * kernel writes D_i and lse (log2 units) to the workspace, then one launch
+ * runs the query-side (dq) and key-side (dk, dv) workgroups together;
+ * MHA_F32 inputs take sdpa_backward's fp32 kernels, which form their own
+ * statistics, and do not read lse.  B*h*Lq must stay below 2^31
+ * (MHA_ENOTSUP otherwise).  Everything else as sdpa_backward; the result
+ * equals sdpa_backward's up to rounding when lse is the forward's.
+ */
+mha_status sdpa_backward_lse(mha_dtype in_dt, mha_dtype out_dt,
+                             const void* q, mha_strides sq,
+                             const void* k, mha_strides sk,
+                             const void* v, mha_strides sv,
+                             const void* o, mha_strides so,
+                             const void* dout, mha_strides sdo,
+                             void* dq, mha_strides sdq,
+                             void* dk, mha_strides sdk,
+                             void* dv, mha_strides sdv,
+                             int B, int h, int Lq, int Lk, int d_k, int d_v,
+                             const int* valid_lens, int vl_rank, int causal, const float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * sdpa_decode_noalloc -- sdpa_decode for callers that cannot allocate device

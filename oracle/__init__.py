@@ -57,6 +57,8 @@ def _open(path):
     lib.oracle_sdpa_f64.restype = ctypes.c_int
     lib.oracle_sdpa_f64.argtypes = [_dp, _dp, _dp, _dp, _dp] + [ctypes.c_int] * 6 + [
         _ip, ctypes.c_int, ctypes.c_int, _ip, ctypes.c_int]
+    lib.oracle_sdpa_lse_f64.restype = ctypes.c_int
+    lib.oracle_sdpa_lse_f64.argtypes = [_dp, _dp, _dp] + [ctypes.c_int] * 5 + [_ip, ctypes.c_int, ctypes.c_int]
     lib.oracle_mha_f64.restype = ctypes.c_int
     lib.oracle_mha_f64.argtypes = [_dp] * 11 + [ctypes.c_int] * 5 + [
         _ip, ctypes.c_int, ctypes.c_int, _ip, ctypes.c_int, ctypes.c_int]
@@ -166,6 +168,25 @@ def sdpa(q, k, v, valid_lens=None, causal=False, rows=None, return_weights=False
     if rc != 0:
         raise ValueError("oracle_sdpa_f64 rejected its arguments")
     return (o, p) if return_weights else o
+
+
+def sdpa_lse(q, k, valid_lens=None, causal=False):
+    """Log of each query row's softmax normaliser, log sum_j exp(s_ij), for
+    ``sdpa(q, k, v, valid_lens, causal)``: [B, h, Lq] (masked scores take the
+    fill, so a row with every key masked gives fill + log(Lk))."""
+    q, k = _f64(q), _f64(k)
+    B, h, Lq, dk = q.shape
+    Lk = k.shape[2]
+    assert k.shape == (B, h, Lk, dk)
+    vl = _i32(valid_lens)
+    if vl is not None:
+        assert vl.shape in ((B,), (B, Lq))
+    lse = np.empty((B, h, Lq), dtype=np.float64)
+    rc = _load().oracle_sdpa_lse_f64(_ptr(q), _ptr(k), _ptr(lse), B, h, Lq, Lk, dk, _iptr(vl),
+                                     int(vl is not None and vl.ndim == 2), int(bool(causal)))
+    if rc != 0:
+        raise ValueError("oracle_sdpa_lse_f64 rejected its arguments")
+    return lse
 
 
 def sdpa_backward(q, k, v, dout, valid_lens=None, causal=False):

@@ -100,10 +100,9 @@ static int key_allowed(const int* valid_lens, int vl_per_query, int Lq, int caus
     return 1;
 }
 
-/* One query row of one (batch, head): the attention definition, every key. */
-static void attend_row(const double* qi, const double* k, const double* v,
-                       double* oi, double* pi, double* s,
-                       int Lq, int Lk, int dk, int dv,
+/* The scaled scores of one query row against every key, masked pairs
+ * replaced by the fill. */
+static void row_scores(const double* qi, const double* k, double* s, int Lq, int Lk, int dk,
                        const int* valid_lens, int vl_per_query, int causal, int b, int i)
 {
     const double scale = 1.0 / sqrt((double)dk);
@@ -113,6 +112,15 @@ static void attend_row(const double* qi, const double* k, const double* v,
         s[j] = dot * scale;
         if (!key_allowed(valid_lens, vl_per_query, Lq, causal, b, i, j)) s[j] = ORACLE_MASK_FILL;
     }
+}
+
+/* One query row of one (batch, head): the attention definition, every key. */
+static void attend_row(const double* qi, const double* k, const double* v,
+                       double* oi, double* pi, double* s,
+                       int Lq, int Lk, int dk, int dv,
+                       const int* valid_lens, int vl_per_query, int causal, int b, int i)
+{
+    row_scores(qi, k, s, Lq, Lk, dk, valid_lens, vl_per_query, causal, b, i);
     double mx = s[0];
     for (int j = 1; j < Lk; ++j) if (s[j] > mx) mx = s[j];
     double den = 0.0;
@@ -160,6 +168,45 @@ int oracle_sdpa_f64(const double* q, const double* k, const double* v,
                        o + (bh * R + r) * (long)dv,
                        p ? p + (bh * R + r) * (long)Lk : NULL, s,
                        Lq, Lk, dk, dv, valid_lens, vl_per_query, causal, b, i);
+        }
+        free(s);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * The log of the softmax normaliser of each query row: with s_ij the scaled
+ * scores (masked pairs replaced by the fill; row_scores, as attend_row),
+ *   lse_i = log sum_j exp(s_ij),
+ * so that the weights are exp(s_ij - lse_i) (The Annotated Transformer,
+ * "Attention" section: softmax over the key axis).  Written as
+ * max_j s_ij + log sum_j exp(s_ij - max) so large logits cannot overflow.
+ * A row whose keys are all masked has every score equal to the fill, so its
+ * lse is the fill + log(Lk).
+ *   q [B, h, Lq, dk], k [B, h, Lk, dk] (contiguous); lse [B, h, Lq] written.
+ * Returns 0, or -1 on a bad argument / allocation failure.
+ */
+int oracle_sdpa_lse_f64(const double* q, const double* k, double* lse,
+                        int B, int h, int Lq, int Lk, int dk,
+                        const int* valid_lens, int vl_per_query, int causal)
+{
+    if (B < 0 || h <= 0 || Lq < 0 || Lk <= 0 || dk <= 0) return -1;
+    int bad = 0;
+    long bh;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (bh = 0; bh < (long)B * h; ++bh) {
+        const int b = (int)(bh / h);
+        double* s = (double*)malloc(sizeof(double) * (size_t)Lk);
+        if (!s) { bad = 1; continue; }
+        const double* qb = q + bh * (long)Lq * dk;
+        const double* kb = k + bh * (long)Lk * dk;
+        for (int i = 0; i < Lq; ++i) {
+            row_scores(qb + (long)i * dk, kb, s, Lq, Lk, dk, valid_lens, vl_per_query, causal, b, i);
+            double mx = s[0];
+            for (int j = 1; j < Lk; ++j) if (s[j] > mx) mx = s[j];
+            double den = 0.0;
+            for (int j = 0; j < Lk; ++j) den += exp(s[j] - mx);
+            lse[bh * (long)Lq + i] = mx + log(den);
         }
         free(s);
     }

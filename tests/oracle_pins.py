@@ -620,4 +620,45 @@ def pin_round_bf16_vs_torch():
     assert np.array_equal(got, ref)
 
 
+def pin_lse_closed_forms():
+    """The log of the softmax normaliser: zero queries score every key 0, so
+    lse = log(number of allowed keys) (causal row i: log(i + 1); length n:
+    log n); one allowed key gives exactly its scaled score; a row with every
+    key masked has all scores equal to the fill: fill + log(Lk)."""
+    r = _rng(60)
+    B, h, L, d = 2, 2, 6, 8
+    k = r.standard_normal((B, h, L, d))
+    q0 = np.zeros((B, h, L, d))
+    lc = oracle.sdpa_lse(q0, k, causal=True)
+    _close(lc, np.broadcast_to(np.log(np.arange(1, L + 1)), lc.shape), 1e-15)
+    lv = oracle.sdpa_lse(q0, k, valid_lens=[3, 5])
+    _close(lv[0], np.full((h, L), math.log(3)), 1e-15)
+    _close(lv[1], np.full((h, L), math.log(5)), 1e-15)
+    q = r.standard_normal((B, h, L, d)) * 3
+    l1 = oracle.sdpa_lse(q, k, valid_lens=[1, 1])
+    _close(l1, np.einsum("bhid,bhd->bhi", q, k[:, :, 0]) / math.sqrt(d), 1e-13)
+    lm = oracle.sdpa_lse(q, k, valid_lens=[0, 6])
+    _close(lm[0], np.full((h, L), -1e9 + math.log(L)), 1e-6)
+
+
+def pin_lse_vs_scipy_logsumexp_and_weights():
+    """Against scipy's logsumexp over the allowed scores of random rows (per
+    query lengths and the causal mask together), and exp(s - lse) equals the
+    oracle's own weights on the allowed keys."""
+    from scipy.special import logsumexp
+    r = _rng(61)
+    B, h, L, d = 2, 3, 9, 16
+    q, k, v = (r.standard_normal((B, h, L, d)) * 2 for _ in range(3))
+    vl = r.integers(1, L + 1, size=(B, L)).astype(np.int32)
+    lse = oracle.sdpa_lse(q, k, valid_lens=vl, causal=True)
+    _, p = oracle.sdpa(q, k, v, valid_lens=vl, causal=True, return_weights=True)
+    for b in range(B):
+        for hd in range(h):
+            for i in range(L):
+                n = min(vl[b, i], i + 1)
+                s = q[b, hd, i] @ k[b, hd, :n].T / math.sqrt(d)
+                _close(lse[b, hd, i], logsumexp(s), 1e-13)
+                _close(np.exp(s - lse[b, hd, i]), p[b, hd, i, :n], 1e-13)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -249,6 +249,39 @@ def test_mha_ex_validation(lib):
     assert mha_ex(lib, p=ctypes.c_void_p(P + 0x900000 + 2)) == EINVAL
 
 
+def sdpa_lse(lib, lse, **kw):
+    a = dict(in_dt=BF16, out_dt=BF16, B=2, h=4, Lq=128, Lk=128)
+    a.update(kw)
+    st = S(4 * 128 * 64, 128 * 64, 64)
+    return lib.sdpa_forward_lse(a["in_dt"], a["out_dt"], ALIGNED[0], st, ALIGNED[1], st, ALIGNED[2], st, ALIGNED[3],
+                                st, a["B"], a["h"], a["Lq"], a["Lk"], 64, 64, None, 0, lse, None)
+
+
+def test_sdpa_lse_validation(lib):
+    assert sdpa_lse(lib, None, B=0) == OK
+    assert sdpa_lse(lib, None) == EINVAL                               # the statistic must go somewhere
+    assert sdpa_lse(lib, ctypes.c_void_p(P + 0x900000 + 2)) == EINVAL  # not 4-byte aligned
+    assert sdpa_lse(lib, ctypes.c_void_p(P + 0x300000 + 64)) == EINVAL  # overlaps o
+    assert sdpa_lse(lib, ALIGNED[9], in_dt=F32, out_dt=BF16) == ENOTSUP
+
+
+def bwd_lse(lib, lse, **kw):
+    B, h, Lq = kw.get("B", 2), kw.get("h", 4), kw.get("Lq", 64)
+    st = S(4 * 64 * 64, 64 * 64, 64)
+    need = lib.sdpa_backward_workspace_bytes(B, h, Lq)
+    return lib.sdpa_backward_lse(BF16, F32, ALIGNED[0], st, ALIGNED[1], st, ALIGNED[2], st, ALIGNED[3], st,
+                                 ALIGNED[4], st, ALIGNED[5], st, ALIGNED[6], st, ALIGNED[7], st, B, h, Lq, 64,
+                                 64, 64, None, 1, 0, lse, ALIGNED[8], need, None)
+
+
+def test_backward_lse_validation(lib):
+    assert bwd_lse(lib, None, B=0) == OK
+    assert bwd_lse(lib, None) == EINVAL
+    assert bwd_lse(lib, ctypes.c_void_p(P + 0x900000 + 1)) == EINVAL   # not 4-byte aligned
+    assert bwd_lse(lib, ctypes.c_void_p(P + 0x500000 + 16)) == EINVAL  # overlaps dq
+    assert bwd_lse(lib, ctypes.c_void_p(P + 0x800000)) == EINVAL       # overlaps the workspace
+
+
 def bwd(lib, **kw):
     a = dict(in_dt=BF16, out_dt=F32, B=2, h=4, Lq=64, Lk=64, dk=64, dv=64, vl=None, vl_rank=1, causal=0,
              ws=ALIGNED[8], wsb=None, dq=ALIGNED[5], dk_=ALIGNED[6], dv_=ALIGNED[7], st=None)

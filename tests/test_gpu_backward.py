@@ -65,6 +65,38 @@ def test_backward_vs_oracle(B, h, Lq, Lk, causal, kind, dt):
         print(name, e)
 
 
+@pytest.mark.parametrize("B,h,Lq,Lk,causal,kind,dt", [c for c in CASES if c[6] == "bf16"])
+def test_backward_with_forward_lse_vs_oracle(B, h, Lq, Lk, causal, kind, dt):
+    """The path a training step takes: the forward keeps each query's
+    log-sum-exp and the backward recomputes the weights from it (one launch
+    for the query- and key-side workgroups).  Lengths per query have no
+    forward with the statistic, so there the oracle's log-sum-exp (in fp32,
+    a fully masked row's fill taken out) is the input."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    rng = np.random.Generator(np.random.PCG64(B * 7919 + Lq * 31 + Lk))
+    q = workloads._finish(rng.standard_normal((B, h, Lq, 64)), dt)
+    k = workloads._finish(rng.standard_normal((B, h, Lk, 64)), dt)
+    v = workloads._finish(rng.standard_normal((B, h, Lk, 64)), dt)
+    g = workloads._finish(rng.standard_normal((B, h, Lq, 64)), dt)
+    vl = _lengths(kind, rng, B, Lq, Lk)
+    tq, tk, tv, tg = (to_device(x, torch.bfloat16) for x in (q, k, v, g))
+    if kind == "2d":
+        o = mha.sdpa_forward(tq, tk, tv, valid_lens=vl, causal=causal)
+        ref_lse = oracle.sdpa_lse(q, k, valid_lens=vl, causal=causal)
+        ref_lse[ref_lse < -1e8] += 1e9
+        lse = torch.from_numpy(ref_lse.astype(np.float32)).cuda()
+    else:
+        o, lse = mha.sdpa_forward(tq, tk, tv, valid_lens=vl, causal=causal, return_lse=True)
+    gq, gk, gv = mha.sdpa_backward(tq, tk, tv, o, tg, valid_lens=vl, causal=causal, out_dtype=torch.float32,
+                                   lse=lse)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.sdpa_backward(q, k, v, g, valid_lens=vl, causal=causal)
+    for name, got, ref in (("dq", gq, rq), ("dk", gk, rk), ("dv", gv, rv)):
+        e = assert_bf16(to_host(got), ref, f"{name} with lse B{B} h{h} Lq{Lq} Lk{Lk} causal={causal} lengths={kind}")
+        print(name, e)
+
+
 def test_backward_bf16_outputs_and_strided_views():
     """bf16 gradients into [B, L, h, d] views (strided), lengths per sequence."""
     import torch
@@ -95,13 +127,14 @@ def test_backward_full_size_sampled_heads():
     rng = np.random.Generator(np.random.PCG64(w.seed + 1000))
     g = workloads._finish(rng.standard_normal(q.shape), "bf16")
     tq, tk, tv, tg = (to_device(x, torch.bfloat16) for x in (q, k, v, g))
-    o = mha.sdpa_forward(tq, tk, tv, causal=True)
-    gq, gk, gv = mha.sdpa_backward(tq, tk, tv, o, tg, causal=True, out_dtype=torch.float32)
+    o, lse = mha.sdpa_forward(tq, tk, tv, causal=True, return_lse=True)
+    grads = {"own statistics": mha.sdpa_backward(tq, tk, tv, o, tg, causal=True, out_dtype=torch.float32),
+             "forward lse": mha.sdpa_backward(tq, tk, tv, o, tg, causal=True, out_dtype=torch.float32, lse=lse)}
     torch.cuda.synchronize()
-    gq, gk, gv = to_host(gq), to_host(gk), to_host(gv)
     for b, hd in ((0, 0), (w.B - 1, w.h - 1)):
         sl = lambda x: x[b:b + 1, hd:hd + 1]
         ref = oracle.sdpa_backward(sl(q), sl(k), sl(v), sl(g), causal=True)
-        for name, got, r in (("dq", gq, ref[0]), ("dk", gk, ref[1]), ("dv", gv, ref[2])):
-            e = assert_bf16(sl(got), r, f"{name} full size b{b} h{hd}")
-            print(name, b, hd, e)
+        for path, (gq, gk, gv) in grads.items():
+            for name, got, r in (("dq", gq, ref[0]), ("dk", gk, ref[1]), ("dv", gv, ref[2])):
+                e = assert_bf16(sl(to_host(got)), r, f"{name} full size b{b} h{hd} ({path})")
+                print(path, name, b, hd, e)

@@ -172,3 +172,44 @@ def test_sdpa_fully_masked_rows_are_uniform():
                                      out_dtype=torch.float32))
         mean = v.astype(np.float64).mean(axis=2, keepdims=True)
         assert_bf16(o, np.broadcast_to(mean, o.shape), "fully masked rows")
+
+
+# The log-sum-exp the forward keeps for the backward.  Bar: the bf16 kernel
+# sums the bf16-rounded weights (relative error at most 2^-9 each, so at most
+# 2^-9 in the sum and in its log) and scores the bf16 inputs in fp32; the
+# fp32 kernel is fp32 throughout.  So |lse - ref| <= 2^-9 + 1e-5 max(1, |ref|)
+# (bf16 inputs) or 1e-5 max(1, |ref|) (fp32).  A row with every key masked
+# weighs its keys equally; the oracle's fill makes that fill + log(Lk), the
+# library reports log(Lk) (scores all 0): the test adds the fill back.
+LSE_CASES = [
+    # B, h, Lq, Lk, causal, valid_lens, dtype
+    (2, 3, 200, 200, True, None, "bf16"),
+    (2, 2, 77, 300, False, [0, 150], "bf16"),
+    (1, 4, 513, 513, True, None, "bf16"),
+    (3, 1, 64, 1, False, None, "bf16"),
+    (2, 2, 70, 90, False, [5, 90], "f32"),
+    (2, 3, 64, 64, True, [0, 64], "f32"),
+]
+
+
+@pytest.mark.parametrize("B,h,Lq,Lk,causal,vl,dt", LSE_CASES)
+def test_sdpa_forward_lse_vs_oracle(B, h, Lq, Lk, causal, vl, dt):
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    inp = workloads.make_sdpa_inputs(B, h, Lq, Lk, 64, dt, seed=B * 131 + Lq + Lk)
+    q, k, v = (inp.tensors[n] for n in ("q", "k", "v"))
+    vls = None if vl is None else np.array(vl, np.int32)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    tq, tk, tv = (to_device(x, tdt) for x in (q, k, v))
+    o, lse = mha.sdpa_forward(tq, tk, tv, valid_lens=vls, causal=causal, return_lse=True)
+    o_plain = mha.sdpa_forward(tq, tk, tv, valid_lens=vls, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain), "the output must not change when the statistic is kept"
+    ref = oracle.sdpa_lse(q, k, valid_lens=vls, causal=causal)
+    if vls is not None:
+        ref[vls <= 0] += 1e9                               # the fill, added back
+    got = to_host(lse)
+    bar = (2.0 ** -9 if dt == "bf16" else 0.0) + 1e-5 * np.maximum(1.0, np.abs(ref))
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got)) and np.all(err <= bar), f"lse error {err.max()} (bar {bar.min()})"
+    print("max lse error", err.max())

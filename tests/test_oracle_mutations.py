@@ -39,6 +39,8 @@ MUTATIONS = [
     ("layer_norm_eps_inside_root_for_kind0", "den = sqrt(ss / (D - 1)) + eps;", "den = sqrt(ss / (D - 1) + eps);"),
     ("layer_norm_eps_outside_root_for_kind1", "else den = sqrt(ss / D + eps);", "else den = sqrt(ss / D) + eps;"),
     ("per_query_length_ignores_query", "valid_lens[(long)b * Lq + i]", "valid_lens[(long)b * Lq]"),
+    ("lse_drops_the_max", "lse[bh * (long)Lq + i] = mx + log(den);", "lse[bh * (long)Lq + i] = log(den);"),
+    ("lse_in_log2", "lse[bh * (long)Lq + i] = mx + log(den);", "lse[bh * (long)Lq + i] = mx + log2(den);"),
 ]
 
 

@@ -15,8 +15,11 @@ there is no CPU or PyTorch fallback, and a missing library raises.
     mha_sublayer_forward(x, w_q, w_k, w_v, w_o, ..., ln_gain=None, ln_bias=None,
                          ln_kind=0, ln_eps=1e-6, memory=None, ...)
         x + MHA(norm(x), ...): the pre-norm residual sublayer
-    sdpa_backward(q, k, v, o, dout, valid_lens=None, causal=False)
-        -> dq, dk, dv (gradients of sdpa_forward for the output gradient dout)
+    sdpa_forward(..., return_lse=True) -> o, lse
+        also each query's log-sum-exp [B, h, Lq] (fp32), kept for the backward
+    sdpa_backward(q, k, v, o, dout, valid_lens=None, causal=False, lse=None)
+        -> dq, dk, dv (gradients of sdpa_forward for the output gradient dout;
+        with the forward's lse the weights are recomputed from it)
     sdpa_decode(q, k_cache, v_cache, lens)
         one decoding step: q [B,h,64] against caches [B,h,L,64]
     sdpa_decode_noalloc(q, k_cache, v_cache, lens, out=None)
@@ -93,12 +96,14 @@ def _raise(status, what):
 
 
 def sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None, out=None, return_weights=False,
-                 weights=None):
+                 weights=None, return_lse=False):
     """softmax(q k^T / sqrt(d_k)) v per (batch, head) with key-padding
     ``valid_lens`` ([B] or [B, Lq]) and/or the causal mask; returns
     o [B, h, Lq, d_v], and the weights [B, h, Lq, Lk] (fp32) when
     ``return_weights`` (written into ``weights`` if given: an fp32 tensor of
-    that shape whose last axis is contiguous)."""
+    that shape whose last axis is contiguous), or each query's log-sum-exp
+    of its scaled scores [B, h, Lq] (fp32) when ``return_lse`` (lengths per
+    sequence only; not with the weights)."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check_gpu(n, t)
@@ -114,6 +119,12 @@ def sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None, out=Non
     lib = _lib.load()
     head = (in_dt, _dtype_code(out.dtype), _ptr(q), _strides4(q), _ptr(k), _strides4(k), _ptr(v), _strides4(v),
             _ptr(out), _strides4(out), B, h, Lq, Lk, dk, dv, _ptr(vl))
+    if return_lse:
+        if return_weights or (vl is not None and vl.dim() != 1):
+            raise ValueError("return_lse takes lengths per sequence and no weights")
+        lse = torch.empty((B, h, Lq), dtype=torch.float32, device=q.device)
+        _raise(lib.sdpa_forward_lse(*head, int(bool(causal)), _ptr(lse), _stream()), "sdpa_forward_lse")
+        return out, lse
     if not return_weights and (vl is None or vl.dim() == 1):
         _raise(lib.sdpa_forward(*head, int(bool(causal)), _stream()), "sdpa_forward")
         return out
@@ -132,9 +143,10 @@ def sdpa_forward(q, k, v, valid_lens=None, causal=False, out_dtype=None, out=Non
     return (out, p) if return_weights else out
 
 
-def sdpa_backward(q, k, v, o, dout, valid_lens=None, causal=False, out_dtype=None, workspace=None):
+def sdpa_backward(q, k, v, o, dout, valid_lens=None, causal=False, out_dtype=None, workspace=None, lse=None):
     """Gradients (dq, dk, dv) of sdpa_forward(q, k, v, valid_lens, causal),
-    whose output was ``o``, for the output gradient ``dout``."""
+    whose output was ``o``, for the output gradient ``dout``; ``lse`` is the
+    forward's log-sum-exp (sdpa_forward(..., return_lse=True)), if kept."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _check_gpu(n, t)
@@ -154,6 +166,15 @@ def sdpa_backward(q, k, v, o, dout, valid_lens=None, causal=False, out_dtype=Non
     args = []
     for t in (q, k, v, o, dout, gq, gk, gv):
         args += [_ptr(t), _strides4(t)]
+    if lse is not None:
+        _check_gpu("lse", lse)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, h, Lq) or not lse.is_contiguous():
+            raise ValueError(f"lse must be a contiguous fp32 [{B}, {h}, {Lq}] tensor")
+        st = lib.sdpa_backward_lse(_dtype_code(q.dtype), _dtype_code(out_dtype), *args, B, h, Lq, Lk, dk, dv,
+                                   _ptr(vl), 1 if vl is None else vl.dim(), int(bool(causal)), _ptr(lse),
+                                   _ptr(workspace), workspace.numel(), _stream())
+        _raise(st, "sdpa_backward_lse")
+        return gq, gk, gv
     st = lib.sdpa_backward(_dtype_code(q.dtype), _dtype_code(out_dtype), *args, B, h, Lq, Lk, dk, dv, _ptr(vl),
                            1 if vl is None else vl.dim(), int(bool(causal)), _ptr(workspace), workspace.numel(),
                            _stream())

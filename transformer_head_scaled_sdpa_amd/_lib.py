@@ -18,7 +18,8 @@ MHA_EWORKSPACE = 3
 MHA_EHIP = 4
 
 # Every function the header declares; tests check that each is exported.
-EXPORTED = ("sdpa_forward", "sdpa_forward_ex", "sdpa_backward_workspace_bytes", "sdpa_backward",
+EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_ex", "sdpa_backward_workspace_bytes", "sdpa_backward",
+            "sdpa_backward_lse",
             "sdpa_decode_workspace_bytes", "sdpa_decode", "sdpa_decode_noalloc", "mha_workspace_bytes",
             "mha_workspace_bytes_ex", "mha_forward", "mha_forward_ex", "mha_sublayer_workspace_bytes",
             "mha_sublayer_forward", "mha_status_string", "mha_timing_enable",
@@ -51,6 +52,9 @@ def load():
     lib.sdpa_forward.restype = i
     lib.sdpa_forward.argtypes = [i, i, vp, Strides, vp, Strides, vp, Strides, vp, Strides,
                                  i, i, i, i, i, i, vp, i, vp]
+    lib.sdpa_forward_lse.restype = i
+    lib.sdpa_forward_lse.argtypes = [i, i, vp, Strides, vp, Strides, vp, Strides, vp, Strides,
+                                     i, i, i, i, i, i, vp, i, vp, vp]
     lib.sdpa_forward_ex.restype = i
     lib.sdpa_forward_ex.argtypes = [i, i, vp, Strides, vp, Strides, vp, Strides, vp, Strides,
                                     i, i, i, i, i, i, vp, i, i, vp, Strides, vp]
@@ -58,6 +62,8 @@ def load():
     lib.sdpa_backward_workspace_bytes.argtypes = [i, i, i]
     lib.sdpa_backward.restype = i
     lib.sdpa_backward.argtypes = [i, i] + [vp, Strides] * 8 + [i] * 6 + [vp, i, i, vp, sz, vp]
+    lib.sdpa_backward_lse.restype = i
+    lib.sdpa_backward_lse.argtypes = [i, i] + [vp, Strides] * 8 + [i] * 6 + [vp, i, i, vp, vp, sz, vp]
     lib.sdpa_decode_workspace_bytes.restype = sz
     lib.sdpa_decode_workspace_bytes.argtypes = [i, i, i]
     lib.sdpa_decode.restype = i

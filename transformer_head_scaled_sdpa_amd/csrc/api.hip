@@ -110,110 +110,9 @@ const char* mha_status_string(mha_status s) {
 
 namespace {
 
-// sdpa_forward and sdpa_forward_ex: lengths per sequence (vl_rank 1) or per
-// query (2), optional weights p_attn.
-mha_status sdpa_impl(mha_dtype in_dt, mha_dtype out_dt,
-                     const void* q, mha_strides sq,
-                     const void* k, mha_strides sk,
-                     const void* v, mha_strides sv,
-                     void* o, mha_strides so,
-                     int B, int h, int Lq, int Lk, int d_k, int d_v,
-                     const int* valid_lens, int vl_rank, int causal,
-                     float* p_attn, mha_strides sp, void* stream) {
-    if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
-    if (valid_lens && vl_rank != 1 && vl_rank != 2) return MHA_EINVAL;
-    if (B < 0 || h <= 0 || Lq < 0 || Lk <= 0 || d_k <= 0 || d_v <= 0) return MHA_EINVAL;
-    if (causal && Lq != Lk) return MHA_EINVAL;
-    if (d_k != kHeadDim || d_v != kHeadDim) return MHA_ENOTSUP;
-    if (in_dt == MHA_F32 && out_dt != MHA_F32) return MHA_ENOTSUP;
-    if (B == 0 || Lq == 0) return MHA_OK;
-    if (!q || !k || !v || !o) return MHA_EINVAL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MHA_EINVAL;
-    const long long mult = in_dt == MHA_F32 ? 4 : 8;
-    const long long omult = out_dt == MHA_F32 ? 4 : 8;
-    const mha_strides in_s[3] = {sq, sk, sv};
-    for (const mha_strides& s : in_s)
-        if (s.b < 0 || s.h < 0 || s.l < 0 || s.b % mult || s.h % mult || s.l % mult) return MHA_EINVAL;
-    if (so.b < 0 || so.h < 0 || so.l < 0 || so.b % omult || so.h % omult || so.l % omult) return MHA_EINVAL;
-    const size_t ie = elem_size(in_dt), oe = elem_size(out_dt);
-    if (!tile_rows_fit(sq.l, ie) || !tile_rows_fit(sk.l, ie) || !tile_rows_fit(sv.l, ie) || !tile_rows_fit(so.l, oe))
-        return MHA_ENOTSUP;
-    const Range ro = view_range(o, so, B, h, Lq, d_v, oe);
-    const Range rq = view_range(q, sq, B, h, Lq, d_k, ie), rk = view_range(k, sk, B, h, Lk, d_k, ie),
-                rv = view_range(v, sv, B, h, Lk, d_v, ie);
-    if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv)) return MHA_EINVAL;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (p_attn || (valid_lens && vl_rank == 2)) {
-        if (in_dt == MHA_BF16 && (!rows_fit_buffer(sk.l, Lk, ie) || !rows_fit_buffer(sv.l, Lk, ie))) return MHA_ENOTSUP;
-        if (p_attn) {
-            if (reinterpret_cast<uintptr_t>(p_attn) & 3u) return MHA_EINVAL;
-            if (sp.b < 0 || sp.h < 0 || sp.l < 0) return MHA_EINVAL;
-            const Range rp = view_range(p_attn, sp, B, h, Lq, Lk, 4);
-            if (overlap(rp, ro) || overlap(rp, rq) || overlap(rp, rk) || overlap(rp, rv)) return MHA_EINVAL;
-        }
-        mha::WeightsArgs w;
-        w.q = q; w.k = k; w.v = v; w.o = o;
-        w.sq[0] = sq.b; w.sq[1] = sq.h; w.sq[2] = sq.l;
-        w.sk[0] = sk.b; w.sk[1] = sk.h; w.sk[2] = sk.l;
-        w.sv[0] = sv.b; w.sv[1] = sv.h; w.sv[2] = sv.l;
-        w.so[0] = so.b; w.so[1] = so.h; w.so[2] = so.l;
-        w.B = B; w.H = h; w.Lq = Lq; w.Lk = Lk;
-        w.valid_lens = valid_lens;
-        w.vl_rank = valid_lens ? vl_rank : 0;
-        w.causal = causal ? 1 : 0;
-        w.in_f32 = in_dt == MHA_F32;
-        w.out_f32 = out_dt == MHA_F32;
-        w.p = p_attn;
-        w.sp[0] = sp.b; w.sp[1] = sp.h; w.sp[2] = sp.l;
-        return hip_status(timed("sdpa_weights", s, [&] { return mha::launch_sdpa_weights(w, s); }));
-    }
-
-    mha::SdpaArgs a;
-    a.q = q; a.k = k; a.v = v; a.o = o;
-    a.sq[0] = sq.b; a.sq[1] = sq.h; a.sq[2] = sq.l;
-    a.sk[0] = sk.b; a.sk[1] = sk.h; a.sk[2] = sk.l;
-    a.sv[0] = sv.b; a.sv[1] = sv.h; a.sv[2] = sv.l;
-    a.so[0] = so.b; a.so[1] = so.h; a.so[2] = so.l;
-    a.B = B; a.H = h; a.Lq = Lq; a.Lk = Lk;
-    a.valid_lens = valid_lens;
-    a.causal = causal ? 1 : 0;
-    if (in_dt == MHA_F32) return hip_status(timed("sdpa_f32", s, [&] { return mha::launch_sdpa_f32(a, s); }));
-    return hip_status(timed("sdpa_bf16", s, [&] { return mha::launch_sdpa_bf16(a, out_dt == MHA_F32, s); }));
-}
-
-}  // namespace
-
-extern "C" {
-
-mha_status sdpa_forward(mha_dtype in_dt, mha_dtype out_dt,
-                        const void* q, mha_strides sq,
-                        const void* k, mha_strides sk,
-                        const void* v, mha_strides sv,
-                        void* o, mha_strides so,
-                        int B, int h, int Lq, int Lk, int d_k, int d_v,
-                        const int* valid_lens, int causal, void* stream) {
-    return sdpa_impl(in_dt, out_dt, q, sq, k, sk, v, sv, o, so, B, h, Lq, Lk, d_k, d_v, valid_lens, 1, causal,
-                     nullptr, mha_strides{0, 0, 0}, stream);
-}
-
-mha_status sdpa_forward_ex(mha_dtype in_dt, mha_dtype out_dt,
-                           const void* q, mha_strides sq,
-                           const void* k, mha_strides sk,
-                           const void* v, mha_strides sv,
-                           void* o, mha_strides so,
-                           int B, int h, int Lq, int Lk, int d_k, int d_v,
-                           const int* valid_lens, int vl_rank, int causal,
-                           float* p_attn, mha_strides sp, void* stream) {
-    return sdpa_impl(in_dt, out_dt, q, sq, k, sk, v, sv, o, so, B, h, Lq, Lk, d_k, d_v, valid_lens, vl_rank,
-                     causal, p_attn, sp, stream);
-}
-
-size_t sdpa_backward_workspace_bytes(int B, int h, int Lq) {
-    if (B < 0 || h <= 0 || Lq < 0) return 0;
-    return round_up(mha::backward_workspace_bytes(B, h, Lq), 256);
-}
-
-mha_status sdpa_backward(mha_dtype in_dt, mha_dtype out_dt,
+// sdpa_backward and sdpa_backward_lse (lse: the forward's log-sum-exp of
+// each query, or null).
+mha_status backward_impl(mha_dtype in_dt, mha_dtype out_dt,
                          const void* q, mha_strides sq,
                          const void* k, mha_strides sk,
                          const void* v, mha_strides sv,
@@ -223,7 +122,7 @@ mha_status sdpa_backward(mha_dtype in_dt, mha_dtype out_dt,
                          void* dk, mha_strides sdk,
                          void* dv, mha_strides sdv,
                          int B, int h, int Lq, int Lk, int d_k, int d_v,
-                         const int* valid_lens, int vl_rank, int causal,
+                         const int* valid_lens, int vl_rank, int causal, const float* lse,
                          void* workspace, size_t workspace_bytes, void* stream) {
     if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
     if (valid_lens && vl_rank != 1 && vl_rank != 2) return MHA_EINVAL;
@@ -263,6 +162,14 @@ mha_status sdpa_backward(mha_dtype in_dt, mha_dtype out_dt,
         for (int y = x + 1; y < 4; ++y)
             if (overlap(outs[x], outs[y])) return MHA_EINVAL;
     }
+    if (lse) {
+        if (reinterpret_cast<uintptr_t>(lse) & 3u) return MHA_EINVAL;
+        const uintptr_t lb = reinterpret_cast<uintptr_t>(lse);
+        const Range rl{lb, lb + (uintptr_t)B * h * Lq * 4};
+        for (const Range& r : outs)
+            if (overlap(rl, r)) return MHA_EINVAL;
+        if ((long long)B * h * Lq >= (1ll << 31)) return MHA_ENOTSUP;   // query rows index in 32 bits
+    }
 
     mha::BackwardArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout;
@@ -281,8 +188,165 @@ mha_status sdpa_backward(mha_dtype in_dt, mha_dtype out_dt,
     a.in_f32 = in_dt == MHA_F32;
     a.out_f32 = out_dt == MHA_F32;
     a.rows = static_cast<float*>(workspace);
+    a.lse_in = in_dt == MHA_BF16 ? lse : nullptr;   // the fp32 kernels form their own statistics
     hipStream_t s = static_cast<hipStream_t>(stream);
     return hip_status(timed("sdpa_backward", s, [&] { return mha::launch_sdpa_backward(a, s); }));
+}
+
+
+// sdpa_forward and sdpa_forward_ex: lengths per sequence (vl_rank 1) or per
+// query (2), optional weights p_attn.
+mha_status sdpa_impl(mha_dtype in_dt, mha_dtype out_dt,
+                     const void* q, mha_strides sq,
+                     const void* k, mha_strides sk,
+                     const void* v, mha_strides sv,
+                     void* o, mha_strides so,
+                     int B, int h, int Lq, int Lk, int d_k, int d_v,
+                     const int* valid_lens, int vl_rank, int causal,
+                     float* p_attn, mha_strides sp, float* lse, void* stream) {
+    if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
+    if (valid_lens && vl_rank != 1 && vl_rank != 2) return MHA_EINVAL;
+    if (B < 0 || h <= 0 || Lq < 0 || Lk <= 0 || d_k <= 0 || d_v <= 0) return MHA_EINVAL;
+    if (causal && Lq != Lk) return MHA_EINVAL;
+    if (d_k != kHeadDim || d_v != kHeadDim) return MHA_ENOTSUP;
+    if (in_dt == MHA_F32 && out_dt != MHA_F32) return MHA_ENOTSUP;
+    if (B == 0 || Lq == 0) return MHA_OK;
+    if (!q || !k || !v || !o) return MHA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MHA_EINVAL;
+    const long long mult = in_dt == MHA_F32 ? 4 : 8;
+    const long long omult = out_dt == MHA_F32 ? 4 : 8;
+    const mha_strides in_s[3] = {sq, sk, sv};
+    for (const mha_strides& s : in_s)
+        if (s.b < 0 || s.h < 0 || s.l < 0 || s.b % mult || s.h % mult || s.l % mult) return MHA_EINVAL;
+    if (so.b < 0 || so.h < 0 || so.l < 0 || so.b % omult || so.h % omult || so.l % omult) return MHA_EINVAL;
+    const size_t ie = elem_size(in_dt), oe = elem_size(out_dt);
+    if (!tile_rows_fit(sq.l, ie) || !tile_rows_fit(sk.l, ie) || !tile_rows_fit(sv.l, ie) || !tile_rows_fit(so.l, oe))
+        return MHA_ENOTSUP;
+    const Range ro = view_range(o, so, B, h, Lq, d_v, oe);
+    const Range rq = view_range(q, sq, B, h, Lq, d_k, ie), rk = view_range(k, sk, B, h, Lk, d_k, ie),
+                rv = view_range(v, sv, B, h, Lk, d_v, ie);
+    if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv)) return MHA_EINVAL;
+    if (lse) {
+        if (reinterpret_cast<uintptr_t>(lse) & 3u) return MHA_EINVAL;
+        const uintptr_t lb = reinterpret_cast<uintptr_t>(lse);
+        const Range rl{lb, lb + (uintptr_t)B * h * Lq * 4};
+        if (overlap(rl, ro) || overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv)) return MHA_EINVAL;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p_attn || (valid_lens && vl_rank == 2)) {
+        if (in_dt == MHA_BF16 && (!rows_fit_buffer(sk.l, Lk, ie) || !rows_fit_buffer(sv.l, Lk, ie))) return MHA_ENOTSUP;
+        if (p_attn) {
+            if (reinterpret_cast<uintptr_t>(p_attn) & 3u) return MHA_EINVAL;
+            if (sp.b < 0 || sp.h < 0 || sp.l < 0) return MHA_EINVAL;
+            const Range rp = view_range(p_attn, sp, B, h, Lq, Lk, 4);
+            if (overlap(rp, ro) || overlap(rp, rq) || overlap(rp, rk) || overlap(rp, rv)) return MHA_EINVAL;
+        }
+        mha::WeightsArgs w;
+        w.q = q; w.k = k; w.v = v; w.o = o;
+        w.sq[0] = sq.b; w.sq[1] = sq.h; w.sq[2] = sq.l;
+        w.sk[0] = sk.b; w.sk[1] = sk.h; w.sk[2] = sk.l;
+        w.sv[0] = sv.b; w.sv[1] = sv.h; w.sv[2] = sv.l;
+        w.so[0] = so.b; w.so[1] = so.h; w.so[2] = so.l;
+        w.B = B; w.H = h; w.Lq = Lq; w.Lk = Lk;
+        w.valid_lens = valid_lens;
+        w.vl_rank = valid_lens ? vl_rank : 0;
+        w.causal = causal ? 1 : 0;
+        w.in_f32 = in_dt == MHA_F32;
+        w.out_f32 = out_dt == MHA_F32;
+        w.p = p_attn;
+        w.sp[0] = sp.b; w.sp[1] = sp.h; w.sp[2] = sp.l;
+        return hip_status(timed("sdpa_weights", s, [&] { return mha::launch_sdpa_weights(w, s); }));
+    }
+
+    mha::SdpaArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.sq[0] = sq.b; a.sq[1] = sq.h; a.sq[2] = sq.l;
+    a.sk[0] = sk.b; a.sk[1] = sk.h; a.sk[2] = sk.l;
+    a.sv[0] = sv.b; a.sv[1] = sv.h; a.sv[2] = sv.l;
+    a.so[0] = so.b; a.so[1] = so.h; a.so[2] = so.l;
+    a.B = B; a.H = h; a.Lq = Lq; a.Lk = Lk;
+    a.valid_lens = valid_lens;
+    a.causal = causal ? 1 : 0;
+    a.lse = lse;
+    if (in_dt == MHA_F32) return hip_status(timed("sdpa_f32", s, [&] { return mha::launch_sdpa_f32(a, s); }));
+    return hip_status(timed("sdpa_bf16", s, [&] { return mha::launch_sdpa_bf16(a, out_dt == MHA_F32, s); }));
+}
+
+}  // namespace
+
+extern "C" {
+
+mha_status sdpa_forward(mha_dtype in_dt, mha_dtype out_dt,
+                        const void* q, mha_strides sq,
+                        const void* k, mha_strides sk,
+                        const void* v, mha_strides sv,
+                        void* o, mha_strides so,
+                        int B, int h, int Lq, int Lk, int d_k, int d_v,
+                        const int* valid_lens, int causal, void* stream) {
+    return sdpa_impl(in_dt, out_dt, q, sq, k, sk, v, sv, o, so, B, h, Lq, Lk, d_k, d_v, valid_lens, 1, causal,
+                     nullptr, mha_strides{0, 0, 0}, nullptr, stream);
+}
+
+mha_status sdpa_forward_lse(mha_dtype in_dt, mha_dtype out_dt,
+                            const void* q, mha_strides sq,
+                            const void* k, mha_strides sk,
+                            const void* v, mha_strides sv,
+                            void* o, mha_strides so,
+                            int B, int h, int Lq, int Lk, int d_k, int d_v,
+                            const int* valid_lens, int causal, float* lse, void* stream) {
+    if (!lse && B > 0 && Lq > 0) return MHA_EINVAL;
+    return sdpa_impl(in_dt, out_dt, q, sq, k, sk, v, sv, o, so, B, h, Lq, Lk, d_k, d_v, valid_lens, 1, causal,
+                     nullptr, mha_strides{0, 0, 0}, lse, stream);
+}
+
+mha_status sdpa_forward_ex(mha_dtype in_dt, mha_dtype out_dt,
+                           const void* q, mha_strides sq,
+                           const void* k, mha_strides sk,
+                           const void* v, mha_strides sv,
+                           void* o, mha_strides so,
+                           int B, int h, int Lq, int Lk, int d_k, int d_v,
+                           const int* valid_lens, int vl_rank, int causal,
+                           float* p_attn, mha_strides sp, void* stream) {
+    return sdpa_impl(in_dt, out_dt, q, sq, k, sk, v, sv, o, so, B, h, Lq, Lk, d_k, d_v, valid_lens, vl_rank,
+                     causal, p_attn, sp, nullptr, stream);
+}
+
+size_t sdpa_backward_workspace_bytes(int B, int h, int Lq) {
+    if (B < 0 || h <= 0 || Lq < 0) return 0;
+    return round_up(mha::backward_workspace_bytes(B, h, Lq), 256);
+}
+
+mha_status sdpa_backward(mha_dtype in_dt, mha_dtype out_dt,
+                         const void* q, mha_strides sq,
+                         const void* k, mha_strides sk,
+                         const void* v, mha_strides sv,
+                         const void* o, mha_strides so,
+                         const void* dout, mha_strides sdo,
+                         void* dq, mha_strides sdq,
+                         void* dk, mha_strides sdk,
+                         void* dv, mha_strides sdv,
+                         int B, int h, int Lq, int Lk, int d_k, int d_v,
+                         const int* valid_lens, int vl_rank, int causal,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    return backward_impl(in_dt, out_dt, q, sq, k, sk, v, sv, o, so, dout, sdo, dq, sdq, dk, sdk, dv, sdv, B, h, Lq,
+                         Lk, d_k, d_v, valid_lens, vl_rank, causal, nullptr, workspace, workspace_bytes, stream);
+}
+
+mha_status sdpa_backward_lse(mha_dtype in_dt, mha_dtype out_dt,
+                             const void* q, mha_strides sq,
+                             const void* k, mha_strides sk,
+                             const void* v, mha_strides sv,
+                             const void* o, mha_strides so,
+                             const void* dout, mha_strides sdo,
+                             void* dq, mha_strides sdq,
+                             void* dk, mha_strides sdk,
+                             void* dv, mha_strides sdv,
+                             int B, int h, int Lq, int Lk, int d_k, int d_v,
+                             const int* valid_lens, int vl_rank, int causal, const float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (!lse && B > 0 && Lq > 0) return MHA_EINVAL;
+    return backward_impl(in_dt, out_dt, q, sq, k, sk, v, sv, o, so, dout, sdo, dq, sdq, dk, sdk, dv, sdv, B, h, Lq,
+                         Lk, d_k, d_v, valid_lens, vl_rank, causal, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -15,6 +15,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // log2(e): softmax exponentials are evaluated as exp2 of log2(e)-scaled scores.
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t x) {
     return __uint_as_float(static_cast<uint32_t>(x) << 16);

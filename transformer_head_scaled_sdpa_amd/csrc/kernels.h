@@ -22,6 +22,10 @@ struct SdpaArgs {
     // and come out in log2 units.  Bf16 output only.
     const void* q_lo = nullptr;
     const void* k_lo = nullptr;
+    // Optional output: each query's log-sum-exp of its scaled scores
+    // (natural log, contiguous [B, H, Lq]; ln(Lk) for a row with no allowed
+    // key, whose weights are uniform).
+    float* lse = nullptr;
 };
 
 // C[m, n] = sum_k A[m, k] * W[n, k] + bias[n] for up to three problems that
@@ -112,6 +116,10 @@ struct BackwardArgs {
     int causal;
     bool in_f32, out_f32;
     float* rows;
+    // Optional log-sum-exp of each query's scaled scores (natural log,
+    // contiguous [B, H, Lq]) from the forward; bf16 inputs use it in place
+    // of their own pass over the keys.
+    const float* lse_in = nullptr;
 };
 
 hipError_t launch_sdpa_bf16(const SdpaArgs& a, bool out_f32, hipStream_t s);

@@ -7,25 +7,32 @@
 // a row with no allowed key weights all keys uniformly and passes no
 // gradient to q or k).
 //
-// Two kernels of 8 wave64s per workgroup.  A workgroup owns 64 rows (two
+// Workgroups of 8 wave64s in two roles.  A workgroup owns 64 rows (two
 // groups of 32, one row per lane column of the 32x32 MFMA tile) and streams
 // the other side in steps of 128 rows: four phases of 32, one per wave of a
 // group, so every wave works on its own tile and the four partial sums of a
 // row are added through LDS at the end.  Products run on
 // v_mfma_f32_32x32x16_bf16 in the operand layouts of the forward kernel: an
 // accumulator packed to bf16 feeds the next MFMA as its B operand, and
-// transposed tiles are read from LDS with ds_read_b64_tr_b16 (each tile is
-// stored twice: 144-byte rows for 16-byte fragment reads, 192-byte rows for
-// the transposed reads).
-//  * rows (queries; q and do fragments in registers): one pass over the
-//    keys: S^T = K Q^T and dP^T = V dO^T, unnormalised weights exp2(S - m)
-//    with a lazy per-query offset m (the online softmax), dS^T = P^T (dP^T -
-//    D), and dQ^T += K^T dS^T; the phases' (m, weight sum, dq) are merged at
-//    the end and dq divided by the weight sum.  D_i comes from the supplied
-//    output.  The log-sum-exp and D go to the workspace.
-//  * keys (k and v fragments in registers): S = Q K^T and dP = dO V^T, P and
-//    dS from the stored log-sum-exp and D, then dV^T += dO^T P and
-//    dK^T += Q^T dS.
+// transposed tiles are read from LDS with ds_read_b64_tr_b16 (tiles read both
+// ways are stored twice: 144-byte rows for 16-byte fragment reads, 192-byte
+// rows for the transposed reads).
+//  * rows (queries; q and do fragments in registers): S^T = K Q^T and
+//    dP^T - D = V dO^T - D, the weights P^T, dS^T = P^T (dP^T - D) and
+//    dQ^T += K^T dS^T over the keys.  Without the forward's log-sum-exp the
+//    weights are exp2(S - m) with a lazy per-query offset m (the online
+//    softmax); the phases' (m, weight sum, dq) are merged at the end, dq is
+//    divided by the weight sum, and the log-sum-exp and D_i (from the
+//    supplied output) go to the workspace.  With it they are
+//    exp2(S - lse) directly.
+//  * keys (k and v fragments in registers): S = Q K^T and dP - D = dO V^T - D,
+//    P and dS from the log-sum-exp and D in the workspace, then
+//    dV^T += dO^T P and dK^T += Q^T dS.
+// Without a log-sum-exp the rows kernel runs first and the keys kernel reads
+// its results.  With one, a small kernel writes D_i and the log-sum-exp in
+// log2 units to the workspace, and a single launch holds both roles (they no
+// longer depend on each other): the key side first, each side heaviest
+// blocks first.
 // dS (and P for dV) is rounded to bf16 for its products, as P is in the
 // forward.  Tiles where every pair is allowed skip the mask arithmetic.
 #include "common.h"
@@ -39,7 +46,7 @@ namespace {
 using namespace rows64;
 
 // ---------------------------------------------------------------------------
-// rows: log-sum-exp, D, dq
+// rows: dq (and without a log-sum-exp: the log-sum-exp and D)
 // ---------------------------------------------------------------------------
 // LDS: the K and V tiles in 144-byte rows (score products) in two slots,
 // the K tiles in 192-byte rows (transposed reads for dq) in three: step st
@@ -47,32 +54,48 @@ using namespace rows64;
 // computed during step st, so at step st the K/V slot of st + 1 and the K^T
 // slot of st are read while step st + 2 is written to the slots of st (K/V,
 // last read during step st - 1) and st - 1 (K^T).  The staged Q, dO and O
-// sit in K^T slot 2 before the first step, the dq partials at the start
-// after the last.
+// sit past the K^T slot 1 before the first step, the dq partials at the
+// start after the last, and the per-phase (m, weight sum) after everything.
 constexpr int kRowsSlotR = kPhases * kTileRB;     // one step in 144-byte rows
 constexpr int kRowsSlotT = kPhases * kTileTB;     // one step in 192-byte rows
 constexpr int kRowsKR = 0;
 constexpr int kRowsVR = 2 * kRowsSlotR;
 constexpr int kRowsKT = 4 * kRowsSlotR;
 constexpr int kRowsStage = kRowsKT + 2 * kRowsSlotT;
-constexpr int kRowsLds = kRowsStage + 3 * kStageB;
-static_assert(kRowsKT + 3 * kRowsSlotT <= kRowsLds && kRedAllB <= kRowsLds, "tiles and partials fit");
+constexpr int kRowsStat = kRowsStage + 3 * kStageB;
+constexpr int kRowsLds = kRowsStat + kGroups * kPhases * 2 * 32 * 8;
+static_assert(kRowsKT + 3 * kRowsSlotT <= kRowsStat && kRedAllB <= kRowsStat, "tiles and partials fit");
 
-template <bool kCausal>
-__global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, float c) {
-    __shared__ __attribute__((aligned(16))) char smem[kRowsLds];
-    __shared__ float2 stat_s[kGroups][kPhases][2][32];
+// ---------------------------------------------------------------------------
+// keys: dk, dv
+// ---------------------------------------------------------------------------
+constexpr int kKeysQR = 0;                        // Q, 144-byte rows
+constexpr int kKeysQT = kTileRB;                  // Q, 192-byte rows
+constexpr int kKeysGR = kTileRB + kTileTB;        // dO, 144-byte rows
+constexpr int kKeysGT = 2 * kTileRB + kTileTB;    // dO, 192-byte rows
+constexpr int kKeysPhase = 2 * kTileRB + 2 * kTileTB;
+// The step tiles, reused first for the staged K and V and last for the dv
+// and dk partials; then per streamed query the log-sum-exp, -D, score scale
+// and gradient factor (0 for a row with no allowed key), key limit, and per
+// phase tile the smallest key limit (-1 if a row has none allowed).
+constexpr int kKeysTiles = kPhases * kKeysPhase > 2 * kRedAllB ? kPhases * kKeysPhase : 2 * kRedAllB;
+constexpr int kKeysRowData = kKeysTiles;
+constexpr int kKeysLds = kKeysRowData + 5 * kStep * 4 + kPhases * 4;
+static_assert(2 * kStageB <= kKeysTiles, "staging fits");
+
+constexpr int kFusedLds = kRowsLds > kKeysLds ? kRowsLds : kKeysLds;
+
+template <bool kCausal, bool kLse>
+__device__ __forceinline__ void rows_body(const BackwardArgs& a, float c, int blk, int bh, char* smem) {
+    float2* const stat = reinterpret_cast<float2*>(smem + kRowsStat);   // [grp][phase][half][32]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave % kGroups, ph = wave / kGroups;
     const int hb = lane >> 5, l32 = lane & 31;
-    const int BH = a.B * a.H;
-    const int bh = blockIdx.x % BH;
     const int b = bh / a.H, hd = bh % a.H;
     // Causal rows late in the sequence see the most keys: they go first.
     const int n_wg = (a.Lq + kRowsWg - 1) / kRowsWg;
-    const int blk = blockIdx.x / BH;
     const int q_wg = (kCausal ? n_wg - 1 - blk : blk) * kRowsWg;
     const int i = q_wg + grp * 32 + l32;
     const int Lq = a.Lq, Lk = a.Lk;
@@ -99,13 +122,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
     const bf16_t* kp = static_cast<const bf16_t*>(a.k) + b * a.sk[0] + hd * a.sk[1];
     const bf16_t* vp = static_cast<const bf16_t*>(a.v) + b * a.sv[0] + hd * a.sv[1];
 
-    // This workgroup's 64 rows of Q, dO and O: one range-checked 16-byte
-    // chunk per thread each (zeros past the queries), issued first and
-    // staged through LDS, so the four phase waves of a group read their
-    // fragments from there instead of each loading them.
-    const StepSrc qsrc = step_src(qp, a.sq[2], Lq, tid), gsrc = step_src(gp, a.sdo[2], Lq, tid),
-                  osrc = step_src(op, a.so[2], Lq, tid);
-    const uint4 cq = load_chunk(qsrc, q_wg), cg = load_chunk(gsrc, q_wg), co = load_chunk(osrc, q_wg);
+    // This workgroup's 64 rows of Q and dO (and O when D is formed here):
+    // one range-checked 16-byte chunk per thread each (zeros past the
+    // queries), issued first and staged through LDS, so the four phase waves
+    // of a group read their fragments from there instead of each loading
+    // them.  With a log-sum-exp, that and D come from the workspace.
+    const StepSrc qsrc = step_src(qp, a.sq[2], Lq, tid), gsrc = step_src(gp, a.sdo[2], Lq, tid);
+    const uint4 cq = load_chunk(qsrc, q_wg), cg = load_chunk(gsrc, q_wg);
+    uint4 co = make_uint4(0, 0, 0, 0);
+    float2 given = make_float2(0.0f, 0.0f);   // (log-sum-exp in log2 units, D) with kLse
+    if constexpr (kLse) {
+        // Range-checked: rows past the queries read zeros.
+        typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+        const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+            a.rows + (long long)bh * Lq * 2, (short)0, Lq * 8, kBufWord3);
+        const u32x2v x = __builtin_amdgcn_raw_buffer_load_b64(rr, (uint32_t)i * 8u, 0, 0);
+        given = make_float2(__uint_as_float(x[0]), __uint_as_float(x[1]));
+    } else {
+        co = load_chunk(step_src(op, a.so[2], Lq, tid), q_wg);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // K and V steps go to LDS two steps before their scores are computed
@@ -128,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
     char* const stage = smem + kRowsStage;
     stage_chunk(stage, 0, cq, tid);
     stage_chunk(stage, 1, cg, tid);
-    stage_chunk(stage, 2, co, tid);
+    if constexpr (!kLse) stage_chunk(stage, 2, co, tid);
     put(nk_e, nv_e, 0, 0);
     nk_e = load_step(ksrc, 2 * kStep);
     nv_e = load_step(vsrc, 2 * kStep);
@@ -146,29 +181,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
     for (int kk = 0; kk < 4; ++kk) {
         const uint4 rq = staged_frag(stage, 0, grp * 32 + l32, kk, hb);
         const uint4 rg = staged_frag(stage, 1, grp * 32 + l32, kk, hb);
-        const uint4 ro = staged_frag(stage, 2, grp * 32 + l32, kk, hb);
         qf[kk] = __builtin_bit_cast(bf16x8, rq);
         gf[kk] = __builtin_bit_cast(bf16x8, none ? make_uint4(0, 0, 0, 0) : rg);
-        const uint32_t ug[4] = {rg.x, rg.y, rg.z, rg.w}, uo[4] = {ro.x, ro.y, ro.z, ro.w};
+        if constexpr (!kLse) {
+            const uint4 ro = staged_frag(stage, 2, grp * 32 + l32, kk, hb);
+            const uint32_t ug[4] = {rg.x, rg.y, rg.z, rg.w}, uo[4] = {ro.x, ro.y, ro.z, ro.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            dsum += __uint_as_float(ug[e] << 16) * __uint_as_float(uo[e] << 16) +
-                    __uint_as_float(ug[e] & 0xffff0000u) * __uint_as_float(uo[e] & 0xffff0000u);
+            for (int e = 0; e < 4; ++e)
+                dsum += __uint_as_float(ug[e] << 16) * __uint_as_float(uo[e] << 16) +
+                        __uint_as_float(ug[e] & 0xffff0000u) * __uint_as_float(uo[e] & 0xffff0000u);
+        }
     }
-    dsum = pair_sum(dsum);                  // D_i over both lane halves
+    if constexpr (kLse) dsum = given.y;
+    else dsum = pair_sum(dsum);             // D_i over both lane halves
     // dP^T - D starts from -D in the accumulator (element v of a lane is the
     // lane's query).
     f32x16 neg_d;
 #pragma unroll
     for (int v = 0; v < 16; ++v) neg_d[v] = none ? 0.0f : -dsum;
 
-    // ---- one pass: online softmax with a lazy offset ----
-    // dq accumulates exp2(s - m) (dp - D) k with the offset m of this lane's
+    // ---- the pass over the keys ----
+    // Without a log-sum-exp: online softmax with a lazy offset.  dq
+    // accumulates exp2(s - m) (dp - D) k with the offset m of this lane's
     // query (equal on both lane halves); m moves only when a tile's max
     // exceeds it by more than kLazy, and then dq and the weight sum l (this
-    // lane half's keys) are rescaled.  The phases merge at the end.
+    // lane half's keys) are rescaled.  The phases merge at the end.  With
+    // one, m is the log-sum-exp and never moves.
     constexpr float kLazy = 10.0f;
-    float m = -INFINITY, l = 0.0f;
+    float m = kLse ? given.x : -INFINITY, l = 0.0f;
     f32x16 dq[2] = {};
     // S^T = K Q^T and dP^T - D = V dO^T - D of step st from its K/V slot.
     auto scores = [&](int st, f32x16& s, f32x16& dp) {
@@ -189,32 +229,36 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
         nv = load_step(vsrc, (st + 4) * kStep);
         scores(st + 1, s_n, dp_n);
         const int t0 = st * kStep + ph * kTile;   // this wave's keys t0 .. t0+31
-        // Masked keys score -inf; the tile's row max in log2 units, then the
-        // weights exp2(s * cs - m) (masked: 0).
+        // Masked keys score -inf (weight 0).
         if (t0 + kTile > kmin) {
             const int rel = klim - (t0 + hb * 4);
 #pragma unroll
             for (int v = 0; v < 16; ++v) s[v] = acc_row(v) < rel ? s[v] : -INFINITY;
         }
-        float mx = s[0];
+        if constexpr (!kLse) {
+            // The tile's row max in log2 units; raise the offset if needed.
+            float mx = s[0];
 #pragma unroll
-        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-        float mt = mx == -INFINITY ? -INFINITY : mx * cs;
-        mt = pair_max(mt);
-        if (__any(mt > m + kLazy)) {
-            const float m_new = mt > m + kLazy ? mt : m;
-            const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
-            l *= alpha;
+            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+            float mt = mx == -INFINITY ? -INFINITY : mx * cs;
+            mt = pair_max(mt);
+            if (__any(mt > m + kLazy)) {
+                const float m_new = mt > m + kLazy ? mt : m;
+                const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+                l *= alpha;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                dq[0][v] *= alpha;
-                dq[1][v] *= alpha;
+                for (int v = 0; v < 16; ++v) {
+                    dq[0][v] *= alpha;
+                    dq[1][v] *= alpha;
+                }
+                m = m_new;
             }
-            m = m_new;
         }
-        const float m_use = m == -INFINITY ? 0.0f : m;   // no allowed key yet: every weight is 0
+        // The weights exp2(s * cs - m): without a log-sum-exp, m is 0 until a
+        // row has an allowed key (its weights are 0 until then).
+        const float m_use = (kLse || m != -INFINITY) ? m : 0.0f;
         f32x16 ds;
-        float q4[4];
+        [[maybe_unused]] float q4[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             float pr[4];
@@ -224,9 +268,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
                 pr[e] = __builtin_amdgcn_exp2f(fmaf(s[v], cs, -m_use));
                 ds[v] = pr[e] * dp[v];
             }
-            q4[g] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            if constexpr (!kLse) q4[g] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
         }
-        l += (q4[0] + q4[1]) + (q4[2] + q4[3]);
+        if constexpr (!kLse) l += (q4[0] + q4[1]) + (q4[2] + q4[3]);
         u32x4 w[2];
         pack_b(ds, w);
         const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem + kRowsKT + t3 * kRowsSlotT + ph * kTileTB);
@@ -248,23 +292,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
         t3 = t3 == 2 ? 0 : t3 + 1;
     }
     if (st < n_steps) step(st, t3, nk_e, nv_e, s_e, dp_e, s_o, dp_o);
-    // Merge the phases: common offset M, total weight L, rescaled dq.
-    stat_s[grp][ph][hb][l32] = make_float2(m, l);
-    __syncthreads();
-    float M = -INFINITY;
+
+    float own = 1.0f, dq_scale = 0.125f, lse = 0.0f;
+    if constexpr (!kLse) {
+        // Merge the phases: common offset M, total weight L, rescaled dq.
+        stat[((grp * kPhases + ph) * 2 + hb) * 32 + l32] = make_float2(m, l);
+        __syncthreads();
+        float M = -INFINITY;
 #pragma unroll
-    for (int p = 0; p < kPhases; ++p) M = fmaxf(M, stat_s[grp][p][0][l32].x);
-    float L = 0.0f;
+        for (int p = 0; p < kPhases; ++p) M = fmaxf(M, stat[((grp * kPhases + p) * 2) * 32 + l32].x);
+        float L = 0.0f;
 #pragma unroll
-    for (int p = 0; p < kPhases; ++p)
+        for (int p = 0; p < kPhases; ++p)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float2 x = stat_s[grp][p][h][l32];
-            L += x.x == -INFINITY ? 0.0f : x.y * __builtin_amdgcn_exp2f(x.x - M);
-        }
-    const float own = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-    // v_log_f32 is the base-2 logarithm, matching the log2-unit scores.
-    const float lse = L > 0.0f ? M + __builtin_amdgcn_logf(L) : 0.0f;
+            for (int h = 0; h < 2; ++h) {
+                const float2 x = stat[((grp * kPhases + p) * 2 + h) * 32 + l32];
+                L += x.x == -INFINITY ? 0.0f : x.y * __builtin_amdgcn_exp2f(x.x - M);
+            }
+        own = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+        dq_scale = L > 0.0f ? 0.125f / L : 0.0f;
+        // v_log_f32 is the base-2 logarithm, matching the log2-unit scores.
+        lse = L > 0.0f ? M + __builtin_amdgcn_logf(L) : 0.0f;
+    } else {
+        __syncthreads();
+    }
     // The barrier above also ends every wave's reads of the last step's
     // tiles, so the partials may overwrite them.
     float* red = reinterpret_cast<float*>(smem);
@@ -273,44 +324,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, flo
     float4 r[2];
     part_sum(red, r, grp, ph, lane);
     if (!live) return;
-    if (ph == 0 && hb == 0) {
-        a.rows[((long long)bh * Lq + i) * 2] = lse;
-        a.rows[((long long)bh * Lq + i) * 2 + 1] = dsum;
+    if constexpr (!kLse) {
+        if (ph == 0 && hb == 0)
+            reinterpret_cast<float2*>(a.rows)[(long long)bh * Lq + i] = make_float2(lse, dsum);
     }
-    store_quarter(a.dq, b * a.sdq[0] + hd * a.sdq[1] + (long long)i * a.sdq[2], a.out_f32, r,
-                  L > 0.0f ? 0.125f / L : 0.0f, ph, hb);
+    store_quarter(a.dq, b * a.sdq[0] + hd * a.sdq[1] + (long long)i * a.sdq[2], a.out_f32, r, dq_scale, ph, hb);
 }
 
-// ---------------------------------------------------------------------------
-// keys: dk, dv
-// ---------------------------------------------------------------------------
-constexpr int kKeysQR = 0;                        // Q, 144-byte rows
-constexpr int kKeysQT = kTileRB;                  // Q, 192-byte rows
-constexpr int kKeysGR = kTileRB + kTileTB;        // dO, 144-byte rows
-constexpr int kKeysGT = 2 * kTileRB + kTileTB;    // dO, 192-byte rows
-constexpr int kKeysPhase = 2 * kTileRB + 2 * kTileTB;
-// The step tiles, reused first for the staged K and V and last for the dv
-// and dk partials.
-constexpr int kKeysLds = kPhases * kKeysPhase > 2 * kRedAllB ? kPhases * kKeysPhase : 2 * kRedAllB;
-static_assert(2 * kStageB <= kKeysLds, "staging fits");
-
 template <bool kCausal>
-__global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, float c) {
-    __shared__ __attribute__((aligned(16))) char smem[kKeysLds];
-    // Per streamed query: log-sum-exp, -D, score scale and gradient factor
-    // (0 for a row with no allowed key), key limit.
-    __shared__ __attribute__((aligned(16))) float lse_s[kStep], nd_s[kStep], sc_s[kStep], gw_s[kStep];
-    __shared__ int klim_s[kStep];
-    __shared__ int tmin_s[kPhases];    // per phase tile: smallest key limit (-1 if a row has none allowed)
+__device__ __forceinline__ void keys_body(const BackwardArgs& a, float c, int blk, int bh, char* smem) {
+    float* const lse_s = reinterpret_cast<float*>(smem + kKeysRowData);
+    float* const nd_s = lse_s + kStep;
+    float* const sc_s = nd_s + kStep;
+    float* const gw_s = sc_s + kStep;
+    int* const klim_s = reinterpret_cast<int*>(gw_s + kStep);
+    int* const tmin_s = klim_s + kStep;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave % kGroups, ph = wave / kGroups;
     const int hb = lane >> 5, l32 = lane & 31;
-    const int BH = a.B * a.H;
-    const int bh = blockIdx.x % BH;
     const int b = bh / a.H, hd = bh % a.H;
-    const int k_wg = (blockIdx.x / BH) * kRowsWg;   // causal: early keys see the most queries and go first
+    const int k_wg = blk * kRowsWg;                 // causal: early keys see the most queries and go first
     const int j = k_wg + grp * 32 + l32;            // this lane's key
     const int j_last = k_wg + grp * 32 + 31;
     const int Lq = a.Lq, Lk = a.Lk;
@@ -324,18 +359,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, flo
     // weight none of its keys.
     const int i_begin = (kCausal && a.vl_rank == 0) ? k_wg : 0;
     const int n_steps = (Lq - i_begin + kStep - 1) / kStep;
-    // Q and dO steps are loaded two steps before they are stored (even and
-    // odd steps in their own registers), unconditionally: steps past the
-    // queries read as zeros.
     // This workgroup's 64 rows of K and V: one range-checked 16-byte chunk
     // per thread each (zeros past the keys), staged through LDS like the
-    // rows kernel's Q, dO and O.
+    // rows' Q and dO.
     const StepSrc ksrc = step_src(kp, a.sk[2], Lk, tid), vsrc = step_src(vp, a.sv[2], Lk, tid);
     const uint4 ck = load_chunk(ksrc, k_wg), cv = load_chunk(vsrc, k_wg);
     __builtin_amdgcn_sched_barrier(0);
 
     // Per streamed query (threads below kStep keep them): log-sum-exp and D
-    // from the rows kernel and the query's length, read one step ahead by
+    // from the workspace and the query's length, read one step ahead by
     // range-checked loads (zeros past the queries; the length load has an
     // empty range unless lengths vary by query).
     const __amdgpu_buffer_rsrc_t rows_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -482,23 +514,89 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, flo
 }
 
 template <bool kCausal>
+__global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, float c) {
+    __shared__ __attribute__((aligned(16))) char smem[kRowsLds];
+    const int BH = a.B * a.H;
+    rows_body<kCausal, false>(a, c, blockIdx.x / BH, blockIdx.x % BH, smem);
+}
+
+template <bool kCausal>
+__global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, float c) {
+    __shared__ __attribute__((aligned(16))) char smem[kKeysLds];
+    const int BH = a.B * a.H;
+    keys_body<kCausal>(a, c, blockIdx.x / BH, blockIdx.x % BH, smem);
+}
+
+// With the forward's log-sum-exp: per query row, D = do . o (fp32 sum of the
+// bf16 products) and the log-sum-exp in log2 units, as the rows kernel
+// leaves them.  Eight lanes per row, 16 bytes of do and o each.
+constexpr int kPrepRows = 32;   // rows per 256-thread workgroup
+__global__ __launch_bounds__(256) void bwd_prep(BackwardArgs a) {
+    // B*h*Lq < 2^31 (the launcher checks), so rows index in 32 bits.
+    const int n = a.B * a.H * a.Lq;
+    const int row = blockIdx.x * kPrepRows + (threadIdx.x >> 3);
+    const int part = threadIdx.x & 7;
+    float d = 0.0f;
+    if (row < n) {
+        const int bhh = row / a.Lq;
+        const int i = row - bhh * a.Lq, b = bhh / a.H, hd = bhh - b * a.H;
+        const uint4 g = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.dout) + b * a.sdo[0] +
+                                                         hd * a.sdo[1] + (long long)i * a.sdo[2] + part * 8);
+        const uint4 o = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.o) + b * a.so[0] +
+                                                         hd * a.so[1] + (long long)i * a.so[2] + part * 8);
+        const uint32_t ug[4] = {g.x, g.y, g.z, g.w}, uo[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            d += __uint_as_float(ug[e] << 16) * __uint_as_float(uo[e] << 16) +
+                 __uint_as_float(ug[e] & 0xffff0000u) * __uint_as_float(uo[e] & 0xffff0000u);
+    }
+    d += __shfl_xor(d, 1);
+    d += __shfl_xor(d, 2);
+    d += __shfl_xor(d, 4);
+    if (row < n && part == 0) reinterpret_cast<float2*>(a.rows)[row] = make_float2(a.lse_in[row] * kLog2e, d);
+}
+
+// Both roles in one grid: block index u = blockIdx / (B*h) takes keys block
+// u while u < n_kb, then rows block u - n_kb; each kind's blocks go heaviest
+// first, so the lightest query blocks fill the end.  (Measured: alternating
+// the kinds block by block ran the key side about 15% slower per step.)
+template <bool kCausal>
+__global__ __launch_bounds__(kThreads, 1) void bwd_fused_mfma(BackwardArgs a, float c, int n_kb) {
+    __shared__ __attribute__((aligned(16))) char smem[kFusedLds];
+    const int BH = a.B * a.H;
+    const int bh = blockIdx.x % BH, u = blockIdx.x / BH;
+    if (u < n_kb) keys_body<kCausal>(a, c, u, bh, smem);
+    else rows_body<kCausal, true>(a, c, u - n_kb, bh, smem);
+}
+
+template <bool kCausal>
 hipError_t launch_variant(const BackwardArgs& a, hipStream_t s) {
     const float c = kLog2e / 8.0f;   // log2(e) / sqrt(64)
     const long long BH = (long long)a.B * a.H;
-    const long long gq = BH * ((a.Lq + kRowsWg - 1) / kRowsWg), gk = BH * ((a.Lk + kRowsWg - 1) / kRowsWg);
-    if (gq == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_rows_mfma<kCausal>), dim3((unsigned)gq), dim3(kThreads), 0, s, a, c);
+    const int n_qb = (a.Lq + kRowsWg - 1) / kRowsWg, n_kb = (a.Lk + kRowsWg - 1) / kRowsWg;
+    if (BH == 0 || a.Lq == 0) return hipSuccess;
+    if (a.lse_in) {
+        const long long n = BH * a.Lq;
+        if (n >= (1ll << 31)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(bwd_prep, dim3((unsigned)((n + kPrepRows - 1) / kPrepRows)), dim3(256), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_fused_mfma<kCausal>), dim3((unsigned)(BH * (n_qb + n_kb))), dim3(kThreads), 0, s,
+                           a, c, n_kb);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((bwd_rows_mfma<kCausal>), dim3((unsigned)(BH * n_qb)), dim3(kThreads), 0, s, a, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_keys_mfma<kCausal>), dim3((unsigned)gk), dim3(kThreads), 0, s, a, c);
+    hipLaunchKernelGGL((bwd_keys_mfma<kCausal>), dim3((unsigned)(BH * n_kb)), dim3(kThreads), 0, s, a, c);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_sdpa_backward_bf16(const BackwardArgs& a, hipStream_t s) {
-    if (!fits_buffer(a.sq[2], a.Lq) || !fits_buffer(a.sdo[2], a.Lq) || !fits_buffer(a.sk[2], a.Lk) ||
-        !fits_buffer(a.sv[2], a.Lk))
+    if (!fits_buffer(a.sq[2], a.Lq) || !fits_buffer(a.sdo[2], a.Lq) || !fits_buffer(a.so[2], a.Lq) ||
+        !fits_buffer(a.sk[2], a.Lk) || !fits_buffer(a.sv[2], a.Lk))
         return hipErrorInvalidValue;
     return a.causal ? launch_variant<true>(a, s) : launch_variant<false>(a, s);
 }

@@ -448,7 +448,11 @@ void sdpa_fwd_bf16_pipe(SdpaArgs a, int n_qtiles, float c) {
         slow_stage(s + 1, sc, sn, pb, pa, nk_e, nv_e);
     }
 
-    const float inv = 1.0f / query_sum(l, l32);
+    const float lsum = query_sum(l, l32);
+    const float inv = 1.0f / lsum;
+    // The log-sum-exp of the scaled scores (natural log) when asked for: the
+    // offset m and the weight sum are in log2 units (v_log_f32 is log2).
+    if (a.lse && hb == 0 && i < a.Lq) a.lse[(long long)bh * a.Lq + i] = (m + __builtin_amdgcn_logf(lsum)) * kLn2;
     // O^T element v of block tb: feature tb*32 + (v/4)*8 + hb*4 + v%4, query
     // i.  Every wave is past the last barrier, so the K/V buffers are idle:
     // each wave stages 32 rows x 128 bytes of its output in its own slice

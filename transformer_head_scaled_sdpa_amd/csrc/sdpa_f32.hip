@@ -93,6 +93,8 @@ __global__ __launch_bounds__(64) void sdpa_fwd_f32_d64(SdpaArgs a, int n_qtiles,
 
     if (i >= a.Lq) return;
     const float inv = 1.0f / l;
+    // The log-sum-exp of the scaled scores (natural log) when asked for.
+    if (a.lse) a.lse[(long long)bh * a.Lq + i] = (mc + __builtin_amdgcn_logf(l)) * kLn2;
     float* ob = static_cast<float*>(a.o) + b * a.so[0] + hd * a.so[1] + i * a.so[2];
 #pragma unroll
     for (int t = 0; t < kD; t += 4)
