@@ -108,6 +108,27 @@ def test_graph_sdpa_backward():
                                                    out_dtype=torch.float32))
 
 
+def test_graph_sdpa_forward_and_backward_with_lse():
+    """The training pair: the forward keeping each query's log-sum-exp, and
+    the backward recomputing the weights from it (two launches: D and the
+    statistic, then both gradient sides in one)."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    B, h, L = 2, 3, 300
+    vl = torch.tensor([300, 171], dtype=torch.int32, device="cuda")
+
+    def make(r):
+        return [_rand((B, h, L, 64), 400 * r + i, torch.bfloat16) for i in range(4)]
+
+    def call(t):
+        o, lse = mha.sdpa_forward(t[0], t[1], t[2], valid_lens=vl, causal=True, return_lse=True)
+        grads = mha.sdpa_backward(t[0], t[1], t[2], o, t[3], valid_lens=vl, causal=True,
+                                  out_dtype=torch.float32, lse=lse)
+        return (o, lse) + tuple(grads)
+
+    _graph_check(make, call)
+
+
 def test_graph_sdpa_weights_per_query_lengths():
     """The inspection path (weights exported) with one length per query."""
     import torch

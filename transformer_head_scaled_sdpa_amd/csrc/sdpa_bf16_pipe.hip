@@ -33,11 +33,11 @@
 //    barrier per stage.
 //  * Weights are exp2(s * c - m) with c = log2(e)/sqrt(d_k) applied by one
 //    FMA on the fp32 score.  The offset m is the row max of the first tile;
-//    later tiles keep it unless a lane's sum of weights for the tile exceeds
-//    2^20, in which case the tile's row max is folded into m, the
+//    later tiles keep it unless a query's sum of weights for the tile
+//    exceeds 2^22, in which case the tile's row max is folded into m, the
 //    accumulators are rescaled and the tile's weights recomputed.  Weights
-//    stay below 2^20 * 32 per lane and tile, far from fp32 and bf16 limits,
-//    and no per-tile max reduction runs in the common case.  Row sums of
+//    stay below 2^22, far from fp32 and bf16 limits, and no per-tile max
+//    reduction runs in the common case.  Row sums of
 //    the bf16 weights run on the matrix core (a 16x16x32 MFMA with a 0/1
 //    selector per 16-key slice), which idles half the time, instead of the
 //    VALU, which bounds the loop.
