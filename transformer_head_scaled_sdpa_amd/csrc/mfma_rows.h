@@ -2,9 +2,13 @@
 // workgroup and stream the other side (the attention backward and the
 // weights-export kernel), d = 64, gfx950.
 //
-// A workgroup is 8 wave64s: two groups of 32 rows (one row per lane column
-// of the 32x32 MFMA tile) times four phases; a step streams 128 rows, 32 per
-// phase, so each wave works on its own 32x32 tile.  Products run on
+// A workgroup is MFMA_ROWS_WAVES wave64s (the including file defines it: 4
+// or 8): two groups of 32 rows (one row per lane column of the 32x32 MFMA
+// tile) times kPhases = waves / 2 phases; a step streams 32 rows per phase,
+// so each wave works on its own 32x32 tile.  With 4 waves two workgroups
+// share a CU (one wave of each per SIMD), so one workgroup's prologue,
+// barriers and epilogue overlap the other's steps; with 8, one workgroup
+// fills a CU with twice the rows per step.  Products run on
 // v_mfma_f32_32x32x16_bf16: an accumulator packed to bf16 feeds the next MFMA
 // as its B operand, and transposed tiles are read from LDS with
 // ds_read_b64_tr_b16.  Streamed tiles are stored in 144-byte rows for 16-byte
@@ -14,11 +18,22 @@
 
 #include "common.h"
 
+#if !defined(MFMA_ROWS_WAVES) || (MFMA_ROWS_WAVES != 4 && MFMA_ROWS_WAVES != 8)
+#error "define MFMA_ROWS_WAVES (4 or 8) before including mfma_rows.h"
+#endif
+
 namespace mha {
 namespace rows64 {
+// The geometry names the inner namespace, so files built with different
+// geometries never share a symbol.
+#if MFMA_ROWS_WAVES == 4
+inline namespace waves4 {
+#else
+inline namespace waves8 {
+#endif
 
 constexpr int kD = 64;
-constexpr int kWaves = 8;
+constexpr int kWaves = MFMA_ROWS_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGroups = 2;                   // row groups of 32 per workgroup
 constexpr int kPhases = kWaves / kGroups;    // streamed tiles per step
@@ -144,23 +159,37 @@ __device__ __forceinline__ Chunks load_step(const StepSrc& s, int r0) {
 // Store a step into the per-phase tiles: row r goes to phase r / 32, in
 // 144-byte rows at byte offset offR of the phase area (if offR >= 0) and in
 // 192-byte rows at offT (if offT >= 0).
-// Chunk tid of the 64 rows r0 .. r0+63 (row tid / 8, features (tid % 8) * 8
-// ..), zero past row L - 1: the first chunk of a step.
-__device__ __forceinline__ uint4 load_chunk(const StepSrc& s, int r0) {
+// The 64 rows r0 .. r0+63 as 512 chunks (chunk c: row c / 8, features
+// (c % 8) * 8 ..), kStageChunks per thread (chunk tid + n * kThreads), zero
+// past row L - 1: the first chunks of a step.
+constexpr int kStageChunks = kRowsWg * 8 / kThreads;
+struct StageChunks {
+    uint4 c[kStageChunks];
+};
+__device__ __forceinline__ StageChunks load_chunks(const StepSrc& s, int r0) {
     const unsigned long long skip = (unsigned long long)(uint32_t)r0 * s.row_bytes;
     const bool any = skip < s.range;
     const uint32_t left = any ? s.range - (uint32_t)skip : 0u;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(s.base + (any ? skip : 0ull)), (short)0, (int)left, kBufWord3);
     typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, s.voff[0], 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
+    StageChunks t;
+#pragma unroll
+    for (int n = 0; n < kStageChunks; ++n) {
+        const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, s.voff[n], 0, 0);
+        t.c[n] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    return t;
 }
-// 64-row staging tiles of 144-byte rows in LDS: store chunk tid of tile t,
+// 64-row staging tiles of 144-byte rows in LDS: store the chunks of tile t,
 // read the fragment of row r, features kk*16 + hb*8 .. +7.
 constexpr int kStageB = kRowsWg * kLdsR * 2;
-__device__ __forceinline__ void stage_chunk(char* smem, int t, uint4 c, int tid) {
-    *reinterpret_cast<uint4*>(smem + t * kStageB + (tid >> 3) * (kLdsR * 2) + (tid & 7) * 16) = c;
+__device__ __forceinline__ void stage_chunks(char* smem, int t, const StageChunks& c, int tid) {
+#pragma unroll
+    for (int n = 0; n < kStageChunks; ++n) {
+        const int ch = tid + n * kThreads;
+        *reinterpret_cast<uint4*>(smem + t * kStageB + (ch >> 3) * (kLdsR * 2) + (ch & 7) * 16) = c.c[n];
+    }
 }
 __device__ __forceinline__ uint4 staged_frag(const char* smem, int t, int r, int kk, int hb) {
     return *reinterpret_cast<const uint4*>(smem + t * kStageB + r * (kLdsR * 2) + kk * 32 + hb * 16);
@@ -199,9 +228,10 @@ __device__ __forceinline__ int key_limit(const Args& a, int b, int i, bool& none
 }
 
 // Sum the per-phase partials of a 32-row accumulator pair through LDS: the
-// waves of phases 1..3 write theirs, the phase-0 wave of the group adds them.
-// Leaves the result in `acc` of the phase-0 waves.  `red` holds 6 slots of
-// 8 KiB; the caller brackets the calls with barriers.
+// waves of phases 1.. write theirs, the phase-0 wave of the group adds them.
+// Leaves the result in `acc` of the phase-0 waves.  `red` holds
+// kGroups * (kPhases - 1) slots of 8 KiB; the caller brackets the calls with
+// barriers.
 __device__ __forceinline__ void reduce_write(float* red, const f32x16 (&acc)[2], int grp, int ph, int lane) {
     if (ph == 0) return;
     float* slot = red + (grp * (kPhases - 1) + ph - 1) * 32 * 64;
@@ -222,12 +252,12 @@ __device__ __forceinline__ void reduce_read(const float* red, f32x16 (&acc)[2], 
     }
 }
 
-// The same sum spread over all four phase waves, one quarter of the 64
+// The same sum spread over all the phase waves, an equal share of the 64
 // features each.  part_write: every wave writes its partial times `scale` to
 // its own 8 KiB slot (values 4q .. 4q+3 of lane l, q = tb*4 + g4, at float
 // (q*64 + l)*4, 16-byte accesses).  After a barrier (the caller's),
-// part_sum: wave ph adds feature block tb = ph/2, groups g4 = 2*(ph%2) + n
-// (n = 0, 1) over the four slots of its group.  The slots take kRedAllB bytes.
+// part_sum: wave ph adds its groups q over the kPhases slots of its group.
+// The slots take kRedAllB bytes.
 constexpr int kRedSlotF = 32 * 64;
 constexpr int kRedAllB = kGroups * kPhases * kRedSlotF * 4;
 __device__ __forceinline__ void part_write(float* red, const f32x16 (&acc)[2], float scale, int grp, int ph,
@@ -241,11 +271,13 @@ __device__ __forceinline__ void part_write(float* red, const f32x16 (&acc)[2], f
                 make_float4(acc[tb][g4 * 4] * scale, acc[tb][g4 * 4 + 1] * scale, acc[tb][g4 * 4 + 2] * scale,
                             acc[tb][g4 * 4 + 3] * scale);
 }
-__device__ __forceinline__ void part_sum(const float* red, float4 (&r)[2], int grp, int ph, int lane) {
-    const int tb = ph >> 1;
+// Wave ph sums and stores kPartQ of the 8 groups q = tb*4 + g4 of four
+// features (features tb*32 + g4*8 + hb*4 .. +3): q = ph * kPartQ + n.
+constexpr int kPartQ = 8 / kPhases;
+__device__ __forceinline__ void part_sum(const float* red, float4 (&r)[kPartQ], int grp, int ph, int lane) {
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int q = tb * 4 + (ph & 1) * 2 + n;
+    for (int n = 0; n < kPartQ; ++n) {
+        const int q = ph * kPartQ + n;
         float4 t = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
         for (int p = 0; p < kPhases; ++p) {
@@ -258,13 +290,12 @@ __device__ __forceinline__ void part_sum(const float* red, float4 (&r)[2], int g
         r[n] = t;
     }
 }
-// Store wave ph's quarter from part_sum times `scale` (features
-// tb*32 + g4*8 + hb*4 .. +3 for its two groups g4).
-__device__ __forceinline__ void store_quarter(void* base, long long off, bool out_f32, const float4 (&r)[2],
+__device__ __forceinline__ void store_part(void* base, long long off, bool out_f32, const float4 (&r)[kPartQ],
                                               float scale, int ph, int hb) {
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int t = (ph >> 1) * 32 + ((ph & 1) * 2 + n) * 8 + hb * 4;
+    for (int n = 0; n < kPartQ; ++n) {
+        const int q = ph * kPartQ + n;
+        const int t = (q >> 2) * 32 + (q & 3) * 8 + hb * 4;
         const float y0 = r[n].x * scale, y1 = r[n].y * scale, y2 = r[n].z * scale, y3 = r[n].w * scale;
         if (out_f32)
             *reinterpret_cast<float4*>(static_cast<float*>(base) + off + t) = make_float4(y0, y1, y2, y3);
@@ -294,5 +325,6 @@ __device__ __forceinline__ void store_rowT(void* base, long long off, bool out_f
 }
 
 
+}  // inline namespace
 }  // namespace rows64
 }  // namespace mha

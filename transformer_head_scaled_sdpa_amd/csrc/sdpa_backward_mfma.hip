@@ -7,11 +7,11 @@
 // a row with no allowed key weights all keys uniformly and passes no
 // gradient to q or k).
 //
-// Workgroups of 8 wave64s in two roles.  A workgroup owns 64 rows (two
-// groups of 32, one row per lane column of the 32x32 MFMA tile) and streams
-// the other side in steps of 128 rows: four phases of 32, one per wave of a
-// group, so every wave works on its own tile and the four partial sums of a
-// row are added through LDS at the end.  Products run on
+// Workgroups of 4 wave64s in two roles, two workgroups per CU.  A workgroup
+// owns 64 rows (two groups of 32, one row per lane column of the 32x32 MFMA
+// tile) and streams the other side in steps of 64 rows: two phases of 32,
+// one per wave of a group, so every wave works on its own tile and the two
+// partial sums of a row are added through LDS at the end.  Products run on
 // v_mfma_f32_32x32x16_bf16 in the operand layouts of the forward kernel: an
 // accumulator packed to bf16 feeds the next MFMA as its B operand, and
 // transposed tiles are read from LDS with ds_read_b64_tr_b16 (tiles read both
@@ -37,6 +37,7 @@
 // forward.  Tiles where every pair is allowed skip the mask arithmetic.
 #include "common.h"
 #include "kernels.h"
+#define MFMA_ROWS_WAVES 4
 #include "mfma_rows.h"
 
 namespace mha {
@@ -54,15 +55,17 @@ using namespace rows64;
 // computed during step st, so at step st the K/V slot of st + 1 and the K^T
 // slot of st are read while step st + 2 is written to the slots of st (K/V,
 // last read during step st - 1) and st - 1 (K^T).  The staged Q, dO and O
-// sit past the K^T slot 1 before the first step, the dq partials at the
-// start after the last, and the per-phase (m, weight sum) after everything.
+// sit at the start until every wave has read its fragments (then the first
+// two steps are stored), the dq partials at the start after the last step,
+// and the per-phase (m, weight sum) after everything.  75 KB in all, so two
+// workgroups fit a CU.
 constexpr int kRowsSlotR = kPhases * kTileRB;     // one step in 144-byte rows
 constexpr int kRowsSlotT = kPhases * kTileTB;     // one step in 192-byte rows
 constexpr int kRowsKR = 0;
 constexpr int kRowsVR = 2 * kRowsSlotR;
 constexpr int kRowsKT = 4 * kRowsSlotR;
-constexpr int kRowsStage = kRowsKT + 2 * kRowsSlotT;
-constexpr int kRowsStat = kRowsStage + 3 * kStageB;
+constexpr int kRowsStat = kRowsKT + 3 * kRowsSlotT;
+static_assert(3 * kStageB <= kRowsStat, "staging fits");
 constexpr int kRowsLds = kRowsStat + kGroups * kPhases * 2 * 32 * 8;
 static_assert(kRowsKT + 3 * kRowsSlotT <= kRowsStat && kRedAllB <= kRowsStat, "tiles and partials fit");
 
@@ -124,12 +127,12 @@ __device__ __forceinline__ void rows_body(const BackwardArgs& a, float c, int bl
 
     // This workgroup's 64 rows of Q and dO (and O when D is formed here):
     // one range-checked 16-byte chunk per thread each (zeros past the
-    // queries), issued first and staged through LDS, so the four phase waves
+    // queries), issued first and staged through LDS, so the phase waves
     // of a group read their fragments from there instead of each loading
     // them.  With a log-sum-exp, that and D come from the workspace.
     const StepSrc qsrc = step_src(qp, a.sq[2], Lq, tid), gsrc = step_src(gp, a.sdo[2], Lq, tid);
-    const uint4 cq = load_chunk(qsrc, q_wg), cg = load_chunk(gsrc, q_wg);
-    uint4 co = make_uint4(0, 0, 0, 0);
+    const StageChunks cq = load_chunks(qsrc, q_wg), cg = load_chunks(gsrc, q_wg);
+    StageChunks co;
     float2 given = make_float2(0.0f, 0.0f);   // (log-sum-exp in log2 units, D) with kLse
     if constexpr (kLse) {
         // Range-checked: rows past the queries read zeros.
@@ -139,7 +142,7 @@ __device__ __forceinline__ void rows_body(const BackwardArgs& a, float c, int bl
         const u32x2v x = __builtin_amdgcn_raw_buffer_load_b64(rr, (uint32_t)i * 8u, 0, 0);
         given = make_float2(__uint_as_float(x[0]), __uint_as_float(x[1]));
     } else {
-        co = load_chunk(step_src(op, a.so[2], Lq, tid), q_wg);
+        co = load_chunks(step_src(op, a.so[2], Lq, tid), q_wg);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -160,16 +163,10 @@ __device__ __forceinline__ void rows_body(const BackwardArgs& a, float c, int bl
         store_step(nv, smem + kRowsVR + slot2 * kRowsSlotR, kTileRB, 0, -1, tid);
         store_step(nk, smem + kRowsKT + slot3 * kRowsSlotT, kTileTB, -1, 0, tid);
     };
-    char* const stage = smem + kRowsStage;
-    stage_chunk(stage, 0, cq, tid);
-    stage_chunk(stage, 1, cg, tid);
-    if constexpr (!kLse) stage_chunk(stage, 2, co, tid);
-    put(nk_e, nv_e, 0, 0);
-    nk_e = load_step(ksrc, 2 * kStep);
-    nv_e = load_step(vsrc, 2 * kStep);
-    put(nk_o, nv_o, 1, 1);
-    nk_o = load_step(ksrc, 3 * kStep);
-    nv_o = load_step(vsrc, 3 * kStep);
+    char* const stage = smem;   // overlaps the tile slots: read out before the first steps go in
+    stage_chunks(stage, 0, cq, tid);
+    stage_chunks(stage, 1, cg, tid);
+    if constexpr (!kLse) stage_chunks(stage, 2, co, tid);
     __syncthreads();
 
     // Q and dO fragments (B operands: query lane%32, features kk*16 + hb*8 ..);
@@ -194,6 +191,14 @@ __device__ __forceinline__ void rows_body(const BackwardArgs& a, float c, int bl
     }
     if constexpr (kLse) dsum = given.y;
     else dsum = pair_sum(dsum);             // D_i over both lane halves
+    __syncthreads();                        // every wave's fragments read: the steps may overwrite the staging
+    put(nk_e, nv_e, 0, 0);
+    nk_e = load_step(ksrc, 2 * kStep);
+    nv_e = load_step(vsrc, 2 * kStep);
+    put(nk_o, nv_o, 1, 1);
+    nk_o = load_step(ksrc, 3 * kStep);
+    nv_o = load_step(vsrc, 3 * kStep);
+    __syncthreads();
     // dP^T - D starts from -D in the accumulator (element v of a lane is the
     // lane's query).
     f32x16 neg_d;
@@ -321,14 +326,14 @@ __device__ __forceinline__ void rows_body(const BackwardArgs& a, float c, int bl
     float* red = reinterpret_cast<float*>(smem);
     part_write(red, dq, own, grp, ph, lane);
     __syncthreads();
-    float4 r[2];
+    float4 r[kPartQ];
     part_sum(red, r, grp, ph, lane);
     if (!live) return;
     if constexpr (!kLse) {
         if (ph == 0 && hb == 0)
             reinterpret_cast<float2*>(a.rows)[(long long)bh * Lq + i] = make_float2(lse, dsum);
     }
-    store_quarter(a.dq, b * a.sdq[0] + hd * a.sdq[1] + (long long)i * a.sdq[2], a.out_f32, r, dq_scale, ph, hb);
+    store_part(a.dq, b * a.sdq[0] + hd * a.sdq[1] + (long long)i * a.sdq[2], a.out_f32, r, dq_scale, ph, hb);
 }
 
 template <bool kCausal>
@@ -363,7 +368,7 @@ __device__ __forceinline__ void keys_body(const BackwardArgs& a, float c, int bl
     // per thread each (zeros past the keys), staged through LDS like the
     // rows' Q and dO.
     const StepSrc ksrc = step_src(kp, a.sk[2], Lk, tid), vsrc = step_src(vp, a.sv[2], Lk, tid);
-    const uint4 ck = load_chunk(ksrc, k_wg), cv = load_chunk(vsrc, k_wg);
+    const StageChunks ck = load_chunks(ksrc, k_wg), cv = load_chunks(vsrc, k_wg);
     __builtin_amdgcn_sched_barrier(0);
 
     // Per streamed query (threads below kStep keep them): log-sum-exp and D
@@ -401,8 +406,8 @@ __device__ __forceinline__ void keys_body(const BackwardArgs& a, float c, int bl
     __builtin_amdgcn_sched_barrier(0);
     Chunks nq_o = load_step(qsrc, i_begin + kStep), ng_o = load_step(gsrc, i_begin + kStep);
     __builtin_amdgcn_sched_barrier(0);
-    stage_chunk(smem, 0, ck, tid);
-    stage_chunk(smem, 1, cv, tid);
+    stage_chunks(smem, 0, ck, tid);
+    stage_chunks(smem, 1, cv, tid);
     __syncthreads();
     // K and V fragments (B operands: key lane%32, features kk*16 + hb*8 ..).
     bf16x8 kf[4], vf[4];
@@ -505,23 +510,23 @@ __device__ __forceinline__ void keys_body(const BackwardArgs& a, float c, int bl
     part_write(red, dv, 1.0f, grp, ph, lane);
     part_write(red + kRedAllB / 4, dk, 1.0f / 8.0f, grp, ph, lane);
     __syncthreads();
-    float4 rv[2], rk[2];
+    float4 rv[kPartQ], rk[kPartQ];
     part_sum(red, rv, grp, ph, lane);
     part_sum(red + kRedAllB / 4, rk, grp, ph, lane);
     if (j >= Lk) return;
-    store_quarter(a.dk, b * a.sdk[0] + hd * a.sdk[1] + (long long)j * a.sdk[2], a.out_f32, rk, 1.0f, ph, hb);
-    store_quarter(a.dv, b * a.sdv[0] + hd * a.sdv[1] + (long long)j * a.sdv[2], a.out_f32, rv, 1.0f, ph, hb);
+    store_part(a.dk, b * a.sdk[0] + hd * a.sdk[1] + (long long)j * a.sdk[2], a.out_f32, rk, 1.0f, ph, hb);
+    store_part(a.dv, b * a.sdv[0] + hd * a.sdv[1] + (long long)j * a.sdv[2], a.out_f32, rv, 1.0f, ph, hb);
 }
 
 template <bool kCausal>
-__global__ __launch_bounds__(kThreads, 1) void bwd_rows_mfma(BackwardArgs a, float c) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_rows_mfma(BackwardArgs a, float c) {
     __shared__ __attribute__((aligned(16))) char smem[kRowsLds];
     const int BH = a.B * a.H;
     rows_body<kCausal, false>(a, c, blockIdx.x / BH, blockIdx.x % BH, smem);
 }
 
 template <bool kCausal>
-__global__ __launch_bounds__(kThreads, 1) void bwd_keys_mfma(BackwardArgs a, float c) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_keys_mfma(BackwardArgs a, float c) {
     __shared__ __attribute__((aligned(16))) char smem[kKeysLds];
     const int BH = a.B * a.H;
     keys_body<kCausal>(a, c, blockIdx.x / BH, blockIdx.x % BH, smem);
@@ -561,7 +566,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BackwardArgs a) {
 // first, so the lightest query blocks fill the end.  (Measured: alternating
 // the kinds block by block ran the key side about 15% slower per step.)
 template <bool kCausal>
-__global__ __launch_bounds__(kThreads, 1) void bwd_fused_mfma(BackwardArgs a, float c, int n_kb) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_fused_mfma(BackwardArgs a, float c, int n_kb) {
     __shared__ __attribute__((aligned(16))) char smem[kFusedLds];
     const int BH = a.B * a.H;
     const int bh = blockIdx.x % BH, u = blockIdx.x / BH;

@@ -10,19 +10,22 @@
 //   keys weigh exactly 0; a row with none allowed weighs all Lk keys 1/Lk),
 //   o_i = sum_j p_ij v_j.
 //
-// Layout of mfma_rows.h: 64 queries per workgroup, keys streamed in steps of
-// 128 (four phases of 32).  Two passes over the keys:
+// Layout of mfma_rows.h with 8 waves: 64 queries per workgroup, keys
+// streamed in steps of 128 (four phases of 32; measured faster here than 4
+// waves with two workgroups per CU: 16.0 against 18.4 us on B4 h8 L512).
+// Two passes over the keys:
 //  * pass 1: S^T = K Q^T on the MFMA (exact bf16 products, fp32 sums), an
 //    online (max, sum) per lane half and phase, merged into each query's
 //    log-sum-exp;
 //  * pass 2: the scores again, p = exp2(s - lse) in fp32 written as the final
 //    weights, and O^T += V^T P^T with P split into two bf16 terms (hi + lo,
 //    about 16 significant bits), so the output keeps fp32-level accuracy.
-// The four phases' partial outputs are summed through LDS.  Causal launches
+// The phases' partial outputs are summed through LDS.  Causal launches
 // without lengths stream only the keys the triangle allows and fill the rest
 // of the weight rows with zeros.
 #include "common.h"
 #include "kernels.h"
+#define MFMA_ROWS_WAVES 8
 #include "mfma_rows.h"
 
 namespace mha {
