@@ -62,6 +62,9 @@ def _open(path):
     lib.oracle_mha_f64.restype = ctypes.c_int
     lib.oracle_mha_f64.argtypes = [_dp] * 11 + [ctypes.c_int] * 5 + [
         _ip, ctypes.c_int, ctypes.c_int, _ip, ctypes.c_int, ctypes.c_int]
+    lib.oracle_mha_backward_f64.restype = ctypes.c_int
+    lib.oracle_mha_backward_f64.argtypes = [_dp] * 20 + [ctypes.c_int] * 5 + [_ip, ctypes.c_int, ctypes.c_int,
+                                                                             ctypes.c_int]
     lib.oracle_sdpa_backward_f64.restype = ctypes.c_int
     lib.oracle_sdpa_backward_f64.argtypes = [_dp] * 7 + [ctypes.c_int] * 6 + [_ip, ctypes.c_int, ctypes.c_int]
     lib.oracle_layer_norm_f64.restype = None
@@ -207,6 +210,41 @@ def sdpa_backward(q, k, v, dout, valid_lens=None, causal=False):
     if rc != 0:
         raise ValueError("oracle_sdpa_backward_f64 rejected its arguments")
     return dq, dkk, dvv
+
+
+def mha_backward(x_q, x_kv, w_q, w_k, w_v, w_o, dout, b_q=None, b_k=None, b_v=None, h=8, valid_lens=None,
+                 causal=False, bf16_stages=False):
+    """Gradients of ``mha(x_q, x_kv, ...)`` (all query rows) for the output
+    gradient ``dout`` [B, Lq, D].  Returns a dict: dx_q [B,Lq,D] (through the
+    query projection), dx_kv [B,Lk,D] (through the key and value projections;
+    with self-attention the input's gradient is dx_q + dx_kv), dw_q, dw_k,
+    dw_v, dw_o [D,D] and db_q, db_k, db_v, db_o [D].  The output bias does
+    not enter any gradient."""
+    xq, xkv, g = _f64(x_q), _f64(x_kv), _f64(dout)
+    B, Lq, D = xq.shape
+    Lk = xkv.shape[1]
+    assert xkv.shape == (B, Lk, D) and g.shape == (B, Lq, D)
+    ws = [_f64(w) for w in (w_q, w_k, w_v, w_o)]
+    for w in ws:
+        assert w.shape == (D, D)
+    bs = [None if b is None else _f64(b) for b in (b_q, b_k, b_v)]
+    vl = _i32(valid_lens)
+    if vl is not None:
+        assert vl.shape in ((B,), (B, Lq))
+    r = {"dx_q": np.empty((B, Lq, D)), "dx_kv": np.empty((B, Lk, D))}
+    for n in ("q", "k", "v", "o"):
+        r["dw_" + n] = np.empty((D, D))
+        r["db_" + n] = np.empty(D)
+    rc = _load().oracle_mha_backward_f64(
+        _ptr(xq), _ptr(xkv), _ptr(ws[0]), _ptr(bs[0]), _ptr(ws[1]), _ptr(bs[1]), _ptr(ws[2]), _ptr(bs[2]),
+        _ptr(ws[3]), _ptr(g), _ptr(r["dx_q"]), _ptr(r["dx_kv"]),
+        _ptr(r["dw_q"]), _ptr(r["db_q"]), _ptr(r["dw_k"]), _ptr(r["db_k"]),
+        _ptr(r["dw_v"]), _ptr(r["db_v"]), _ptr(r["dw_o"]), _ptr(r["db_o"]),
+        B, Lq, Lk, D, h, _iptr(vl), int(vl is not None and vl.ndim == 2), int(bool(causal)),
+        int(bool(bf16_stages)))
+    if rc != 0:
+        raise ValueError("oracle_mha_backward_f64 rejected its arguments")
+    return r
 
 
 def layer_norm(x, gain=None, bias=None, kind=0, eps=1e-6):

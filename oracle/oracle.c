@@ -1,5 +1,6 @@
 /*
- * Plain fp64 CPU oracle for multi-head scaled dot-product attention (forward).
+ * Plain fp64 CPU oracle for multi-head scaled dot-product attention (forward
+ * and backward).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call
  * this file: only the test suite, the smoke check and the benchmark's CPU
@@ -390,6 +391,159 @@ int oracle_sdpa_backward_f64(const double* q, const double* k, const double* v, 
         free(p); free(s); free(o); free(dp);
     }
     return bad ? -1 : 0;
+}
+
+/*
+ * Gradients of one linear layer y = x W^T + b (W [Dout, Din] stored [out,
+ * in]) for the output gradient dy [M, Dout], by the chain rule on
+ * y[m, n] = sum_c x[m, c] W[n, c] + b[n]:
+ *   dx[m, c] (+)= sum_n dy[m, n] W[n, c]     (added to dx when accumulate)
+ *   dW[n, c]    = sum_m dy[m, n] x[m, c]
+ *   db[n]       = sum_m dy[m, n]             (when db is not NULL)
+ */
+static void linear_backward(const double* dy, const double* x, const double* w,
+                            double* dx, double* dw, double* db, long M, int Din, int Dout, int accumulate)
+{
+    long m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m)
+        for (int c = 0; c < Din; ++c) {
+            double acc = 0.0;
+            for (int n = 0; n < Dout; ++n) acc += dy[m * Dout + n] * w[(long)n * Din + c];
+            dx[m * Din + c] = (accumulate ? dx[m * Din + c] : 0.0) + acc;
+        }
+    int n;
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < Dout; ++n) {
+        for (int c = 0; c < Din; ++c) {
+            double acc = 0.0;
+            for (long r = 0; r < M; ++r) acc += dy[r * Dout + n] * x[r * Din + c];
+            dw[(long)n * Din + c] = acc;
+        }
+        if (db) {
+            double acc = 0.0;
+            for (long r = 0; r < M; ++r) acc += dy[r * Dout + n];
+            db[n] = acc;
+        }
+    }
+}
+
+/* [B, L, h*dk] rows <-> [B, h, L, dk] heads: head hd owns features
+ * [hd*dk, (hd+1)*dk) of each row (the split of oracle_mha_f64); to_heads
+ * selects the direction. */
+static void head_permute(double* rows, double* heads, int B, int L, int h, int dk, int to_heads)
+{
+    for (int b = 0; b < B; ++b)
+        for (int hd = 0; hd < h; ++hd)
+            for (int l = 0; l < L; ++l)
+                for (int t = 0; t < dk; ++t) {
+                    double* r = rows + ((long)b * L + l) * h * dk + hd * dk + t;
+                    double* e = heads + (((long)b * h + hd) * L + l) * dk + t;
+                    if (to_heads) *e = *r;
+                    else *r = *e;
+                }
+}
+
+/*
+ * Gradients of the multi-head layer of oracle_mha_f64 (all query rows) for an
+ * output gradient dout [B, Lq, D]: the training pass the pages take through
+ * it (The Annotated Transformer and the d2l digest train these models end to
+ * end), by the chain rule through each forward step in reverse:
+ *   out = Ocat Wo^T + bo        -> dOcat, dWo, dbo   (linear_backward)
+ *   head merge                  -> split dOcat into heads
+ *   attention per head          -> dq, dk, dv        (oracle_sdpa_backward_f64)
+ *   head split                  -> merge dQ, dK, dV
+ *   Q = Xq Wq^T + bq            -> dXq, dWq, dbq
+ *   K = Xkv Wk^T + bk, V = ...  -> dXkv = dK Wk + dV Wv, dWk, dbk, dWv, dbv
+ * dxq [B, Lq, D] is the gradient through the query projection and dxkv
+ * [B, Lk, D] the gradient through the key and value projections; when one
+ * tensor feeds both (self-attention) its gradient is their sum.  dw_* [D, D],
+ * db_* [D] (db_* may be NULL).
+ * bf16_stages != 0: as in oracle_mha_f64, Q, K, V and the merged heads are
+ * rounded to bfloat16 where they are made, and so are the gradients of the
+ * merged heads and of Q, K and V (the storage precision of a bf16 pipeline).
+ * Returns 0, or -1 on a bad argument / allocation failure.
+ */
+int oracle_mha_backward_f64(const double* xq, const double* xkv,
+                            const double* w_q, const double* b_q,
+                            const double* w_k, const double* b_k,
+                            const double* w_v, const double* b_v,
+                            const double* w_o, const double* dout,
+                            double* dxq, double* dxkv,
+                            double* dw_q, double* db_q, double* dw_k, double* db_k,
+                            double* dw_v, double* db_v, double* dw_o, double* db_o,
+                            int B, int Lq, int Lk, int D, int h,
+                            const int* valid_lens, int vl_per_query, int causal, int bf16_stages)
+{
+    if (B < 0 || Lq < 0 || Lk <= 0 || D <= 0 || h <= 0 || D % h != 0) return -1;
+    const int dk = D / h;
+    const long Mq = (long)B * Lq, Mk = (long)B * Lk;
+    double* Qf = (double*)malloc(sizeof(double) * (size_t)(Mq * D + 1));
+    double* Kf = (double*)malloc(sizeof(double) * (size_t)(Mk * D + 1));
+    double* Vf = (double*)malloc(sizeof(double) * (size_t)(Mk * D + 1));
+    double* qh = (double*)malloc(sizeof(double) * (size_t)(Mq * D + 1));
+    double* kh = (double*)malloc(sizeof(double) * (size_t)(Mk * D + 1));
+    double* vh = (double*)malloc(sizeof(double) * (size_t)(Mk * D + 1));
+    double* oh = (double*)malloc(sizeof(double) * (size_t)(Mq * D + 1));
+    double* ocat = (double*)malloc(sizeof(double) * (size_t)(Mq * D + 1));
+    double* docat = (double*)malloc(sizeof(double) * (size_t)(Mq * D + 1));
+    double* doh = (double*)malloc(sizeof(double) * (size_t)(Mq * D + 1));
+    double* dqh = (double*)malloc(sizeof(double) * (size_t)(Mq * D + 1));
+    double* dkh = (double*)malloc(sizeof(double) * (size_t)(Mk * D + 1));
+    double* dvh = (double*)malloc(sizeof(double) * (size_t)(Mk * D + 1));
+    double* dQ = (double*)malloc(sizeof(double) * (size_t)(Mq * D + 1));
+    double* dK = (double*)malloc(sizeof(double) * (size_t)(Mk * D + 1));
+    double* dV = (double*)malloc(sizeof(double) * (size_t)(Mk * D + 1));
+    double* s = (double*)malloc(sizeof(double) * (size_t)Lk + 1);
+    int rc = 0;
+    if (!Qf || !Kf || !Vf || !qh || !kh || !vh || !oh || !ocat || !docat || !doh || !dqh || !dkh || !dvh ||
+        !dQ || !dK || !dV || !s) { rc = -1; goto done; }
+
+    /* The forward, keeping what the backward reads. */
+    oracle_linear_f64(xq, w_q, b_q, Qf, Mq, D, D);
+    oracle_linear_f64(xkv, w_k, b_k, Kf, Mk, D, D);
+    oracle_linear_f64(xkv, w_v, b_v, Vf, Mk, D, D);
+    if (bf16_stages) {
+        round_all(Qf, Mq * D);
+        round_all(Kf, Mk * D);
+        round_all(Vf, Mk * D);
+    }
+    head_permute(Qf, qh, B, Lq, h, dk, 1);
+    head_permute(Kf, kh, B, Lk, h, dk, 1);
+    head_permute(Vf, vh, B, Lk, h, dk, 1);
+    for (long bh = 0; bh < (long)B * h; ++bh)
+        for (int i = 0; i < Lq; ++i)
+            attend_row(qh + (bh * Lq + i) * dk, kh + bh * Lk * dk, vh + bh * Lk * dk, oh + (bh * Lq + i) * dk,
+                       NULL, s, Lq, Lk, dk, dk, valid_lens, vl_per_query, causal, (int)(bh / h), i);
+    head_permute(ocat, oh, B, Lq, h, dk, 0);
+    if (bf16_stages) round_all(ocat, Mq * D);
+
+    /* Output projection. */
+    linear_backward(dout, ocat, w_o, docat, dw_o, db_o, Mq, D, D, 0);
+    if (bf16_stages) round_all(docat, Mq * D);
+
+    /* Attention, head by head. */
+    head_permute(docat, doh, B, Lq, h, dk, 1);
+    if (oracle_sdpa_backward_f64(qh, kh, vh, doh, dqh, dkh, dvh, B, h, Lq, Lk, dk, dk,
+                                 valid_lens, vl_per_query, causal) != 0) { rc = -1; goto done; }
+    head_permute(dQ, dqh, B, Lq, h, dk, 0);
+    head_permute(dK, dkh, B, Lk, h, dk, 0);
+    head_permute(dV, dvh, B, Lk, h, dk, 0);
+    if (bf16_stages) {
+        round_all(dQ, Mq * D);
+        round_all(dK, Mk * D);
+        round_all(dV, Mk * D);
+    }
+
+    /* Input projections: K and V both read xkv, so their input gradients add. */
+    linear_backward(dQ, xq, w_q, dxq, dw_q, db_q, Mq, D, D, 0);
+    linear_backward(dK, xkv, w_k, dxkv, dw_k, db_k, Mk, D, D, 0);
+    linear_backward(dV, xkv, w_v, dxkv, dw_v, db_v, Mk, D, D, 1);
+
+done:
+    free(Qf); free(Kf); free(Vf); free(qh); free(kh); free(vh); free(oh); free(ocat);
+    free(docat); free(doh); free(dqh); free(dkh); free(dvh); free(dQ); free(dK); free(dV); free(s);
+    return rc;
 }
 
 /*

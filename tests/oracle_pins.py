@@ -661,4 +661,149 @@ def pin_lse_vs_scipy_logsumexp_and_weights():
                 _close(np.exp(s - lse[b, hd, i]), p[b, hd, i, :n], 1e-13)
 
 
+# ---------------------------------------------------------------------------
+# gradients of the multi-head layer
+# ---------------------------------------------------------------------------
+_GRADS = ("dx_q", "dx_kv", "dw_q", "dw_k", "dw_v", "dw_o", "db_q", "db_k", "db_v", "db_o")
+
+
+def _mha_case(r, B, Lq, Lk, D):
+    xq, xkv = r.standard_normal((B, Lq, D)), r.standard_normal((B, Lk, D))
+    ws = [r.standard_normal((D, D)) / math.sqrt(D) for _ in range(4)]
+    bs = [r.standard_normal(D) * 0.1 for _ in range(4)]
+    g = r.standard_normal((B, Lq, D))
+    return xq, xkv, ws, bs, g
+
+
+def _torch_mha_grads(xq, xkv, ws, bs, g, h, vl, causal, bf16_stages=False):
+    """torch float64 CPU autograd of sum(MHA(xq, xkv) * g) through its own
+    multi-head attention (in fp64) or, for the bf16-storage reading, through
+    linear / scaled_dot_product_attention with a rounding step that rounds
+    the value going forward and its gradient going back."""
+    torch = _torch()
+    F = torch.nn.functional
+    leaf = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
+    txq, txkv = leaf(xq), leaf(xkv)
+    tw = [leaf(w) for w in ws]
+    tb = [leaf(b) for b in bs]
+    B, Lq, D = xq.shape
+    Lk = xkv.shape[1]
+    if not bf16_stages:
+        kpm = None
+        if vl is not None:
+            kpm = torch.arange(Lk)[None, :] >= torch.tensor(np.asarray(vl))[:, None]
+        am = torch.triu(torch.ones(Lq, Lk, dtype=torch.bool), diagonal=1) if causal else None
+        out, _ = F.multi_head_attention_forward(
+            txq.transpose(0, 1), txkv.transpose(0, 1), txkv.transpose(0, 1), D, h,
+            torch.cat(tw[:3]), torch.cat(tb[:3]), None, None, False, 0.0, tw[3], tb[3], training=False,
+            key_padding_mask=kpm, need_weights=False, attn_mask=am)
+        out = out.transpose(0, 1)
+    else:
+        class Round(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, x):
+                return x.to(torch.bfloat16).to(torch.float64)
+
+            @staticmethod
+            def backward(ctx, gr):
+                return gr.to(torch.bfloat16).to(torch.float64)
+
+        q = Round.apply(F.linear(txq, tw[0], tb[0]))
+        k = Round.apply(F.linear(txkv, tw[1], tb[1]))
+        v = Round.apply(F.linear(txkv, tw[2], tb[2]))
+        dk = D // h
+        sp = lambda t: t.view(B, -1, h, dk).transpose(1, 2)
+        allowed = torch.ones(B, 1, Lq, Lk, dtype=torch.bool)
+        if vl is not None:
+            allowed &= (torch.arange(Lk)[None, :] < torch.tensor(np.asarray(vl))[:, None])[:, None, None, :]
+        if causal:
+            allowed &= torch.tril(torch.ones(Lq, Lk, dtype=torch.bool))[None, None]
+        o = F.scaled_dot_product_attention(sp(q), sp(k), sp(v), attn_mask=allowed)
+        o = Round.apply(o.transpose(1, 2).reshape(B, Lq, D))
+        out = F.linear(o, tw[3], tb[3])
+    (out * torch.tensor(g)).sum().backward()
+    t = {"dx_q": txq.grad, "dx_kv": txkv.grad}
+    for n, w, b in zip("qkvo", tw, tb):
+        t["dw_" + n] = w.grad
+        t["db_" + n] = b.grad
+    return {n: a.numpy() for n, a in t.items()}
+
+
+def pin_mha_backward_vs_torch_autograd():
+    """Every gradient of the multi-head layer against torch's float64
+    autograd through its own multi-head attention: causal self-attention with
+    padding, cross-attention with padding, and no mask."""
+    r = _rng(61)
+    for (B, Lq, Lk, D, h, causal, vl) in [(2, 7, 7, 16, 2, True, [7, 3]),
+                                          (2, 5, 9, 24, 3, False, [9, 2]),
+                                          (1, 6, 4, 8, 1, False, None)]:
+        xq, xkv, ws, bs, g = _mha_case(r, B, Lq, Lk, D)
+        got = oracle.mha_backward(xq, xkv, *ws, g, *bs[:3], h=h, valid_lens=vl, causal=causal)
+        ref = _torch_mha_grads(xq, xkv, ws, bs, g, h, vl, causal)
+        for n in _GRADS:
+            _close(got[n], ref[n], 1e-11)
+
+
+def pin_mha_backward_bf16_stages_vs_torch():
+    """The bf16-storage reading of the backward (Q, K, V, the merged heads and
+    the gradients of those four rounded to bf16 where they are made) against
+    torch autograd with a rounding step at the same four places."""
+    r = _rng(62)
+    B, Lq, Lk, D, h = 2, 6, 8, 16, 2
+    xq, xkv, ws, bs, g = _mha_case(r, B, Lq, Lk, D)
+    got = oracle.mha_backward(xq, xkv, *ws, g, *bs[:3], h=h, valid_lens=[8, 5], bf16_stages=True)
+    ref = _torch_mha_grads(xq, xkv, ws, bs, g, h, [8, 5], False, bf16_stages=True)
+    plain = oracle.mha_backward(xq, xkv, *ws, g, *bs[:3], h=h, valid_lens=[8, 5])
+    for n in _GRADS:
+        _close(got[n], ref[n], 1e-10)
+    # the rounding is really applied, on both sides of the attention
+    assert np.max(np.abs(got["dw_o"] - plain["dw_o"])) > 1e-5
+    assert np.max(np.abs(got["dw_q"] - plain["dw_q"])) > 1e-5
+
+
+def pin_mha_backward_finite_differences():
+    """Each gradient element equals the central difference of
+    sum(mha(...) * g) in that input, weight or bias (the output bias
+    included), for cross-attention with padding and causal self-attention
+    fed from separate query and key/value inputs."""
+    r = _rng(63)
+    for (B, Lq, Lk, D, h, causal, vl) in [(2, 3, 4, 4, 2, False, [4, 2]), (1, 3, 3, 4, 2, True, None)]:
+        xq, xkv, ws, bs, g = _mha_case(r, B, Lq, Lk, D)
+        got = oracle.mha_backward(xq, xkv, *ws, g, *bs[:3], h=h, valid_lens=vl, causal=causal)
+        loss = lambda: np.sum(oracle.mha(xq, xkv, *ws, *bs, h=h, valid_lens=vl, causal=causal) * g)
+        named = [("dx_q", xq), ("dx_kv", xkv)] + [("dw_" + n, w) for n, w in zip("qkvo", ws)] + \
+                [("db_" + n, b) for n, b in zip("qkvo", bs)]
+        for name, x in named:
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                e = 1e-6
+                x[idx] += e
+                up = loss()
+                x[idx] -= 2 * e
+                dn = loss()
+                x[idx] += e
+                fd[idx] = (up - dn) / (2 * e)
+            _close(got[name], fd, 1e-7)
+
+
+def pin_mha_backward_single_key_closed_form():
+    """With one key the weights are 1 whatever the scores, so the layer is
+    out_i = (x_kv W_v^T + b_v) W_o^T + b_o for every query: the query and key
+    projections get no gradient, and the rest follow from two linear layers."""
+    r = _rng(64)
+    B, Lq, D, h = 2, 5, 8, 2
+    xq, xkv, ws, bs, g = _mha_case(r, B, Lq, 1, D)
+    got = oracle.mha_backward(xq, xkv, *ws, g, *bs[:3], h=h)
+    for n in ("dx_q", "dw_q", "dw_k", "db_q", "db_k"):
+        _close(got[n], np.zeros_like(got[n]))
+    v = xkv[:, 0] @ ws[2].T + bs[2]                 # [B, D], the one value row
+    gsum = g.sum(axis=1)                            # [B, D]
+    dv = gsum @ ws[3]                               # gradient of each batch's value row
+    _close(got["db_o"], g.sum(axis=(0, 1)))
+    _close(got["dw_o"], gsum.T @ v)
+    _close(got["db_v"], dv.sum(axis=0))
+    _close(got["dw_v"], dv.T @ xkv[:, 0])
+    _close(got["dx_kv"][:, 0], dv @ ws[2])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -17,7 +17,8 @@ MUTATIONS = [
     ("valid_len_off_by_one", "!(j < valid_lens[b])", "!(j <= valid_lens[b])"),
     ("fill_added_not_replaced", "s[j] = ORACLE_MASK_FILL;", "s[j] += ORACLE_MASK_FILL;"),
     ("fill_too_small", "#define ORACLE_MASK_FILL (-1e9)", "#define ORACLE_MASK_FILL (-1e1)"),
-    ("weight_transposed", "w[(long)n * Din + c]", "w[(long)c * Dout + n]"),
+    ("weight_transposed", "acc += x[m * Din + c] * w[(long)n * Din + c];",
+     "acc += x[m * Din + c] * w[(long)c * Dout + n];"),
     ("bias_dropped", "acc + (b ? b[n] : 0.0)", "acc"),
     ("head_split_interleaved",
      "Qf[((long)b * R + r) * D + hd * dk + t]", "Qf[((long)b * R + r) * D + t * h + hd]"),
@@ -26,7 +27,9 @@ MUTATIONS = [
     ("value_index_transposed", "v[(long)j * dv + t]", "v[(long)t * Lk + j]"),
     ("softmax_not_normalised", "s[j] /= den;", "s[j] /= (den > 1.0 ? 1.0 : den);"),
     ("bf16_ties_away", "(fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0", "fl + 1.0"),
-    ("bf16_merge_not_rounded", "if (bf16_stages) round_all(ocat", "if (0) round_all(ocat"),
+    ("bf16_merge_not_rounded", "if (bf16_stages) round_all(ocat, (long)B * R * D);",
+     "if (0) round_all(ocat, (long)B * R * D);"),
+    ("mha_backward_merge_not_rounded", "if (bf16_stages) round_all(ocat, Mq * D);", "if (0) round_all(ocat, Mq * D);"),
     ("mask_uses_query_length", "if (valid_lens && !(j < valid_lens[b]))",
      "if (valid_lens && !(i < valid_lens[b]))"),
     ("per_query_length_rows_reversed", "valid_lens[(long)b * Lq + i]", "valid_lens[(long)b * Lq + (Lq - 1 - i)]"),
@@ -41,6 +44,18 @@ MUTATIONS = [
     ("per_query_length_ignores_query", "valid_lens[(long)b * Lq + i]", "valid_lens[(long)b * Lq]"),
     ("lse_drops_the_max", "lse[bh * (long)Lq + i] = mx + log(den);", "lse[bh * (long)Lq + i] = log(den);"),
     ("lse_in_log2", "lse[bh * (long)Lq + i] = mx + log(den);", "lse[bh * (long)Lq + i] = mx + log2(den);"),
+    ("linear_backward_dw_transposed", "dw[(long)n * Din + c] = acc;", "dw[(long)c * Dout + n] = acc;"),
+    ("linear_backward_dx_uses_w_transposed", "acc += dy[m * Dout + n] * w[(long)n * Din + c];",
+     "acc += dy[m * Dout + n] * w[(long)c * Dout + n];"),
+    ("linear_backward_bias_first_row_only", "for (long r = 0; r < M; ++r) acc += dy[r * Dout + n];",
+     "for (long r = 0; r < 1; ++r) acc += dy[r * Dout + n];"),
+    ("mha_backward_value_path_overwrites_key_path", "linear_backward(dV, xkv, w_v, dxkv, dw_v, db_v, Mk, D, D, 1);",
+     "linear_backward(dV, xkv, w_v, dxkv, dw_v, db_v, Mk, D, D, 0);"),
+    ("mha_backward_heads_interleaved", "double* r = rows + ((long)b * L + l) * h * dk + hd * dk + t;",
+     "double* r = rows + ((long)b * L + l) * h * dk + t * h + hd;"),
+    ("mha_backward_merged_head_gradient_not_rounded", "if (bf16_stages) round_all(docat, Mq * D);",
+     "if (0) round_all(docat, Mq * D);"),
+    ("mha_backward_query_gradient_not_rounded", "round_all(dQ, Mq * D);", ""),
 ]
 
 
