@@ -188,7 +188,9 @@ mha_status sdpa_decode(mha_dtype in_dt, mha_dtype out_dt,
  * products, as the forward rounds its weights); MHA_F32 inputs in fp32 FMA.
  * Requirements otherwise as for sdpa_forward; for MHA_BF16 inputs each
  * (batch, head)'s rows of q, k, v, o and dout must span less than 2 GiB, as
- * must 128 rows at each one's row stride (MHA_ENOTSUP otherwise).
+ * must 128 rows at each one's row stride (MHA_ENOTSUP otherwise).  B == 0
+ * is a no-op; Lq == 0 with B > 0 writes dk and dv as zeros (their defining
+ * sums are empty) and reads nothing else.
  */
 size_t sdpa_backward_workspace_bytes(int B, int h, int Lq);
 
@@ -386,6 +388,66 @@ mha_status mha_sublayer_forward(mha_dtype in_dt, mha_dtype out_dt,
                                 int B, int L, int Lk, int d_model, int h, int d_k,
                                 const int* valid_lens, int causal,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mha_backward -- the gradients of mha_forward's output for an output
+ * gradient `dout`: the training pass the pages take through the multi-head
+ * layer (The Annotated Transformer and the d2l Transformer digest train
+ * these models end to end; the layer is the "Transformer" study notes'
+ * multi-head attention class, four linear layers stored [out, in]).  By the
+ * chain rule through each step of the forward in reverse:
+ *   out = Ocat W_o^T + b_o    : dOcat = dout W_o, dW_o = dout^T Ocat,
+ *                               db_o = sum over rows of dout
+ *   attention per head        : dQ, dK, dV as sdpa_backward computes them
+ *   Q = x_q W_q^T + b_q, ...  : dx_q = dQ W_q, dW_q = dQ^T x_q, db_q = sum dQ,
+ *                               dx_kv = dK W_k + dV W_v, dW_k = dK^T x_kv, ...
+ *   in_dt : MHA_BF16 only (MHA_F32 is MHA_ENOTSUP).  The gradients are fp32.
+ *   x_q, x_kv, w_q, w_k, w_v, w_o, b_q, b_k, b_v, sizes, valid_lens ([B]),
+ *          causal : the forward's arguments, as for mha_forward (b_o does
+ *          not enter any gradient and is not taken).
+ *   dout : [B, Lq, d_model] bf16, the gradient of the forward's output.
+ *   dx_q : [B, Lq, d_model] fp32, the gradient through the query projection.
+ *   dx_kv : [B, Lk, d_model] fp32, the gradient through the key and value
+ *          projections; or NULL when x_kv == x_q (self-attention, Lq == Lk),
+ *          and then dx_q receives the whole gradient of that input (the sum
+ *          of both paths).
+ *   dw_q, dw_k, dw_v, dw_o : [d_model, d_model] fp32, [out, in] like the
+ *          weights.
+ *   db_q, db_k, db_v, db_o : [d_model] fp32, all four or none (NULL).
+ *   workspace : at least mha_backward_workspace_bytes(...) bytes, 256-byte
+ *          aligned; its contents are scratch.
+ * Outputs are 16-byte aligned (bias gradients 4-byte) and overlap no input,
+ * each other or the workspace.  B * L * d_model must stay below 2^31 / 6 for
+ * L = Lq and L = Lk (the stacked [dQ | dK | dV] operand's bytes index in 31
+ * bits; MHA_ENOTSUP otherwise).
+ * The forward is recomputed, not taken from the caller: one GEMM launch
+ * projects Q, K, V (bf16), the attention forward writes the merged heads
+ * (bf16) and each query's log-sum-exp, a GEMM forms dOcat (bf16), the
+ * attention backward recomputes the weights from the log-sum-exp and writes
+ * dQ, dK, dV (bf16) side by side, one GEMM forms the input gradients (for
+ * self-attention with dx_kv == NULL a single product of [dQ | dK | dV] with
+ * the stacked transposed weights), and one launch pair forms the weight
+ * and bias gradients as split sums over the rows, added in a fixed order.
+ * With B == 0 or Lq == 0 every weight and bias gradient and dx_kv are
+ * written as zeros (empty sums).
+ */
+size_t mha_backward_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h);
+
+mha_status mha_backward(mha_dtype in_dt,
+                        const void* x_q, const void* x_kv,
+                        const void* w_q, const void* b_q,
+                        const void* w_k, const void* b_k,
+                        const void* w_v, const void* b_v,
+                        const void* w_o,
+                        const void* dout,
+                        float* dx_q, float* dx_kv,
+                        float* dw_q, float* db_q,
+                        float* dw_k, float* db_k,
+                        float* dw_v, float* db_v,
+                        float* dw_o, float* db_o,
+                        int B, int Lq, int Lk, int d_model, int h, int d_k,
+                        const int* valid_lens, int causal,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* mha_status_string(mha_status s);

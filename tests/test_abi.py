@@ -339,3 +339,47 @@ def test_sublayer_workspace_and_validation(lib):
     assert sub(lib, D=256, h=8, dk=32) == ENOTSUP
     assert sub(lib, x=ctypes.c_void_p(P + 8)) == EINVAL
     assert sub(lib, mem=ALIGNED[7], Lk=12) == EINVAL   # memory overlaps the workspace
+
+
+def mbwd(lib, **kw):
+    """mha_backward on fake addresses, 1 MiB apart (B2 L10 d_model 256)."""
+    a = dict(in_dt=BF16, xq=ALIGNED[0], xkv=ALIGNED[1], dout=ALIGNED[6], dxq=ALIGNED[7], dxkv=ALIGNED[8],
+             dw=[ALIGNED[9], ALIGNED[10], ALIGNED[11], ALIGNED[12]],
+             db=[ctypes.c_void_p(P + 0xD00000 + 0x1000 * n) for n in range(4)],
+             B=2, Lq=10, Lk=10, D=256, h=4, dk=64, vl=None, causal=0, ws=ALIGNED[15], wsb=None)
+    a.update(kw)
+    need = lib.mha_backward_workspace_bytes(a["in_dt"], a["B"], a["Lq"], a["Lk"], a["D"], a["h"])
+    wsb = need if a["wsb"] is None else a["wsb"]
+    dw, db = a["dw"], a["db"]
+    return lib.mha_backward(a["in_dt"], a["xq"], a["xkv"], ALIGNED[2], None, ALIGNED[3], None, ALIGNED[4], None,
+                            ALIGNED[5], a["dout"], a["dxq"], a["dxkv"], dw[0], db[0], dw[1], db[1], dw[2], db[2],
+                            dw[3], db[3], a["B"], a["Lq"], a["Lk"], a["D"], a["h"], a["dk"], a["vl"], a["causal"],
+                            a["ws"], wsb, None)
+
+
+def test_mha_backward_workspace_and_validation(lib):
+    ws = lib.mha_backward_workspace_bytes
+    assert ws(F32, 2, 10, 10, 256, 4) == 0                 # bf16 only
+    assert ws(BF16, 2, 10, 10, 250, 5) == 0                # d_model % 64
+    assert ws(BF16, 1, 1 << 20, 8, 512, 8) == 0            # stacked gradients past 31-bit byte offsets
+    small, big = ws(BF16, 2, 10, 10, 256, 4), ws(BF16, 2, 20, 10, 256, 4)
+    assert 0 < small < big and small % 256 == 0
+    # Q, K, V, merged heads and their gradient, dQ|dK|dV (bf16), the four transposed weights
+    assert small >= 2 * 10 * 256 * 2 * 8 + 4 * 256 * 256 * 2
+    assert mbwd(lib, in_dt=F32) == ENOTSUP
+    assert mbwd(lib, in_dt=7) == EINVAL
+    assert mbwd(lib, D=512, h=16, dk=32) == ENOTSUP
+    assert mbwd(lib, dk=32) == EINVAL                      # d_model != h * d_k
+    assert mbwd(lib, causal=1, Lk=12) == EINVAL
+    assert mbwd(lib, Lk=0) == EINVAL
+    assert mbwd(lib, dxkv=None) == EINVAL                  # the fused input gradient needs x_kv == x_q
+    assert mbwd(lib, db=[ALIGNED[13], None, None, None]) == EINVAL   # all four bias gradients or none
+    assert mbwd(lib, dw=[ALIGNED[9], ALIGNED[9], ALIGNED[11], ALIGNED[12]]) == EINVAL   # dw_k overlaps dw_q
+    assert mbwd(lib, dw=[ALIGNED[9], ALIGNED[10], ALIGNED[11], ctypes.c_void_p(P + 0xC00000 + 4)]) == EINVAL
+    assert mbwd(lib, dw=[ALIGNED[9], ALIGNED[10], ALIGNED[11], None]) == EINVAL
+    assert mbwd(lib, dxq=ALIGNED[0]) == EINVAL             # dx_q overlaps x_q
+    assert mbwd(lib, dxq=None) == EINVAL
+    assert mbwd(lib, ws=ALIGNED[6]) == EINVAL              # workspace overlaps dout
+    assert mbwd(lib, ws=None) == EINVAL
+    assert mbwd(lib, wsb=100) == EWORK
+    assert mbwd(lib, B=1, Lq=1 << 20, Lk=8, D=512, h=8) == ENOTSUP

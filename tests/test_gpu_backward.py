@@ -115,6 +115,22 @@ def test_backward_bf16_outputs_and_strided_views():
         assert_bf16(to_host(got), ref, "bf16 gradients")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_backward_no_queries_zeroes_key_gradients(dt):
+    """No query rows: dk and dv are empty sums, written as zeros over
+    whatever the buffers held."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    B, h, Lk = 2, 3, 50
+    q = torch.empty((B, h, 0, 64), dtype=tdt, device="cuda")
+    k, v = (torch.randn((B, h, Lk, 64), device="cuda").to(tdt) for _ in range(2))
+    gq, gk, gv = mha.sdpa_backward(q, k, v, q, q, valid_lens=[50, 7])
+    torch.cuda.synchronize()
+    assert gq.numel() == 0
+    assert torch.all(gk == 0).item() and torch.all(gv == 0).item()
+
+
 def test_backward_full_size_sampled_heads():
     """The causal backward workload at full size (B=4 h=8 L=1024, bf16 in,
     fp32 gradients) as the benchmark launches it; two (batch, head) slices,

@@ -20,6 +20,11 @@ there is no CPU or PyTorch fallback, and a missing library raises.
     sdpa_backward(q, k, v, o, dout, valid_lens=None, causal=False, lse=None)
         -> dq, dk, dv (gradients of sdpa_forward for the output gradient dout;
         with the forward's lse the weights are recomputed from it)
+    mha_backward(x_q, x_kv, w_q, w_k, w_v, w_o, dout, b_q=None, ..., h=8,
+                 valid_lens=None, causal=False) -> dict of fp32 gradients
+        dx_q, dx_kv (None for self-attention: x_kv is x_q, dx_q holds the
+        whole input gradient), dw_q, dw_k, dw_v, dw_o, db_q, ..., db_o
+        (bf16 inputs; the bias gradients when b_q is given)
     sdpa_decode(q, k_cache, v_cache, lens)
         one decoding step: q [B,h,64] against caches [B,h,L,64]
     sdpa_decode_noalloc(q, k_cache, v_cache, lens, out=None)
@@ -35,7 +40,7 @@ import ctypes
 from . import _lib
 from ._lib import MhaError, MHA_BF16, MHA_F32, MHA_OK, Strides
 
-__all__ = ["sdpa_forward", "sdpa_backward", "sdpa_decode", "sdpa_decode_noalloc", "mha_forward", "mha_sublayer_forward", "workspace_bytes", "kernel_timing", "MhaError", "library"]
+__all__ = ["sdpa_forward", "sdpa_backward", "sdpa_decode", "sdpa_decode_noalloc", "mha_forward", "mha_sublayer_forward", "mha_backward", "workspace_bytes", "kernel_timing", "MhaError", "library"]
 
 
 def library():
@@ -303,6 +308,46 @@ def mha_sublayer_forward(x, w_q, w_k, w_v, w_o, b_q=None, b_k=None, b_v=None, b_
                                   _ptr(vl), int(bool(causal)), _ptr(workspace), workspace.numel(), _stream())
     _raise(st, "mha_sublayer_forward")
     return out
+
+
+def mha_backward(x_q, x_kv, w_q, w_k, w_v, w_o, dout, b_q=None, b_k=None, b_v=None, h=8, valid_lens=None,
+                 causal=False, bias_grads=None, workspace=None):
+    """Gradients of mha_forward (bf16) for the output gradient ``dout``
+    [B, Lq, d_model]: a dict of fp32 tensors dx_q, dx_kv, dw_q, dw_k, dw_v,
+    dw_o and, with ``bias_grads`` (default: when b_q is given), db_q, db_k,
+    db_v, db_o.  When x_kv is x_q (self-attention) dx_kv is None and dx_q is
+    the input's whole gradient."""
+    torch = _torch()
+    args = dict(x_q=x_q, x_kv=x_kv, w_q=w_q, w_k=w_k, w_v=w_v, w_o=w_o, dout=dout, b_q=b_q, b_k=b_k, b_v=b_v)
+    for n, t in args.items():
+        _check_gpu(n, t)
+        if t is not None and (not t.is_contiguous() or t.dtype != x_q.dtype):
+            raise ValueError(f"{n} must be contiguous and share x_q's dtype")
+    B, Lq, D = x_q.shape
+    Lk = x_kv.shape[1]
+    dev = x_q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    self_attn = x_kv is x_q or (x_kv.data_ptr() == x_q.data_ptr() and x_kv.shape == x_q.shape)
+    bias_grads = (b_q is not None) if bias_grads is None else bool(bias_grads)
+    r = {"dx_q": torch.empty((B, Lq, D), **f32),
+         "dx_kv": None if self_attn else torch.empty((B, Lk, D), **f32)}
+    for n in "qkvo":
+        r["dw_" + n] = torch.empty((D, D), **f32)
+        r["db_" + n] = torch.empty((D,), **f32) if bias_grads else None
+    lib = _lib.load()
+    in_dt = _dtype_code(x_q.dtype)
+    need = int(lib.mha_backward_workspace_bytes(in_dt, B, Lq, Lk, D, h))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    vl = _valid_lens(valid_lens, B, dev)
+    st = lib.mha_backward(in_dt, _ptr(x_q), _ptr(x_kv), _ptr(w_q), _ptr(b_q), _ptr(w_k), _ptr(b_k), _ptr(w_v),
+                          _ptr(b_v), _ptr(w_o), _ptr(dout), _ptr(r["dx_q"]), _ptr(r["dx_kv"]),
+                          _ptr(r["dw_q"]), _ptr(r["db_q"]), _ptr(r["dw_k"]), _ptr(r["db_k"]),
+                          _ptr(r["dw_v"]), _ptr(r["db_v"]), _ptr(r["dw_o"]), _ptr(r["db_o"]),
+                          B, Lq, Lk, D, h, D // h if h else 0, _ptr(vl), int(bool(causal)),
+                          _ptr(workspace), workspace.numel(), _stream())
+    _raise(st, "mha_backward")
+    return r
 
 
 class kernel_timing:

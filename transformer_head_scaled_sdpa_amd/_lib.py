@@ -22,7 +22,8 @@ EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_ex", "sdpa_backwar
             "sdpa_backward_lse",
             "sdpa_decode_workspace_bytes", "sdpa_decode", "sdpa_decode_noalloc", "mha_workspace_bytes",
             "mha_workspace_bytes_ex", "mha_forward", "mha_forward_ex", "mha_sublayer_workspace_bytes",
-            "mha_sublayer_forward", "mha_status_string", "mha_timing_enable",
+            "mha_sublayer_forward", "mha_backward_workspace_bytes", "mha_backward", "mha_status_string",
+            "mha_timing_enable",
             "mha_timing_read")
 
 
@@ -77,6 +78,10 @@ def load():
     lib.mha_forward.restype = i
     lib.mha_forward.argtypes = [i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 i, i, i, i, i, i, vp, i, vp, sz, vp]
+    lib.mha_backward_workspace_bytes.restype = sz
+    lib.mha_backward_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.mha_backward.restype = i
+    lib.mha_backward.argtypes = [i] + [vp] * 20 + [i] * 6 + [vp, i, vp, sz, vp]
     lib.mha_workspace_bytes_ex.restype = sz
     lib.mha_workspace_bytes_ex.argtypes = [i, i, i, i, i, i]
     lib.mha_forward_ex.restype = i

@@ -14,7 +14,8 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmha.so")
 SOURCES = ["api.hip", "sdpa_bf16_pipe.hip", "mha_fused.hip", "mha_fused_small.hip", "sdpa_decode.hip",
            "sdpa_weights.hip", "sdpa_weights_mfma.hip", "sdpa_backward.hip", "sdpa_backward_mfma.hip",
-           "layer_norm.hip", "sdpa_f32.hip", "gemm.hip"]
+           "layer_norm.hip", "sdpa_f32.hip", "gemm.hip", "gemm_tn.hip",
+           "zero.hip"]
 
 # Packed fp32 VALU ops are disabled for every HIP translation unit.
 # -fno-honor-nans: inputs are finite, so max/min need not quiet signalling

@@ -130,20 +130,33 @@ mha_status backward_impl(mha_dtype in_dt, mha_dtype out_dt,
     if (causal && Lq != Lk) return MHA_EINVAL;
     if (d_k != kHeadDim || d_v != kHeadDim) return MHA_ENOTSUP;
     if (in_dt == MHA_F32 && out_dt != MHA_F32) return MHA_ENOTSUP;
-    if (B == 0 || Lq == 0) return MHA_OK;
+    if (B == 0) return MHA_OK;
+    const long long mult = in_dt == MHA_F32 ? 4 : 8, omult = out_dt == MHA_F32 ? 4 : 8;
+    const size_t ie = elem_size(in_dt), oe = elem_size(out_dt);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (Lq == 0) {
+        // No query rows: dk and dv are sums over nothing, written as zeros.
+        if (!dk || !dv || !aligned16(dk) || !aligned16(dv)) return MHA_EINVAL;
+        for (const mha_strides& st : {sdk, sdv})
+            if (st.b < 0 || st.h < 0 || st.l < 0 || st.b % omult || st.h % omult || st.l % omult) return MHA_EINVAL;
+        const Range rk = view_range(dk, sdk, B, h, Lk, d_k, oe), rv = view_range(dv, sdv, B, h, Lk, d_v, oe);
+        if (overlap(rk, rv)) return MHA_EINVAL;
+        const long long zk[3] = {sdk.b, sdk.h, sdk.l}, zv[3] = {sdv.b, sdv.h, sdv.l};
+        hipError_t e = mha::launch_zero_view(dk, zk, B, h, Lk, (int)oe, s);
+        if (e == hipSuccess) e = mha::launch_zero_view(dv, zv, B, h, Lk, (int)oe, s);
+        return hip_status(e);
+    }
     const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv, workspace};
     for (const void* p : ptrs)
         if (!p || !aligned16(p)) return MHA_EINVAL;
     const size_t need = sdpa_backward_workspace_bytes(B, h, Lq);
     if (workspace_bytes < need) return MHA_EWORKSPACE;
-    const long long mult = in_dt == MHA_F32 ? 4 : 8, omult = out_dt == MHA_F32 ? 4 : 8;
     const mha_strides in_s[5] = {sq, sk, sv, so, sdo};
     for (const mha_strides& st : in_s)
         if (st.b < 0 || st.h < 0 || st.l < 0 || st.b % mult || st.h % mult || st.l % mult) return MHA_EINVAL;
     const mha_strides out_s[3] = {sdq, sdk, sdv};
     for (const mha_strides& st : out_s)
         if (st.b < 0 || st.h < 0 || st.l < 0 || st.b % omult || st.h % omult || st.l % omult) return MHA_EINVAL;
-    const size_t ie = elem_size(in_dt), oe = elem_size(out_dt);
     if (in_dt == MHA_BF16 && (!rows_fit_buffer(sq.l, Lq, ie) || !rows_fit_buffer(sdo.l, Lq, ie) ||
                               !rows_fit_buffer(so.l, Lq, ie) || !rows_fit_buffer(sk.l, Lk, ie) ||
                               !rows_fit_buffer(sv.l, Lk, ie) || !tile_rows_fit(sq.l, ie) ||
@@ -189,7 +202,6 @@ mha_status backward_impl(mha_dtype in_dt, mha_dtype out_dt,
     a.out_f32 = out_dt == MHA_F32;
     a.rows = static_cast<float*>(workspace);
     a.lse_in = in_dt == MHA_BF16 ? lse : nullptr;   // the fp32 kernels form their own statistics
-    hipStream_t s = static_cast<hipStream_t>(stream);
     return hip_status(timed("sdpa_backward", s, [&] { return mha::launch_sdpa_backward(a, s); }));
 }
 
@@ -738,6 +750,282 @@ mha_status mha_forward_ex(mha_dtype in_dt, mha_dtype out_dt,
                           void* workspace, size_t workspace_bytes, void* stream) {
     return mha_impl(in_dt, out_dt, x_q, x_kv, w_q, b_q, w_k, b_k, w_v, b_v, w_o, b_o, out, B, Lq, Lk, d_model, h,
                     d_k, valid_lens, vl_rank, causal, p_attn, sp, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of mha_backward, byte offsets (each 256-byte aligned): Q, K, V,
+// the merged heads and their gradient (bf16), the log-sum-exp and the
+// attention backward's row statistics (fp32), dQ, dK, dV (bf16: one [M, 3D]
+// block for the fused input gradient of self-attention, or dQ [Mq, D] then
+// [dK | dV] [Mk, 2D]), the transposed weights (bf16: W_o^T, then W_q^T,
+// W_k^T, W_v^T side by side or apart) and the weight-gradient partials.
+struct BwdLayout {
+    size_t q, k, v, ocat, docat, lse, rows, dqkv, dkv, wt, tn, total;
+};
+
+BwdLayout bwd_layout(int B, int Lq, int Lk, int D, int h) {
+    BwdLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        const size_t o = off;
+        off = round_up(off + n, 256);
+        return o;
+    };
+    const size_t mq = (size_t)B * Lq * D * 2, mk = (size_t)B * Lk * D * 2;
+    L.q = take(mq);
+    L.k = take(mk);
+    L.v = take(mk);
+    L.ocat = take(mq);
+    L.docat = take(mq);
+    L.lse = take((size_t)B * h * Lq * 4);
+    L.rows = take(mha::backward_workspace_bytes(B, h, Lq));
+    L.dqkv = take(round_up(mq, 256) + 2 * mk);
+    L.dkv = L.dqkv + round_up(mq, 256);
+    L.wt = take((size_t)4 * D * D * 2);
+    const int M[3] = {B * Lq, B * Lq, B * Lk}, N1[3] = {D, D, 2 * D}, N2[3] = {D, D, D};
+    L.tn = take(mha::gemm_tn_workspace_bytes(M, N1, N2, 3));
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mha_backward_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h) {
+    if (in_dt != MHA_BF16 || B < 0 || Lq < 0 || Lk < 0 || d_model <= 0 || h <= 0 || d_model % h) return 0;
+    if (d_model % 64 || !mha_rows_fit(B, Lq, 6 * d_model) || !mha_rows_fit(B, Lk, 6 * d_model)) return 0;
+    return bwd_layout(B, Lq, Lk, d_model, h).total;
+}
+
+mha_status mha_backward(mha_dtype in_dt,
+                        const void* x_q, const void* x_kv,
+                        const void* w_q, const void* b_q,
+                        const void* w_k, const void* b_k,
+                        const void* w_v, const void* b_v,
+                        const void* w_o,
+                        const void* dout,
+                        float* dx_q, float* dx_kv,
+                        float* dw_q, float* db_q,
+                        float* dw_k, float* db_k,
+                        float* dw_v, float* db_v,
+                        float* dw_o, float* db_o,
+                        int B, int Lq, int Lk, int d_model, int h, int d_k,
+                        const int* valid_lens, int causal,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(in_dt)) return MHA_EINVAL;
+    if (B < 0 || Lq < 0 || Lk <= 0 || d_model <= 0 || h <= 0 || d_k <= 0) return MHA_EINVAL;
+    if ((long long)h * d_k != d_model) return MHA_EINVAL;
+    if (causal && Lq != Lk) return MHA_EINVAL;
+    if (d_k != kHeadDim || in_dt != MHA_BF16) return MHA_ENOTSUP;
+    const int D = d_model;
+    const bool any_db = db_q || db_k || db_v || db_o, all_db = db_q && db_k && db_v && db_o;
+    if (any_db && !all_db) return MHA_EINVAL;
+    if (!dw_q || !dw_k || !dw_v || !dw_o) return MHA_EINVAL;
+    // dx_kv == NULL: self-attention, dx_q takes both paths.
+    const bool fused_dx = dx_kv == nullptr;
+    if (fused_dx && (x_kv != x_q || Lq != Lk)) return MHA_EINVAL;
+    if (!mha_rows_fit(B, Lq, 6 * D) || !mha_rows_fit(B, Lk, 6 * D)) return MHA_ENOTSUP;
+
+    // Output ranges (fp32).
+    const size_t dd = (size_t)D * D * 4;
+    auto rng = [](const void* p, size_t n) {
+        const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+        return Range{b, b + n};
+    };
+    Range outs[10];
+    int n_out = 0;
+    for (float* p : {dw_q, dw_k, dw_v, dw_o}) {
+        if (!aligned16(p)) return MHA_EINVAL;
+        outs[n_out++] = rng(p, dd);
+    }
+    if (all_db)
+        for (float* p : {db_q, db_k, db_v, db_o}) {
+            if (reinterpret_cast<uintptr_t>(p) & 3u) return MHA_EINVAL;
+            outs[n_out++] = rng(p, (size_t)D * 4);
+        }
+    if (dx_kv) {
+        if (!aligned16(dx_kv)) return MHA_EINVAL;
+        outs[n_out++] = rng(dx_kv, (size_t)B * Lk * D * 4);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool empty = B == 0 || Lq == 0;
+    if (!empty) {
+        if (!dx_q || !aligned16(dx_q)) return MHA_EINVAL;
+        outs[n_out++] = rng(dx_q, (size_t)B * Lq * D * 4);
+    }
+    for (int x = 0; x < n_out; ++x)
+        for (int y = x + 1; y < n_out; ++y)
+            if (overlap(outs[x], outs[y])) return MHA_EINVAL;
+    if (empty) {
+        // Every gradient is a sum over no query rows.
+        hipError_t e = hipSuccess;
+        for (float* p : {dw_q, dw_k, dw_v, dw_o})
+            if (e == hipSuccess) e = mha::launch_zero_f32(p, (long long)D * D, s);
+        if (all_db)
+            for (float* p : {db_q, db_k, db_v, db_o})
+                if (e == hipSuccess) e = mha::launch_zero_f32(p, D, s);
+        if (dx_kv && e == hipSuccess) e = mha::launch_zero_f32(dx_kv, (long long)B * Lk * D, s);
+        return hip_status(e);
+    }
+
+    const void* ptrs[] = {x_q, x_kv, w_q, w_k, w_v, w_o, dout, workspace, b_q, b_k, b_v};
+    for (int x = 0; x < 11; ++x) {
+        if (!ptrs[x] && x < 8) return MHA_EINVAL;
+        if (ptrs[x] && !aligned16(ptrs[x])) return MHA_EINVAL;
+    }
+    const BwdLayout L = bwd_layout(B, Lq, Lk, D, h);
+    if (workspace_bytes < L.total) return MHA_EWORKSPACE;
+    const size_t dw2 = (size_t)D * D * 2;
+    const Range ins[] = {rng(x_q, (size_t)B * Lq * D * 2), rng(x_kv, (size_t)B * Lk * D * 2), rng(w_q, dw2),
+                         rng(w_k, dw2), rng(w_v, dw2), rng(w_o, dw2), rng(dout, (size_t)B * Lq * D * 2),
+                         rng(b_q, b_q ? (size_t)D * 2 : 0), rng(b_k, b_k ? (size_t)D * 2 : 0),
+                         rng(b_v, b_v ? (size_t)D * 2 : 0)};
+    const Range rws = rng(workspace, L.total);
+    for (int x = 0; x < n_out; ++x) {
+        if (overlap(outs[x], rws)) return MHA_EINVAL;
+        for (const Range& r : ins)
+            if (overlap(outs[x], r)) return MHA_EINVAL;
+    }
+    for (const Range& r : ins)
+        if (overlap(rws, r)) return MHA_EINVAL;
+
+    using mha::bf16_t;
+    char* w = static_cast<char*>(workspace);
+    bf16_t* Q = reinterpret_cast<bf16_t*>(w + L.q);
+    bf16_t* K = reinterpret_cast<bf16_t*>(w + L.k);
+    bf16_t* V = reinterpret_cast<bf16_t*>(w + L.v);
+    bf16_t* Ocat = reinterpret_cast<bf16_t*>(w + L.ocat);
+    bf16_t* dOcat = reinterpret_cast<bf16_t*>(w + L.docat);
+    float* lse = reinterpret_cast<float*>(w + L.lse);
+    bf16_t* dQ = reinterpret_cast<bf16_t*>(w + L.dqkv);
+    // [dK | dV]: right of dQ in the [M, 3D] block, or its own [Mk, 2D] block.
+    bf16_t* dKV = fused_dx ? dQ + D : reinterpret_cast<bf16_t*>(w + L.dkv);
+    const long long ld_q = fused_dx ? 3 * D : D, ld_kv = fused_dx ? 3 * D : 2 * D;
+    bf16_t* WoT = reinterpret_cast<bf16_t*>(w + L.wt);
+    bf16_t* WqT = WoT + (size_t)D * D;              // [D, 3D] (fused) or [D, D]
+    bf16_t* WkvT = WoT + (size_t)2 * D * D;         // [D, 2D] (apart)
+    const uint16_t* xq16 = static_cast<const uint16_t*>(x_q);
+    const uint16_t* xkv16 = static_cast<const uint16_t*>(x_kv);
+    hipError_t e;
+
+    // 1. Transposed weights: dOcat = dout W_o and dx = dQ W_q + ... are
+    // products with W (not W^T), which the GEMM takes as [N, K] = W^T.
+    mha::TransposeArgs t;
+    t.n = D;
+    t.count = 4;
+    t.w[0] = static_cast<const uint16_t*>(w_o); t.dst[0] = WoT; t.col0[0] = 0; t.ld[0] = D;
+    t.w[1] = static_cast<const uint16_t*>(w_q);
+    t.w[2] = static_cast<const uint16_t*>(w_k);
+    t.w[3] = static_cast<const uint16_t*>(w_v);
+    if (fused_dx) {
+        for (int x = 1; x < 4; ++x) { t.dst[x] = WqT; t.col0[x] = (x - 1) * D; t.ld[x] = 3 * D; }
+    } else {
+        t.dst[1] = WqT; t.col0[1] = 0; t.ld[1] = D;
+        t.dst[2] = WkvT; t.col0[2] = 0; t.ld[2] = 2 * D;
+        t.dst[3] = WkvT; t.col0[3] = D; t.ld[3] = 2 * D;
+    }
+    e = timed("bwd_transpose_w", s, [&] { return mha::launch_transpose_bf16(t, s); });
+    if (e != hipSuccess) return MHA_EHIP;
+
+    // 2. The forward's Q, K, V (bf16) in one launch.
+    mha::GemmArgs g;
+    g.nprob = 3;
+    g.N = D;
+    g.K = D;
+    g.p[0] = {x_q, w_q, b_q, Q, B * Lq};
+    g.p[1] = {x_kv, w_k, b_k, K, B * Lk};
+    g.p[2] = {x_kv, w_v, b_v, V, B * Lk};
+    e = timed("bwd_qkv_proj", s, [&] { return mha::launch_gemm_bf16(g, false, s); });
+    if (e != hipSuccess) return MHA_EHIP;
+
+    // 3. Attention forward on the head views: merged heads and log-sum-exp.
+    mha::SdpaArgs a;
+    a.q = Q; a.k = K; a.v = V; a.o = Ocat;
+    a.sq[0] = (long long)Lq * D; a.sq[1] = kHeadDim; a.sq[2] = D;
+    a.sk[0] = (long long)Lk * D; a.sk[1] = kHeadDim; a.sk[2] = D;
+    a.sv[0] = (long long)Lk * D; a.sv[1] = kHeadDim; a.sv[2] = D;
+    a.so[0] = (long long)Lq * D; a.so[1] = kHeadDim; a.so[2] = D;
+    a.B = B; a.H = h; a.Lq = Lq; a.Lk = Lk;
+    a.valid_lens = valid_lens;
+    a.causal = causal ? 1 : 0;
+    a.lse = lse;
+    e = timed("bwd_attn_forward", s, [&] { return mha::launch_sdpa_bf16(a, false, s); });
+    if (e != hipSuccess) return MHA_EHIP;
+
+    // 4. dOcat = dout W_o (bf16).
+    mha::GemmArgs go;
+    go.nprob = 1;
+    go.N = D;
+    go.K = D;
+    go.p[0] = {dout, WoT, nullptr, dOcat, B * Lq};
+    e = timed("bwd_out_proj", s, [&] { return mha::launch_gemm_bf16(go, false, s); });
+    if (e != hipSuccess) return MHA_EHIP;
+
+    // 5. Attention backward: dQ, dK, dV (bf16) beside each other.
+    mha::BackwardArgs ba;
+    ba.q = Q; ba.k = K; ba.v = V; ba.o = Ocat; ba.dout = dOcat;
+    ba.dq = dQ; ba.dk = dKV; ba.dv = dKV + D;
+    const long long lq_rows[3] = {(long long)Lq * D, kHeadDim, D}, lk_rows[3] = {(long long)Lk * D, kHeadDim, D};
+    for (int x = 0; x < 3; ++x) {
+        ba.sq[x] = lq_rows[x]; ba.so[x] = lq_rows[x]; ba.sdo[x] = lq_rows[x];
+        ba.sk[x] = lk_rows[x]; ba.sv[x] = lk_rows[x];
+    }
+    ba.sdq[0] = (long long)Lq * ld_q; ba.sdq[1] = kHeadDim; ba.sdq[2] = ld_q;
+    ba.sdk[0] = (long long)Lk * ld_kv; ba.sdk[1] = kHeadDim; ba.sdk[2] = ld_kv;
+    for (int x = 0; x < 3; ++x) ba.sdv[x] = ba.sdk[x];
+    ba.B = B; ba.H = h; ba.Lq = Lq; ba.Lk = Lk;
+    ba.valid_lens = valid_lens;
+    ba.vl_rank = valid_lens ? 1 : 0;
+    ba.causal = causal ? 1 : 0;
+    ba.in_f32 = false;
+    ba.out_f32 = false;
+    ba.rows = reinterpret_cast<float*>(w + L.rows);
+    ba.lse_in = lse;
+    e = timed("bwd_attn", s, [&] { return mha::launch_sdpa_backward(ba, s); });
+    if (e != hipSuccess) return MHA_EHIP;
+
+    // 6. Input gradients (fp32).
+    mha::GemmArgs gx;
+    gx.nprob = 1;
+    gx.N = D;
+    if (fused_dx) {
+        gx.K = 3 * D;
+        gx.p[0] = {dQ, WqT, nullptr, dx_q, B * Lq};
+        e = timed("bwd_dx", s, [&] { return mha::launch_gemm_bf16(gx, true, s); });
+    } else {
+        gx.K = D;
+        gx.p[0] = {dQ, WqT, nullptr, dx_q, B * Lq};
+        e = timed("bwd_dx_q", s, [&] { return mha::launch_gemm_bf16(gx, true, s); });
+        if (e != hipSuccess) return MHA_EHIP;
+        gx.K = 2 * D;
+        gx.p[0] = {dKV, WkvT, nullptr, dx_kv, B * Lk};
+        e = timed("bwd_dx_kv", s, [&] { return mha::launch_gemm_bf16(gx, true, s); });
+    }
+    if (e != hipSuccess) return MHA_EHIP;
+
+    // 7. Weight and bias gradients: dW_o = dout^T Ocat, dW_q = dQ^T x_q and
+    // [dW_k; dW_v] = [dK | dV]^T x_kv, one launch pair.
+    mha::TnArgs tn;
+    tn.nprob = 3;
+    tn.p[0].y = static_cast<const uint16_t*>(dout); tn.p[0].ldy = D;
+    tn.p[0].x = Ocat; tn.p[0].ldx = D;
+    tn.p[0].M = B * Lq; tn.p[0].N1 = D; tn.p[0].N2 = D;
+    tn.p[0].dw = dw_o; tn.p[0].db = db_o;
+    tn.p[1].y = dQ; tn.p[1].ldy = ld_q;
+    tn.p[1].x = xq16; tn.p[1].ldx = D;
+    tn.p[1].M = B * Lq; tn.p[1].N1 = D; tn.p[1].N2 = D;
+    tn.p[1].dw = dw_q; tn.p[1].db = db_q;
+    tn.p[2].y = dKV; tn.p[2].ldy = ld_kv;
+    tn.p[2].x = xkv16; tn.p[2].ldx = D;
+    tn.p[2].M = B * Lk; tn.p[2].N1 = 2 * D; tn.p[2].N2 = D;
+    tn.p[2].dw = dw_k; tn.p[2].db = db_k;
+    tn.p[2].dw2 = dw_v; tn.p[2].db2 = db_v;
+    e = timed("bwd_dw", s, [&] { return mha::launch_gemm_tn(tn, w + L.tn, s); });
+    return hip_status(e);
 }
 
 size_t mha_sublayer_workspace_bytes(mha_dtype in_dt, int B, int L, int Lk, int d_model, int h) {

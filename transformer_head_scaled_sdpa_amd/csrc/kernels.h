@@ -148,4 +148,45 @@ hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 hipError_t launch_layer_norm(const void* x, const void* gain, const void* bias, void* y, int M, int D, int kind,
                              float eps, bool f32, hipStream_t s);
 
+// Weight and bias gradients of linear layers, dW = dy^T x and db = the column
+// sums of dy (bf16 in, fp32 out), for up to three problems in one launch
+// pair (slice partials, then their sum in a fixed order).
+struct TnProblem {
+    const uint16_t* y;          // dy [M, N1] bf16, row stride ldy (elements)
+    const uint16_t* x;          // x [M, N2] bf16, row stride ldx
+    long long ldy, ldx;
+    int M, N1, N2;              // N1, N2 multiples of 64
+    float* dw;                  // [N1, N2] fp32, contiguous
+    float* db;                  // [N1] fp32, or nullptr
+    float* dw2 = nullptr;       // when set, rows N1/2 .. of dW (and db) go to dw2 (db2): two stacked layers
+    float* db2 = nullptr;
+    // Set by launch_gemm_tn.
+    int slices = 0, rows_per_slice = 0, tiles1 = 0, tiles2 = 0, blocks = 0, reduce_blocks = 0;
+    float* w_part = nullptr;
+    float* db_part = nullptr;
+};
+struct TnArgs {
+    TnProblem p[3];
+    int nprob;
+};
+int gemm_tn_slices(int M, int N1, int N2);
+size_t gemm_tn_workspace_bytes(const int* M, const int* N1, const int* N2, int nprob);
+hipError_t launch_gemm_tn(TnArgs g, void* workspace, hipStream_t s);
+// Transposes of square bf16 weights: dst[q] = w[q]^T, [n, n] each, written
+// at column offset col0[q] of a row-major destination with row stride ld.
+struct TransposeArgs {
+    const uint16_t* w[4];
+    uint16_t* dst[4];
+    int col0[4];
+    long long ld[4];
+    int n, count;
+};
+hipError_t launch_transpose_bf16(const TransposeArgs& a, hipStream_t s);
+
+// Zeros written into a [B, H, L, 64] view (element strides {batch, head,
+// position}, 16-byte aligned rows) of 2- or 4-byte elements, and into n
+// contiguous floats.
+hipError_t launch_zero_view(void* p, const long long s[3], int B, int H, int L, int elem, hipStream_t st);
+hipError_t launch_zero_f32(float* p, long long n, hipStream_t st);
+
 }  // namespace mha
