@@ -404,27 +404,33 @@ int oracle_sdpa_backward_f64(const double* q, const double* k, const double* v, 
 static void linear_backward(const double* dy, const double* x, const double* w,
                             double* dx, double* dw, double* db, long M, int Din, int Dout, int accumulate)
 {
+    /* Each sum runs over its index in ascending order; the loops visit the
+     * operands row by row (the per-element order of additions is that of
+     * the formulas above). */
     long m;
 #pragma omp parallel for schedule(static)
-    for (m = 0; m < M; ++m)
-        for (int c = 0; c < Din; ++c) {
-            double acc = 0.0;
-            for (int n = 0; n < Dout; ++n) acc += dy[m * Dout + n] * w[(long)n * Din + c];
-            dx[m * Din + c] = (accumulate ? dx[m * Din + c] : 0.0) + acc;
+    for (m = 0; m < M; ++m) {
+        double* row = dx + m * Din;
+        double acc[Din];
+        for (int c = 0; c < Din; ++c) acc[c] = 0.0;
+        for (int n = 0; n < Dout; ++n) {
+            const double a = dy[m * Dout + n];
+            for (int c = 0; c < Din; ++c) acc[c] += a * w[(long)n * Din + c];
         }
+        for (int c = 0; c < Din; ++c) row[c] = (accumulate ? row[c] : 0.0) + acc[c];
+    }
     int n;
 #pragma omp parallel for schedule(static)
     for (n = 0; n < Dout; ++n) {
-        for (int c = 0; c < Din; ++c) {
-            double acc = 0.0;
-            for (long r = 0; r < M; ++r) acc += dy[r * Dout + n] * x[r * Din + c];
-            dw[(long)n * Din + c] = acc;
+        double* wrow = dw + (long)n * Din;
+        for (int c = 0; c < Din; ++c) wrow[c] = 0.0;
+        double bsum = 0.0;
+        for (long r = 0; r < M; ++r) {
+            const double a = dy[r * Dout + n];
+            for (int c = 0; c < Din; ++c) wrow[c] += a * x[r * Din + c];
+            bsum += a;
         }
-        if (db) {
-            double acc = 0.0;
-            for (long r = 0; r < M; ++r) acc += dy[r * Dout + n];
-            db[n] = acc;
-        }
+        if (db) db[n] = bsum;
     }
 }
 
@@ -494,10 +500,9 @@ int oracle_mha_backward_f64(const double* xq, const double* xkv,
     double* dQ = (double*)malloc(sizeof(double) * (size_t)(Mq * D + 1));
     double* dK = (double*)malloc(sizeof(double) * (size_t)(Mk * D + 1));
     double* dV = (double*)malloc(sizeof(double) * (size_t)(Mk * D + 1));
-    double* s = (double*)malloc(sizeof(double) * (size_t)Lk + 1);
     int rc = 0;
     if (!Qf || !Kf || !Vf || !qh || !kh || !vh || !oh || !ocat || !docat || !doh || !dqh || !dkh || !dvh ||
-        !dQ || !dK || !dV || !s) { rc = -1; goto done; }
+        !dQ || !dK || !dV) { rc = -1; goto done; }
 
     /* The forward, keeping what the backward reads. */
     oracle_linear_f64(xq, w_q, b_q, Qf, Mq, D, D);
@@ -511,10 +516,20 @@ int oracle_mha_backward_f64(const double* xq, const double* xkv,
     head_permute(Qf, qh, B, Lq, h, dk, 1);
     head_permute(Kf, kh, B, Lk, h, dk, 1);
     head_permute(Vf, vh, B, Lk, h, dk, 1);
-    for (long bh = 0; bh < (long)B * h; ++bh)
-        for (int i = 0; i < Lq; ++i)
-            attend_row(qh + (bh * Lq + i) * dk, kh + bh * Lk * dk, vh + bh * Lk * dk, oh + (bh * Lq + i) * dk,
-                       NULL, s, Lq, Lk, dk, dk, valid_lens, vl_per_query, causal, (int)(bh / h), i);
+    {
+        long bh;
+        int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+        for (bh = 0; bh < (long)B * h; ++bh) {
+            double* srow = (double*)malloc(sizeof(double) * (size_t)Lk);
+            if (!srow) { bad = 1; continue; }
+            for (int i = 0; i < Lq; ++i)
+                attend_row(qh + (bh * Lq + i) * dk, kh + bh * Lk * dk, vh + bh * Lk * dk, oh + (bh * Lq + i) * dk,
+                           NULL, srow, Lq, Lk, dk, dk, valid_lens, vl_per_query, causal, (int)(bh / h), i);
+            free(srow);
+        }
+        if (bad) { rc = -1; goto done; }
+    }
     head_permute(ocat, oh, B, Lq, h, dk, 0);
     if (bf16_stages) round_all(ocat, Mq * D);
 
@@ -542,7 +557,7 @@ int oracle_mha_backward_f64(const double* xq, const double* xkv,
 
 done:
     free(Qf); free(Kf); free(Vf); free(qh); free(kh); free(vh); free(oh); free(ocat);
-    free(docat); free(doh); free(dqh); free(dkh); free(dvh); free(dQ); free(dK); free(dV); free(s);
+    free(docat); free(doh); free(dqh); free(dkh); free(dvh); free(dQ); free(dK); free(dV);
     return rc;
 }
 

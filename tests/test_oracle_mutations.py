@@ -44,11 +44,10 @@ MUTATIONS = [
     ("per_query_length_ignores_query", "valid_lens[(long)b * Lq + i]", "valid_lens[(long)b * Lq]"),
     ("lse_drops_the_max", "lse[bh * (long)Lq + i] = mx + log(den);", "lse[bh * (long)Lq + i] = log(den);"),
     ("lse_in_log2", "lse[bh * (long)Lq + i] = mx + log(den);", "lse[bh * (long)Lq + i] = mx + log2(den);"),
-    ("linear_backward_dw_transposed", "dw[(long)n * Din + c] = acc;", "dw[(long)c * Dout + n] = acc;"),
-    ("linear_backward_dx_uses_w_transposed", "acc += dy[m * Dout + n] * w[(long)n * Din + c];",
-     "acc += dy[m * Dout + n] * w[(long)c * Dout + n];"),
-    ("linear_backward_bias_first_row_only", "for (long r = 0; r < M; ++r) acc += dy[r * Dout + n];",
-     "for (long r = 0; r < 1; ++r) acc += dy[r * Dout + n];"),
+    ("linear_backward_dw_wrong_output_feature", "const double a = dy[r * Dout + n];", "const double a = dy[r * Dout + (n + 1) % Dout];"),
+    ("linear_backward_dx_uses_w_transposed", "acc[c] += a * w[(long)n * Din + c];",
+     "acc[c] += a * w[(long)c * Dout + n];"),
+    ("linear_backward_bias_first_row_only", "bsum += a;", "bsum += (r == 0) ? a : 0.0;"),
     ("mha_backward_value_path_overwrites_key_path", "linear_backward(dV, xkv, w_v, dxkv, dw_v, db_v, Mk, D, D, 1);",
      "linear_backward(dV, xkv, w_v, dxkv, dw_v, db_v, Mk, D, D, 0);"),
     ("mha_backward_heads_interleaved", "double* r = rows + ((long)b * L + l) * h * dk + hd * dk + t;",

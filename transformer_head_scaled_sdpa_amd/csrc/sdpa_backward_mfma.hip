@@ -114,9 +114,14 @@ __device__ __forceinline__ void rows_body(const BackwardArgs& a, float c, int bl
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) kmin = min(kmin, __shfl_xor(kmin, o));
     kmin = __builtin_amdgcn_readfirstlane(kmin);
-    // Keys this workgroup must visit: up to the causal bound unless lengths
-    // are given (a fully masked row then spans all keys).
-    const int kv_end = (kCausal && a.vl_rank == 0) ? min(Lk, q_wg + kRowsWg) : Lk;
+    // Keys this workgroup must visit.  With one length per sequence, a
+    // positive length bounds every row's keys (and the causal bound still
+    // holds), while a length <= 0 spreads each row over all Lk keys; lengths
+    // per query keep every key.
+    const int len_b = a.vl_rank == 1 ? a.valid_lens[b] : 0;
+    const bool len_bound = a.vl_rank == 1 && len_b > 0;
+    int kv_end = len_bound ? min(Lk, len_b) : Lk;
+    if (kCausal && (a.vl_rank == 0 || len_bound)) kv_end = min(kv_end, q_wg + kRowsWg);
     const int n_steps = (kv_end + kStep - 1) / kStep;
 
     const bf16_t* qp = static_cast<const bf16_t*>(a.q) + b * a.sq[0] + hd * a.sq[1];
@@ -360,10 +365,14 @@ __device__ __forceinline__ void keys_body(const BackwardArgs& a, float c, int bl
     const bf16_t* qp = static_cast<const bf16_t*>(a.q) + b * a.sq[0] + hd * a.sq[1];
     const bf16_t* gp = static_cast<const bf16_t*>(a.dout) + b * a.sdo[0] + hd * a.sdo[1];
 
-    // Causal without lengths: queries before the workgroup's first key
-    // weight none of its keys.
-    const int i_begin = (kCausal && a.vl_rank == 0) ? k_wg : 0;
-    const int n_steps = (Lq - i_begin + kStep - 1) / kStep;
+    // Under the causal rule queries before the workgroup's first key weigh
+    // none of its keys, unless a length <= 0 (or lengths per query) may
+    // spread a query over all keys.  With one positive length per sequence,
+    // keys at or past it are weighed by no query: their gradients are zero.
+    const int len_all = a.vl_rank == 1 ? a.valid_lens[b] : Lk;
+    const bool len_bound = a.vl_rank == 1 && len_all > 0;
+    const int i_begin = (kCausal && (a.vl_rank == 0 || len_bound)) ? k_wg : 0;
+    const int n_steps = (len_bound && k_wg >= len_all) ? 0 : (Lq - i_begin + kStep - 1) / kStep;
     // This workgroup's 64 rows of K and V: one range-checked 16-byte chunk
     // per thread each (zeros past the keys), staged through LDS like the
     // rows' Q and dO.
@@ -380,7 +389,6 @@ __device__ __forceinline__ void keys_body(const BackwardArgs& a, float c, int bl
     const __amdgpu_buffer_rsrc_t len_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int*>(a.vl_rank == 2 ? a.valid_lens + (long long)b * Lq : a.valid_lens), (short)0,
         a.vl_rank == 2 ? Lq * 4 : 0, kBufWord3);
-    const int len_all = a.vl_rank == 1 ? a.valid_lens[b] : Lk;
     struct RowRaw {
         float lse, dsum;
         int len;
