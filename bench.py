@@ -236,6 +236,46 @@ class PreparedBackward:
             raise RuntimeError(f"sdpa_backward failed with status {st}")
 
 
+class PreparedMhaBackward:
+    """mha_backward (bf16 inputs, fp32 gradients) on an MHA workload's inputs
+    and a seeded output gradient, its arguments marshalled once."""
+
+    def __init__(self, inp):
+        import torch
+        from transformer_head_scaled_sdpa_amd import _lib
+        w = inp.workload
+        dev = torch.device("cuda:0")
+        T = lambda a: None if a is None else torch.from_numpy(a).to(dev).to(torch.bfloat16)
+        self.t = {n: T(a) for n, a in inp.tensors.items()}
+        if w.self_attn:
+            self.t["x_kv"] = self.t["x_q"]
+        rng = np.random.Generator(np.random.PCG64(w.seed + 1000))
+        self.g = T(rng.standard_normal((w.B, w.Lq, w.d_model)).astype(np.float32))
+        self.vl = None if inp.valid_lens is None else torch.from_numpy(inp.valid_lens).to(dev)
+        D = w.d_model
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.dx_q = torch.empty((w.B, w.Lq, D), **f32)
+        self.dx_kv = None if w.self_attn else torch.empty((w.B, w.Lk, D), **f32)
+        self.dw = [torch.empty((D, D), **f32) for _ in range(4)]
+        self.db = [torch.empty((D,), **f32) for _ in range(4)]
+        self.lib = _lib.load()
+        need = int(self.lib.mha_backward_workspace_bytes(_lib.MHA_BF16, w.B, w.Lq, w.Lk, D, w.h))
+        self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        p = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
+        t = self.t
+        self.args = [_lib.MHA_BF16, p(t["x_q"]), p(t["x_kv"]), p(t["w_q"]), p(t["b_q"]), p(t["w_k"]), p(t["b_k"]),
+                     p(t["w_v"]), p(t["b_v"]), p(t["w_o"]), p(self.g), p(self.dx_q), p(self.dx_kv)]
+        for dw, db in zip(self.dw, self.db):
+            self.args += [p(dw), p(db)]
+        self.args += [w.B, w.Lq, w.Lk, D, w.h, w.d_k, p(self.vl), int(w.causal), p(self.ws), need]
+        self.torch = torch
+
+    def __call__(self):
+        st = self.lib.mha_backward(*self.args, ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"mha_backward failed with status {st}")
+
+
 class PreparedWeights:
     """sdpa_forward_ex returning the attention weights (inspection path)."""
 
@@ -647,6 +687,31 @@ def extras(result, args, w):
         "own_statistics_avg_us": round(bt[False] * 1e3, 2),
         "note": "8*d_k flops per allowed pair (dV, dP, dQ, dK products); recomputed scores not counted; "
                 "own_statistics: sdpa_backward without the log-sum-exp (a pass of its own finds it)"}
+
+    # backward of the multi-head layer on the decoder workload: algorithmic
+    # work of the gradients themselves (dOcat, dW_o, the attention backward's
+    # 8*d_k per allowed pair, the input and weight gradients of the three
+    # input projections); the recomputed forward (Q/K/V projections and
+    # attention) is reported beside it, not counted
+    mw = workloads.BY_NAME["decoder_causal"]
+    minp = workloads.make_inputs(mw)
+    mf = PreparedMhaBackward(minp)
+    mms, _ = time_steps(mf, 100, 50)
+    mkt = kernel_times(mf, 10, args.repeat)
+    del mf
+    Mq, Mk, D = mw.B * mw.Lq, mw.B * mw.Lk, mw.d_model
+    mpairs = allowed_pairs(mw, minp.valid_lens)
+    grad_fl = 2 * Mq * D * D * 2 + 8 * mw.d_k * mpairs + 2 * D * D * (2 * Mq + 4 * Mk)
+    recompute_fl = 2 * D * D * (Mq + 2 * Mk) + 4 * mw.d_k * mpairs
+    result["mha_backward"] = {
+        "workload": mw.description + ", output gradient N(0,1); all gradients fp32",
+        "avg_us": round(mms * 1e3, 2),
+        "alg_tflops": round(grad_fl / (mms * 1e-3) / 1e12, 2),
+        "frac_bf16_mfma_peak": round(grad_fl / (mms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "with_recompute_tflops": round((grad_fl + recompute_fl) / (mms * 1e-3) / 1e12, 2),
+        "kernels_us": {n: round(v * 1e3, 2) for n, v in mkt.items()},
+        "note": "alg: 4*M*D^2 (dOcat, dW_o) + 8*d_k per allowed pair + 2*D^2*(2*Mq + 4*Mk) (input and weight "
+                "gradients of W_Q, W_K, W_V); with_recompute adds the forward's projections and attention"}
 
     # inspection path: HBM-bound on the fp32 weights it writes; its matrix
     # work counted as the forward's algorithmic 4*d_k per allowed pair

@@ -22,6 +22,12 @@ int oracle_sdpa_backward_f64(const double* q, const double* k, const double* v, 
                              const int* valid_lens, int vl_per_query, int causal);
 void oracle_layer_norm_f64(const double* x, const double* a, const double* b, double* y, long M, int D, int kind,
                            double eps);
+int oracle_mha_backward_f64(const double* xq, const double* xkv, const double* w_q, const double* b_q,
+                            const double* w_k, const double* b_k, const double* w_v, const double* b_v,
+                            const double* w_o, const double* dout, double* dxq, double* dxkv, double* dw_q,
+                            double* db_q, double* dw_k, double* db_k, double* dw_v, double* db_v, double* dw_o,
+                            double* db_o, int B, int Lq, int Lk, int D, int h, const int* valid_lens,
+                            int vl_per_query, int causal, int bf16_stages);
 
 static double* filled(long n, unsigned seed) {
     double* a = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
@@ -89,6 +95,27 @@ int main(void) {
                        NULL, 0, 0) != -1)
         rc |= 1;                                       /* D not a multiple of h */
     printf("mha %.12f\n", sum(out, (long)B * 3 * D));
+
+    {
+        double* gout = filled((long)B * Lq * D, 17);
+        double *dxq = filled((long)B * Lq * D, 18), *dxkv = filled((long)B * Lk * D, 19);
+        double* dwb[8];
+        for (int i = 0; i < 8; ++i) dwb[i] = filled(i < 4 ? (long)D * D : D, 40 + i);
+        rc |= oracle_mha_backward_f64(xq, xkv, w[0], bias[0], w[1], bias[1], w[2], bias[2], w[3], gout, dxq, dxkv,
+                                      dwb[0], dwb[4], dwb[1], dwb[5], dwb[2], dwb[6], dwb[3], dwb[7], B, Lq, Lk, D, 2,
+                                      vl1, 0, 0, 1);
+        rc |= oracle_mha_backward_f64(xq, xkv, w[0], NULL, w[1], NULL, w[2], NULL, w[3], gout, dxq, dxkv, dwb[0],
+                                      NULL, dwb[1], NULL, dwb[2], NULL, dwb[3], NULL, B, Lq, Lk, D, 2, vl2, 1, 0, 0);
+        rc |= oracle_mha_backward_f64(xq, xkv, w[0], NULL, w[1], NULL, w[2], NULL, w[3], gout, dxq, dxkv, dwb[0],
+                                      dwb[4], dwb[1], dwb[5], dwb[2], dwb[6], dwb[3], dwb[7], B, 0, Lk, D, 2, NULL, 0,
+                                      0, 0);                     /* no queries: zero weight gradients */
+        if (oracle_mha_backward_f64(xq, xkv, w[0], NULL, w[1], NULL, w[2], NULL, w[3], gout, dxq, dxkv, dwb[0], NULL,
+                                    dwb[1], NULL, dwb[2], NULL, dwb[3], NULL, B, Lq, Lk, 15, 2, NULL, 0, 0, 0) != -1)
+            rc |= 1;                                   /* D not a multiple of h */
+        printf("mha backward %.12f %.12f\n", sum(dxkv, (long)B * Lk * D), sum(dwb[0], (long)D * D));
+        free(gout); free(dxq); free(dxkv);
+        for (int i = 0; i < 8; ++i) free(dwb[i]);
+    }
 
     double* y = filled((long)B * Lq * D, 16);
     oracle_layer_norm_f64(xq, w[0], bias[0], y, (long)B * Lq, D, 0, 1e-6);

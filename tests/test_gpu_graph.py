@@ -183,3 +183,32 @@ def test_graph_mha_sublayer():
         return mha.mha_sublayer_forward(x, wq, wk, wv, wo, h=h, ln_gain=g, ln_bias=bb, valid_lens=vl)
 
     _graph_check(make, call)
+
+
+@pytest.mark.parametrize("self_attn", [True, False])
+def test_graph_mha_backward(self_attn):
+    """mha_backward's ten launches (transposes, projections, attention forward
+    and backward, input and weight gradients) in one graph; outputs and
+    workspace allocated once, outside the capture."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    B, L, Lk, D, h = 2, 200, 200 if self_attn else 130, 256, 4
+    need = mha.library().mha_backward_workspace_bytes(mha.MHA_BF16, B, L, Lk, D, h)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def make(r):
+        x = _rand((B, L, D), 10 * r + 1, torch.bfloat16)
+        xkv = x if self_attn else _rand((B, Lk, D), 10 * r + 9, torch.bfloat16)
+        ws_ = [_rand((D, D), 10 * r + 2 + i, torch.bfloat16, D ** -0.5) for i in range(4)]
+        bs = [_rand((D,), 10 * r + 6 + i, torch.bfloat16, 0.1) for i in range(3)]
+        g = _rand((B, L, D), 10 * r + 5, torch.bfloat16)
+        vl = torch.tensor([Lk, 61], dtype=torch.int32).roll(r).cuda()
+        return [x, None if self_attn else xkv] + ws_ + bs + [g, vl]
+
+    def call(t):
+        x, xkv = t[0], (t[0] if self_attn else t[1])
+        r = mha.mha_backward(x, xkv, *t[2:6], t[9], *t[6:9], h=h, valid_lens=t[10], causal=self_attn,
+                             bias_grads=True, workspace=ws)
+        return tuple(r[n] for n in sorted(r) if r[n] is not None)
+
+    _graph_check(make, call)
