@@ -40,6 +40,7 @@ constexpr int kTnTile = 128;                       // output tile edge
 constexpr int kSubB = kTnRows * kLdsT * 2;         // one [32][64] sub-tile, 192-byte rows
 constexpr int kStageTnB = 4 * kSubB;               // dy: 2 sub-tiles, x: 2 sub-tiles
 constexpr int kBufTnWord3 = 0x00020000;            // raw buffer, 32-bit data format
+constexpr int kTnWgs = 512;                        // workgroups per launch to aim for (two per CU)
 
 // Buffer resource over rows r0 .. M-1 of a row-major [M, cols] bf16 operand
 // with row stride ld: the range ends with row M - 1's last column, so rows at
@@ -211,32 +212,51 @@ hipError_t launch_transpose_bf16(const TransposeArgs& a, hipStream_t s) {
 }
 
 size_t gemm_tn_workspace_bytes(const int* M, const int* N1, const int* N2, int nprob) {
+    int slices[3];
+    gemm_tn_slices(M, N1, N2, nprob, slices);
     size_t bytes = 0;
     for (int q = 0; q < nprob; ++q) {
-        const int slices = gemm_tn_slices(M[q], N1[q], N2[q]);
-        bytes += (size_t)slices * ((size_t)N1[q] * N2[q] + N1[q]) * 4;
+        bytes += (size_t)slices[q] * ((size_t)N1[q] * N2[q] + N1[q]) * 4;
         bytes = (bytes + 255) / 256 * 256;
     }
     return bytes;
 }
 
-int gemm_tn_slices(int M, int N1, int N2) {
-    const int tiles = ((N1 + kTnTile - 1) / kTnTile) * ((N2 + kTnTile - 1) / kTnTile);
-    // About two workgroups per CU of 256, each slice at least 4 steps long.
-    const int want = (512 + tiles - 1) / tiles;
-    const int most = max(1, (M + 4 * kTnRows - 1) / (4 * kTnRows));
-    return max(1, min(want, most));
+void gemm_tn_slices(const int* M, const int* N1, const int* N2, int nprob, int* slices) {
+    // The launch's workgroups (about kTnWgs in all) are shared among the
+    // problems in proportion to their work; each slice is at least 4 steps
+    // long.  Fewer, longer slices mean fewer partials to write and add.
+    double work[3], total = 0.0;
+    int tiles[3];
+    for (int q = 0; q < nprob; ++q) {
+        tiles[q] = ((N1[q] + kTnTile - 1) / kTnTile) * ((N2[q] + kTnTile - 1) / kTnTile);
+        work[q] = (double)M[q] * tiles[q];
+        total += work[q];
+    }
+    for (int q = 0; q < nprob; ++q) {
+        const int want = total > 0.0 ? (int)(kTnWgs * work[q] / total / tiles[q] + 0.5) : 1;
+        const int most = max(1, (M[q] + 4 * kTnRows - 1) / (4 * kTnRows));
+        slices[q] = max(1, min(want, most));
+    }
 }
 
 hipError_t launch_gemm_tn(TnArgs g, void* workspace, hipStream_t s) {
     char* ws = static_cast<char*>(workspace);
     long long blocks = 0, rblocks = 0;
+    if (g.nprob < 1 || g.nprob > 3) return hipErrorInvalidValue;
+    int M[3], N1[3], N2[3], slices[3];
+    for (int q = 0; q < g.nprob; ++q) {
+        M[q] = g.p[q].M;
+        N1[q] = g.p[q].N1;
+        N2[q] = g.p[q].N2;
+    }
+    gemm_tn_slices(M, N1, N2, g.nprob, slices);
     for (int q = 0; q < g.nprob; ++q) {
         TnProblem& p = g.p[q];
         if (p.N1 % 64 || p.N2 % 64 || p.M < 0) return hipErrorInvalidValue;
         // The operands' buffer ranges count bytes in 31 bits.
         if ((long long)p.M * (p.ldy > p.ldx ? p.ldy : p.ldx) * 2 >= (1ll << 31)) return hipErrorInvalidValue;
-        p.slices = gemm_tn_slices(p.M, p.N1, p.N2);
+        p.slices = slices[q];
         p.rows_per_slice = ((p.M + p.slices - 1) / p.slices + kTnRows - 1) / kTnRows * kTnRows;
         p.tiles1 = (p.N1 + kTnTile - 1) / kTnTile;
         p.tiles2 = (p.N2 + kTnTile - 1) / kTnTile;

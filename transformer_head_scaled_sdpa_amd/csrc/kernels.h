@@ -169,7 +169,8 @@ struct TnArgs {
     TnProblem p[3];
     int nprob;
 };
-int gemm_tn_slices(int M, int N1, int N2);
+// Row slices of each problem (the launch's workgroups shared by work).
+void gemm_tn_slices(const int* M, const int* N1, const int* N2, int nprob, int* slices);
 size_t gemm_tn_workspace_bytes(const int* M, const int* N1, const int* N2, int nprob);
 hipError_t launch_gemm_tn(TnArgs g, void* workspace, hipStream_t s);
 // Transposes of square bf16 weights: dst[q] = w[q]^T, [n, n] each, written
