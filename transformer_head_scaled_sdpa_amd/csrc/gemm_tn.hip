@@ -51,11 +51,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tn_rows(const bf16_t* p, long 
                                              (int)left, kBufTnWord3);
 }
 
-__global__ __launch_bounds__(kTnThreads, 1) void gemm_tn_partial(TnArgs g) {
+__global__ __launch_bounds__(kTnThreads, 1) void gemm_tn_partial(TnArgs g, int blocks, int per_xcd) {
     __shared__ __attribute__((aligned(16))) char smem[2 * kStageTnB];
 
+    // XCD-aware order: the hardware deals workgroup ids to the eight XCDs
+    // round-robin, so ids x, x+8, ... (one XCD) take a contiguous range of
+    // logical blocks: the tiles of one slice, which read the same rows of
+    // both operands, then share that XCD's L2.
+    int blk = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3), pi = 0;
+    if (blk >= blocks) return;
     // Block -> (problem, row tile, column tile, slice).
-    int blk = blockIdx.x, pi = 0;
     while (pi + 1 < g.nprob && blk >= g.p[pi].blocks) {
         blk -= g.p[pi].blocks;
         ++pi;
@@ -272,7 +277,8 @@ hipError_t launch_gemm_tn(TnArgs g, void* workspace, hipStream_t s) {
         rblocks += p.reduce_blocks;
     }
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(gemm_tn_partial, dim3((unsigned)blocks), dim3(kTnThreads), 0, s, g);
+    const int per_xcd = (int)((blocks + 7) / 8);
+    hipLaunchKernelGGL(gemm_tn_partial, dim3(8u * per_xcd), dim3(kTnThreads), 0, s, g, (int)blocks, per_xcd);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gemm_tn_reduce, dim3((unsigned)rblocks), dim3(256), 0, s, g);
