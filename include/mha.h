@@ -152,6 +152,9 @@ mha_status sdpa_forward_lse(mha_dtype in_dt, mha_dtype out_dt,
  *   Requirements: in_dt == MHA_BF16 (MHA_ENOTSUP otherwise), d_k == d_v == 64,
  *   B >= 0, h >= 1, L >= 1, pointers 16-byte aligned, strides multiples of 8
  *   elements (output: 8 bf16 or 4 fp32), o must not overlap q, k, v.
+ *   The row strides of k and v must stay below 2^21 elements (a slice of
+ *   512 cached rows is addressed with 31-bit byte offsets; MHA_ENOTSUP
+ *   otherwise).
  *   B == 0 is a no-op.  Computed in fp32 from the bf16 inputs (no reduced-
  *   precision weights) over slices of 512 keys (256 when B*h is small); a
  *   cache of one slice is finished in one launch, longer ones are split and

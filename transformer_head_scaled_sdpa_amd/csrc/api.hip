@@ -419,6 +419,8 @@ mha_status decode_impl(mha_dtype in_dt, mha_dtype out_dt,
     const mha_strides in_s[3] = {sq, sk, sv};
     for (const mha_strides& s : in_s)
         if (s.b < 0 || s.h < 0 || s.l < 0 || s.b % 8 || s.h % 8 || s.l % 8) return MHA_EINVAL;
+    // A slice's 512 cached rows are addressed with 31-bit byte offsets.
+    if (sk.l * 2 * 512 >= (1ll << 31) || sv.l * 2 * 512 >= (1ll << 31)) return MHA_ENOTSUP;
     if (so.b < 0 || so.h < 0 || so.b % omult || so.h % omult) return MHA_EINVAL;
     const size_t need = round_up(mha::decode_workspace_bytes(B, h, L), 256);
     if (use_scratch ? need > kDecodeScratchBytes : workspace_bytes < need) return MHA_EWORKSPACE;

@@ -89,29 +89,47 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a, int n_spl
     const bf16_t* kp = static_cast<const bf16_t*>(a.k) + b * a.sk[0] + hd * a.sk[1];
     const bf16_t* vp = static_cast<const bf16_t*>(a.v) + b * a.sv[0] + hd * a.sv[1];
 
-    // ---- every load of the slice, issued up front ----
+    // ---- every load of the slice, issued up front: the query first, then
+    // K in the order the score passes use it, then V, all unconditional (a
+    // buffer range ending with the slice's last key: rows past it read as
+    // zeros), so each pass waits only for its own keys and the V loads are
+    // still landing while the scores and the softmax run.
     const int half = tid & 1;
     const int f8 = (tid & 7) * 8, jg = tid >> 3;
+    uint4 qr[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) qr[x] = *reinterpret_cast<const uint4*>(qp + half * 32 + x * 8);
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    constexpr int kBufWord3 = 0x00020000;       // raw buffer, 32-bit data format
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(kp + (long long)j0 * a.sk[2]), (short)0,
+        (int)((long long)(cnt - 1) * a.sk[2] * 2 + kD * 2), kBufWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(vp + (long long)j0 * a.sv[2]), (short)0,
+        (int)((long long)(cnt - 1) * a.sv[2] * 2 + kD * 2), kBufWord3);
+    auto ld = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    };
     uint4 kr[kKPass][4], vr[kVKeys];
 #pragma unroll
     for (int p = 0; p < kKPass; ++p) {
         const int jl = p * (kThreads / 2) + (tid >> 1);
-        const bf16_t* row = kp + (long long)(j0 + jl) * a.sk[2] + half * 32;
+        const uint32_t row = (uint32_t)(jl * a.sk[2] * 2) + half * 64;
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-            kr[p][x] = jl < cnt ? *reinterpret_cast<const uint4*>(row + x * 8) : make_uint4(0, 0, 0, 0);
+        for (int x = 0; x < 4; ++x) kr[p][x] = ld(krs, row + x * 16);
     }
 #pragma unroll
     for (int i = 0; i < kVKeys; ++i) {
         const int jl = jg + i * (kThreads / 8);
-        vr[i] = jl < cnt ? *reinterpret_cast<const uint4*>(vp + (long long)(j0 + jl) * a.sv[2] + f8)
-                         : make_uint4(0, 0, 0, 0);
+        vr[i] = ld(vrs, (uint32_t)(jl * a.sv[2] * 2) + f8 * 2);
     }
+    __builtin_amdgcn_sched_barrier(0);   // every load out before the first wait
     float qf[32];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         float f[8];
-        unpack8(*reinterpret_cast<const uint4*>(qp + half * 32 + x * 8), f);
+        unpack8(qr[x], f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) qf[x * 8 + e] = f[e];
     }
