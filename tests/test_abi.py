@@ -147,7 +147,7 @@ def decode(lib, **kw):
     a.update(kw)
     st = S(4 * 300 * 64, 300 * 64, 64)
     s1 = kw.get("sq", S(4 * 64, 64, 0))
-    return lib.sdpa_decode(a["in_dt"], a["out_dt"], a["q"], s1, a["k"], kw.get("sk", st), a["v"], st, a["o"],
+    return lib.sdpa_decode(a["in_dt"], a["out_dt"], a["q"], s1, a["k"], kw.get("sk", st), a["v"], kw.get("sv", st), a["o"],
                            kw.get("so", S(4 * 64, 64, 0)), a["B"], a["h"], a["L"], a["dk"], a["dv"], a["lens"],
                            a["ws"], a["ws_bytes"], None)
 
@@ -190,6 +190,8 @@ def test_decode_validation(lib):
     assert decode(lib, ws_bytes=100) == EWORK
     assert decode(lib, k=ctypes.c_void_p(P + 8)) == EINVAL               # misaligned
     assert decode(lib, sk=S(4 * 300 * 64, 300 * 64, 60)) == EINVAL      # stride not a multiple of 8
+    assert decode(lib, sk=S(0, 0, 1 << 21)) == ENOTSUP                  # 512 rows past 31-bit offsets
+    assert decode(lib, sv=S(0, 0, 1 << 21)) == ENOTSUP
     assert decode(lib, o=ALIGNED[1]) == EINVAL       # output overlaps the key cache
     assert decode(lib, ws=ALIGNED[2]) == EINVAL      # workspace overlaps the value cache
 
