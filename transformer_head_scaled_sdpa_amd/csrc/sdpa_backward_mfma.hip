@@ -104,8 +104,14 @@ __device__ __forceinline__ void rows_body(const BackwardArgs& a, float c, int bl
     const int Lq = a.Lq, Lk = a.Lk;
     const bool live = i < Lq;
 
+    // One length per sequence is read once as a scalar: a per-lane read of it
+    // (under the lane's `live` test) would be a vector load whose wait comes
+    // before the prologue's loads are issued.
+    const int len_b = a.vl_rank == 1 ? a.valid_lens[b] : 0;
     bool none = false;
-    const int klim = live ? key_limit<kCausal>(a, b, i, none) : Lk;
+    const int klim = !live ? Lk
+                           : (a.vl_rank == 2 ? key_limit<kCausal>(a, b, i, none)
+                                             : limit_from_len<kCausal>(a, a.vl_rank == 1 ? len_b : Lk, i, none));
     // Score scale (log2 units).  A row with no allowed key weights its keys
     // equally: its scale 2^-100 makes every finite score's exponent round to
     // the same value while masked keys (-inf) still weigh 0.
@@ -118,7 +124,6 @@ __device__ __forceinline__ void rows_body(const BackwardArgs& a, float c, int bl
     // positive length bounds every row's keys (and the causal bound still
     // holds), while a length <= 0 spreads each row over all Lk keys; lengths
     // per query keep every key.
-    const int len_b = a.vl_rank == 1 ? a.valid_lens[b] : 0;
     const bool len_bound = a.vl_rank == 1 && len_b > 0;
     int kv_end = len_bound ? min(Lk, len_b) : Lk;
     if (kCausal && (a.vl_rank == 0 || len_bound)) kv_end = min(kv_end, q_wg + kRowsWg);
