@@ -276,6 +276,48 @@ class PreparedMhaBackward:
             raise RuntimeError(f"mha_backward failed with status {st}")
 
 
+class PreparedTrainingPair:
+    """One training pass of the multi-head layer: mha_forward_train (bf16
+    output, Q, K, V, the merged heads and the log-sum-exp kept) then
+    mha_backward_saved on the kept tensors, arguments marshalled once."""
+
+    def __init__(self, inp):
+        import torch
+        from transformer_head_scaled_sdpa_amd import _lib
+        self.bwd = PreparedMhaBackward(inp)
+        w = inp.workload
+        dev = torch.device("cuda:0")
+        t = self.bwd.t
+        lib = self.lib = self.bwd.lib
+        D = w.d_model
+        self.out = torch.empty((w.B, w.Lq, D), dtype=torch.bfloat16, device=dev)
+        sb = int(lib.mha_saved_bytes(_lib.MHA_BF16, w.B, w.Lq, w.Lk, D, w.h))
+        self.saved = torch.empty(sb, dtype=torch.uint8, device=dev)
+        need = int(lib.mha_backward_saved_workspace_bytes(_lib.MHA_BF16, w.B, w.Lq, w.Lk, D, w.h))
+        self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        self.bwd.ws = None                      # the recomputing backward's workspace is not needed
+        p = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
+        vl, bwd = p(self.bwd.vl), self.bwd
+        self.fargs = [_lib.MHA_BF16, _lib.MHA_BF16, p(t["x_q"]), p(t["x_kv"]), p(t["w_q"]), p(t["b_q"]), p(t["w_k"]),
+                      p(t["b_k"]), p(t["w_v"]), p(t["b_v"]), p(t["w_o"]), p(t["b_o"]), p(self.out),
+                      w.B, w.Lq, w.Lk, D, w.h, w.d_k, vl, int(w.causal), p(self.saved), sb]
+        self.bargs = [_lib.MHA_BF16, p(t["x_q"]), p(t["x_kv"]), p(t["w_q"]), p(t["w_k"]), p(t["w_v"]), p(t["w_o"]),
+                      p(self.saved), sb, p(bwd.g), p(bwd.dx_q), p(bwd.dx_kv)]
+        for dw, db in zip(bwd.dw, bwd.db):
+            self.bargs += [p(dw), p(db)]
+        self.bargs += [w.B, w.Lq, w.Lk, D, w.h, w.d_k, vl, int(w.causal), p(self.ws), need]
+        self.torch = torch
+
+    def __call__(self):
+        s = ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        st = self.lib.mha_forward_train(*self.fargs, s)
+        if st != 0:
+            raise RuntimeError(f"mha_forward_train failed with status {st}")
+        st = self.lib.mha_backward_saved(*self.bargs, s)
+        if st != 0:
+            raise RuntimeError(f"mha_backward_saved failed with status {st}")
+
+
 class PreparedWeights:
     """sdpa_forward_ex returning the attention weights (inspection path)."""
 
@@ -712,6 +754,23 @@ def extras(result, args, w):
         "kernels_us": {n: round(v * 1e3, 2) for n, v in mkt.items()},
         "note": "alg: 4*M*D^2 (dOcat, dW_o) + 8*d_k per allowed pair + 2*D^2*(2*Mq + 4*Mk) (input and weight "
                 "gradients of W_Q, W_K, W_V); with_recompute adds the forward's projections and attention"}
+
+    # the training pass (forward kept, backward on what it kept) on the same
+    # workload: the forward's algorithmic work (projections, 4*d_k per
+    # allowed pair) plus the gradients' above
+    tf = PreparedTrainingPair(minp)
+    tms, _ = time_steps(tf, 100, 50)
+    tkt = kernel_times(tf, 10, args.repeat)
+    del tf
+    fwd_fl = 2 * D * D * (2 * Mq + 2 * Mk) + 4 * mw.d_k * mpairs
+    result["mha_training_pass"] = {
+        "workload": mw.description + ", mha_forward_train (bf16 output) then mha_backward_saved",
+        "avg_us": round(tms * 1e3, 2),
+        "alg_tflops": round((fwd_fl + grad_fl) / (tms * 1e-3) / 1e12, 2),
+        "frac_bf16_mfma_peak": round((fwd_fl + grad_fl) / (tms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernels_us": {n: round(v * 1e3, 2) for n, v in tkt.items()},
+        "note": "alg: forward 2*D^2*(2*Mq + 2*Mk) (four projections) + 4*d_k per allowed pair, plus the "
+                "gradients' flops of mha_backward; nothing recomputed"}
 
     # inspection path: HBM-bound on the fp32 weights it writes; its matrix
     # work counted as the forward's algorithmic 4*d_k per allowed pair

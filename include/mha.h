@@ -452,6 +452,60 @@ mha_status mha_backward(mha_dtype in_dt,
                         const int* valid_lens, int causal,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The training pair: a forward that keeps what the backward needs, and a
+ * backward that takes it instead of recomputing it (the saved-statistic
+ * form of the backward; the pages train these models end to end).
+ *
+ * mha_forward_train -- mha_forward for bf16 inputs that also fills `saved`
+ * (device buffer of at least mha_saved_bytes(...) bytes, 16-byte aligned,
+ * caller-owned, not overlapping any input or `out`) with Q, K, V (bf16
+ * [B*L, d_model] each, unscaled, biases added), the merged heads (bf16
+ * [B*Lq, d_model]) and each query's log-sum-exp (fp32 [B, h, Lq]).  One GEMM
+ * launch projects Q, K, V, the split-head attention kernel writes the merged
+ * heads and the statistic, and the output projection follows.  Its scores
+ * are single bf16 products of the stored Q and K (mha_forward keeps Q and K
+ * as hi + lo pairs for large logits); the output is the oracle's
+ * bf16-storage reading, and the backward's weights are recomputed from the
+ * same Q, K and statistic.  Arguments, sizes and errors otherwise as
+ * mha_forward (B * L * d_model below 2^31 / 6 as for mha_backward).
+ *
+ * mha_backward_saved -- mha_backward given `saved` from mha_forward_train
+ * with the same inputs, weights, biases, lengths and causal flag (the biases
+ * are then not needed: they are inside the saved Q, K, V).  Skips the
+ * forward's recomputation (one GEMM and one attention launch); the
+ * workspace is at least mha_backward_saved_workspace_bytes(...) bytes and
+ * must not overlap `saved`.  The gradients equal mha_backward's bit for bit.
+ */
+size_t mha_saved_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h);
+
+mha_status mha_forward_train(mha_dtype in_dt, mha_dtype out_dt,
+                             const void* x_q, const void* x_kv,
+                             const void* w_q, const void* b_q,
+                             const void* w_k, const void* b_k,
+                             const void* w_v, const void* b_v,
+                             const void* w_o, const void* b_o,
+                             void* out,
+                             int B, int Lq, int Lk, int d_model, int h, int d_k,
+                             const int* valid_lens, int causal,
+                             void* saved, size_t saved_bytes, void* stream);
+
+size_t mha_backward_saved_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h);
+
+mha_status mha_backward_saved(mha_dtype in_dt,
+                              const void* x_q, const void* x_kv,
+                              const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                              const void* saved, size_t saved_bytes,
+                              const void* dout,
+                              float* dx_q, float* dx_kv,
+                              float* dw_q, float* db_q,
+                              float* dw_k, float* db_k,
+                              float* dw_v, float* db_v,
+                              float* dw_o, float* db_o,
+                              int B, int Lq, int Lk, int d_model, int h, int d_k,
+                              const int* valid_lens, int causal,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* mha_status_string(mha_status s);
 

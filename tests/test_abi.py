@@ -385,3 +385,75 @@ def test_mha_backward_workspace_and_validation(lib):
     assert mbwd(lib, ws=None) == EINVAL
     assert mbwd(lib, wsb=100) == EWORK
     assert mbwd(lib, B=1, Lq=1 << 20, Lk=8, D=512, h=8) == ENOTSUP
+
+
+def ftrain(lib, **kw):
+    """mha_forward_train on fake addresses, 1 MiB apart (B2 L10 d_model 256)."""
+    a = dict(in_dt=BF16, out_dt=F32, xq=ALIGNED[0], xkv=ALIGNED[1], out=ALIGNED[7], saved=ALIGNED[14], sb=None,
+             B=2, Lq=10, Lk=10, D=256, h=4, dk=64, vl=None, causal=0, bias=None)
+    a.update(kw)
+    need = lib.mha_saved_bytes(a["in_dt"], a["B"], a["Lq"], a["Lk"], a["D"], a["h"])
+    sb = need if a["sb"] is None else a["sb"]
+    b = a["bias"] or [None] * 4
+    return lib.mha_forward_train(a["in_dt"], a["out_dt"], a["xq"], a["xkv"], ALIGNED[2], b[0], ALIGNED[3], b[1],
+                                 ALIGNED[4], b[2], ALIGNED[5], b[3], a["out"], a["B"], a["Lq"], a["Lk"], a["D"],
+                                 a["h"], a["dk"], a["vl"], a["causal"], a["saved"], sb, None)
+
+
+def test_mha_forward_train_validation(lib):
+    sb = lib.mha_saved_bytes
+    assert sb(F32, 2, 10, 10, 256, 4) == 0
+    assert sb(BF16, 2, 10, 10, 250, 5) == 0
+    # Q, K, V and the merged heads (bf16) and one fp32 statistic per query and head
+    assert sb(BF16, 2, 10, 10, 256, 4) >= 4 * 2 * 10 * 256 * 2 + 2 * 4 * 10 * 4
+    assert sb(BF16, 2, 10, 10, 256, 4) % 256 == 0
+    assert ftrain(lib, B=0) == OK and ftrain(lib, Lq=0) == OK
+    assert ftrain(lib, in_dt=F32) == ENOTSUP
+    assert ftrain(lib, out_dt=9) == EINVAL
+    assert ftrain(lib, dk=32) == EINVAL
+    assert ftrain(lib, D=512, h=16, dk=32) == ENOTSUP
+    assert ftrain(lib, causal=1, Lk=12) == EINVAL
+    assert ftrain(lib, Lk=0) == EINVAL
+    assert ftrain(lib, saved=None) == EINVAL
+    assert ftrain(lib, out=None) == EINVAL
+    assert ftrain(lib, sb=1000) == EWORK
+    assert ftrain(lib, saved=ALIGNED[1]) == EINVAL          # saved overlaps x_kv
+    assert ftrain(lib, out=ALIGNED[14]) == EINVAL           # out overlaps saved
+    assert ftrain(lib, out=ALIGNED[5]) == EINVAL            # out overlaps w_o
+    assert ftrain(lib, xq=ctypes.c_void_p(P + 8)) == EINVAL
+    assert ftrain(lib, bias=[ctypes.c_void_p(P + 0xD00000 + 8), None, None, None]) == EINVAL
+    assert ftrain(lib, B=1, Lq=1 << 20, Lk=8, D=512, h=8) == ENOTSUP
+
+
+def mbwd_saved(lib, **kw):
+    """mha_backward_saved on fake addresses (B2 L10 d_model 256)."""
+    a = dict(xq=ALIGNED[0], xkv=ALIGNED[1], saved=ALIGNED[14], sb=None, dout=ALIGNED[6], dxq=ALIGNED[7],
+             dxkv=ALIGNED[8], dw=[ALIGNED[9], ALIGNED[10], ALIGNED[11], ALIGNED[12]], db=[None] * 4,
+             B=2, Lq=10, Lk=10, D=256, h=4, dk=64, causal=0, ws=ALIGNED[15], wsb=None)
+    a.update(kw)
+    need = lib.mha_backward_saved_workspace_bytes(BF16, a["B"], a["Lq"], a["Lk"], a["D"], a["h"])
+    saved = lib.mha_saved_bytes(BF16, a["B"], a["Lq"], a["Lk"], a["D"], a["h"])
+    wsb = need if a["wsb"] is None else a["wsb"]
+    sb = saved if a["sb"] is None else a["sb"]
+    dw, db = a["dw"], a["db"]
+    return lib.mha_backward_saved(BF16, a["xq"], a["xkv"], ALIGNED[2], ALIGNED[3], ALIGNED[4], ALIGNED[5],
+                                  a["saved"], sb, a["dout"], a["dxq"], a["dxkv"], dw[0], db[0], dw[1], db[1], dw[2],
+                                  db[2], dw[3], db[3], a["B"], a["Lq"], a["Lk"], a["D"], a["h"], a["dk"], None,
+                                  a["causal"], a["ws"], wsb, None)
+
+
+def test_mha_backward_saved_validation(lib):
+    full = lib.mha_backward_workspace_bytes(BF16, 2, 10, 10, 256, 4)
+    part = lib.mha_backward_saved_workspace_bytes(BF16, 2, 10, 10, 256, 4)
+    saved = lib.mha_saved_bytes(BF16, 2, 10, 10, 256, 4)
+    # the forward's tensors move from the workspace into the saved buffer
+    assert 0 < part < full and part + saved == full
+    assert lib.mha_backward_saved_workspace_bytes(F32, 2, 10, 10, 256, 4) == 0
+    assert mbwd_saved(lib, saved=None) == EINVAL
+    assert mbwd_saved(lib, saved=ctypes.c_void_p(P + 0xE00000 + 8)) == EINVAL
+    assert mbwd_saved(lib, sb=1000) == EWORK
+    assert mbwd_saved(lib, wsb=part - 256) == EWORK
+    assert mbwd_saved(lib, saved=ALIGNED[9]) == EINVAL       # saved overlaps dw_q
+    assert mbwd_saved(lib, ws=ALIGNED[14]) == EINVAL         # workspace overlaps saved
+    assert mbwd_saved(lib, dxkv=None) == EINVAL
+    assert mbwd_saved(lib, causal=1, Lk=12) == EINVAL

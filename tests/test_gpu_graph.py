@@ -212,3 +212,33 @@ def test_graph_mha_backward(self_attn):
         return tuple(r[n] for n in sorted(r) if r[n] is not None)
 
     _graph_check(make, call)
+
+
+def test_graph_mha_training_pair():
+    """mha_forward_train then mha_backward_saved (the forward's tensors kept
+    in the saved buffer between the two) captured as one graph."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    B, L, D, h = 2, 160, 256, 4
+    lib = mha.library()
+    saved = torch.empty(lib.mha_saved_bytes(mha.MHA_BF16, B, L, L, D, h), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(lib.mha_backward_saved_workspace_bytes(mha.MHA_BF16, B, L, L, D, h), dtype=torch.uint8,
+                     device="cuda")
+
+    def make(r):
+        x = _rand((B, L, D), 10 * r + 1, torch.bfloat16)
+        ws_ = [_rand((D, D), 10 * r + 2 + i, torch.bfloat16, D ** -0.5) for i in range(4)]
+        bs = [_rand((D,), 10 * r + 6 + i, torch.bfloat16, 0.1) for i in range(4)]
+        g = _rand((B, L, D), 10 * r + 5, torch.bfloat16)
+        vl = torch.tensor([L, 47], dtype=torch.int32).roll(r).cuda()
+        return [x] + ws_ + bs + [g, vl]
+
+    def call(t):
+        x, wq, wk, wv, wo, bq, bk, bv, bo, g, vl = t
+        out, _ = mha.mha_forward_train(x, x, wq, wk, wv, wo, bq, bk, bv, bo, h=h, valid_lens=vl, causal=True,
+                                       saved=saved)
+        r = mha.mha_backward(x, x, wq, wk, wv, wo, g, h=h, valid_lens=vl, causal=True, bias_grads=True,
+                             workspace=ws, saved=saved)
+        return (out,) + tuple(r[n] for n in sorted(r) if r[n] is not None)
+
+    _graph_check(make, call)

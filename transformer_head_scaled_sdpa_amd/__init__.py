@@ -20,6 +20,8 @@ there is no CPU or PyTorch fallback, and a missing library raises.
     sdpa_backward(q, k, v, o, dout, valid_lens=None, causal=False, lse=None)
         -> dq, dk, dv (gradients of sdpa_forward for the output gradient dout;
         with the forward's lse the weights are recomputed from it)
+    mha_forward_train(x_q, x_kv, w_q, ..., h=8, valid_lens=None, causal=False)
+        -> out, saved (Q, K, V, merged heads and statistic kept for the backward)
     mha_backward(x_q, x_kv, w_q, w_k, w_v, w_o, dout, b_q=None, ..., h=8,
                  valid_lens=None, causal=False) -> dict of fp32 gradients
         dx_q, dx_kv (None for self-attention: x_kv is x_q, dx_q holds the
@@ -40,7 +42,7 @@ import ctypes
 from . import _lib
 from ._lib import MhaError, MHA_BF16, MHA_F32, MHA_OK, Strides
 
-__all__ = ["sdpa_forward", "sdpa_backward", "sdpa_decode", "sdpa_decode_noalloc", "mha_forward", "mha_sublayer_forward", "mha_backward", "workspace_bytes", "kernel_timing", "MhaError", "library"]
+__all__ = ["sdpa_forward", "sdpa_backward", "sdpa_decode", "sdpa_decode_noalloc", "mha_forward", "mha_sublayer_forward", "mha_backward", "mha_forward_train", "workspace_bytes", "kernel_timing", "MhaError", "library"]
 
 
 def library():
@@ -310,13 +312,43 @@ def mha_sublayer_forward(x, w_q, w_k, w_v, w_o, b_q=None, b_k=None, b_v=None, b_
     return out
 
 
+def mha_forward_train(x_q, x_kv, w_q, w_k, w_v, w_o, b_q=None, b_k=None, b_v=None, b_o=None, h=8, valid_lens=None,
+                      causal=False, out_dtype=None, out=None, saved=None):
+    """mha_forward for training (bf16): returns (out, saved), where ``saved``
+    (a uint8 device tensor) holds Q, K, V, the merged heads and each query's
+    log-sum-exp for mha_backward(..., saved=saved)."""
+    torch = _torch()
+    args = dict(x_q=x_q, x_kv=x_kv, w_q=w_q, w_k=w_k, w_v=w_v, w_o=w_o, b_q=b_q, b_k=b_k, b_v=b_v, b_o=b_o)
+    for n, t in args.items():
+        _check_gpu(n, t)
+        if t is not None and (not t.is_contiguous() or t.dtype != x_q.dtype):
+            raise ValueError(f"{n} must be contiguous and share x_q's dtype")
+    B, Lq, D = x_q.shape
+    Lk = x_kv.shape[1]
+    in_dt = _dtype_code(x_q.dtype)
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, Lq, D), dtype=out_dtype, device=x_q.device)
+    lib = _lib.load()
+    need = int(lib.mha_saved_bytes(in_dt, B, Lq, Lk, D, h))
+    if saved is None:
+        saved = torch.empty(max(need, 1), dtype=torch.uint8, device=x_q.device)
+    vl = _valid_lens(valid_lens, B, x_q.device)
+    st = lib.mha_forward_train(in_dt, _dtype_code(out.dtype), _ptr(x_q), _ptr(x_kv), _ptr(w_q), _ptr(b_q), _ptr(w_k),
+                               _ptr(b_k), _ptr(w_v), _ptr(b_v), _ptr(w_o), _ptr(b_o), _ptr(out), B, Lq, Lk, D, h,
+                               D // h if h else 0, _ptr(vl), int(bool(causal)), _ptr(saved), saved.numel(), _stream())
+    _raise(st, "mha_forward_train")
+    return out, saved
+
+
 def mha_backward(x_q, x_kv, w_q, w_k, w_v, w_o, dout, b_q=None, b_k=None, b_v=None, h=8, valid_lens=None,
-                 causal=False, bias_grads=None, workspace=None):
+                 causal=False, bias_grads=None, workspace=None, saved=None):
     """Gradients of mha_forward (bf16) for the output gradient ``dout``
     [B, Lq, d_model]: a dict of fp32 tensors dx_q, dx_kv, dw_q, dw_k, dw_v,
     dw_o and, with ``bias_grads`` (default: when b_q is given), db_q, db_k,
     db_v, db_o.  When x_kv is x_q (self-attention) dx_kv is None and dx_q is
-    the input's whole gradient."""
+    the input's whole gradient.  With ``saved`` from mha_forward_train (same
+    inputs) the forward is not recomputed."""
     torch = _torch()
     args = dict(x_q=x_q, x_kv=x_kv, w_q=w_q, w_k=w_k, w_v=w_v, w_o=w_o, dout=dout, b_q=b_q, b_k=b_k, b_v=b_v)
     for n, t in args.items():
@@ -336,17 +368,24 @@ def mha_backward(x_q, x_kv, w_q, w_k, w_v, w_o, dout, b_q=None, b_k=None, b_v=No
         r["db_" + n] = torch.empty((D,), **f32) if bias_grads else None
     lib = _lib.load()
     in_dt = _dtype_code(x_q.dtype)
-    need = int(lib.mha_backward_workspace_bytes(in_dt, B, Lq, Lk, D, h))
+    size_fn = lib.mha_backward_workspace_bytes if saved is None else lib.mha_backward_saved_workspace_bytes
+    need = int(size_fn(in_dt, B, Lq, Lk, D, h))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     vl = _valid_lens(valid_lens, B, dev)
-    st = lib.mha_backward(in_dt, _ptr(x_q), _ptr(x_kv), _ptr(w_q), _ptr(b_q), _ptr(w_k), _ptr(b_k), _ptr(w_v),
-                          _ptr(b_v), _ptr(w_o), _ptr(dout), _ptr(r["dx_q"]), _ptr(r["dx_kv"]),
-                          _ptr(r["dw_q"]), _ptr(r["db_q"]), _ptr(r["dw_k"]), _ptr(r["db_k"]),
-                          _ptr(r["dw_v"]), _ptr(r["db_v"]), _ptr(r["dw_o"]), _ptr(r["db_o"]),
-                          B, Lq, Lk, D, h, D // h if h else 0, _ptr(vl), int(bool(causal)),
-                          _ptr(workspace), workspace.numel(), _stream())
-    _raise(st, "mha_backward")
+    grads = [_ptr(r["dx_q"]), _ptr(r["dx_kv"]), _ptr(r["dw_q"]), _ptr(r["db_q"]), _ptr(r["dw_k"]), _ptr(r["db_k"]),
+             _ptr(r["dw_v"]), _ptr(r["db_v"]), _ptr(r["dw_o"]), _ptr(r["db_o"])]
+    tail = [B, Lq, Lk, D, h, D // h if h else 0, _ptr(vl), int(bool(causal)), _ptr(workspace), workspace.numel(),
+            _stream()]
+    if saved is None:
+        st = lib.mha_backward(in_dt, _ptr(x_q), _ptr(x_kv), _ptr(w_q), _ptr(b_q), _ptr(w_k), _ptr(b_k), _ptr(w_v),
+                              _ptr(b_v), _ptr(w_o), _ptr(dout), *grads, *tail)
+        _raise(st, "mha_backward")
+    else:
+        _check_gpu("saved", saved)
+        st = lib.mha_backward_saved(in_dt, _ptr(x_q), _ptr(x_kv), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o),
+                                    _ptr(saved), saved.numel() * saved.element_size(), _ptr(dout), *grads, *tail)
+        _raise(st, "mha_backward_saved")
     return r
 
 

@@ -22,7 +22,8 @@ EXPORTED = ("sdpa_forward", "sdpa_forward_lse", "sdpa_forward_ex", "sdpa_backwar
             "sdpa_backward_lse",
             "sdpa_decode_workspace_bytes", "sdpa_decode", "sdpa_decode_noalloc", "mha_workspace_bytes",
             "mha_workspace_bytes_ex", "mha_forward", "mha_forward_ex", "mha_sublayer_workspace_bytes",
-            "mha_sublayer_forward", "mha_backward_workspace_bytes", "mha_backward", "mha_status_string",
+            "mha_sublayer_forward", "mha_backward_workspace_bytes", "mha_backward", "mha_saved_bytes",
+            "mha_forward_train", "mha_backward_saved_workspace_bytes", "mha_backward_saved", "mha_status_string",
             "mha_timing_enable",
             "mha_timing_read")
 
@@ -78,6 +79,14 @@ def load():
     lib.mha_forward.restype = i
     lib.mha_forward.argtypes = [i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 i, i, i, i, i, i, vp, i, vp, sz, vp]
+    lib.mha_saved_bytes.restype = sz
+    lib.mha_saved_bytes.argtypes = [i, i, i, i, i, i]
+    lib.mha_forward_train.restype = i
+    lib.mha_forward_train.argtypes = [i, i] + [vp] * 11 + [i] * 6 + [vp, i, vp, sz, vp]
+    lib.mha_backward_saved_workspace_bytes.restype = sz
+    lib.mha_backward_saved_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.mha_backward_saved.restype = i
+    lib.mha_backward_saved.argtypes = [i] + [vp] * 6 + [vp, sz] + [vp] * 11 + [i] * 6 + [vp, i, vp, sz, vp]
     lib.mha_backward_workspace_bytes.restype = sz
     lib.mha_backward_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.mha_backward.restype = i

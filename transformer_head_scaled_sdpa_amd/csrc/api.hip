@@ -764,12 +764,19 @@ namespace {
 // block for the fused input gradient of self-attention, or dQ [Mq, D] then
 // [dK | dV] [Mk, 2D]), the transposed weights (bf16: W_o^T, then W_q^T,
 // W_k^T, W_v^T side by side or apart) and the weight-gradient partials.
+// With `forward` false the forward's tensors (Q, K, V, merged heads,
+// log-sum-exp) are not in the workspace: they come from mha_forward_train's
+// saved buffer, whose layout is the same five segments (SavedLayout).
 struct BwdLayout {
     size_t q, k, v, ocat, docat, lse, rows, dqkv, dkv, wt, tn, total;
 };
 
-BwdLayout bwd_layout(int B, int Lq, int Lk, int D, int h) {
-    BwdLayout L{};
+struct SavedLayout {
+    size_t q, k, v, ocat, lse, total;
+};
+
+SavedLayout saved_layout(int B, int Lq, int Lk, int D, int h) {
+    SavedLayout L{};
     size_t off = 0;
     auto take = [&](size_t n) {
         const size_t o = off;
@@ -781,8 +788,30 @@ BwdLayout bwd_layout(int B, int Lq, int Lk, int D, int h) {
     L.k = take(mk);
     L.v = take(mk);
     L.ocat = take(mq);
-    L.docat = take(mq);
     L.lse = take((size_t)B * h * Lq * 4);
+    L.total = off;
+    return L;
+}
+
+BwdLayout bwd_layout(int B, int Lq, int Lk, int D, int h, bool forward = true) {
+    BwdLayout L{};
+    size_t off = 0;
+    if (forward) {
+        const SavedLayout S = saved_layout(B, Lq, Lk, D, h);
+        L.q = S.q;
+        L.k = S.k;
+        L.v = S.v;
+        L.ocat = S.ocat;
+        L.lse = S.lse;
+        off = S.total;
+    }
+    auto take = [&](size_t n) {
+        const size_t o = off;
+        off = round_up(off + n, 256);
+        return o;
+    };
+    const size_t mq = (size_t)B * Lq * D * 2, mk = (size_t)B * Lk * D * 2;
+    L.docat = take(mq);
     L.rows = take(mha::backward_workspace_bytes(B, h, Lq));
     L.dqkv = take(round_up(mq, 256) + 2 * mk);
     L.dkv = L.dqkv + round_up(mq, 256);
@@ -793,31 +822,30 @@ BwdLayout bwd_layout(int B, int Lq, int Lk, int D, int h) {
     return L;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t mha_backward_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h) {
-    if (in_dt != MHA_BF16 || B < 0 || Lq < 0 || Lk < 0 || d_model <= 0 || h <= 0 || d_model % h) return 0;
-    if (d_model % 64 || !mha_rows_fit(B, Lq, 6 * d_model) || !mha_rows_fit(B, Lk, 6 * d_model)) return 0;
-    return bwd_layout(B, Lq, Lk, d_model, h).total;
+// Sizes the multi-head training entry points accept (shared checks).
+bool mha_train_sizes_ok(int B, int Lq, int Lk, int d_model, int h) {
+    return B >= 0 && Lq >= 0 && Lk >= 0 && d_model > 0 && h > 0 && d_model % h == 0 && d_model % 64 == 0 &&
+           mha_rows_fit(B, Lq, 6 * d_model) && mha_rows_fit(B, Lk, 6 * d_model);
 }
 
-mha_status mha_backward(mha_dtype in_dt,
-                        const void* x_q, const void* x_kv,
-                        const void* w_q, const void* b_q,
-                        const void* w_k, const void* b_k,
-                        const void* w_v, const void* b_v,
-                        const void* w_o,
-                        const void* dout,
-                        float* dx_q, float* dx_kv,
-                        float* dw_q, float* db_q,
-                        float* dw_k, float* db_k,
-                        float* dw_v, float* db_v,
-                        float* dw_o, float* db_o,
-                        int B, int Lq, int Lk, int d_model, int h, int d_k,
-                        const int* valid_lens, int causal,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+// mha_backward (saved == nullptr: the forward is recomputed into the
+// workspace) and mha_backward_saved (the forward's tensors from `saved`).
+mha_status mha_backward_impl(mha_dtype in_dt,
+                             const void* x_q, const void* x_kv,
+                             const void* w_q, const void* b_q,
+                             const void* w_k, const void* b_k,
+                             const void* w_v, const void* b_v,
+                             const void* w_o,
+                             const void* saved, size_t saved_bytes,
+                             const void* dout,
+                             float* dx_q, float* dx_kv,
+                             float* dw_q, float* db_q,
+                             float* dw_k, float* db_k,
+                             float* dw_v, float* db_v,
+                             float* dw_o, float* db_o,
+                             int B, int Lq, int Lk, int d_model, int h, int d_k,
+                             const int* valid_lens, int causal,
+                             void* workspace, size_t workspace_bytes, void* stream, bool use_saved) {
     if (!valid_dtype(in_dt)) return MHA_EINVAL;
     if (B < 0 || Lq < 0 || Lk <= 0 || d_model <= 0 || h <= 0 || d_k <= 0) return MHA_EINVAL;
     if ((long long)h * d_k != d_model) return MHA_EINVAL;
@@ -879,7 +907,10 @@ mha_status mha_backward(mha_dtype in_dt,
         if (!ptrs[x] && x < 8) return MHA_EINVAL;
         if (ptrs[x] && !aligned16(ptrs[x])) return MHA_EINVAL;
     }
-    const BwdLayout L = bwd_layout(B, Lq, Lk, D, h);
+    if (use_saved && (!saved || !aligned16(saved))) return MHA_EINVAL;
+    const SavedLayout SL = saved_layout(B, Lq, Lk, D, h);
+    if (use_saved && saved_bytes < SL.total) return MHA_EWORKSPACE;
+    const BwdLayout L = bwd_layout(B, Lq, Lk, D, h, !use_saved);
     if (workspace_bytes < L.total) return MHA_EWORKSPACE;
     const size_t dw2 = (size_t)D * D * 2;
     const Range ins[] = {rng(x_q, (size_t)B * Lq * D * 2), rng(x_kv, (size_t)B * Lk * D * 2), rng(w_q, dw2),
@@ -887,22 +918,28 @@ mha_status mha_backward(mha_dtype in_dt,
                          rng(b_q, b_q ? (size_t)D * 2 : 0), rng(b_k, b_k ? (size_t)D * 2 : 0),
                          rng(b_v, b_v ? (size_t)D * 2 : 0)};
     const Range rws = rng(workspace, L.total);
+    const Range rsv = rng(saved, use_saved ? SL.total : 0);
     for (int x = 0; x < n_out; ++x) {
-        if (overlap(outs[x], rws)) return MHA_EINVAL;
+        if (overlap(outs[x], rws) || overlap(outs[x], rsv)) return MHA_EINVAL;
         for (const Range& r : ins)
             if (overlap(outs[x], r)) return MHA_EINVAL;
     }
     for (const Range& r : ins)
         if (overlap(rws, r)) return MHA_EINVAL;
+    if (overlap(rws, rsv)) return MHA_EINVAL;
 
     using mha::bf16_t;
     char* w = static_cast<char*>(workspace);
-    bf16_t* Q = reinterpret_cast<bf16_t*>(w + L.q);
-    bf16_t* K = reinterpret_cast<bf16_t*>(w + L.k);
-    bf16_t* V = reinterpret_cast<bf16_t*>(w + L.v);
-    bf16_t* Ocat = reinterpret_cast<bf16_t*>(w + L.ocat);
+    // The forward's tensors: recomputed into the workspace, or the saved ones.
+    char* fw = use_saved ? static_cast<char*>(const_cast<void*>(saved)) : w;
+    const size_t oq = use_saved ? SL.q : L.q, ok = use_saved ? SL.k : L.k, ov = use_saved ? SL.v : L.v;
+    const size_t oo = use_saved ? SL.ocat : L.ocat, ol = use_saved ? SL.lse : L.lse;
+    bf16_t* Q = reinterpret_cast<bf16_t*>(fw + oq);
+    bf16_t* K = reinterpret_cast<bf16_t*>(fw + ok);
+    bf16_t* V = reinterpret_cast<bf16_t*>(fw + ov);
+    bf16_t* Ocat = reinterpret_cast<bf16_t*>(fw + oo);
     bf16_t* dOcat = reinterpret_cast<bf16_t*>(w + L.docat);
-    float* lse = reinterpret_cast<float*>(w + L.lse);
+    float* lse = reinterpret_cast<float*>(fw + ol);
     bf16_t* dQ = reinterpret_cast<bf16_t*>(w + L.dqkv);
     // [dK | dV]: right of dQ in the [M, 3D] block, or its own [Mk, 2D] block.
     bf16_t* dKV = fused_dx ? dQ + D : reinterpret_cast<bf16_t*>(w + L.dkv);
@@ -933,6 +970,7 @@ mha_status mha_backward(mha_dtype in_dt,
     e = timed("bwd_transpose_w", s, [&] { return mha::launch_transpose_bf16(t, s); });
     if (e != hipSuccess) return MHA_EHIP;
 
+    if (!use_saved) {
     // 2. The forward's Q, K, V (bf16) in one launch.
     mha::GemmArgs g;
     g.nprob = 3;
@@ -957,6 +995,7 @@ mha_status mha_backward(mha_dtype in_dt,
     a.lse = lse;
     e = timed("bwd_attn_forward", s, [&] { return mha::launch_sdpa_bf16(a, false, s); });
     if (e != hipSuccess) return MHA_EHIP;
+    }
 
     // 4. dOcat = dout W_o (bf16).
     mha::GemmArgs go;
@@ -1027,6 +1066,144 @@ mha_status mha_backward(mha_dtype in_dt,
     tn.p[2].dw = dw_k; tn.p[2].db = db_k;
     tn.p[2].dw2 = dw_v; tn.p[2].db2 = db_v;
     e = timed("bwd_dw", s, [&] { return mha::launch_gemm_tn(tn, w + L.tn, s); });
+    return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mha_backward_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h) {
+    if (in_dt != MHA_BF16 || !mha_train_sizes_ok(B, Lq, Lk, d_model, h)) return 0;
+    return bwd_layout(B, Lq, Lk, d_model, h).total;
+}
+
+size_t mha_backward_saved_workspace_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h) {
+    if (in_dt != MHA_BF16 || !mha_train_sizes_ok(B, Lq, Lk, d_model, h)) return 0;
+    return bwd_layout(B, Lq, Lk, d_model, h, false).total;
+}
+
+size_t mha_saved_bytes(mha_dtype in_dt, int B, int Lq, int Lk, int d_model, int h) {
+    if (in_dt != MHA_BF16 || !mha_train_sizes_ok(B, Lq, Lk, d_model, h)) return 0;
+    return saved_layout(B, Lq, Lk, d_model, h).total;
+}
+
+mha_status mha_backward(mha_dtype in_dt,
+                        const void* x_q, const void* x_kv,
+                        const void* w_q, const void* b_q,
+                        const void* w_k, const void* b_k,
+                        const void* w_v, const void* b_v,
+                        const void* w_o,
+                        const void* dout,
+                        float* dx_q, float* dx_kv,
+                        float* dw_q, float* db_q,
+                        float* dw_k, float* db_k,
+                        float* dw_v, float* db_v,
+                        float* dw_o, float* db_o,
+                        int B, int Lq, int Lk, int d_model, int h, int d_k,
+                        const int* valid_lens, int causal,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    return mha_backward_impl(in_dt, x_q, x_kv, w_q, b_q, w_k, b_k, w_v, b_v, w_o, nullptr, 0, dout, dx_q, dx_kv,
+                             dw_q, db_q, dw_k, db_k, dw_v, db_v, dw_o, db_o, B, Lq, Lk, d_model, h, d_k, valid_lens,
+                             causal, workspace, workspace_bytes, stream, false);
+}
+
+mha_status mha_backward_saved(mha_dtype in_dt,
+                              const void* x_q, const void* x_kv,
+                              const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                              const void* saved, size_t saved_bytes,
+                              const void* dout,
+                              float* dx_q, float* dx_kv,
+                              float* dw_q, float* db_q,
+                              float* dw_k, float* db_k,
+                              float* dw_v, float* db_v,
+                              float* dw_o, float* db_o,
+                              int B, int Lq, int Lk, int d_model, int h, int d_k,
+                              const int* valid_lens, int causal,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    return mha_backward_impl(in_dt, x_q, x_kv, w_q, nullptr, w_k, nullptr, w_v, nullptr, w_o, saved, saved_bytes, dout,
+                             dx_q, dx_kv, dw_q, db_q, dw_k, db_k, dw_v, db_v, dw_o, db_o, B, Lq, Lk, d_model, h, d_k,
+                             valid_lens, causal, workspace, workspace_bytes, stream, true);
+}
+
+mha_status mha_forward_train(mha_dtype in_dt, mha_dtype out_dt,
+                             const void* x_q, const void* x_kv,
+                             const void* w_q, const void* b_q,
+                             const void* w_k, const void* b_k,
+                             const void* w_v, const void* b_v,
+                             const void* w_o, const void* b_o,
+                             void* out,
+                             int B, int Lq, int Lk, int d_model, int h, int d_k,
+                             const int* valid_lens, int causal,
+                             void* saved, size_t saved_bytes, void* stream) {
+    if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return MHA_EINVAL;
+    if (B < 0 || Lq < 0 || Lk <= 0 || d_model <= 0 || h <= 0 || d_k <= 0) return MHA_EINVAL;
+    if ((long long)h * d_k != d_model) return MHA_EINVAL;
+    if (causal && Lq != Lk) return MHA_EINVAL;
+    if (d_k != kHeadDim || in_dt != MHA_BF16) return MHA_ENOTSUP;
+    if (!mha_train_sizes_ok(B, Lq, Lk, d_model, h)) return MHA_ENOTSUP;
+    if (B == 0 || Lq == 0) return MHA_OK;
+    const int D = d_model;
+    const void* ptrs[] = {x_q, x_kv, w_q, w_k, w_v, w_o, out, saved, b_q, b_k, b_v, b_o};
+    for (int x = 0; x < 12; ++x) {
+        if (!ptrs[x] && x < 8) return MHA_EINVAL;
+        if (ptrs[x] && !aligned16(ptrs[x])) return MHA_EINVAL;
+    }
+    const SavedLayout SL = saved_layout(B, Lq, Lk, D, h);
+    if (saved_bytes < SL.total) return MHA_EWORKSPACE;
+    auto rng = [](const void* p, size_t n) {
+        const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+        return Range{b, b + n};
+    };
+    const size_t dw2 = (size_t)D * D * 2;
+    const Range ins[] = {rng(x_q, (size_t)B * Lq * D * 2), rng(x_kv, (size_t)B * Lk * D * 2), rng(w_q, dw2),
+                         rng(w_k, dw2), rng(w_v, dw2), rng(w_o, dw2), rng(b_q, b_q ? (size_t)D * 2 : 0),
+                         rng(b_k, b_k ? (size_t)D * 2 : 0), rng(b_v, b_v ? (size_t)D * 2 : 0),
+                         rng(b_o, b_o ? (size_t)D * 2 : 0)};
+    const Range rout = rng(out, (size_t)B * Lq * D * elem_size(out_dt)), rsv = rng(saved, SL.total);
+    if (overlap(rout, rsv)) return MHA_EINVAL;
+    for (const Range& r : ins)
+        if (overlap(rout, r) || overlap(rsv, r)) return MHA_EINVAL;
+
+    using mha::bf16_t;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* sv = static_cast<char*>(saved);
+    bf16_t* Q = reinterpret_cast<bf16_t*>(sv + SL.q);
+    bf16_t* K = reinterpret_cast<bf16_t*>(sv + SL.k);
+    bf16_t* V = reinterpret_cast<bf16_t*>(sv + SL.v);
+    bf16_t* Ocat = reinterpret_cast<bf16_t*>(sv + SL.ocat);
+    float* lse = reinterpret_cast<float*>(sv + SL.lse);
+    hipError_t e;
+    // 1. Q, K, V (bf16) in one launch.
+    mha::GemmArgs g;
+    g.nprob = 3;
+    g.N = D;
+    g.K = D;
+    g.p[0] = {x_q, w_q, b_q, Q, B * Lq};
+    g.p[1] = {x_kv, w_k, b_k, K, B * Lk};
+    g.p[2] = {x_kv, w_v, b_v, V, B * Lk};
+    e = timed("train_qkv_proj", s, [&] { return mha::launch_gemm_bf16(g, false, s); });
+    if (e != hipSuccess) return MHA_EHIP;
+    // 2. Attention on the head views: merged heads and log-sum-exp.
+    mha::SdpaArgs a;
+    a.q = Q; a.k = K; a.v = V; a.o = Ocat;
+    a.sq[0] = (long long)Lq * D; a.sq[1] = kHeadDim; a.sq[2] = D;
+    a.sk[0] = (long long)Lk * D; a.sk[1] = kHeadDim; a.sk[2] = D;
+    a.sv[0] = (long long)Lk * D; a.sv[1] = kHeadDim; a.sv[2] = D;
+    a.so[0] = (long long)Lq * D; a.so[1] = kHeadDim; a.so[2] = D;
+    a.B = B; a.H = h; a.Lq = Lq; a.Lk = Lk;
+    a.valid_lens = valid_lens;
+    a.causal = causal ? 1 : 0;
+    a.lse = lse;
+    e = timed("train_attn", s, [&] { return mha::launch_sdpa_bf16(a, false, s); });
+    if (e != hipSuccess) return MHA_EHIP;
+    // 3. Output projection.
+    mha::GemmArgs go;
+    go.nprob = 1;
+    go.N = D;
+    go.K = D;
+    go.p[0] = {Ocat, w_o, b_o, out, B * Lq};
+    e = timed("train_out_proj", s, [&] { return mha::launch_gemm_bf16(go, out_dt == MHA_F32, s); });
     return hip_status(e);
 }
 
