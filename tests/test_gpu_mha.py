@@ -106,6 +106,32 @@ def test_mha_bf16_projected_route_large_logits():
     print("vs fp64 oracle", e)
 
 
+# Projections large enough for the 256 x 256 GEMM tiles: self-attention
+# (Q/K/V over one input) with a row count past the last full tile, and
+# cross-attention whose query projection, key/value projections and output
+# projection all take them, the last two with ragged row counts.  The oracle
+# checks sampled rows of every batch.
+LARGE_PROJECTION_CASES = [
+    # B, Lq, Lk, D, h, self_attn, lengths
+    (2, 5500, 5500, 512, 8, True, [5500, 3001]),
+    (2, 8200, 300, 1024, 16, False, [300, 17]),
+]
+
+
+@pytest.mark.parametrize("B,Lq,Lk,D,h,self_attn,lens", LARGE_PROJECTION_CASES)
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_mha_bf16_large_projections(B, Lq, Lk, D, h, self_attn, lens, out_f32):
+    from parity import sample_rows
+    inp = workloads.make_mha_inputs(B, Lq, Lk, D, h, "bf16", seed=9100 + Lq, vl_range=(1, Lk),
+                                    self_attn=self_attn, bias=True)
+    inp.valid_lens = np.array(lens, dtype=np.int32)
+    g = run_gpu(inp, out_f32)
+    rows = sample_rows(Lq, 40, np.random.Generator(np.random.PCG64(Lq)))
+    e = assert_bf16(g[:, rows], run_oracle(inp, bf16_stages=False, rows=rows),
+                    f"mha bf16 large projections B{B} Lq{Lq} Lk{Lk} D{D}")
+    print("vs fp64 oracle", e)
+
+
 MHA_F32_CASES = [
     (2, 10, 10, 512, 8, False, (3, 10), False, True),
     (2, 33, 45, 256, 4, False, (0, 45), True, False),
