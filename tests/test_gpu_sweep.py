@@ -1,0 +1,107 @@
+"""A seeded sweep of odd shapes through the bf16 entry points against the
+fp64 oracle: query and key counts on either side of the kernels' tile edges
+(32, 64, 128, 256), Lq different from Lk, lengths of 0, 1, the full count
+and past it, with and without the causal rule, both output dtypes.  The
+shapes come from a fixed generator, so every run checks the same cases."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import assert_bf16, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+EDGES = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300]
+
+
+def _cases(n, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for c in range(n):
+        B = int(rng.integers(1, 4))
+        causal = bool(rng.integers(0, 2))
+        Lq = int(rng.choice(EDGES))
+        Lk = Lq if causal else int(rng.choice(EDGES))
+        kind = int(rng.integers(0, 4))          # 0: none, 1: random, 2: with 0 and full, 3: past the end
+        if kind == 0:
+            lens = None
+        elif kind == 1:
+            lens = rng.integers(1, Lk + 1, size=B).tolist()
+        elif kind == 2:
+            lens = ([0, Lk] + rng.integers(1, Lk + 1, size=B).tolist())[:B]
+        else:
+            lens = (Lk + rng.integers(1, 50, size=B)).tolist()
+        out.append((c, B, Lq, Lk, causal, lens))
+    return out
+
+
+SDPA_CASES = _cases(24, 2024)
+
+
+@pytest.mark.parametrize("c,B,Lq,Lk,causal,lens", SDPA_CASES)
+def test_sweep_sdpa_bf16(c, B, Lq, Lk, causal, lens):
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    h = 1 + c % 3
+    inp = workloads.make_sdpa_inputs(B, h, Lq, Lk, 64, "bf16", seed=500 + c)
+    vl = None if lens is None else np.array(lens, dtype=np.int32)
+    q, k, v = (inp.tensors[n] for n in ("q", "k", "v"))
+    out_dtype = torch.float32 if c % 2 else torch.bfloat16
+    o = mha.sdpa_forward(to_device(q, torch.bfloat16), to_device(k, torch.bfloat16), to_device(v, torch.bfloat16),
+                         valid_lens=vl, causal=causal, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    e = assert_bf16(to_host(o), oracle.sdpa(q, k, v, valid_lens=vl, causal=causal),
+                    f"sweep sdpa case {c}: B{B} h{h} Lq{Lq} Lk{Lk} causal{int(causal)} lengths {lens}")
+    print(c, e)
+
+
+MHA_CASES = _cases(12, 77)
+
+
+@pytest.mark.parametrize("c,B,Lq,Lk,causal,lens", MHA_CASES)
+def test_sweep_mha_bf16(c, B, Lq, Lk, causal, lens):
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    h = 1 + c % 4
+    D = 64 * h
+    self_attn = causal or c % 3 == 0
+    if self_attn:
+        Lk = Lq
+        if lens is not None:
+            lens = [min(x, Lq + 7) if x > Lq else x for x in lens]
+    inp = workloads.make_mha_inputs(B, Lq, Lk, D, h, "bf16", seed=900 + c, causal=causal, self_attn=self_attn,
+                                    bias=c % 2 == 0)
+    vl = None if lens is None else np.array(lens, dtype=np.int32)
+    t = {n: (None if a is None else to_device(a, torch.bfloat16)) for n, a in inp.tensors.items()}
+    if self_attn:
+        t["x_kv"] = t["x_q"]
+    out = mha.mha_forward(t["x_q"], t["x_kv"], t["w_q"], t["w_k"], t["w_v"], t["w_o"], t["b_q"], t["b_k"], t["b_v"],
+                          t["b_o"], h=h, valid_lens=vl, causal=causal, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    r = inp.tensors
+    ref = oracle.mha(r["x_q"], r["x_kv"], r["w_q"], r["w_k"], r["w_v"], r["w_o"], r["b_q"], r["b_k"], r["b_v"], r["b_o"],
+                     h=h, valid_lens=vl, causal=causal)
+    e = assert_bf16(to_host(out), ref,
+                    f"sweep mha case {c}: B{B} Lq{Lq} Lk{Lk} D{D} causal{int(causal)} lengths {lens}")
+    print(c, e)
+
+
+DECODE_CASES = [(c, B, Lk, lens) for c, B, Lq, Lk, causal, lens in _cases(10, 5)]
+
+
+@pytest.mark.parametrize("c,B,L,lens", DECODE_CASES)
+def test_sweep_decode_bf16(c, B, L, lens):
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    h = 1 + c % 4
+    inp = workloads.make_sdpa_inputs(B, h, 1, L, 64, "bf16", seed=1300 + c)
+    lens = lens if lens is not None else [L] * B
+    vl = np.array(lens, dtype=np.int32)
+    q, k, v = (inp.tensors[n] for n in ("q", "k", "v"))
+    o = mha.sdpa_decode(to_device(q[:, :, 0], torch.bfloat16), to_device(k, torch.bfloat16),
+                        to_device(v, torch.bfloat16), vl)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa(q, k, v, valid_lens=vl)[:, :, 0]
+    e = assert_bf16(to_host(o), ref, f"sweep decode case {c}: B{B} h{h} L{L} lengths {lens}")
+    print(c, e)
