@@ -1,8 +1,9 @@
 """A seeded sweep of odd shapes through the bf16 entry points against the
 fp64 oracle: query and key counts on either side of the kernels' tile edges
 (32, 64, 128, 256), Lq different from Lk, lengths of 0, 1, the full count
-and past it, with and without the causal rule, both output dtypes.  The
-shapes come from a fixed generator, so every run checks the same cases."""
+and past it, with and without the causal rule, both output dtypes; the
+attention core's backward on both of its statistic paths.  The shapes come
+from a fixed generator, so every run checks the same cases."""
 import numpy as np
 import pytest
 
@@ -105,3 +106,29 @@ def test_sweep_decode_bf16(c, B, L, lens):
     ref = oracle.sdpa(q, k, v, valid_lens=vl)[:, :, 0]
     e = assert_bf16(to_host(o), ref, f"sweep decode case {c}: B{B} h{h} L{L} lengths {lens}")
     print(c, e)
+
+
+BWD_CASES = _cases(16, 4242)
+
+
+@pytest.mark.parametrize("c,B,Lq,Lk,causal,lens", BWD_CASES)
+def test_sweep_backward_bf16(c, B, Lq, Lk, causal, lens):
+    """sdpa_backward on both of its paths (the statistic found in its own
+    pass, and given by the forward) against the oracle's gradients."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    h = 1 + c % 3
+    rng = np.random.Generator(np.random.PCG64(7700 + c))
+    q, k, v, g = (workloads._finish(rng.standard_normal((B, h, L, 64)), "bf16") for L in (Lq, Lk, Lk, Lq))
+    vl = None if lens is None else np.array(lens, dtype=np.int32)
+    tq, tk, tv, tg = (to_device(x, torch.bfloat16) for x in (q, k, v, g))
+    o, lse = mha.sdpa_forward(tq, tk, tv, valid_lens=vl, causal=causal, return_lse=True)
+    own = mha.sdpa_backward(tq, tk, tv, o, tg, valid_lens=vl, causal=causal, out_dtype=torch.float32)
+    given = mha.sdpa_backward(tq, tk, tv, o, tg, valid_lens=vl, causal=causal, out_dtype=torch.float32, lse=lse)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa_backward(q, k, v, g, valid_lens=vl, causal=causal)
+    for path, grads in (("own statistic", own), ("forward statistic", given)):
+        for name, got, r in zip(("dq", "dk", "dv"), grads, ref):
+            e = assert_bf16(to_host(got), r, f"sweep backward case {c} ({path}) {name}: B{B} h{h} Lq{Lq} Lk{Lk} "
+                                             f"causal{int(causal)} lengths {lens}")
+            print(c, path, name, e)
