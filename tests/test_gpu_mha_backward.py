@@ -68,6 +68,12 @@ def check(got, inp, g, what, storage_diag=True):
                 print(what, n, b, e)
             continue
         scale = max(rms(ref[n]), rms(ref["dw_" + n[-1]])) if n.startswith("db_") else rms(ref[n])
+        if scale == 0.0 and n[-1] in "qk":
+            # Every row has one allowed key: the softmax is the constant 1
+            # and passes Q and K no gradient.  The GPU's is the rounding
+            # left where dP and its row sum cancel; those terms have the
+            # size of the value gradient.
+            scale = rms(ref["dw_v"])
         e = assert_grad_bf16(got[n], ref[n], scale, f"{what} {n}")
         e16 = float(np.max(np.abs(got[n] - ref16[n])) / scale)
         print(what, n, "vs fp64", e, "max vs bf16-storage", e16 if storage_diag else "-")

@@ -2,7 +2,8 @@
 fp64 oracle: query and key counts on either side of the kernels' tile edges
 (32, 64, 128, 256), Lq different from Lk, lengths of 0, 1, the full count
 and past it, with and without the causal rule, both output dtypes; the
-attention core's backward on both of its statistic paths.  The shapes come
+attention core's backward on both of its statistic paths, and the layer's
+training pair against its recomputing backward.  The shapes come
 from a fixed generator, so every run checks the same cases."""
 import numpy as np
 import pytest
@@ -10,6 +11,8 @@ import pytest
 import oracle
 import workloads
 from parity import assert_bf16, to_device, to_host
+from test_gpu_mha_backward import GRADS, check, make
+from test_gpu_mha_train import oracle_out, run_pair
 
 pytestmark = pytest.mark.gpu
 
@@ -132,3 +135,32 @@ def test_sweep_backward_bf16(c, B, Lq, Lk, causal, lens):
             e = assert_bf16(to_host(got), r, f"sweep backward case {c} ({path}) {name}: B{B} h{h} Lq{Lq} Lk{Lk} "
                                              f"causal{int(causal)} lengths {lens}")
             print(c, path, name, e)
+
+
+LAYER_BWD_CASES = _cases(10, 31337)
+
+
+@pytest.mark.parametrize("c,B,Lq,Lk,causal,lens", LAYER_BWD_CASES)
+def test_sweep_layer_backward_bf16(c, B, Lq, Lk, causal, lens):
+    """mha_forward_train, mha_backward_saved and mha_backward on odd shapes:
+    the output and every gradient against the oracle, and the saved-tensor
+    gradients equal, bit for bit, to the recomputing backward's."""
+    h = 1 + c % 4
+    D = 64 * h
+    self_attn = causal or c % 3 == 0
+    if self_attn:
+        Lk = Lq
+        if lens is not None:
+            lens = [min(x, Lq + 7) if x > Lq else x for x in lens]
+    inp, g = make(B, Lq, Lk, D, h, causal, None, c % 2 == 0, self_attn, seed=2600 + c)
+    inp.valid_lens = None if lens is None else np.array(lens, dtype=np.int32)
+    what = f"sweep layer backward case {c}: B{B} Lq{Lq} Lk{Lk} D{D} causal{int(causal)} lengths {lens}"
+    out, kept, again = run_pair(inp, g, out_f32=c % 2 == 1)
+    e = assert_bf16(out, oracle_out(inp, False), what + " output")
+    print(what, "output", e)
+    for n in GRADS:
+        if again[n] is None:
+            assert kept[n] is None, n
+            continue
+        np.testing.assert_array_equal(kept[n], again[n], err_msg=f"{what} {n}: saved vs recomputed forward")
+    check(again, inp, g, what, storage_diag=False)
