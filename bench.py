@@ -694,11 +694,15 @@ def extras(result, args, w):
     dinp = workloads.make_inputs(dw)
     df = PreparedDecode(dinp)
     dms, _ = time_steps(df, 200, 20)
+    dk = sum(kernel_times(df, 20, args.repeat).values())
     f, b = decode_alg(dw, dinp.valid_lens)
     result["decode_step"] = {
         "workload": dw.description, "avg_us": round(dms * 1e3, 2),
         "alg_GBs": round(b / (dms * 1e-3) / 1e9, 1),
-        "frac_hbm_peak": round(b / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        "frac_hbm_peak": round(b / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "kernel_us": round(dk * 1e3, 2), "kernel_frac_hbm_peak": round(b / (dk * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "note": "avg_us: calls issued back to back from Python; kernel_us: the library's events around "
+                "back-to-back launches of the kernel alone"}
     del df
 
     ew = workloads.BY_NAME["encoder_self"]
@@ -777,14 +781,17 @@ def extras(result, args, w):
     iw = workloads.BY_NAME["inspect_weights"]
     iinp = workloads.make_inputs(iw)
     wf = PreparedWeights(iinp)
-    wms, _ = time_steps(wf, 20, 5)
+    sms_w, _ = time_steps(wf, 20, 5)
+    wms = sum(kernel_times(wf, 10, args.repeat).values())
     wbytes = iw.B * iw.h * (iw.Lq * iw.Lk * 4 + (2 * iw.Lq + 2 * iw.Lk) * iw.d_k * 2)
     wfl = 4 * iw.d_k * allowed_pairs(iw, iinp.valid_lens)
     result["sdpa_weights"] = {
         "workload": iw.description, "avg_us": round(wms * 1e3, 2), "bound": "hbm",
         "GBs": round(wbytes / (wms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(wbytes / (wms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "alg_tflops": round(wfl / (wms * 1e-3) / 1e12, 2),
-        "note": "bytes: fp32 weights written plus q, k, v read and o written; tflops: 4*d_k per allowed pair"}
+        "alg_tflops": round(wfl / (wms * 1e-3) / 1e12, 2), "step_us": round(sms_w * 1e3, 2),
+        "note": "avg_us: the library's events around back-to-back launches of the kernel; step_us: calls issued "
+                "back to back from Python (bound by the host's call overhead when the kernel is shorter); bytes: "
+                "fp32 weights written plus q, k, v read and o written; tflops: 4*d_k per allowed pair"}
     del wf
 
 
