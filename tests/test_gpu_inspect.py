@@ -154,10 +154,17 @@ def test_inspect_weights_workload_full_size():
     (1, 2, 70, True, None),       # rows of 70 weights: the last 16-byte piece of a row is partial
     (2, 3, 150, False, "1d"),
     (2, 2, 99, True, "2d"),
+    (2, 2, 512, False, "2d"),     # the longest rows whose scores stay in registers
+    (2, 2, 512, True, None),      # the same length, causal without lengths: the two-pass kernel
+    (1, 2, 513, True, None),
+    (1, 2, 600, False, "1d"),     # past 512 keys: the two-pass kernel with lengths
+    (1, 2, 530, True, "2d"),      # ... causal with lengths per query, rows not 16-byte aligned
 ])
 def test_weights_overwrite_every_entry(B, h, L, causal, kind):
-    """bf16 inputs (MFMA inspection kernel) into a weights buffer pre-filled
-    with NaN: every entry must be written, masked ones as exact zeros."""
+    """bf16 inputs (MFMA inspection kernels) into a weights buffer pre-filled
+    with NaN: every entry must be written, masked ones as exact zeros.  Rows
+    of up to 512 keys take the kernel that keeps its scores in registers,
+    longer rows and causal launches without lengths the two-pass one."""
     import torch
     import transformer_head_scaled_sdpa_amd as mha
     rng = np.random.Generator(np.random.PCG64(B * 31 + L))
