@@ -182,3 +182,27 @@ def test_weights_overwrite_every_entry(B, h, L, causal, kind):
     assert_fp32(g, rp, "weights")
     assert np.all(g[rp == 0.0] == 0.0)
     assert_fp32(to_host(o), ro, "output")
+
+
+@pytest.mark.parametrize("B,h,L", [(2, 3, 300), (1, 2, 512), (2, 2, 97)])
+def test_weights_kernels_agree_bit_for_bit(B, h, L):
+    """Causal rows with every length equal to L take the kernel that keeps its
+    scores in registers; causal rows without lengths take the two-pass
+    kernel.  Both allow the same keys and do the same arithmetic in the same
+    order (the extra steps of the first are wholly masked and leave the
+    running statistics unchanged), so weights and outputs agree bit for
+    bit; both also match the oracle."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    rng = np.random.Generator(np.random.PCG64(B * 7 + L))
+    q, k, v = (workloads._finish(rng.standard_normal((B, h, L, 64)), "bf16") for _ in range(3))
+    tq, tk, tv = (to_device(x, torch.bfloat16) for x in (q, k, v))
+    full = np.full(B, L, dtype=np.int32)
+    o1, p1 = mha.sdpa_forward(tq, tk, tv, valid_lens=full, causal=True, out_dtype=torch.float32, return_weights=True)
+    o2, p2 = mha.sdpa_forward(tq, tk, tv, causal=True, out_dtype=torch.float32, return_weights=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(p1), to_host(p2))
+    np.testing.assert_array_equal(to_host(o1), to_host(o2))
+    ro, rp = oracle.sdpa(q, k, v, causal=True, return_weights=True)
+    assert_fp32(to_host(p1), rp, "weights")
+    assert_bf16(to_host(o1), ro, "output")
