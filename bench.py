@@ -684,6 +684,17 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(w, inp)
+        if "configs" in result:
+            # The oracle once on every other configuration too (a bounded
+            # sample each), beside the GPU's step rate on the same count.
+            per = {}
+            for name, cfg in result["configs"].items():
+                cw = workloads.BY_NAME[name]
+                cb = cpu_baseline(cw, workloads.make_inputs(cw), budget_s=2.0)
+                gpu = cfg.get("attention_alg_tflops")
+                per[name] = {"value": cb["value"], "unit": cb["unit"], "sample": cb["sample"],
+                             "gpu_over_oracle": round(gpu / cb["value"], 1) if gpu and cb["value"] else None}
+            result["cpu_baseline"]["configs"] = per
 
     print(json.dumps(result), flush=True)
 
