@@ -677,8 +677,7 @@ def main():
                 continue
             cw = workloads.BY_NAME[name]
             log(f"config {name} ...")
-            result["configs"][name] = measure_workload(cw, workloads.make_inputs(cw), 100, 50, args.repeat,
-                                                       cold=False)
+            result["configs"][name] = measure_workload(cw, workloads.make_inputs(cw), 100, 50, args.repeat)
         extras(result, args, w)
 
     if not args.no_cpu_baseline:
