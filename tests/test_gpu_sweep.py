@@ -2,15 +2,16 @@
 fp64 oracle: query and key counts on either side of the kernels' tile edges
 (32, 64, 128, 256), Lq different from Lk, lengths of 0, 1, the full count
 and past it, with and without the causal rule, both output dtypes; the
-attention core's backward on both of its statistic paths, and the layer's
-training pair against its recomputing backward.  The shapes come
-from a fixed generator, so every run checks the same cases."""
+attention core's backward on both of its statistic paths, the layer's
+training pair against its recomputing backward, and the weights export.
+The shapes come from a fixed generator, so every run checks the same
+cases."""
 import numpy as np
 import pytest
 
 import oracle
 import workloads
-from parity import assert_bf16, to_device, to_host
+from parity import assert_bf16, assert_fp32, to_device, to_host
 from test_gpu_mha_backward import GRADS, check, make
 from test_gpu_mha_train import oracle_out, run_pair
 
@@ -164,3 +165,28 @@ def test_sweep_layer_backward_bf16(c, B, Lq, Lk, causal, lens):
             continue
         np.testing.assert_array_equal(kept[n], again[n], err_msg=f"{what} {n}: saved vs recomputed forward")
     check(again, inp, g, what, storage_diag=False)
+
+
+WEIGHTS_CASES = _cases(14, 8080)
+
+
+@pytest.mark.parametrize("c,B,Lq,Lk,causal,lens", WEIGHTS_CASES)
+def test_sweep_weights_bf16(c, B, Lq, Lk, causal, lens):
+    """The weights export on odd shapes; odd cases take one length per query
+    (drawn around the case's per-sequence length, 0 and past Lk included)."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    h = 1 + c % 3
+    inp = workloads.make_sdpa_inputs(B, h, Lq, Lk, 64, "bf16", seed=3100 + c)
+    q, k, v = (inp.tensors[n] for n in ("q", "k", "v"))
+    vl = None if lens is None else np.array(lens, dtype=np.int32)
+    if vl is not None and c % 2:
+        rng = np.random.Generator(np.random.PCG64(3200 + c))
+        vl = np.clip(vl[:, None] + rng.integers(-8, 9, size=(B, Lq)), 0, Lk + 20).astype(np.int32)
+    o, p = mha.sdpa_forward(to_device(q, torch.bfloat16), to_device(k, torch.bfloat16), to_device(v, torch.bfloat16),
+                            valid_lens=vl, causal=causal, out_dtype=torch.float32, return_weights=True)
+    torch.cuda.synchronize()
+    ro, rp = oracle.sdpa(q, k, v, valid_lens=vl, causal=causal, return_weights=True)
+    what = f"sweep weights case {c}: B{B} h{h} Lq{Lq} Lk{Lk} causal{int(causal)} lengths {lens}"
+    assert_fp32(to_host(p), rp, what + " weights")
+    assert_bf16(to_host(o), ro, what + " output")
