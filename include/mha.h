@@ -311,8 +311,10 @@ mha_status mha_forward(mha_dtype in_dt, mha_dtype out_dt,
  *             4-byte aligned, not overlapping any other argument.  It receives the normalised weights
  *             softmax_j(q_i . k_j / sqrt(d_k)) with masked keys exactly 0.
  * With p_attn == NULL and lengths per sequence this is sdpa_forward.  Else
- * it runs the inspection kernel, two passes over the keys (slower than
- * sdpa_forward; meant for debugging and visualisation): for MHA_BF16 inputs
+ * it runs the inspection kernel, one pass over the keys for each query's
+ * log-sum-exp and one for the weights (rows of at most 512 keys keep their
+ * scores in registers between the two; slower than sdpa_forward, meant for
+ * debugging and visualisation): for MHA_BF16 inputs
  * bf16 MFMA products with fp32 sums, the weights in fp32 and P.V with the
  * weights as two bf16 terms (about 16 significant bits); for MHA_F32 inputs
  * fp32 FMA throughout.  With MHA_BF16 inputs each (batch, head)'s rows of k
