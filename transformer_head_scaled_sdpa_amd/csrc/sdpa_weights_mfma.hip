@@ -247,11 +247,12 @@ __global__ __launch_bounds__(kThreads, 1) void weights_mfma(WeightsArgs a, float
 // Rows of at most kShortSteps steps (Lk <= 512; not the causal rule without
 // lengths, whose short rows the two-pass kernel cuts to the triangle): every
 // K and V load and the Q fragments are issued at the start, so the workgroup
-// pays one memory round trip; K is stored to LDS once, each wave keeps its scores in registers
-// from the log-sum-exp pass to the weights pass, and V is then stored once in
-// the space K used.  Three barriers in all instead of two per step and pass.
-// The products, the online (max, sum) update and its order, and the weights
-// are those of weights_mfma, so every result is bit for bit the same.
+// pays one memory round trip; K is stored to LDS once, each wave keeps its
+// scores in registers from the log-sum-exp pass to the weights pass, and V
+// is then stored once in the space K used.  Three barriers before the output
+// reduction instead of two per step and pass.  The products, the online
+// (max, sum) update and its order, and the weights are those of
+// weights_mfma, so every result is bit for bit the same.
 constexpr int kShortSteps = 4;
 constexpr int kKvB = kShortSteps * kPhases * kTileTB;   // V in 192-byte rows (96 KiB); K takes 72
 static_assert(kKvB >= kShortSteps * kPhases * kTileRB && kKvB >= kRedB, "K tiles and reduction slots fit");
