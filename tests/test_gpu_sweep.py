@@ -3,9 +3,9 @@ fp64 oracle: query and key counts on either side of the kernels' tile edges
 (32, 64, 128, 256), Lq different from Lk, lengths of 0, 1, the full count
 and past it, with and without the causal rule, both output dtypes; the
 attention core's backward on both of its statistic paths, the layer's
-training pair against its recomputing backward, and the weights export.
-The shapes come from a fixed generator, so every run checks the same
-cases."""
+training pair against its recomputing backward, and the weights export of
+the attention core and of the multi-head layer.  The shapes come from a
+fixed generator, so every run checks the same cases."""
 import numpy as np
 import pytest
 
@@ -190,3 +190,38 @@ def test_sweep_weights_bf16(c, B, Lq, Lk, causal, lens):
     what = f"sweep weights case {c}: B{B} h{h} Lq{Lq} Lk{Lk} causal{int(causal)} lengths {lens}"
     assert_fp32(to_host(p), rp, what + " weights")
     assert_bf16(to_host(o), ro, what + " output")
+
+
+MHA_WEIGHTS_CASES = _cases(8, 4321)
+
+
+@pytest.mark.parametrize("c,B,Lq,Lk,causal,lens", MHA_WEIGHTS_CASES)
+def test_sweep_mha_weights_bf16(c, B, Lq, Lk, causal, lens):
+    """The multi-head layer exporting its weights on odd shapes (projections
+    to fp32 Q, K, V, then the inspection kernel): output and per-head
+    weights against the oracle."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    from test_gpu_inspect import _oracle_mha_weights
+    h = 1 + c % 4
+    D = 64 * h
+    self_attn = causal or c % 2 == 0
+    if self_attn:
+        Lk = Lq
+        if lens is not None:
+            lens = [min(x, Lq + 3) for x in lens]
+    inp = workloads.make_mha_inputs(B, Lq, Lk, D, h, "bf16", seed=4400 + c, causal=causal, self_attn=self_attn,
+                                    bias=c % 3 == 0)
+    vl = None if lens is None else np.array(lens, dtype=np.int32)
+    t = {n: (None if a is None else to_device(a, torch.bfloat16)) for n, a in inp.tensors.items()}
+    if self_attn:
+        t["x_kv"] = t["x_q"]
+    out, p = mha.mha_forward(t["x_q"], t["x_kv"], t["w_q"], t["w_k"], t["w_v"], t["w_o"], t["b_q"], t["b_k"], t["b_v"],
+                             t["b_o"], h=h, valid_lens=vl, causal=causal, out_dtype=torch.float32, return_weights=True)
+    torch.cuda.synchronize()
+    r = inp.tensors
+    ref = oracle.mha(r["x_q"], r["x_kv"], r["w_q"], r["w_k"], r["w_v"], r["w_o"], r["b_q"], r["b_k"], r["b_v"], r["b_o"],
+                     h=h, valid_lens=vl, causal=causal)
+    what = f"sweep mha weights case {c}: B{B} Lq{Lq} Lk{Lk} D{D} causal{int(causal)} lengths {lens}"
+    assert_bf16(to_host(out), ref, what + " output")
+    assert_bf16(to_host(p), _oracle_mha_weights(inp, vl), what + " weights")
