@@ -3,9 +3,9 @@ fp64 oracle: query and key counts on either side of the kernels' tile edges
 (32, 64, 128, 256), Lq different from Lk, lengths of 0, 1, the full count
 and past it, with and without the causal rule, both output dtypes; the
 attention core's backward on both of its statistic paths, the layer's
-training pair against its recomputing backward, and the weights export of
-the attention core and of the multi-head layer.  The shapes come from a
-fixed generator, so every run checks the same cases."""
+training pair against its recomputing backward, the weights export of the
+attention core and of the multi-head layer, and the pre-norm sublayer.  The
+shapes come from a fixed generator, so every run checks the same cases."""
 import numpy as np
 import pytest
 
@@ -225,3 +225,43 @@ def test_sweep_mha_weights_bf16(c, B, Lq, Lk, causal, lens):
     what = f"sweep mha weights case {c}: B{B} Lq{Lq} Lk{Lk} D{D} causal{int(causal)} lengths {lens}"
     assert_bf16(to_host(out), ref, what + " output")
     assert_bf16(to_host(p), _oracle_mha_weights(inp, vl), what + " weights")
+
+
+SUBLAYER_CASES = _cases(8, 2718)
+
+
+@pytest.mark.parametrize("c,B,Lq,Lk,causal,lens", SUBLAYER_CASES)
+def test_sweep_sublayer_bf16(c, B, Lq, Lk, causal, lens):
+    """x + MHA(LayerNorm(x)) on odd shapes, both LayerNorm forms, with and
+    without gain and bias, self-attention or attention to a memory."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    h = 1 + c % 4
+    D = 64 * h
+    self_attn = causal or c % 2 == 0
+    if self_attn:
+        Lk = Lq
+        if lens is not None:
+            lens = [min(x, Lq + 3) for x in lens]
+    inp = workloads.make_mha_inputs(B, Lq, Lk, D, h, "bf16", seed=5500 + c, causal=causal, self_attn=self_attn,
+                                    bias=True)
+    vl = None if lens is None else np.array(lens, dtype=np.int32)
+    t = inp.tensors
+    rng = np.random.Generator(np.random.PCG64(5600 + c))
+    x = workloads._finish(np.asarray(t["x_q"], np.float64) * 1.5 - 0.25, "bf16")
+    affine = c % 3 != 0
+    g = workloads._finish(1.0 + 0.2 * rng.standard_normal(D), "bf16") if affine else None
+    bb = workloads._finish(0.1 * rng.standard_normal(D), "bf16") if affine else None
+    kind, eps = c % 2, (1e-6 if c % 2 == 0 else 1e-5)
+    mem = None if self_attn else t["x_kv"]
+    dv = lambda a: None if a is None else to_device(a, torch.bfloat16)
+    out = mha.mha_sublayer_forward(dv(x), dv(t["w_q"]), dv(t["w_k"]), dv(t["w_v"]), dv(t["w_o"]), dv(t["b_q"]),
+                                   dv(t["b_k"]), dv(t["b_v"]), dv(t["b_o"]), h=h, ln_gain=dv(g), ln_bias=dv(bb),
+                                   ln_kind=kind, ln_eps=eps, memory=dv(mem), valid_lens=vl, causal=causal,
+                                   out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.mha_sublayer(x, t["w_q"], t["w_k"], t["w_v"], t["w_o"], t["b_q"], t["b_k"], t["b_v"], t["b_o"], h=h,
+                              ln_gain=g, ln_bias=bb, ln_kind=kind, ln_eps=eps, memory=mem, valid_lens=vl,
+                              causal=causal)
+    assert_bf16(to_host(out), ref, f"sweep sublayer case {c}: B{B} Lq{Lq} Lk{Lk} D{D} causal{int(causal)} "
+                                   f"lengths {lens} kind{kind}")
