@@ -4,8 +4,9 @@ fp64 oracle: query and key counts on either side of the kernels' tile edges
 and past it, with and without the causal rule, both output dtypes; the
 attention core's backward on both of its statistic paths, the layer's
 training pair against its recomputing backward, the weights export of the
-attention core and of the multi-head layer, and the pre-norm sublayer.  The
-shapes come from a fixed generator, so every run checks the same cases."""
+attention core and of the multi-head layer, the pre-norm sublayer, and the
+fp32 entry points.  The shapes come from a fixed generator, so every run
+checks the same cases."""
 import numpy as np
 import pytest
 
@@ -265,3 +266,42 @@ def test_sweep_sublayer_bf16(c, B, Lq, Lk, causal, lens):
                               causal=causal)
     assert_bf16(to_host(out), ref, f"sweep sublayer case {c}: B{B} Lq{Lq} Lk{Lk} D{D} causal{int(causal)} "
                                    f"lengths {lens} kind{kind}")
+
+
+F32_CASES = _cases(10, 1234)
+
+
+@pytest.mark.parametrize("c,B,Lq,Lk,causal,lens", F32_CASES)
+def test_sweep_fp32(c, B, Lq, Lk, causal, lens):
+    """The fp32 entry points on odd shapes against the fp32 bar: the
+    attention core and, on even cases, the multi-head layer."""
+    import torch
+    import transformer_head_scaled_sdpa_amd as mha
+    h = 1 + c % 3
+    vl = None if lens is None else np.array(lens, dtype=np.int32)
+    inp = workloads.make_sdpa_inputs(B, h, Lq, Lk, 64, "f32", seed=6600 + c)
+    q, k, v = (inp.tensors[n] for n in ("q", "k", "v"))
+    o = mha.sdpa_forward(to_device(q, torch.float32), to_device(k, torch.float32), to_device(v, torch.float32),
+                         valid_lens=vl, causal=causal)
+    torch.cuda.synchronize()
+    what = f"sweep fp32 case {c}: B{B} h{h} Lq{Lq} Lk{Lk} causal{int(causal)} lengths {lens}"
+    assert_fp32(to_host(o), oracle.sdpa(q, k, v, valid_lens=vl, causal=causal), what + " sdpa")
+    if c % 2:
+        return
+    D = 64 * h
+    self_attn = causal
+    Lk2 = Lq if self_attn else Lk
+    lens2 = None if lens is None else [min(x, Lk2 + 3) for x in lens]
+    vl2 = None if lens2 is None else np.array(lens2, dtype=np.int32)
+    mi = workloads.make_mha_inputs(B, Lq, Lk2, D, h, "f32", seed=6700 + c, causal=causal, self_attn=self_attn,
+                                   bias=True)
+    t = {n: (None if a is None else to_device(a, torch.float32)) for n, a in mi.tensors.items()}
+    if self_attn:
+        t["x_kv"] = t["x_q"]
+    out = mha.mha_forward(t["x_q"], t["x_kv"], t["w_q"], t["w_k"], t["w_v"], t["w_o"], t["b_q"], t["b_k"], t["b_v"],
+                          t["b_o"], h=h, valid_lens=vl2, causal=causal)
+    torch.cuda.synchronize()
+    r = mi.tensors
+    ref = oracle.mha(r["x_q"], r["x_kv"], r["w_q"], r["w_k"], r["w_v"], r["w_o"], r["b_q"], r["b_k"], r["b_v"], r["b_o"],
+                     h=h, valid_lens=vl2, causal=causal)
+    assert_fp32(to_host(out), ref, what + f" mha D{D}")
